@@ -1,0 +1,141 @@
+"""Python access to the CPU oracle (msa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg. The product path never imports this package.
+The oracle is plain double-precision C; see msa_oracle.h for the definitions
+it writes out and the passages of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msa_oracle.c")
+_HDR = os.path.join(_HERE, "msa_oracle.h")
+_LIB = os.path.join(_HERE, "libmsa_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, D, P,
+                                                I64, P, P, I]
+        lib.oracle_sparse_attention.restype = I
+        lib.oracle_paged_sparse_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                                      I, I, D, P, I64, P, P, I]
+        lib.oracle_paged_sparse_attention.restype = I
+        lib.oracle_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P]
+        lib.oracle_k2q_csr.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _shape_out(o, lse, rows, B, Sq, Hq, D):
+    if rows is None:
+        return o.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
+    return o, lse
+
+
+def sparse_attention(q, k, v, q2k, *, causal: bool, blk: int = 128,
+                     softmax_scale: Optional[float] = None, seqused_k=None, rows=None,
+                     nthreads: int = 0):
+    """Oracle forward, contiguous K/V.
+
+    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] as uint16 bf16 bits; q2k [B,Hkv,Sq,topk].
+    rows=None: returns O [B,Sq,Hq,D] and LSE [B,Hq,Sq] (float64).
+    rows = array of b*Sq+q ids: returns O [n,Hq,D] and LSE [n,Hq].
+    """
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    q2k = _c(q2k, np.int32)
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    topk = q2k.shape[-1]
+    assert q2k.shape == (B, Hkv, Sq, topk) and v.shape == k.shape
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    seq = _c(seqused_k, np.int32)
+    rws = _c(rows, np.int64)
+    n = B * Sq if rws is None else rws.size
+    o = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    rc = _load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(seq), B, Sq,
+                                         Skv, Hq, Hkv, D, topk, blk, int(causal), scale,
+                                         _ptr(rws), n, _ptr(o), _ptr(lse), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_sparse_attention: invalid arguments")
+    return _shape_out(o, lse, rws, B, Sq, Hq, D)
+
+
+def paged_sparse_attention(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,
+                           softmax_scale: Optional[float] = None, rows=None, nthreads: int = 0):
+    """Oracle forward, paged K/V pool [num_pages,Hkv,page_size,D], page_table [B,max_pages]."""
+    q, k_pool, v_pool = _c(q, np.uint16), _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    page_table, seqused_k, q2k = (_c(page_table, np.int32), _c(seqused_k, np.int32),
+                                  _c(q2k, np.int32))
+    B, Sq, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    topk = q2k.shape[-1]
+    assert q2k.shape == (B, Hkv, Sq, topk) and page_table.shape[0] == B
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    rws = _c(rows, np.int64)
+    n = B * Sq if rws is None else rws.size
+    o = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    rc = _load().oracle_paged_sparse_attention(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seqused_k), _ptr(q2k), B, Sq,
+        Hq, Hkv, D, topk, page_size, num_pages, max_pages, int(causal), scale, _ptr(rws), n,
+        _ptr(o), _ptr(lse), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_paged_sparse_attention: invalid arguments")
+    return _shape_out(o, lse, rws, B, Sq, Hq, D)
+
+
+def k2q_csr(q2k, nblk: int, with_slot: bool = True):
+    """Oracle kv-block -> query CSR of q2k [B,Hkv,Sq,topk].
+
+    Returns (row_ptr [Hkv, B*nblk+1], q_idx [Hkv, B*Sq*topk], slot or None); entries
+    past row_ptr[h, -1] are -1.
+    """
+    q2k = _c(q2k, np.int32)
+    B, Hkv, Sq, topk = q2k.shape
+    row_ptr = np.empty((Hkv, B * nblk + 1), dtype=np.int32)
+    q_idx = np.full((Hkv, B * Sq * topk), -1, dtype=np.int32)
+    slot = np.full((Hkv, B * Sq * topk), -1, dtype=np.int32) if with_slot else None
+    rc = _load().oracle_k2q_csr(_ptr(q2k), B, Hkv, Sq, topk, nblk, _ptr(row_ptr), _ptr(q_idx),
+                                _ptr(slot))
+    if rc != 0:
+        raise ValueError("oracle_k2q_csr: invalid arguments")
+    return row_ptr, q_idx, slot
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,74 @@
+/*
+ * CPU oracle for top-k block-sparse GQA attention (forward) and its k2q CSR.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it. It shares no code with the HIP
+ * library. All pointers are host memory. bf16 tensors are passed as their
+ * 16-bit patterns and widened exactly; all arithmetic is in double.
+ *
+ * Definitions follow the page "MiniMax-AI/MSA python/fmha_sm100/cute/
+ * test_sparse_atten.py": the golden reference `sparse_attention_ref`
+ * (block mask from the index table with set semantics, -1 ignored, GQA head
+ * map by repeat-interleave, seqused_k mask, bottom-right causal limit
+ * q + seqused_k - Sq, masked logsumexp in natural log, empty rows give
+ * O = 0 and LSE = -inf), the paged packer `pack_paged_kv` (pool
+ * [num_pages, Hkv, page_size, D] addressed through page_table[b][j / page])
+ * and the page "MSA interface.py" (`sparse_atten_func`: default scale
+ * D^-0.5; `build_k2q_csr`: kv-block -> query CSR, done once per call site).
+ */
+#ifndef MSA_ORACLE_H
+#define MSA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Sparse attention, contiguous K/V.
+ *   q        [B, Sq, Hq, D]   bf16 bits
+ *   k, v     [B, Skv, Hkv, D] bf16 bits
+ *   q2k      [B, Hkv, Sq, topk] int32 block ids, -1 (or any id outside
+ *            [0, Skv/blk)) = unused slot; duplicates count once
+ *   seqused_k NULL or [B]: keys j >= seqused_k[b] are masked and the causal
+ *            limit uses seqused_k[b] in place of Skv
+ *   rows     NULL (all B*Sq rows, in order) or nrows global row ids b*Sq+q
+ *   o        [nrows, Hq, D] double;  lse [nrows, Hq] double (natural log)
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* q2k, const int32_t* seqused_k, int B, int Sq, int Skv,
+                            int Hq, int Hkv, int D, int topk, int blk, int causal, double scale,
+                            const int64_t* rows, int64_t nrows, double* o, double* lse,
+                            int nthreads);
+
+/*
+ * Sparse attention, paged K/V. Logical block s of sequence b is physical page
+ * page_table[b * max_pages + s] (page_size == block size); a page id outside
+ * [0, num_pages) makes that block contribute nothing. Keys j >= seqused_k[b]
+ * are masked and the causal limit is q + seqused_k[b] - Sq. Valid block ids
+ * are [0, max_pages). Other arguments as above.
+ */
+int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
+                                  const uint16_t* v_pool, const int32_t* page_table,
+                                  const int32_t* seqused_k, const int32_t* q2k, int B, int Sq,
+                                  int Hq, int Hkv, int D, int topk, int page_size, int num_pages,
+                                  int max_pages, int causal, double scale, const int64_t* rows,
+                                  int64_t nrows, double* o, double* lse, int nthreads);
+
+/*
+ * kv-block -> query CSR of a [B, Hkv, Sq, topk] index table.
+ * Rows r = b * nblk + s per KV head. row_ptr [Hkv, B*nblk + 1];
+ * q_idx and slot [Hkv, B*Sq*topk]: row r lists the global query ids b*Sq+q
+ * whose row holds s, ascending in q then slot t, and slot[] holds that t.
+ * Entries beyond row_ptr[h][B*nblk] are left untouched. slot may be NULL.
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
+                   int32_t* row_ptr, int32_t* q_idx, int32_t* slot);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,180 @@
+"""Seeded synthetic workloads for top-k block-sparse GQA attention.
+
+The shapes follow the workloads of the MSA sparse-attention test and benchmark
+harness (page "MiniMax-AI/MSA python/fmha_sm100/cute/test_sparse_atten.py":
+the generator ``generate_test_data``, the paged packer ``pack_paged_kv`` and
+the benchmark cases ``ring48k`` / ``ulysses384k``). Random numbers come from
+the counter-based C generator in ``gen.c``; nothing here computes attention.
+
+Everything returns host numpy arrays: bf16 tensors as ``uint16`` bit
+patterns, index tables as ``int32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gen.c")
+_LIB = os.path.join(_HERE, "libmsa_workloads.so")
+
+# sub-stream ids of one seed
+STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX, STREAM_PAGES = 1, 2, 3, 4, 5
+MODE_PERM, MODE_SINK, MODE_CAUSAL = 0, 1, 2
+DEFAULT_SEED = 42
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gen.c into libmsa_workloads.so (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.wl_normal_bf16.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p]
+        lib.wl_normal_bf16.restype = None
+        lib.wl_q2k.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
+        lib.wl_q2k.restype = ctypes.c_int
+        lib.wl_permutation.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                       ctypes.c_void_p]
+        lib.wl_permutation.restype = None
+        lib.wl_draw64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        lib.wl_draw64.restype = ctypes.c_uint64
+        lib.wl_stream_key.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        lib.wl_stream_key.restype = ctypes.c_uint64
+        _lib = lib
+    return _lib
+
+
+def normal_bf16(seed: int, stream: int, shape, first: int = 0) -> np.ndarray:
+    """N(0,1) values rounded to bf16 (uint16 bit patterns), elements first.. of a stream."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    _load().wl_normal_bf16(seed, stream, first, n, out.ctypes.data)
+    return out.reshape(shape)
+
+
+def q2k_table(seed: int, mode: int, B: int, Hkv: int, Sq: int, kvlen, blk: int, topk: int,
+              stream: int = STREAM_IDX) -> np.ndarray:
+    """Index table [B, Hkv, Sq, topk] int32 under one of the recipes of gen.c."""
+    kv = np.ascontiguousarray(np.broadcast_to(np.asarray(kvlen, dtype=np.int32), (B,)))
+    out = np.empty((B, Hkv, Sq, topk), dtype=np.int32)
+    rc = _load().wl_q2k(seed, stream, mode, B, Hkv, Sq, kv.ctypes.data, blk, topk, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("bad q2k generator arguments")
+    return out
+
+
+def permutation(seed: int, stream: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.int32)
+    _load().wl_permutation(seed, stream, n, out.ctypes.data)
+    return out
+
+
+def bf16_to_f32(x: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Workload:
+    """One synthetic workload (shapes, masking, index recipe)."""
+    name: str
+    B: int
+    Sq: int
+    Skv: int
+    Hkv: int
+    qpk: int
+    topk: int
+    causal: bool
+    mode: int
+    D: int = 128
+    blk: int = 128
+    paged: bool = False
+    seqused_trim: int = 0          # paged: seqused_k = Skv - trim
+    shuffle_pages: bool = True
+    seed: int = DEFAULT_SEED
+    note: str = ""
+
+    @property
+    def Hq(self) -> int:
+        return self.Hkv * self.qpk
+
+    @property
+    def max_pages(self) -> int:
+        return (self.Skv + self.blk - 1) // self.blk
+
+    @property
+    def kvlen(self) -> int:
+        return self.Skv - self.seqused_trim if self.paged else self.Skv
+
+    def effective_flops(self) -> int:
+        """4 * B * Sq * Hq * (topk * blk) * D: every slot counted as a full block."""
+        return 4 * self.B * self.Sq * self.Hq * self.topk * self.blk * self.D
+
+    def scaled(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    "c1": Workload("c1_b1_s1k_hq2_hkv1_top4_noncausal", B=1, Sq=1024, Skv=1024, Hkv=1, qpk=2,
+                   topk=4, causal=False, mode=MODE_PERM),
+    "c2": Workload("c2_b1_s8k_hq64_hkv4_top16_causal", B=1, Sq=8192, Skv=8192, Hkv=4, qpk=16,
+                   topk=16, causal=True, mode=MODE_CAUSAL),
+    "c3u": Workload("c3_b1_s32k_hq64_hkv4_top16_uniform", B=1, Sq=32768, Skv=32768, Hkv=4,
+                    qpk=16, topk=16, causal=False, mode=MODE_PERM),
+    "c3s": Workload("c3_b1_s32k_hq64_hkv4_top16_sink", B=1, Sq=32768, Skv=32768, Hkv=4, qpk=16,
+                    topk=16, causal=False, mode=MODE_SINK),
+    "c4a": Workload("c4a_b1_s48k_hq16_hkv1_top16_causal", B=1, Sq=49152, Skv=49152, Hkv=1,
+                    qpk=16, topk=16, causal=True, mode=MODE_CAUSAL),
+    "c4b": Workload("c4b_b1_s384k_hq2_hkv1_top16_causal", B=1, Sq=393216, Skv=393216, Hkv=1,
+                    qpk=2, topk=16, causal=True, mode=MODE_CAUSAL),
+    "c5": Workload("c5_paged_decode_b32_sq8_hq64_hkv4_kv64k_top16", B=32, Sq=8, Skv=65536,
+                   Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL, paged=True,
+                   seqused_trim=17),
+}
+
+
+def make_inputs(w: Workload, q2k: Optional[np.ndarray] = None) -> dict:
+    """Host inputs for a workload: q, k, v (or k_pool, v_pool, page_table, seqused_k), q2k."""
+    out = {}
+    out["q"] = normal_bf16(w.seed, STREAM_Q, (w.B, w.Sq, w.Hq, w.D))
+    if w.paged:
+        num_pages = w.B * w.max_pages
+        shape = (num_pages, w.Hkv, w.blk, w.D)
+        out["k_pool"] = normal_bf16(w.seed, STREAM_K, shape)
+        out["v_pool"] = normal_bf16(w.seed, STREAM_V, shape)
+        if w.shuffle_pages:
+            pt = permutation(w.seed, STREAM_PAGES, num_pages)
+        else:
+            pt = np.arange(num_pages, dtype=np.int32)
+        out["page_table"] = pt.reshape(w.B, w.max_pages).copy()
+        out["seqused_k"] = np.full((w.B,), w.kvlen, dtype=np.int32)
+    else:
+        out["k"] = normal_bf16(w.seed, STREAM_K, (w.B, w.Skv, w.Hkv, w.D))
+        out["v"] = normal_bf16(w.seed, STREAM_V, (w.B, w.Skv, w.Hkv, w.D))
+    if q2k is None:
+        q2k = q2k_table(w.seed, w.mode, w.B, w.Hkv, w.Sq, w.kvlen, w.blk, w.topk)
+    out["q2k"] = q2k
+    return out
