@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the top-k block-sparse GQA attention forward on one MI355X.
+
+A step is one full forward call (msa_sparse_fwd, or msa_paged_sparse_fwd for the
+paged decode workload) over one batch of seeded synthetic inputs already
+resident in HBM: for the kv-centric path that includes the k2q CSR build, the
+schedule, the per-block kernel and the combine. Prints one JSON line.
+
+Metrics (the pages' benchmark harness, "test_sparse_atten.py"):
+  prefill: effective TFLOP/s = 4 * B * Sq * Hq * (topk * 128) * D / time
+           (every slot counted as a full 128-token block, -1 and masked included)
+  decode:  GB/s of algorithmic bytes = distinct selected K/V blocks of each
+           (sequence, KV head) * 64 KiB + Q + O + LSE + q2k + page table
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
+                       [--path auto|q|kv] [--extra c5,c3u] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense
+HBM_PEAK_GBS = 8000.0
+PATHS = {"auto": 0, "q": 1, "kv": 2}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_algorithmic_bytes(w, inp) -> int:
+    """Distinct valid selected blocks per (b, hkv) x 128 tokens x D x 2 B x 2 (K and V),
+    plus Q, O, LSE, q2k, page table and seqused."""
+    q2k = inp["q2k"]
+    blocks = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ids = q2k[b, h].reshape(-1)
+            ids = ids[(ids >= 0) & (ids < w.max_pages)]
+            blocks += np.unique(ids).size
+    kv = blocks * 128 * w.D * 2 * 2
+    q = w.B * w.Sq * w.Hq * w.D * 2
+    return int(kv + 2 * q + w.B * w.Sq * w.Hq * 4 + q2k.nbytes + inp["page_table"].nbytes +
+               inp["seqused_k"].nbytes)
+
+
+class Case:
+    """One workload uploaded to the GPU with a callable that runs one step."""
+
+    def __init__(self, key: str, path: str):
+        import torch
+        import block_sparse_attention_top_amd as msa
+        import workloads as wl
+        self.key, self.w = key, wl.WORKLOADS[key]
+        w = self.w
+        t0 = time.time()
+        self.inp = wl.make_inputs(w)
+        log(f"[bench] {key}: inputs generated in {time.time() - t0:.1f}s")
+        dev = lambda x: (torch.from_numpy(x).view(torch.bfloat16) if x.dtype == np.uint16
+                         else torch.from_numpy(x)).to("cuda")
+        self.t = {k: dev(v) for k, v in self.inp.items()}
+        self.o = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+        t = self.t
+        if w.paged:
+            nb = msa.msa_paged_sparse_fwd_workspace_size(w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk,
+                                                        w.blk, w.max_pages, 0)
+            ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+            self.path_name = "paged-split"
+            self.step = lambda: msa.msa_paged_sparse_fwd(
+                t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"],
+                causal=w.causal, o=self.o, lse=self.lse, workspace=ws)
+            self.bytes = decode_algorithmic_bytes(w, self.inp)
+        else:
+            p = PATHS[path]
+            if p == 0:
+                p = 1 if w.qpk >= 8 else 2
+            self.path_name = {1: "q-centric", 2: "kv-centric"}[p]
+            nb = msa.msa_sparse_fwd_workspace_size(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, w.topk,
+                                                   w.blk, p)
+            ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+            self.step = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"],
+                                                   causal=w.causal, path=p, o=self.o,
+                                                   lse=self.lse, workspace=ws)
+            self.bytes = None
+        self.flops = w.effective_flops()
+
+    def time_steps(self, steps: int, warmup: int) -> float:
+        """Mean ms per step over `steps` back-to-back calls (events on the launch stream)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            self.step()
+        end.record()
+        end.synchronize()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def metric(self, ms: float) -> dict:
+        if self.w.paged:
+            gbs = self.bytes / (ms * 1e-3) / 1e9
+            return {"ms": ms, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": self.bytes, "path": self.path_name}
+        tf = self.flops / (ms * 1e-3) / 1e12
+        return {"ms": ms, "TFLOP_per_s": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                "effective_flop": self.flops, "path": self.path_name}
+
+
+def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
+    """The oracle (unchanged) on a bounded sample of the same workload's rows."""
+    import oracle
+    w, inp = case.w, case.inp
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    rng = np.random.default_rng(0)
+    total_rows = w.B * w.Sq
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, size=min(n, total_rows), replace=False))
+        t0 = time.perf_counter()
+        if w.paged:
+            oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                          inp["page_table"], inp["seqused_k"], inp["q2k"],
+                                          causal=w.causal, rows=rows, nthreads=threads)
+        else:
+            oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"], causal=w.causal,
+                                    rows=rows, nthreads=threads)
+        return rows.size, time.perf_counter() - t0
+
+    n, dt = run(max(threads, 16))
+    per_row = dt / n
+    n_target = int(min(total_rows, max(n, budget_s / max(per_row, 1e-9))))
+    n, dt = run(n_target)
+    frac = n / total_rows
+    if w.paged:
+        value = case.bytes * frac / dt / 1e9
+        unit = "GB/s"
+    else:
+        value = w.effective_flops() * frac / dt / 1e12
+        unit = "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows (all heads) of {w.name}, "
+                      f"{dt:.1f} s, fp64 C oracle with OpenMP"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--path", default="auto", choices=sorted(PATHS))
+    ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sparse forward has no multi-GPU path in this build)", file=sys.stderr)
+        return 2
+
+    import torch
+    case = Case(args.workload, args.path)
+    log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
+        f"({case.path_name})")
+    ms = case.time_steps(args.steps, args.warmup)
+    m = case.metric(ms)
+    log(f"[bench] {args.workload}: {m}")
+    w = case.w
+    if w.paged:
+        value, unit, metric = m["GB_per_s"], "GB/s", "paged sparse decode GB/s"
+        roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": m["hbm_frac"], "traffic": None}
+    else:
+        value, unit = m["TFLOP_per_s"], "TFLOP/s"
+        metric = "sparse-attn fwd effective TFLOP/s"
+        roof = {"bound": "mfma", "achieved": m["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": m["mfma_frac"], "traffic": None}
+    extra = {}
+    for key in [k for k in args.extra.split(",") if k]:
+        c = Case(key, args.path)
+        extra[key] = c.metric(c.time_steps(args.steps, args.warmup))
+        log(f"[bench] {key}: {extra[key]}")
+        del c
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a row sample)")
+        cpu = cpu_baseline(case)
+        log(f"[bench] cpu baseline: {cpu}")
+    line = {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
+                   "causal": w.causal, "path": case.path_name, "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

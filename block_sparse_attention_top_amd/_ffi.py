@@ -1,0 +1,213 @@
+"""ctypes marshalling for libmsa.so (see include/msa.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_VALUE, MSA_ERR_NOT_SUPPORTED, MSA_ERR_HIP = 0, 1, 2, 3
+MSA_PATH_AUTO, MSA_PATH_QCENTRIC, MSA_PATH_KVCENTRIC = 0, 1, 2
+
+_lib = None
+
+
+class MsaError(RuntimeError):
+    """A failed libmsa call (status MSA_ERR_HIP or unknown)."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[msa status {code}] {msg}")
+        self.code = code
+
+
+class MsaValueError(MsaError, ValueError):
+    """MSA_ERR_INVALID_VALUE: bad pointer, size or workspace."""
+
+
+class MsaNotSupportedError(MsaError, NotImplementedError):
+    """MSA_ERR_NOT_SUPPORTED: a shape or option outside the supported set."""
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmsa.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m block_sparse_attention_top_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.msa_sparse_fwd_workspace_size.argtypes = [I] * 9
+    lib.msa_sparse_fwd_workspace_size.restype = S
+    lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, P, P,
+                                   S, P]
+    lib.msa_sparse_fwd.restype = I
+    lib.msa_build_k2q_csr_workspace_size.argtypes = [I] * 5
+    lib.msa_build_k2q_csr_workspace_size.restype = S
+    lib.msa_build_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P, P, S, P]
+    lib.msa_build_k2q_csr.restype = I
+    lib.msa_paged_sparse_fwd_workspace_size.argtypes = [I] * 9
+    lib.msa_paged_sparse_fwd_workspace_size.restype = S
+    lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P,
+                                         P, P, S, P]
+    lib.msa_paged_sparse_fwd.restype = I
+    lib.msa_last_error.argtypes = []
+    lib.msa_last_error.restype = ctypes.c_char_p
+    lib.msa_version.argtypes = []
+    lib.msa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def msa_last_error() -> str:
+    return load_library().msa_last_error().decode()
+
+
+def msa_version() -> str:
+    return load_library().msa_version().decode()
+
+
+def _check(rc: int) -> None:
+    if rc == MSA_OK:
+        return
+    msg = msa_last_error()
+    if rc == MSA_ERR_INVALID_VALUE:
+        raise MsaValueError(rc, msg)
+    if rc == MSA_ERR_NOT_SUPPORTED:
+        raise MsaNotSupportedError(rc, msg)
+    raise MsaError(rc, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", torch.uint8)
+    return workspace, workspace.numel()
+
+
+def msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv=128,
+                                  path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv,
+                                                            path))
+
+
+def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None, *,
+                   causal: bool, softmax_scale: float = 0.0, path: int = MSA_PATH_AUTO,
+                   blk_kv: int = 128, o=None, lse=None, workspace=None, stream=None):
+    """Sparse forward with contiguous K/V. Returns (O bf16 [B,Sq,Hq,D], LSE fp32 [B,Hq,Sq])."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
+    _dev(q2k, "q2k", torch.int32)
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    topk = q2k.shape[-1]
+    for t, nm in ((csr_row_ptr, "csr_row_ptr"), (csr_q_idx, "csr_q_idx"), (csr_slot, "csr_slot")):
+        if t is not None:
+            _dev(t, nm, torch.int32)
+    if o is None:
+        o = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    nbytes = int(lib.msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv, path))
+    ws, wsn = _workspace(nbytes, q.device, workspace)
+    rc = lib.msa_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(csr_row_ptr),
+                            _ptr(csr_q_idx), _ptr(csr_slot), B, Sq, Skv, Hq, Hkv, D, topk, blk_kv,
+                            int(bool(causal)), float(softmax_scale), int(path), _ptr(o), _ptr(lse),
+                            _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    return o, lse
+
+
+def msa_build_k2q_csr_workspace_size(B, Hkv, Sq, topk, num_kv_blocks) -> int:
+    return int(load_library().msa_build_k2q_csr_workspace_size(B, Hkv, Sq, topk, num_kv_blocks))
+
+
+def msa_build_k2q_csr(q2k, num_kv_blocks: int, *, row_ptr=None, q_idx=None, slot=None,
+                      with_slot: bool = True, workspace=None, stream=None):
+    """kv-block -> query CSR of q2k [B,Hkv,Sq,topk]. Returns (row_ptr, q_idx, slot or None)."""
+    lib = load_library()
+    _dev(q2k, "q2k", torch.int32)
+    B, Hkv, Sq, topk = q2k.shape
+    dev = q2k.device
+    if row_ptr is None:
+        row_ptr = torch.empty((Hkv, B * num_kv_blocks + 1), dtype=torch.int32, device=dev)
+    if q_idx is None:
+        q_idx = torch.empty((Hkv, B * Sq * topk), dtype=torch.int32, device=dev)
+    if slot is None and with_slot:
+        slot = torch.empty((Hkv, B * Sq * topk), dtype=torch.int32, device=dev)
+    nbytes = int(lib.msa_build_k2q_csr_workspace_size(B, Hkv, Sq, topk, num_kv_blocks))
+    ws, wsn = _workspace(nbytes, dev, workspace)
+    rc = lib.msa_build_k2q_csr(_ptr(q2k), B, Hkv, Sq, topk, num_kv_blocks, _ptr(row_ptr),
+                               _ptr(q_idx), _ptr(slot), _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    return row_ptr, q_idx, slot
+
+
+def msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size, max_pages,
+                                        num_splits=0) -> int:
+    return int(load_library().msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk,
+                                                                  page_size, max_pages,
+                                                                  num_splits))
+
+
+def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,
+                         softmax_scale: float = 0.0, num_splits: int = 0, o=None, lse=None,
+                         workspace=None, stream=None):
+    """Sparse forward through a page table. Returns (O, LSE) as msa_sparse_fwd."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16), _dev(page_table, "page_table", torch.int32)
+    _dev(seqused_k, "seqused_k", torch.int32), _dev(q2k, "q2k", torch.int32)
+    B, Sq, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    topk = q2k.shape[-1]
+    if o is None:
+        o = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    nbytes = int(lib.msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size,
+                                                         max_pages, num_splits))
+    ws, wsn = _workspace(nbytes, q.device, workspace)
+    rc = lib.msa_paged_sparse_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                  _ptr(seqused_k), _ptr(q2k), B, Sq, Hq, Hkv, D, topk, page_size,
+                                  num_pages, max_pages, int(bool(causal)), float(softmax_scale),
+                                  int(num_splits), _ptr(o), _ptr(lse), _ptr(ws), wsn,
+                                  _stream(stream))
+    _check(rc)
+    return o, lse

@@ -1,0 +1,296 @@
+// C ABI of libmsa: host-side validation, workspace layout and dispatch.
+// Declarations and the contract of every entry point are in include/msa.h.
+#include "../../include/msa.h"
+#include "msa_internal.hpp"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+using namespace msa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool qpk_supported(int qpk) { return qpk == 1 || qpk == 2 || qpk == 4 || qpk == 8 || qpk == 16; }
+
+// Checks shared by the forward entry points; returns MSA_OK or an error code.
+int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
+  if (B <= 0 || Sq <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0)
+    return fail(MSA_ERR_INVALID_VALUE, "B, Sq, Hq, Hkv and topk must be positive");
+  if (D != kD) return fail(MSA_ERR_NOT_SUPPORTED, "head dim %d not supported (only 128)", D);
+  if (blk != kBlk) return fail(MSA_ERR_NOT_SUPPORTED, "block/page size %d not supported (only 128)", blk);
+  if (Hq % Hkv != 0) return fail(MSA_ERR_INVALID_VALUE, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!qpk_supported(Hq / Hkv))
+    return fail(MSA_ERR_NOT_SUPPORTED, "qhead_per_kv %d not supported (1, 2, 4, 8 or 16)", Hq / Hkv);
+  if (topk > kMaxTopk) return fail(MSA_ERR_NOT_SUPPORTED, "topk %d not supported (1..32)", topk);
+  if (static_cast<long long>(B) * Sq * topk > 0x7FFFFFFFLL)
+    return fail(MSA_ERR_INVALID_VALUE, "B*Sq*topk exceeds the int32 index range");
+  return MSA_OK;
+}
+
+int resolve_path(int path, int qpk) {
+  if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC) return path;
+  return qpk >= 8 ? MSA_PATH_QCENTRIC : MSA_PATH_KVCENTRIC;
+}
+
+// Entries per kv-centric work item: about 2048 (query, head) rows.
+int chunk_entries_for(int qpk) { return std::max(32, 2048 / qpk); }
+
+struct KvLayout {
+  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, o_part, lse_part, total;
+};
+
+KvLayout kv_layout(int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
+  const int nblk = Skv / kBlk;
+  const long long nrows = static_cast<long long>(B) * nblk;
+  const long long cap = static_cast<long long>(B) * Sq * topk;
+  const long long nchunk = static_cast<long long>(Hkv) * nrows;
+  KvLayout L;
+  size_t off = 0;
+  L.row_ptr = off; off += align256(Hkv * (nrows + 1) * 4);
+  L.q_idx = off; off += align256(Hkv * cap * 4);
+  L.slot = off; off += align256(Hkv * cap * 4);
+  L.csr_ws = off; off += align256(csr_workspace_bytes(B, Hkv, Sq, topk, static_cast<int>(nrows)));
+  L.chunk_counts = off; off += align256(nchunk * 4);
+  L.chunk_ptr = off; off += align256((nchunk + 1) * 4);
+  L.scan_tmp = off; off += align256(scan_tmp_ints(nchunk) * 4);
+  L.o_part = off; off += align256(static_cast<size_t>(cap) * Hq * kD * 2);
+  L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 4);
+  L.total = off;
+  return L;
+}
+
+int auto_splits(int B, int Sq, int Hkv, int topk) {
+  const long long rows = static_cast<long long>(B) * Hkv * Sq;
+  long long s = (4096 + rows - 1) / rows;
+  s = std::max<long long>(1, std::min<long long>(s, std::min(topk, 8)));
+  return static_cast<int>(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+const char* msa_version(void) { return "msa-gfx950 0.1.0"; }
+
+size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
+                                     int blk_kv, int path) {
+  if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
+      blk_kv != kBlk || Skv % kBlk || Hq % Hkv)
+    return 0;
+  if (resolve_path(path, Hq / Hkv) == MSA_PATH_QCENTRIC) return 0;
+  return kv_layout(B, Sq, Skv, Hq, Hkv, topk).total;
+}
+
+int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
+                   const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
+                   int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
+                   float softmax_scale, int path, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_common(B, Sq, Hq, Hkv, D, topk, blk_kv);
+  if (rc) return rc;
+  if (Skv <= 0 || Skv % kBlk)
+    return fail(MSA_ERR_INVALID_VALUE, "Skv (%d) must be a positive multiple of 128", Skv);
+  if (!q || !k || !v || !q2k || !o || !lse)
+    return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(q2k, 4) || !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
+  if (path < MSA_PATH_AUTO || path > MSA_PATH_KVCENTRIC)
+    return fail(MSA_ERR_INVALID_VALUE, "unknown path %d", path);
+  const bool have_csr = csr_row_ptr || csr_q_idx || csr_slot;
+  if (have_csr && !(csr_row_ptr && csr_q_idx && csr_slot))
+    return fail(MSA_ERR_INVALID_VALUE, "csr_row_ptr, csr_q_idx and csr_slot go together");
+  const int qpk = Hq / Hkv;
+  const int nblk = Skv / kBlk;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int which = resolve_path(path, qpk);
+
+  if (which == MSA_PATH_QCENTRIC) {
+    QcParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.q2k = q2k;
+    p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+    p.nblk = nblk; p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.splits = 1;
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    hipError_t e = launch_qcentric(p, false, st);
+    return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric forward");
+  }
+
+  // kv-centric
+  const long long nrows = static_cast<long long>(B) * nblk;
+  if (nrows > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: B*Skv/128 = %lld exceeds %d", nrows,
+                kMaxCsrRows);
+  const KvLayout L = kv_layout(B, Sq, Skv, Hq, Hkv, topk);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu", L.total,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const int32_t* row_ptr = csr_row_ptr;
+  const int32_t* q_idx = csr_q_idx;
+  const int32_t* slot = csr_slot;
+  hipError_t e;
+  if (!have_csr) {
+    int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
+    int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
+    int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
+    e = launch_build_csr(q2k, B, Hkv, Sq, topk, nblk, rp, qi, sl, ws + L.csr_ws, st);
+    if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
+    row_ptr = rp; q_idx = qi; slot = sl;
+  }
+  const int chunk = chunk_entries_for(qpk);
+  int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
+  e = launch_chunk_schedule(row_ptr, Hkv, static_cast<int>(nrows), chunk,
+                            reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
+                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
+  KvParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot; p.chunk_ptr = chunk_ptr;
+  p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+  p.nblk = nblk; p.nrows = static_cast<int>(nrows);
+  p.cap = static_cast<long long>(B) * Sq * topk;
+  p.chunk_entries = chunk;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
+  p.lse_part = reinterpret_cast<float*>(ws + L.lse_part);
+  // upper bound on the work items: sum over rows of ceil(len / chunk) <= nnz / chunk + rows
+  const long long grid = static_cast<long long>(Hkv) * (p.cap / chunk + nrows + 1);
+  if (grid > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
+  e = launch_kvcentric(p, static_cast<int>(grid), st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
+  e = launch_combine_slots(p.o_part, p.lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
+                           static_cast<uint16_t*>(o), lse, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "combine");
+}
+
+size_t msa_build_k2q_csr_workspace_size(int B, int Hkv, int Sq, int topk, int num_kv_blocks) {
+  if (B <= 0 || Hkv <= 0 || Sq <= 0 || topk <= 0 || num_kv_blocks <= 0) return 0;
+  return csr_workspace_bytes(B, Hkv, Sq, topk, B * num_kv_blocks);
+}
+
+int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int num_kv_blocks,
+                      int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || Hkv <= 0 || Sq <= 0 || topk <= 0 || num_kv_blocks <= 0)
+    return fail(MSA_ERR_INVALID_VALUE, "B, Hkv, Sq, topk and num_kv_blocks must be positive");
+  if (topk > kMaxTopk) return fail(MSA_ERR_NOT_SUPPORTED, "topk %d not supported (1..32)", topk);
+  if (static_cast<long long>(B) * Sq * topk > 0x7FFFFFFFLL)
+    return fail(MSA_ERR_INVALID_VALUE, "B*Sq*topk exceeds the int32 index range");
+  const long long nrows = static_cast<long long>(B) * num_kv_blocks;
+  if (nrows > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED, "B*num_kv_blocks = %lld exceeds %d", nrows, kMaxCsrRows);
+  if (!q2k || !row_ptr || !q_idx) return fail(MSA_ERR_INVALID_VALUE, "null pointer");
+  if (!aligned(q2k, 4) || !aligned(row_ptr, 4) || !aligned(q_idx, 4) || (slot && !aligned(slot, 4)))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned int32 pointer");
+  const size_t need = csr_workspace_bytes(B, Hkv, Sq, topk, static_cast<int>(nrows));
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  hipError_t e = launch_build_csr(q2k, B, Hkv, Sq, topk, num_kv_blocks, row_ptr, q_idx, slot,
+                                  workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "k2q CSR build");
+}
+
+size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
+                                           int page_size, int max_pages, int num_splits) {
+  if (B <= 0 || Sq <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD || page_size != kBlk ||
+      max_pages <= 0 || Hq % Hkv)
+    return 0;
+  const int splits = num_splits > 0 ? std::min(num_splits, topk) : auto_splits(B, Sq, Hkv, topk);
+  if (splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * Sq * Hq;
+  return align256(splits * rows * kD * 4) + align256(splits * rows * 4);
+}
+
+int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
+                         int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
+                         int num_pages, int max_pages, int causal, float softmax_scale,
+                         int num_splits, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_common(B, Sq, Hq, Hkv, D, topk, page_size);
+  if (rc) return rc;
+  if (num_pages <= 0 || max_pages <= 0)
+    return fail(MSA_ERR_INVALID_VALUE, "num_pages and max_pages must be positive");
+  if (!q || !k_pool || !v_pool || !page_table || !seqused_k || !q2k || !o || !lse)
+    return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+      !aligned(q2k, 4) || !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seqused_k, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
+  if (num_splits < 0) return fail(MSA_ERR_INVALID_VALUE, "num_splits must be >= 0");
+  const int splits = num_splits > 0 ? std::min(num_splits, topk) : auto_splits(B, Sq, Hkv, topk);
+  const int qpk = Hq / Hkv;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  QcParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_pool);
+  p.v = static_cast<const uint16_t*>(v_pool);
+  p.q2k = q2k;
+  p.page_table = page_table;
+  p.seqused = seqused_k;
+  p.B = B; p.Sq = Sq; p.Skv = max_pages * kBlk; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+  p.nblk = max_pages; p.max_pages = max_pages; p.num_pages = num_pages;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.splits = splits;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  if (splits > 1) {
+    const size_t rows = static_cast<size_t>(B) * Sq * Hq;
+    const size_t need = align256(splits * rows * kD * 4) + align256(splits * rows * 4);
+    if (!workspace || workspace_bytes < need)
+      return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
+    if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+    p.o_part = static_cast<float*>(workspace);
+    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(splits * rows * kD * 4));
+  }
+  hipError_t e = launch_qcentric(p, true, st);
+  if (e != hipSuccess) return hip_fail(e, "paged forward");
+  if (splits > 1) {
+    e = launch_combine_splits(p.o_part, p.lse_part, B, Sq, Hq, splits, static_cast<uint16_t*>(o), lse, st);
+    if (e != hipSuccess) return hip_fail(e, "split combine");
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Log-sum-exp merge of partial attention outputs.
+//
+// For query row (b, q) and head h with partials (O_s, L_s) over disjoint key
+// sets: L = log sum_s exp(L_s) and O = sum_s exp(L_s - L) O_s; a partial with
+// L_s = -inf (no visible key) carries no weight, and when every partial is
+// empty the result is (O = 0, LSE = -inf). This is the `combine` step of
+// `sparse_atten_func` (page "MSA interface.py") and the split-K accumulation
+// of `sparse_attention_ref` (page "test_sparse_atten.py").
+//
+// One thread per (row, head, 8-dim chunk): 16-byte partial loads, fp32
+// accumulation, one 16-byte bf16 store; the first chunk also writes the LSE.
+#include "msa_internal.hpp"
+
+#include <math.h>
+
+namespace msa {
+
+namespace {
+
+// slot partials [B*Sq][topk][Hq][D] (bf16) and [B*Sq][topk][Hq]; slot t of
+// (b, q, h) exists iff q2k[b][h/qpk][q][t] is a valid block id
+__global__ __launch_bounds__(256) void combine_slots_kernel(
+    const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int32_t* __restrict__ q2k, int B, int Sq, int Hq, int Hkv, int topk, int nblk,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long long total = static_cast<long long>(B) * Sq * Hq * 16;
+  if (idx >= total) return;
+  const int dc = static_cast<int>(idx & 15);
+  const long long rest = idx >> 4;
+  const int head = static_cast<int>(rest % Hq);
+  const long long gq = rest / Hq;
+  const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+  const int hkv = head / (Hq / Hkv);
+  const int32_t* sel = q2k + ((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk;
+
+  float lv[kMaxTopk];
+  float m = -INFINITY;
+  for (int t = 0; t < topk; ++t) {
+    const int s = sel[t];
+    float l = -INFINITY;
+    if (s >= 0 && s < nblk) l = lse_part[(gq * topk + t) * Hq + head];
+    lv[t] = l;
+    m = fmaxf(m, l);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = -INFINITY;
+  if (m != -INFINITY) {
+    float sum = 0.f;
+    for (int t = 0; t < topk; ++t) sum += expf(lv[t] - m);
+    L = m + logf(sum);
+    for (int t = 0; t < topk; ++t) {
+      if (lv[t] == -INFINITY) continue;
+      const float wgt = expf(lv[t] - L);
+      const u32x4 raw =
+          *reinterpret_cast<const u32x4*>(o_part + ((gq * topk + t) * Hq + head) * kD + 8 * dc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wgt * __uint_as_float(raw[i] << 16);
+        acc[2 * i + 1] += wgt * __uint_as_float(raw[i] & 0xFFFF0000u);
+      }
+    }
+  }
+  const u32x4 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  *reinterpret_cast<u32x4*>(o + (gq * Hq + head) * kD + 8 * dc) = out;
+  if (dc == 0) lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = L;
+}
+
+// split partials [splits][B*Sq][Hq][D] (fp32) and [splits][B*Sq][Hq]
+__global__ __launch_bounds__(256) void combine_splits_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, int B, int Sq, int Hq,
+    int splits, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long long rows = static_cast<long long>(B) * Sq * Hq;
+  if (idx >= rows * 16) return;
+  const int dc = static_cast<int>(idx & 15);
+  const long long rh = idx >> 4;  // (gq, head)
+  const int head = static_cast<int>(rh % Hq);
+  const long long gq = rh / Hq;
+  float m = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) m = fmaxf(m, lse_part[sp * rows + rh]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = -INFINITY;
+  if (m != -INFINITY) {
+    float sum = 0.f;
+    for (int sp = 0; sp < splits; ++sp) sum += expf(lse_part[sp * rows + rh] - m);
+    L = m + logf(sum);
+    for (int sp = 0; sp < splits; ++sp) {
+      const float l = lse_part[sp * rows + rh];
+      if (l == -INFINITY) continue;
+      const float wgt = expf(l - L);
+      const float* src = o_part + (sp * rows + rh) * kD + 8 * dc;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wgt * a[i];
+        acc[4 + i] += wgt * c[i];
+      }
+    }
+  }
+  const u32x4 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  *reinterpret_cast<u32x4*>(o + rh * kD + 8 * dc) = out;
+  if (dc == 0) {
+    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+    lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = L;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine_slots(const uint16_t* o_part, const float* lse_part, const int32_t* q2k,
+                                int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
+                                float* lse, hipStream_t stream) {
+  const long long total = static_cast<long long>(B) * Sq * Hq * 16;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_slots_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, o_part, lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk, o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_splits(const float* o_part, const float* lse_part, int B, int Sq, int Hq,
+                                 int splits, uint16_t* o, float* lse, hipStream_t stream) {
+  const long long total = static_cast<long long>(B) * Sq * Hq * 16;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_splits_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, o_part, lse_part, B, Sq, Hq, splits, o, lse);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,303 @@
+// kv-block -> query CSR builder, device exclusive scan and the kv-centric
+// work schedule.
+//
+// The CSR is the one `build_k2q_csr` produces on the page "MSA interface.py"
+// (row r = b * nblk + s of each KV head lists the global query ids b*Sq + q
+// whose index row selects block s; the page "test_sparse_atten.py" checks it
+// bit-exact against a reference). Entries are ordered by query, then slot, so
+// the result is unique and every call writes the same bits.
+//
+// Method (a stable counting sort, no order-dependent atomics):
+//   1. count:   the entry sequence of each KV head, in (query, slot) order, is
+//               cut into tiles of whole queries; each tile histograms its rows
+//               in LDS (commutative adds) into counts[hkv][row][tile].
+//   2. scan:    one exclusive scan of counts in (hkv, row, tile) order gives
+//               every (row, tile) its first output position.
+//   3. scatter: one wave per tile walks its entries in order, 64 at a time;
+//               entries of one batch that share a row are ranked by ballot /
+//               popcount (lower lane first), and a per-row cursor in LDS
+//               carries the offset from batch to batch.
+//   4. row_ptr: read off the scanned counts at tile 0 of each row.
+#include "msa_internal.hpp"
+
+#include <algorithm>
+
+namespace msa {
+
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kScanThreads * kScanItems;
+
+// exclusive scan of one value per thread across a 256-thread block; returns the
+// block total in *total
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wave_sums[kScanThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_sums[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    if (w < wave) before += wave_sums[w];
+    all += wave_sums[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_tile_sums(const int32_t* in, long long n,
+                                                               int32_t* sums) {
+  const long long base = static_cast<long long>(blockIdx.x) * kScanTile;
+  int acc = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const long long k = base + static_cast<long long>(threadIdx.x) * kScanItems + i;
+    if (k < n) acc += in[k];
+  }
+  int total;
+  block_exclusive_scan(acc, &total);
+  if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+// single block: exclusive scan of the tile sums, in place
+__global__ __launch_bounds__(kScanThreads) void scan_tile_offsets(int32_t* sums, int ntiles) {
+  int carry = 0;
+  for (int base = 0; base < ntiles; base += kScanTile) {
+    int v[kScanItems];
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      const int k = base + threadIdx.x * kScanItems + i;
+      v[i] = k < ntiles ? sums[k] : 0;
+      acc += v[i];
+    }
+    int total;
+    int run = block_exclusive_scan(acc, &total) + carry;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      const int k = base + threadIdx.x * kScanItems + i;
+      if (k < ntiles) sums[k] = run;
+      run += v[i];
+    }
+    carry += total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_apply(const int32_t* in, long long n,
+                                                           const int32_t* offsets, int32_t* out) {
+  const long long base = static_cast<long long>(blockIdx.x) * kScanTile;
+  int v[kScanItems];
+  int acc = 0;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const long long k = base + static_cast<long long>(threadIdx.x) * kScanItems + i;
+    v[i] = k < n ? in[k] : 0;
+    acc += v[i];
+  }
+  int total;
+  int run = block_exclusive_scan(acc, &total) + offsets[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const long long k = base + static_cast<long long>(threadIdx.x) * kScanItems + i;
+    if (k < n) out[k] = run;
+    run += v[i];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kScanThreads - 1) out[n] = run;
+}
+
+// ---------------------------------------------------------------------------
+// CSR passes. Grid (ntiles, Hkv). Tile `tile` of KV head hkv covers global
+// queries [tile * tile_q, min(B*Sq, (tile+1) * tile_q)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ q2k, int B,
+                                                        int Hkv, int Sq, int topk, int nblk,
+                                                        int tile_q, int ntiles,
+                                                        int32_t* __restrict__ counts) {
+  extern __shared__ int cnt[];
+  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int nrows = B * nblk;
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x) cnt[r] = 0;
+  __syncthreads();
+  const long long nq = static_cast<long long>(B) * Sq;
+  const long long g0 = static_cast<long long>(tile) * tile_q;
+  const long long g1 = std::min<long long>(nq, g0 + tile_q);
+  for (long long e = g0 * topk + threadIdx.x; e < g1 * topk; e += blockDim.x) {
+    const long long gq = e / topk;
+    const int t = static_cast<int>(e % topk);
+    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+    const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
+    if (s >= 0 && s < nblk) atomicAdd(&cnt[b * nblk + s], 1);
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x)
+    counts[(static_cast<long long>(hkv) * nrows + r) * ntiles + tile] = cnt[r];
+}
+
+__global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ q2k, int B,
+                                                         int Hkv, int Sq, int topk, int nblk,
+                                                         int tile_q, int ntiles,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ q_idx,
+                                                         int32_t* __restrict__ slot) {
+  extern __shared__ int cursor[];
+  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int nrows = B * nblk;
+  const long long cap = static_cast<long long>(B) * Sq * topk;
+  const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
+  const int base_h = offsets[seg];
+  for (int r = lane; r < nrows; r += 64)
+    cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
+  __syncthreads();
+  const long long nq = static_cast<long long>(B) * Sq;
+  const long long g0 = static_cast<long long>(tile) * tile_q;
+  const long long g1 = std::min<long long>(nq, g0 + tile_q);
+  int32_t* qi = q_idx + hkv * cap;
+  int32_t* sl = slot ? slot + hkv * cap : nullptr;
+  for (long long eb = g0 * topk; eb < g1 * topk; eb += 64) {
+    const long long e = eb + lane;
+    int row = -1;
+    long long gq = 0;
+    int t = 0;
+    if (e < g1 * topk) {
+      gq = e / topk;
+      t = static_cast<int>(e % topk);
+      const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+      const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
+      if (s >= 0 && s < nblk) row = b * nblk + s;
+    }
+    // rank among lower lanes with the same row
+    unsigned long long pending = __ballot(row >= 0);
+    int rank = 0, cnt = 0;
+    while (pending) {
+      const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+      const int lrow = __shfl(row, leader);
+      const unsigned long long peers = __ballot(row == lrow);
+      if (row == lrow) {
+        rank = __popcll(peers & __lanemask_lt());
+        cnt = __popcll(peers);
+      }
+      pending &= ~peers;
+    }
+    int pos = 0;
+    if (row >= 0) pos = cursor[row] + rank;
+    __syncthreads();
+    if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
+    if (row >= 0) {
+      qi[pos] = static_cast<int32_t>(gq);
+      if (sl) sl[pos] = t;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void csr_row_ptr_kernel(const int32_t* __restrict__ offsets, int Hkv, int nrows,
+                                   int ntiles, int32_t* __restrict__ row_ptr) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long long>(Hkv) * (nrows + 1)) return;
+  const int hkv = static_cast<int>(idx / (nrows + 1)), r = static_cast<int>(idx % (nrows + 1));
+  const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
+  row_ptr[idx] = offsets[seg + static_cast<long long>(r) * ntiles] - offsets[seg];
+}
+
+__global__ void chunk_count_kernel(const int32_t* __restrict__ row_ptr, int Hkv, int nrows,
+                                   int chunk_entries, int32_t* __restrict__ counts) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long long>(Hkv) * nrows) return;
+  const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
+  const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
+  const int len = rp[r + 1] - rp[r];
+  counts[idx] = (len + chunk_entries - 1) / chunk_entries;
+}
+
+inline unsigned blocks_for(long long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+}  // namespace
+
+size_t scan_tmp_ints(long long n) { return static_cast<size_t>((n + kScanTile - 1) / kScanTile) + 1; }
+
+hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, long long n, int32_t* tmp,
+                                 hipStream_t stream) {
+  if (n <= 0) return hipErrorInvalidValue;
+  const long long ntiles = (n + kScanTile - 1) / kScanTile;
+  if (ntiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_tile_sums, dim3(static_cast<unsigned>(ntiles)), dim3(kScanThreads), 0,
+                     stream, in, n, tmp);
+  hipLaunchKernelGGL(scan_tile_offsets, dim3(1), dim3(kScanThreads), 0, stream, tmp,
+                     static_cast<int>(ntiles));
+  hipLaunchKernelGGL(scan_apply, dim3(static_cast<unsigned>(ntiles)), dim3(kScanThreads), 0,
+                     stream, in, n, tmp, out);
+  return hipGetLastError();
+}
+
+CsrPlan csr_plan(int B, int Hkv, int Sq, int topk, int nrows) {
+  (void)topk;
+  const long long nq = static_cast<long long>(B) * Sq;
+  long long ntiles = (nq + 255) / 256;  // ~256 queries per tile
+  const long long max_counts = 4LL << 20;
+  const long long cap_tiles = std::max<long long>(1, max_counts / (static_cast<long long>(Hkv) * nrows));
+  ntiles = std::max<long long>(1, std::min(ntiles, cap_tiles));
+  CsrPlan plan;
+  plan.tile_q = static_cast<int>((nq + ntiles - 1) / ntiles);
+  plan.ntiles = static_cast<int>((nq + plan.tile_q - 1) / plan.tile_q);
+  plan.counts = static_cast<long long>(Hkv) * nrows * plan.ntiles;
+  return plan;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows) {
+  const CsrPlan plan = csr_plan(B, Hkv, Sq, topk, nrows);
+  return align256(plan.counts * 4) + align256((plan.counts + 1) * 4) +
+         align256(scan_tmp_ints(plan.counts) * 4);
+}
+
+hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
+                            int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
+                            hipStream_t stream) {
+  const int nrows = B * nblk;
+  const CsrPlan plan = csr_plan(B, Hkv, Sq, topk, nrows);
+  char* base = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base);
+  base += align256(plan.counts * 4);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base);
+  base += align256((plan.counts + 1) * 4);
+  int32_t* tmp = reinterpret_cast<int32_t*>(base);
+  const size_t lds = static_cast<size_t>(nrows) * sizeof(int);
+  const dim3 grid(plan.ntiles, Hkv);
+  hipLaunchKernelGGL(csr_count_kernel, grid, dim3(256), lds, stream, q2k, B, Hkv, Sq, topk, nblk,
+                     plan.tile_q, plan.ntiles, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(csr_scatter_kernel, grid, dim3(64), lds, stream, q2k, B, Hkv, Sq, topk, nblk,
+                     plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  const long long nrp = static_cast<long long>(Hkv) * (nrows + 1);
+  hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
+                     offsets, Hkv, nrows, plan.ntiles, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
+                                 int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
+                                 hipStream_t stream) {
+  const long long n = static_cast<long long>(Hkv) * nrows;
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, stream, row_ptr,
+                     Hkv, nrows, chunk_entries, chunk_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_exclusive_scan(chunk_counts, chunk_ptr, n, scan_tmp, stream);
+}
+
+}  // namespace msa

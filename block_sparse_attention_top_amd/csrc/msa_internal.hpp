@@ -1,0 +1,154 @@
+// Internal declarations shared by the HIP translation units of libmsa.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA 16x16x32 / 32x32x16, ds_read_b64_tr_b16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kD = 128;      // head dim (the only one supported)
+constexpr int kBlk = 128;    // KV block / page size
+constexpr int kMaxTopk = 32;
+constexpr int kMaxCsrRows = 16384;  // B * num_kv_blocks: the CSR passes keep one int per row in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round to nearest even; inputs here are finite
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile of 128-dim bf16 rows (256 B = 16 chunks of 16 B per row).
+// Chunk c of row r lives at chunk position c ^ swz(r). swz takes 8 distinct
+// values over any 8 consecutive rows starting at a multiple of 8 (so the
+// 16-byte fragment reads of 8 neighbouring rows hit distinct banks) and
+// swz(r) >> 1 takes 4 distinct values over 4 rows starting at a multiple of
+// 4 (so a transposed 4-row read of a 32-byte column band is conflict free).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int lds_chunk_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
+// (j % 4) of the 8-byte words addressed by lanes 4*i + j/4, i = 0..3.
+// With lane l' of a group addressing row k0 + l'/4, columns d0 + 4*(l'%4)..+3
+// of a row-major tile, lane j receives column d0 + j of rows k0..k0+3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(lds_ptr));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.442695040888963407359f;
+
+// floor(a / b) for b > 0
+__host__ __device__ __forceinline__ long long floor_div(long long a, long long b) {
+  long long q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() after its launches).
+// ---------------------------------------------------------------------------
+struct QcParams {
+  const uint16_t* q;
+  const uint16_t* k;         // contiguous [B,Skv,Hkv,D] or pool [num_pages,Hkv,128,D]
+  const uint16_t* v;
+  const int32_t* q2k;        // [B,Hkv,Sq,topk]
+  const int32_t* page_table; // paged only: [B,max_pages]
+  const int32_t* seqused;    // paged only: [B]
+  int B, Sq, Skv, Hq, Hkv, qpk, topk;
+  int nblk;                  // valid block ids are [0, nblk)
+  int max_pages, num_pages;
+  int causal;
+  float scale_log2;          // softmax_scale * log2(e)
+  int splits;                // 1 = write final O/LSE
+  uint16_t* o;               // bf16 [B,Sq,Hq,D]
+  float* lse;                // [B,Hq,Sq]
+  float* o_part;             // [splits][B*Sq][Hq][D]
+  float* lse_part;           // [splits][B*Sq][Hq]
+};
+hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream);
+
+struct KvParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* row_ptr;    // [Hkv, nrows+1]
+  const int32_t* q_idx;      // [Hkv, cap]
+  const int32_t* slot;       // [Hkv, cap]
+  const int32_t* chunk_ptr;  // [Hkv*nrows + 1] exclusive prefix of per-row chunk counts
+  int B, Sq, Skv, Hq, Hkv, qpk, topk, nblk, nrows;
+  long long cap;             // B*Sq*topk
+  int chunk_entries;         // CSR entries per work item
+  int causal;
+  float scale_log2;
+  uint16_t* o_part;          // bf16 [B*Sq][topk][Hq][D]
+  float* lse_part;           // [B*Sq][topk][Hq]
+};
+hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
+
+// combine of slot partials (kv-centric): valid slots are the q2k entries in [0, nblk)
+hipError_t launch_combine_slots(const uint16_t* o_part, const float* lse_part, const int32_t* q2k,
+                                int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
+                                float* lse, hipStream_t stream);
+// combine of split partials (split-KV q-centric / paged decode)
+hipError_t launch_combine_splits(const float* o_part, const float* lse_part, int B, int Sq, int Hq,
+                                 int splits, uint16_t* o, float* lse, hipStream_t stream);
+
+// exclusive scan of n int32 values: out[0..n] (out[n] = total); tmp >= scan_tmp_ints(n) ints
+size_t scan_tmp_ints(long long n);
+hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, long long n, int32_t* tmp,
+                                 hipStream_t stream);
+
+struct CsrPlan {
+  int ntiles;        // query tiles per KV head
+  int tile_q;        // queries per tile
+  long long counts;  // Hkv * nrows * ntiles
+};
+CsrPlan csr_plan(int B, int Hkv, int Sq, int topk, int nrows);
+size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows);
+hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
+                            int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
+                            hipStream_t stream);
+// per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix
+hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
+                                 int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
+                                 hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,242 @@
+// q-centric fused sparse attention forward (one wave per index row).
+//
+// The operation is the sparse attention of `sparse_attention_ref` on the page
+// "MiniMax-AI/MSA python/fmha_sm100/cute/test_sparse_atten.py": for query
+// (b, q) and KV head hkv, the qhead_per_kv query heads that share the index
+// row q2k[b][hkv][q][:] attend to the union of its valid blocks, masked by
+// seqused_k (paged) and the bottom-right causal limit q + kvlen - Sq, with a
+// natural-log LSE and (O = 0, LSE = -inf) for an empty key set.
+//
+// Layout on gfx950: the qpk heads of one row are the N = 16 columns of
+// v_mfma_f32_16x16x32_bf16 (zero-padded when qpk < 16). Each selected block
+// is streamed as four 32-token sub-tiles: K and V are fetched with 16-byte
+// loads into registers one sub-tile ahead, stored to LDS (XOR-swizzled), and
+// consumed as S^T = K Q^T (K fragments by ds_read_b128) and
+// O^T += V^T P^T (V fragments by the transposing ds_read_b64_tr_b16), so each
+// head's softmax statistics stay in its own lane column. Online softmax in
+// fp32 with exp2 and the scale folded into log2 units.
+//
+// With splits > 1 a wave handles a contiguous share of the slots and writes a
+// normalised fp32 partial (O, LSE) that the split combine merges (the
+// split-KV decode of `sparse_decode_atten_func` on the page "MSA interface.py").
+#include "msa_internal.hpp"
+
+#include <math.h>
+
+namespace msa {
+
+namespace {
+
+constexpr int kSub = 32;  // tokens per sub-tile
+
+template <bool PAGED>
+__global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSub * 256];
+  uint8_t* ks = lds;
+  uint8_t* vs = lds + kSub * 256;
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;  // head column
+  const int g = lane >> 4;  // 16-lane group
+
+  long long item = blockIdx.x;
+  const int sp = static_cast<int>(item % p.splits);
+  item /= p.splits;
+  const int qpos = static_cast<int>(item % p.Sq);
+  item /= p.Sq;
+  const int hkv = static_cast<int>(item % p.Hkv);
+  const int b = static_cast<int>(item / p.Hkv);
+
+  const int head = hkv * p.qpk + n;
+  const bool head_ok = n < p.qpk;
+  const long long grow = static_cast<long long>(b) * p.Sq + qpos;
+
+  // Q fragments: lane (n, g) holds dims 32*kq + 8*g .. +7 of head n.
+  bf16x8 qf[4];
+  {
+    const uint16_t* qrow = p.q + (grow * p.Hq + (head_ok ? head : hkv * p.qpk)) * kD + 8 * g;
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * kq);
+      if (!head_ok) v = u32x4{0, 0, 0, 0};
+      qf[kq] = as_bf16x8(v);
+    }
+  }
+
+  const long long kvlen = PAGED ? static_cast<long long>(p.seqused[b]) : p.Skv;
+  long long end = kvlen;  // keys [0, end) are visible
+  if (p.causal) {
+    const long long lim = qpos + kvlen - p.Sq;
+    if (lim + 1 < end) end = lim + 1;
+  }
+
+  const int32_t* sel = p.q2k + ((static_cast<long long>(b) * p.Hkv + hkv) * p.Sq + qpos) * p.topk;
+  const int per = (p.topk + p.splits - 1) / p.splits;
+  const int t0 = sp * per;
+  const int t1 = min(p.topk, t0 + per);
+
+  // (t, u): slot t, sub-tile u; advance to the first visible one at or after it
+  auto seek = [&](int& t, int& u, int& s, int& pg) {
+    while (t < t1) {
+      if (u < 4) {
+        s = sel[t];
+        bool ok = s >= 0 && s < p.nblk &&
+                  static_cast<long long>(s) * kBlk + kSub * u < end;
+        if (ok && PAGED) {
+          pg = p.page_table[static_cast<long long>(b) * p.max_pages + s];
+          ok = pg >= 0 && pg < p.num_pages;
+        }
+        if (ok) return;
+      }
+      ++t;
+      u = 0;
+    }
+  };
+
+  u32x4 kr[8], vr[8];
+  auto load = [&](int s, int pg, int u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ci = i * 64 + lane;
+      const int row = ci >> 4, c = ci & 15;
+      long long off;
+      if (PAGED)
+        off = ((static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * u + row) * kD + c * 8;
+      else
+        off = ((static_cast<long long>(b) * p.Skv + static_cast<long long>(s) * kBlk + kSub * u + row) *
+                   p.Hkv + hkv) * kD + c * 8;
+      kr[i] = *reinterpret_cast<const u32x4*>(p.k + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(p.v + off);
+    }
+  };
+  // keys past `end` are stored as zeros so that no value there can leak into P*V
+  auto store = [&](int s, int u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ci = i * 64 + lane;
+      const int row = ci >> 4, c = ci & 15;
+      const bool ok = static_cast<long long>(s) * kBlk + kSub * u + row < end;
+      const u32x4 z = {0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(ks + lds_chunk_off(row, c)) = ok ? kr[i] : z;
+      *reinterpret_cast<u32x4*>(vs + lds_chunk_off(row, c)) = ok ? vr[i] : z;
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int lq = lane & 15, rr = lq >> 2, cq = lq & 3;
+
+  auto compute = [&](int s, int u) {
+    // S^T sub-tile: 32 tokens x 16 heads, two 16-token M tiles
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const bf16x8 a =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(ks + lds_chunk_off(16 * mt + n, 4 * kq + g)));
+        sacc[mt] = mfma16(a, qf[kq], sacc[mt]);
+      }
+    // lane (n, g) holds tokens 16*mt + 4*g + i of head n
+    const long long jb = static_cast<long long>(s) * kBlk + kSub * u;
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long j = jb + 16 * mt + 4 * g + i;
+        x[mt][i] = j < end ? sacc[mt][i] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[mt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: key jb is visible
+    const float alpha = fast_exp2(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[mt][i] = fast_exp2(x[mt][i] - m_new);
+        ps += x[mt][i];
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+    // P^T as the B operand: k slots 8g..8g+3 = tokens 4g+i, 8g+4..8g+7 = tokens 16+4g+i
+    const u32x4 pw = {pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
+                      pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+    const bf16x8 pb = as_bf16x8(pw);
+    const int r1 = 4 * g + rr, r2 = 16 + 4 * g + rr;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int c = 2 * dt + (cq >> 1);
+      const int half = (cq & 1) * 8;
+      const i16x4 lo = lds_read_tr16(vs + lds_chunk_off(r1, c) + half);
+      const i16x4 hi = lds_read_tr16(vs + lds_chunk_off(r2, c) + half);
+      oacc[dt] = mfma16(cat_tr(lo, hi), pb, oacc[dt]);
+    }
+  };
+
+  int t = t0, u = 0, s = 0, pg = 0;
+  seek(t, u, s, pg);
+  if (t < t1) load(s, pg, u);
+  while (t < t1) {
+    int tn = t, un = u + 1, sn = s, pgn = pg;
+    seek(tn, un, sn, pgn);
+    __syncthreads();
+    store(s, u);
+    if (tn < t1) load(sn, pgn, un);
+    __syncthreads();
+    compute(s, u);
+    t = tn;
+    u = un;
+    s = sn;
+    pg = pgn;
+  }
+
+  // epilogue: lane (n, g) holds dims 16*dt + 4*g + i of head n
+  const bool any = l_run > 0.f;
+  const float inv = any ? 1.f / l_run : 0.f;
+  const float lse_v = any ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
+  if (!head_ok) return;
+  if (p.splits == 1) {
+    uint16_t* orow = p.o + (grow * p.Hq + head) * kD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x2 w = {pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv),
+                       pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
+    }
+    if (g == 0) p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos] = lse_v;
+  } else {
+    const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;
+    float* orow = p.o_part + prow * kD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = oacc[dt] * inv;
+    if (g == 0) p.lse_part[prow] = lse_v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
+  const long long items = static_cast<long long>(p.B) * p.Hkv * p.Sq * p.splits;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(items));
+  if (paged)
+    hipLaunchKernelGGL(qcentric_kernel<true>, grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(qcentric_kernel<false>, grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace msa

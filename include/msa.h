@@ -1,0 +1,140 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) top-k block-sparse GQA attention library.
+ *
+ * The operation is the forward pass of the sparse attention defined on the
+ * page "MiniMax-AI/MSA python/fmha_sm100/cute/test_sparse_atten.py"
+ * (golden reference `sparse_attention_ref`) and exposed on the page
+ * "MSA interface.py" (`sparse_atten_func`, `build_k2q_csr`,
+ * `sparse_decode_atten_func`). For query row q of sequence b and query head
+ * h (KV head hkv = h / (Hq / Hkv), the repeat-interleave GQA map):
+ *
+ *   selected  S = { q2k[b][hkv][q][t] : 0 <= value < nblk }   (a set; -1 = unused)
+ *   keys      J = { j = blk*s + r : s in S, r < blk, j < kvlen_b,
+ *                   and, if causal, j <= q + kvlen_b - Sq }      (bottom-right)
+ *   O[b][q][h]   = sum_j softmax_j(scale * <Q, K_j>) V_j        (bf16 out)
+ *   LSE[b][h][q] = log sum_j exp(scale * <Q, K_j>)               (natural log, fp32)
+ *   J empty  ->  O = 0, LSE = -inf.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers unless stated. bf16 tensors are raw 16-bit patterns.
+ *     Every tensor is dense row-major in the stated shape, 16-byte aligned.
+ *   - The caller owns all memory and the stream. The library never allocates
+ *     device memory, never synchronises the stream and keeps no state
+ *     between calls (beyond the thread-local error text); calls are
+ *     asynchronous on `stream` (a hipStream_t, NULL = the default stream).
+ *   - Inputs are read only; outputs are fully overwritten; workspaces are
+ *     scratch whose contents on entry do not matter.
+ *   - D must be 128 and the block / page size 128; Hq / Hkv must be one of
+ *     1, 2, 4, 8, 16; 1 <= topk <= 32 (the pages support D = 128 only and
+ *     qhead_per_kv in {1, 2, 4, 8, 16}, topk in {4, 8, 16, 32}).
+ *   - Index values outside [0, nblk) and page-table entries outside
+ *     [0, num_pages) are treated as unused slots (no device-side error).
+ *     The slots of one index row must name distinct blocks; repeated ids
+ *     give unspecified results.
+ *   - Return value: MSA_OK, or an error code with a message available from
+ *     msa_last_error(). Argument errors are detected on the host before any
+ *     launch, and then nothing is written.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_VALUE = 1, /* null / misaligned pointer, bad size, workspace too small */
+  MSA_ERR_NOT_SUPPORTED = 2, /* D != 128, block != 128, Hq/Hkv or topk unsupported */
+  MSA_ERR_HIP = 3            /* a HIP launch or runtime call failed */
+};
+
+enum msa_path {
+  MSA_PATH_AUTO = 0,      /* pick by qhead_per_kv */
+  MSA_PATH_QCENTRIC = 1,  /* one fused pass per (b, hkv, q) index row */
+  MSA_PATH_KVCENTRIC = 2  /* CSR-driven per-block partials + LSE merge */
+};
+
+/*
+ * Sparse forward, contiguous K/V (sparse_atten_func, dense KV layout).
+ *   q        bf16 [B, Sq, Hq, D]
+ *   k, v     bf16 [B, Skv, Hkv, D]       Skv % blk_kv == 0, nblk = Skv / blk_kv
+ *   q2k      int32 [B, Hkv, Sq, topk]
+ *   csr_row_ptr, csr_q_idx, csr_slot
+ *            optional prebuilt k2q CSR from msa_build_k2q_csr (all three or
+ *            none); used by the kv-centric path, ignored by the q-centric
+ *            one. When NULL the kv-centric path builds it in the workspace.
+ *   causal   0 none, 1 bottom-right (limit q + Skv - Sq)
+ *   softmax_scale  <= 0 selects D^-0.5
+ *   path     enum msa_path
+ *   o        bf16 [B, Sq, Hq, D]   (out)
+ *   lse      fp32 [B, Hq, Sq]      (out)
+ *   workspace / workspace_bytes   at least msa_sparse_fwd_workspace_size(...)
+ */
+size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
+                                     int blk_kv, int path);
+int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
+                   const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
+                   int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
+                   float softmax_scale, int path, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * kv-block -> query CSR (build_k2q_csr on the page "MSA interface.py";
+ * bit-exact checked by test_k2q_csr_builder_matches_torch_reference on the
+ * test page). Row r = b * num_kv_blocks + s of KV head hkv lists the global
+ * query ids b * Sq + q whose index row holds block s, ascending in q and
+ * then in slot t; csr_slot holds that t.
+ *   q2k       int32 [B, Hkv, Sq, topk]
+ *   row_ptr   int32 [Hkv, B * num_kv_blocks + 1]   (out)
+ *   q_idx     int32 [Hkv, B * Sq * topk]           (out; entries past the row
+ *                                                   total are unspecified)
+ *   slot      int32 [Hkv, B * Sq * topk] or NULL   (out)
+ *   workspace at least msa_build_k2q_csr_workspace_size(...)
+ * Deterministic: every call writes the same bits.
+ */
+size_t msa_build_k2q_csr_workspace_size(int B, int Hkv, int Sq, int topk, int num_kv_blocks);
+int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int num_kv_blocks,
+                      int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse forward, paged K/V (sparse_atten_func with page_table / seqused_k,
+ * and the split-KV decode of sparse_decode_atten_func on the page
+ * "MSA interface.py"; paging as in pack_paged_kv on the test page).
+ *   q           bf16 [B, Sq, Hq, D]
+ *   k_pool, v_pool  bf16 [num_pages, Hkv, page_size, D]
+ *   page_table  int32 [B, max_pages]: logical block s of sequence b is page
+ *               page_table[b][s]
+ *   seqused_k   int32 [B]: valid KV length of each sequence
+ *               (1 <= seqused_k[b] <= max_pages * page_size; keys at or past it
+ *               are masked and never influence the result)
+ *   q2k         int32 [B, Hkv, Sq, topk], valid ids [0, max_pages)
+ *   causal      bottom-right with the limit q + seqused_k[b] - Sq
+ *   num_splits  0 = automatic; else split each index row's blocks into that
+ *               many partial passes merged by log-sum-exp (1..topk)
+ *   o, lse      as msa_sparse_fwd
+ *   workspace   at least msa_paged_sparse_fwd_workspace_size(...)
+ */
+size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
+                                           int page_size, int max_pages, int num_splits);
+int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
+                         int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
+                         int num_pages, int max_pages, int causal, float softmax_scale,
+                         int num_splits, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* Library version string. */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

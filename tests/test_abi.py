@@ -1,0 +1,102 @@
+"""The C ABI library loads, exports every entry point include/msa.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: every call
+here fails validation, so no device memory is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_top_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"msa_sparse_fwd", "msa_build_k2q_csr", "msa_paged_sparse_fwd",
+            "msa_last_error"} <= set(names)
+    lib = ctypes.CDLL(msa.lib_path())
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version():
+    assert msa.msa_version().startswith("msa-gfx950")
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails host validation first
+
+
+def fwd(**kw):
+    lib = msa.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, rp=None, qi=None, sl=None, B=1, Sq=256, Skv=256,
+             Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1, scale=0.0, path=0, o=FAKE, lse=FAKE,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.msa_sparse_fwd(a["q"], a["k"], a["v"], a["q2k"], a["rp"], a["qi"], a["sl"], a["B"],
+                              a["Sq"], a["Skv"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
+                              a["causal"], a["scale"], a["path"], a["o"], a["lse"], a["ws"],
+                              a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), 2), (dict(blk=64), 2), (dict(Hq=3, Hkv=1), 2), (dict(Hq=32, Hkv=1), 2),
+    (dict(Hq=6, Hkv=4), 1), (dict(topk=33), 2), (dict(topk=0), 1), (dict(B=0), 1),
+    (dict(Sq=0), 1), (dict(Skv=200), 1), (dict(q=None), 1), (dict(o=FAKE + 8), 1),
+    (dict(lse=FAKE + 2), 1), (dict(path=7), 1), (dict(rp=FAKE), 1),
+    # kv-centric without (enough) workspace
+    (dict(path=2), 1), (dict(path=2, ws=FAKE, wsb=16), 1),
+    # kv-centric with too many CSR rows for the LDS-resident passes
+    (dict(path=2, Skv=128 * 20000), 2),
+])
+def test_sparse_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+    assert msa.msa_last_error() != ""
+
+
+def test_workspace_queries():
+    # q-centric needs none; kv-centric needs partials (topk * rows * heads * 256 B) and more
+    assert msa.msa_sparse_fwd_workspace_size(1, 1024, 1024, 64, 4, 128, 16, 128, 1) == 0
+    n = msa.msa_sparse_fwd_workspace_size(1, 1024, 1024, 64, 4, 128, 16, 128, 2)
+    assert n >= 1024 * 16 * 64 * 128 * 2
+    assert msa.msa_sparse_fwd_workspace_size(1, 1024, 1000, 64, 4, 128, 16, 128, 2) == 0
+    assert msa.msa_build_k2q_csr_workspace_size(1, 4, 8192, 16, 64) > 0
+    # paged: one split needs no workspace, several need fp32 partials
+    assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 1) == 0
+    assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 4) >= \
+        4 * 32 * 8 * 64 * 128 * 4
+
+
+def test_csr_and_paged_reject():
+    lib = msa.load_library()
+    assert lib.msa_build_k2q_csr(FAKE, 1, 1, 16, 33, 8, FAKE, FAKE, None, FAKE, 1 << 20,
+                                 None) == 2
+    assert lib.msa_build_k2q_csr(FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.msa_build_k2q_csr(None, 1, 1, 16, 4, 8, FAKE, FAKE, None, FAKE, 1 << 20,
+                                 None) == 1
+    # paged: page_size != 128, missing seqused_k, forced splits without workspace
+    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, FAKE, FAKE, None, 0,
+                         None]
+    a = list(args); a[12] = 64
+    assert lib.msa_paged_sparse_fwd(*a) == 2
+    a = list(args); a[4] = None
+    assert lib.msa_paged_sparse_fwd(*a) == 1
+    a = list(args); a[17] = 4
+    assert lib.msa_paged_sparse_fwd(*a) == 1
+    a = list(args); a[17] = -1
+    assert lib.msa_paged_sparse_fwd(*a) == 1
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    from block_sparse_attention_top_amd import _ffi
+    monkeypatch.setattr(_ffi, "_lib", None)
+    monkeypatch.setattr(_ffi, "_LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        _ffi.load_library()

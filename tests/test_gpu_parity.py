@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs. Tolerances and comparison rules are in parity_util."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity_util import (compare, full_compare, run_contiguous, run_paged, sample_rows,
+                         sampled_compare, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+Q, KV = 1, 2  # paths
+
+
+def contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal, mode, seed=42):
+    w = wl.Workload("case", B=B, Sq=Sq, Skv=Skv, Hkv=Hkv, qpk=qpk, topk=topk, causal=causal,
+                    mode=mode, seed=seed)
+    return w, wl.make_inputs(w)
+
+
+def check_contiguous(w, inp, path, label, softmax_scale=0.0):
+    say(f"[parity] {label} path={path} B={w.B} Sq={w.Sq} Skv={w.Skv} Hkv={w.Hkv} qpk={w.qpk} "
+        f"topk={w.topk} causal={w.causal}")
+    o, lse = run_contiguous(inp, w.causal, path, softmax_scale=softmax_scale)
+    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                             causal=w.causal,
+                                             softmax_scale=softmax_scale or None)
+    return full_compare(o, lse, o_ref, lse_ref, label), (o, lse)
+
+
+@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("name,B,Sq,Skv,Hkv,qpk,topk,causal,mode", [
+    ("c1-full", 1, 1024, 1024, 1, 2, 4, False, wl.MODE_PERM),
+    ("c2-small", 1, 1152, 1152, 2, 16, 8, True, wl.MODE_CAUSAL),
+    ("c3u-small", 1, 1024, 1024, 2, 16, 4, False, wl.MODE_PERM),
+    ("c3s-small", 1, 1024, 1024, 2, 16, 4, False, wl.MODE_SINK),
+    ("c4b-small", 1, 2048, 2048, 1, 2, 16, True, wl.MODE_CAUSAL),
+    ("batch3", 3, 200, 512, 2, 4, 3, True, wl.MODE_CAUSAL),
+    ("sq-gt-skv", 1, 400, 256, 1, 8, 2, True, wl.MODE_CAUSAL),
+    ("sq-lt-skv", 2, 72, 1024, 2, 16, 5, True, wl.MODE_CAUSAL),
+    ("topk1", 1, 256, 512, 1, 16, 1, False, wl.MODE_PERM),
+    ("topk32", 1, 64, 4096, 1, 4, 32, False, wl.MODE_PERM),
+])
+def test_contiguous_small(path, name, B, Sq, Skv, Hkv, qpk, topk, causal, mode):
+    w, inp = contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal, mode)
+    check_contiguous(w, inp, path, name)
+
+
+@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("qpk", [1, 2, 4, 8, 16])
+def test_qhead_per_kv_sweep(path, qpk):
+    w, inp = contiguous_case(2, 300, 640, 2, qpk, 3, True, wl.MODE_CAUSAL, seed=7)
+    check_contiguous(w, inp, path, f"qpk{qpk}")
+
+
+@pytest.mark.parametrize("path", [Q, KV])
+def test_unused_slots_invalid_ids_and_empty_blocks(path):
+    """-1 rows, ids outside [0, nblk), a block nobody selects, and a custom scale."""
+    w, inp = contiguous_case(1, 256, 1024, 2, 8, 4, False, wl.MODE_PERM, seed=3)
+    q2k = inp["q2k"].copy()
+    nblk = w.Skv // 128
+    q2k[:, :, :17] = -1                     # rows with nothing selected
+    q2k[:, :, 20:40, 1] = nblk + 5          # out-of-range ids
+    q2k[:, :, 40:60, 2] = -3
+    q2k[q2k == 5] = -1                      # block 5 selected by nobody: empty CSR row
+    inp["q2k"] = q2k
+    check_contiguous(w, inp, path, "edge-ids", softmax_scale=0.05)
+
+
+@pytest.mark.parametrize("path", [Q, KV])
+def test_deterministic(path):
+    w, inp = contiguous_case(1, 512, 1024, 2, 16, 4, True, wl.MODE_CAUSAL, seed=5)
+    o1, l1 = run_contiguous(inp, True, path)
+    o2, l2 = run_contiguous(inp, True, path)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paths_agree():
+    w, inp = contiguous_case(1, 640, 1024, 2, 16, 8, True, wl.MODE_CAUSAL, seed=9)
+    oq, lq = run_contiguous(inp, True, Q)
+    ok, lk = run_contiguous(inp, True, KV)
+    assert (oq.float() - ok.float()).abs().max().item() <= 2e-2
+    fin = torch.isfinite(lq)
+    assert torch.equal(fin, torch.isfinite(lk))
+    assert (lq[fin] - lk[fin]).abs().max().item() <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# CSR
+# ---------------------------------------------------------------------------
+def csr_gpu(q2k_np, nblk):
+    import block_sparse_attention_top_amd as msa
+    rp, qi, sl = msa.msa_build_k2q_csr(to_dev(q2k_np), nblk)
+    torch.cuda.synchronize()
+    return rp.cpu().numpy(), qi.cpu().numpy(), sl.cpu().numpy()
+
+
+def assert_csr_equal(q2k_np, nblk, label):
+    say(f"[csr] {label} shape={q2k_np.shape} nblk={nblk}")
+    rp, qi, sl = csr_gpu(q2k_np, nblk)
+    rp_o, qi_o, sl_o = oracle.k2q_csr(q2k_np, nblk)
+    assert np.array_equal(rp, rp_o), f"{label}: row_ptr differs"
+    for h in range(rp.shape[0]):
+        nnz = rp_o[h, -1]
+        assert np.array_equal(qi[h, :nnz], qi_o[h, :nnz]), f"{label}: q_idx differs (h={h})"
+        assert np.array_equal(sl[h, :nnz], sl_o[h, :nnz]), f"{label}: slot differs (h={h})"
+
+
+@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("topk", [4, 8, 16, 32])
+@pytest.mark.parametrize("Sq,Skv", [(2048, 4096), (4096, 4096), (1024, 4096), (4096, 2048)])
+def test_csr_bit_exact_causal(B, topk, Sq, Skv):
+    q2k = wl.q2k_table(17, wl.MODE_CAUSAL, B, 2, Sq, Skv, 128, topk)
+    assert_csr_equal(q2k, Skv // 128, f"causal B{B} k{topk}")
+
+
+@pytest.mark.parametrize("mode", [wl.MODE_PERM, wl.MODE_SINK])
+def test_csr_bit_exact_patterns_with_holes(mode):
+    q2k = wl.q2k_table(19, mode, 2, 3, 3000, 8192, 128, 16)
+    rng = np.random.default_rng(1)
+    q2k[rng.random(q2k.shape) < 0.05] = -1
+    q2k[rng.random(q2k.shape) < 0.01] = 64 + 7
+    q2k[q2k == 9] = -1
+    assert_csr_equal(q2k, 64, f"mode{mode}-holes")
+
+
+def test_csr_deterministic_and_prebuilt_csr_used():
+    w, inp = contiguous_case(1, 700, 2048, 2, 8, 8, True, wl.MODE_CAUSAL, seed=4)
+    import block_sparse_attention_top_amd as msa
+    q2k = to_dev(inp["q2k"])
+    a = msa.msa_build_k2q_csr(q2k, 16)
+    b = msa.msa_build_k2q_csr(q2k, 16)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    o1, l1 = run_contiguous(inp, True, KV)
+    o2, l2 = run_contiguous(inp, True, KV, csr=a)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# paged
+# ---------------------------------------------------------------------------
+def paged_case(B, Sq, Skv, Hkv, qpk, topk, causal, trims, seed=42, shuffle=True):
+    w = wl.Workload("paged", B=B, Sq=Sq, Skv=Skv, Hkv=Hkv, qpk=qpk, topk=topk, causal=causal,
+                    mode=wl.MODE_CAUSAL if causal else wl.MODE_PERM, paged=True,
+                    shuffle_pages=shuffle, seed=seed)
+    inp = wl.make_inputs(w, q2k=np.zeros((1,), np.int32))
+    seqused = np.array([Skv - t for t in trims], dtype=np.int32)
+    inp["seqused_k"] = seqused
+    lens = seqused if causal else np.full(B, Skv, dtype=np.int32)
+    inp["q2k"] = np.concatenate([wl.q2k_table(seed + b, w.mode, 1, Hkv, Sq, int(lens[b]), 128,
+                                              topk) for b in range(B)], 0)
+    return w, inp
+
+
+def check_paged(w, inp, splits, label):
+    say(f"[paged] {label} splits={splits} B={w.B} Sq={w.Sq} Skv={w.Skv} qpk={w.qpk} "
+        f"topk={w.topk} causal={w.causal}")
+    o, lse = run_paged(inp, w.causal, num_splits=splits)
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   inp["q2k"], causal=w.causal)
+    full_compare(o, lse, o_ref, lse_ref, label)
+    return o, lse
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_small(splits, causal):
+    w, inp = paged_case(4, 8, 2048, 2, 16, 8, causal, trims=[17, 0, 1000, 2047])
+    check_paged(w, inp, splits, "c5-small")
+
+
+@pytest.mark.parametrize("qpk", [1, 4, 16])
+def test_paged_prefill_ragged(qpk):
+    w, inp = paged_case(3, 150, 1024, 2, qpk, 4, True, trims=[0, 100, 900])
+    check_paged(w, inp, 0, f"paged-prefill-qpk{qpk}")
+
+
+def test_paged_tail_poison_and_bad_page():
+    """NaN and huge values past seqused_k change nothing; an out-of-range page id
+    drops that block (as the oracle does)."""
+    w, inp = paged_case(2, 8, 1024, 1, 16, 4, True, trims=[17, 300], seed=11)
+    o0, l0 = check_paged(w, inp, 0, "tail-clean")
+    kp, vp, pt = inp["k_pool"].copy(), inp["v_pool"].copy(), inp["page_table"]
+    for b in range(w.B):
+        used = int(inp["seqused_k"][b])
+        for s in range(w.max_pages):
+            lo = max(0, used - s * 128)
+            if lo < 128:
+                kp[pt[b, s], :, lo:] = 0x7FC0  # NaN
+                vp[pt[b, s], :, lo:] = 0x7F80  # +inf
+    inp2 = dict(inp, k_pool=kp, v_pool=vp)
+    o1, l1 = run_paged(inp2, True)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    bad = pt.copy()
+    bad[0, int(inp["q2k"][0, 0, 0, 0])] = 1 << 20
+    check_paged(w, dict(inp, page_table=bad), 0, "bad-page")
+
+
+def test_paged_shuffled_equals_identity_bitwise():
+    """The same logical K/V through a shuffled and through an identity page table."""
+    B, Sq, Skv, Hkv, qpk, topk = 3, 8, 1024, 2, 16, 6
+    w, inp = paged_case(B, Sq, Skv, Hkv, qpk, topk, True, trims=[5, 0, 200], seed=13)
+    pt = inp["page_table"]
+    ident = np.arange(B * w.max_pages, dtype=np.int32).reshape(B, w.max_pages)
+    k2 = np.empty_like(inp["k_pool"])
+    v2 = np.empty_like(inp["v_pool"])
+    k2[ident.reshape(-1)] = inp["k_pool"][pt.reshape(-1)]
+    v2[ident.reshape(-1)] = inp["v_pool"][pt.reshape(-1)]
+    o1, l1 = run_paged(inp, True)
+    o2, l2 = run_paged(dict(inp, k_pool=k2, v_pool=v2, page_table=ident), True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_equals_contiguous():
+    """Paged with seqused == Skv and the identity table matches the contiguous path."""
+    B, Sq, Skv, Hkv, qpk, topk = 2, 64, 1024, 2, 16, 4
+    w, inp = contiguous_case(B, Sq, Skv, Hkv, qpk, topk, True, wl.MODE_CAUSAL, seed=21)
+    mp = Skv // 128
+    pool_k = inp["k"].reshape(B, mp, 128, Hkv, 128).transpose(0, 1, 3, 2, 4).reshape(
+        B * mp, Hkv, 128, 128)
+    pool_v = inp["v"].reshape(B, mp, 128, Hkv, 128).transpose(0, 1, 3, 2, 4).reshape(
+        B * mp, Hkv, 128, 128)
+    pin = dict(q=inp["q"], k_pool=pool_k, v_pool=pool_v, q2k=inp["q2k"],
+               page_table=np.arange(B * mp, dtype=np.int32).reshape(B, mp),
+               seqused_k=np.full(B, Skv, dtype=np.int32))
+    op, lp = run_paged(pin, True, num_splits=1)
+    oc, lc = run_contiguous(inp, True, Q)
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (sampled rows), in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key", ["c1", "c2", "c3u", "c3s", "c4a", "c4b"])
+def test_full_size_sampled(key):
+    w = wl.WORKLOADS[key]
+    say(f"[full] {key} {w.name}: generating inputs")
+    inp = wl.make_inputs(w)
+    say(f"[full] {key}: running GPU (auto path)")
+    o, lse = run_contiguous(inp, w.causal, 0)
+    rows = sample_rows(w.B, w.Sq, 48, seed=1)
+    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                             causal=w.causal, rows=rows)
+    stats = sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, key)
+    # properties that hold at any size: finite, and LSE finite exactly where a key exists
+    assert torch.isfinite(o.float()).all()
+    say(f"[full] {key}: {stats}")
+
+
+def test_full_size_paged_decode():
+    w = wl.WORKLOADS["c5"]
+    say(f"[full] c5 {w.name}: generating inputs")
+    inp = wl.make_inputs(w)
+    say("[full] c5: running GPU (auto splits)")
+    o, lse = run_paged(inp, True)
+    rows = sample_rows(w.B, w.Sq, 64, seed=2)
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   inp["q2k"], causal=True, rows=rows)
+    stats = sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, "c5")
+    say(f"[full] c5: {stats}")
