@@ -50,16 +50,28 @@ int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
   return MSA_OK;
 }
 
-int resolve_path(int path, int qpk) {
+// Automatic choice: the kv-centric path reads each selected K/V block once per
+// chunk of ~2048 (query, head) rows and pays a bf16 partial round trip; the
+// q-centric path re-reads a 64 KiB K/V block per (query, KV head) pair but
+// needs no CSR, schedule or combine launches. Small problems (launch-bound) and
+// problems with more CSR rows than the LDS-resident CSR passes take the
+// q-centric path.
+int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC) return path;
-  return qpk >= 8 ? MSA_PATH_QCENTRIC : MSA_PATH_KVCENTRIC;
+  const long long nrows = static_cast<long long>(B) * (Skv / kBlk);
+  const long long work = static_cast<long long>(B) * Sq * Hq * topk;  // (query, head, slot) triples
+  if (nrows > kMaxCsrRows || work < (1LL << 20)) return MSA_PATH_QCENTRIC;
+  (void)Hkv;
+  return MSA_PATH_KVCENTRIC;
 }
 
-// Entries per kv-centric work item: about 2048 (query, head) rows.
-int chunk_entries_for(int qpk) { return std::max(32, 2048 / qpk); }
+// Entries per kv-centric work item: kKvChunkRows (query, head) rows.
+int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
 struct KvLayout {
-  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, o_part, lse_part, total;
+  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, o_part, lse_part,
+      total;
+  long long max_items;
 };
 
 KvLayout kv_layout(int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
@@ -76,8 +88,11 @@ KvLayout kv_layout(int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   L.chunk_counts = off; off += align256(nchunk * 4);
   L.chunk_ptr = off; off += align256((nchunk + 1) * 4);
   L.scan_tmp = off; off += align256(scan_tmp_ints(nchunk) * 4);
+  // sum over rows of ceil(len / chunk) <= nnz / chunk + rows
+  L.max_items = static_cast<long long>(Hkv) * (cap / chunk_entries_for(Hq / Hkv) + nrows + 1);
+  L.items = off; off += align256(L.max_items * 16);
   L.o_part = off; off += align256(static_cast<size_t>(cap) * Hq * kD * 2);
-  L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 4);
+  L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 8);
   L.total = off;
   return L;
 }
@@ -91,6 +106,19 @@ int auto_splits(int B, int Sq, int Hkv, int topk) {
 
 }  // namespace
 
+int msa::device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 extern "C" {
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
@@ -102,7 +130,7 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
   if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
       blk_kv != kBlk || Skv % kBlk || Hq % Hkv)
     return 0;
-  if (resolve_path(path, Hq / Hkv) == MSA_PATH_QCENTRIC) return 0;
+  if (resolve_path(path, B, Sq, Skv, Hq, Hkv, topk) == MSA_PATH_QCENTRIC) return 0;
   return kv_layout(B, Sq, Skv, Hq, Hkv, topk).total;
 }
 
@@ -130,7 +158,7 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   const int nblk = Skv / kBlk;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const int which = resolve_path(path, qpk);
+  const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
 
   if (which == MSA_PATH_QCENTRIC) {
     QcParams p{};
@@ -167,7 +195,8 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
     int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
     int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
-    e = launch_build_csr(q2k, B, Hkv, Sq, topk, nblk, rp, qi, sl, ws + L.csr_ws, st);
+    e = launch_build_csr(q2k, B, Hkv, Sq, topk, nblk, rp, qi, sl, ws + L.csr_ws, st,
+                         /*ordered=*/false);
     if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
     row_ptr = rp; q_idx = qi; slot = sl;
   }
@@ -189,11 +218,13 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
   p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
-  p.lse_part = reinterpret_cast<float*>(ws + L.lse_part);
-  // upper bound on the work items: sum over rows of ceil(len / chunk) <= nnz / chunk + rows
-  const long long grid = static_cast<long long>(Hkv) * (p.cap / chunk + nrows + 1);
-  if (grid > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
-  e = launch_kvcentric(p, static_cast<int>(grid), st);
+  p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
+  int4* items = reinterpret_cast<int4*>(ws + L.items);
+  p.items = items;
+  e = launch_kv_items(row_ptr, chunk_ptr, Hkv, static_cast<int>(nrows), chunk, items, st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
+  if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
+  e = launch_kvcentric(p, static_cast<int>(L.max_items), st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
   e = launch_combine_slots(p.o_part, p.lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
                            static_cast<uint16_t*>(o), lse, st);

@@ -7,8 +7,8 @@
 // `sparse_atten_func` (page "MSA interface.py") and the split-K accumulation
 // of `sparse_attention_ref` (page "test_sparse_atten.py").
 //
-// One thread per (row, head, 8-dim chunk): 16-byte partial loads, fp32
-// accumulation, one 16-byte bf16 store; the first chunk also writes the LSE.
+// 16 threads per (row, head), one per 8-dim chunk: 16-byte partial loads,
+// fp32 accumulation, one 16-byte bf16 store; the first chunk writes the LSE.
 #include "msa_internal.hpp"
 
 #include <math.h>
@@ -17,54 +17,94 @@ namespace msa {
 
 namespace {
 
-// slot partials [B*Sq][topk][Hq][D] (bf16) and [B*Sq][topk][Hq]; slot t of
-// (b, q, h) exists iff q2k[b][h/qpk][q][t] is a valid block id
+// slot partials: unnormalised U_t (bf16) laid out per (query, slot, KV head) as
+// [16 dim chunks][qpk heads][8 dims], with (LSE_t, M_t) [B*Sq][topk][Hq], so
+// that O = sum_t e^(M_t - L) U_t; slot t of (b, q, h) exists iff
+// q2k[b][h/qpk][q][t] is a valid block id. A block of 256 threads merges 16
+// consecutive (query, head) rows: the slot weights are formed once per row in
+// LDS, then every thread streams its 16-byte chunk of each weighted partial
+// (thread = dim chunk * 16 + row, so a wave reads whole runs of heads).
 __global__ __launch_bounds__(256) void combine_slots_kernel(
-    const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part,
+    const uint16_t* __restrict__ o_part, const float2* __restrict__ lse_part,
     const int32_t* __restrict__ q2k, int B, int Sq, int Hq, int Hkv, int topk, int nblk,
     uint16_t* __restrict__ o, float* __restrict__ lse) {
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long long total = static_cast<long long>(B) * Sq * Hq * 16;
-  if (idx >= total) return;
-  const int dc = static_cast<int>(idx & 15);
-  const long long rest = idx >> 4;
-  const int head = static_cast<int>(rest % Hq);
-  const long long gq = rest / Hq;
-  const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-  const int hkv = head / (Hq / Hkv);
-  const int32_t* sel = q2k + ((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk;
-
-  float lv[kMaxTopk];
-  float m = -INFINITY;
-  for (int t = 0; t < topk; ++t) {
-    const int s = sel[t];
-    float l = -INFINITY;
-    if (s >= 0 && s < nblk) l = lse_part[(gq * topk + t) * Hq + head];
-    lv[t] = l;
-    m = fmaxf(m, l);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = -INFINITY;
-  if (m != -INFINITY) {
-    float sum = 0.f;
-    for (int t = 0; t < topk; ++t) sum += expf(lv[t] - m);
-    L = m + logf(sum);
-    for (int t = 0; t < topk; ++t) {
-      if (lv[t] == -INFINITY) continue;
-      const float wgt = expf(lv[t] - L);
-      const u32x4 raw =
-          *reinterpret_cast<const u32x4*>(o_part + ((gq * topk + t) * Hq + head) * kD + 8 * dc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wgt * __uint_as_float(raw[i] << 16);
-        acc[2 * i + 1] += wgt * __uint_as_float(raw[i] & 0xFFFF0000u);
+  __shared__ float wts[16][kMaxTopk];
+  __shared__ float refm[16][kMaxTopk];
+  __shared__ float row_lse[16];
+  const long long rows = static_cast<long long>(B) * Sq * Hq;
+  const long long rh0 = static_cast<long long>(blockIdx.x) * 16;
+  const int tid = threadIdx.x;
+  const int qpk = Hq / Hkv;
+  for (int idx = tid; idx < 16 * topk; idx += 256) {
+    const int rl = idx / topk, t = idx % topk;
+    const long long rh = rh0 + rl;
+    float l = -INFINITY, mref = 0.f;
+    if (rh < rows) {
+      const long long gq = rh / Hq;
+      const int head = static_cast<int>(rh % Hq);
+      const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+      const int sblk = q2k[((static_cast<long long>(b) * Hkv + head / qpk) * Sq + qpos) * topk + t];
+      if (sblk >= 0 && sblk < nblk) {
+        const float2 lm = lse_part[(gq * topk + t) * Hq + head];
+        l = lm.x;
+        mref = lm.y;
       }
     }
+    wts[rl][t] = l;
+    refm[rl][t] = mref;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float m = -INFINITY;
+    for (int t = 0; t < topk; ++t) m = fmaxf(m, wts[tid][t]);
+    float L = -INFINITY;
+    if (m != -INFINITY) {
+      float sum = 0.f;
+      for (int t = 0; t < topk; ++t) sum += expf(wts[tid][t] - m);
+      L = m + logf(sum);
+      // partials are unnormalised relative to their reference max
+      for (int t = 0; t < topk; ++t)
+        wts[tid][t] = wts[tid][t] == -INFINITY ? 0.f : expf(refm[tid][t] - L);
+    } else {
+      for (int t = 0; t < topk; ++t) wts[tid][t] = 0.f;
+    }
+    row_lse[tid] = L;
+  }
+  __syncthreads();
+  const int rl = tid & 15, dc = tid >> 4;
+  const long long rh = rh0 + rl;
+  if (rh >= rows) return;
+  const long long gq = rh / Hq;
+  const int head = static_cast<int>(rh % Hq);
+  const int hkv = head / qpk, head_i = head % qpk;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t0 = 0; t0 < topk; t0 += 8) {
+    u32x4 raw[8];
+    float wgt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = t0 + k;
+      wgt[k] = t < topk ? wts[rl][t] : 0.f;
+      const long long blk = (gq * topk + t) * Hkv + hkv;
+      raw[k] = wgt[k] > 0.f ? *reinterpret_cast<const u32x4*>(
+                                  o_part + blk * (qpk * kD) + (dc * qpk + head_i) * 8)
+                            : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wgt[k] * __uint_as_float(raw[k][i] << 16);
+        acc[2 * i + 1] += wgt[k] * __uint_as_float(raw[k][i] & 0xFFFF0000u);
+      }
   }
   const u32x4 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-  *reinterpret_cast<u32x4*>(o + (gq * Hq + head) * kD + 8 * dc) = out;
-  if (dc == 0) lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = L;
+  *reinterpret_cast<u32x4*>(o + rh * kD + 8 * dc) = out;
+  if (dc == 0) {
+    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+    lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = row_lse[rl];
+  }
 }
 
 // split partials [splits][B*Sq][Hq][D] (fp32) and [splits][B*Sq][Hq]
@@ -111,7 +151,7 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(
 
 }  // namespace
 
-hipError_t launch_combine_slots(const uint16_t* o_part, const float* lse_part, const int32_t* q2k,
+hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
                                 float* lse, hipStream_t stream) {
   const long long total = static_cast<long long>(B) * Sq * Hq * 16;

@@ -201,6 +201,38 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
   }
 }
 
+// Unordered scatter: every entry of a (row, tile) segment lands inside that
+// segment, slot claimed with an LDS atomic (order within a segment unspecified).
+__global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
+    const int32_t* __restrict__ q2k, int B, int Hkv, int Sq, int topk, int nblk, int tile_q,
+    int ntiles, const int32_t* __restrict__ offsets, int32_t* __restrict__ q_idx,
+    int32_t* __restrict__ slot) {
+  extern __shared__ int cursor[];
+  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int nrows = B * nblk;
+  const long long cap = static_cast<long long>(B) * Sq * topk;
+  const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
+  const int base_h = offsets[seg];
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x)
+    cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
+  __syncthreads();
+  const long long nq = static_cast<long long>(B) * Sq;
+  const long long g0 = static_cast<long long>(tile) * tile_q;
+  const long long g1 = std::min<long long>(nq, g0 + tile_q);
+  int32_t* qi = q_idx + hkv * cap;
+  int32_t* sl = slot ? slot + hkv * cap : nullptr;
+  for (long long e = g0 * topk + threadIdx.x; e < g1 * topk; e += blockDim.x) {
+    const long long gq = e / topk;
+    const int t = static_cast<int>(e % topk);
+    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+    const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
+    if (s < 0 || s >= nblk) continue;
+    const int pos = atomicAdd(&cursor[b * nblk + s], 1);
+    qi[pos] = static_cast<int32_t>(gq);
+    if (sl) sl[pos] = t;
+  }
+}
+
 __global__ void csr_row_ptr_kernel(const int32_t* __restrict__ offsets, int Hkv, int nrows,
                                    int ntiles, int32_t* __restrict__ row_ptr) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -264,7 +296,7 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows) {
 
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool ordered) {
   const int nrows = B * nblk;
   const CsrPlan plan = csr_plan(B, Hkv, Sq, topk, nrows);
   char* base = static_cast<char*>(ws);
@@ -281,8 +313,12 @@ hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(csr_scatter_kernel, grid, dim3(64), lds, stream, q2k, B, Hkv, Sq, topk, nblk,
-                     plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  if (ordered)
+    hipLaunchKernelGGL(csr_scatter_kernel, grid, dim3(64), lds, stream, q2k, B, Hkv, Sq, topk,
+                       nblk, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  else
+    hipLaunchKernelGGL(csr_scatter_unordered_kernel, grid, dim3(256), lds, stream, q2k, B, Hkv,
+                       Sq, topk, nblk, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   const long long nrp = static_cast<long long>(Hkv) * (nrows + 1);
   hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
                      offsets, Hkv, nrows, plan.ntiles, row_ptr);

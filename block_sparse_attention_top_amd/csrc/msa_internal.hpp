@@ -11,6 +11,8 @@ constexpr int kD = 128;      // head dim (the only one supported)
 constexpr int kBlk = 128;    // KV block / page size
 constexpr int kMaxTopk = 32;
 constexpr int kMaxCsrRows = 16384;  // B * num_kv_blocks: the CSR passes keep one int per row in LDS
+constexpr int kKvChunkRows = 2048;  // (query, head) rows per kv-centric work item
+constexpr int kKvMaxEntries = 512;  // CSR entries per kv-centric work item (LDS bound)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -25,27 +27,29 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
-// round to nearest even; inputs here are finite
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile of 128-dim bf16 rows (256 B = 16 chunks of 16 B per row).
-// Chunk c of row r lives at chunk position c ^ swz(r). swz takes 8 distinct
-// values over any 8 consecutive rows starting at a multiple of 8 (so the
-// 16-byte fragment reads of 8 neighbouring rows hit distinct banks) and
-// swz(r) >> 1 takes 4 distinct values over 4 rows starting at a multiple of
-// 4 (so a transposed 4-row read of a 32-byte column band is conflict free).
+// LDS tiles of 128-dim bf16 rows (256 B of data per row), padded so that the
+// address of (row, byte) is linear -- every fragment read is one lane base plus
+// an immediate offset. The strides were chosen by measuring LDS bank-conflict
+// cycles on gfx950 (64 banks of 4 bytes) for the two read patterns used:
+//   K tiles: row stride 272 B (68 banks): the 16-byte fragment reads of 16
+//            consecutive rows start 4 banks apart -> conflict free
+//            (288 B costs 4 conflict cycles per read, 320 B costs 12).
+//   V tiles: row stride 320 B (80 banks): the transposed 8-byte reads of
+//            4 rows x 2 column bands per half wave land on 8 distinct 8-bank
+//            groups -> conflict free (272 B and 288 B cost 6 and 2 cycles).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int lds_chunk_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
+constexpr int kKStride = 272;
+constexpr int kVStride = 320;
+__device__ __forceinline__ int k_off(int r, int c16) { return r * kKStride + c16 * 16; }
+__device__ __forceinline__ int v_off(int r, int c16) { return r * kVStride + c16 * 16; }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 // (j % 4) of the 8-byte words addressed by lanes 4*i + j/4, i = 0..3.
@@ -71,6 +75,12 @@ __device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// c + a.lo * b.lo + a.hi * b.hi with a, b packed bf16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -113,18 +123,25 @@ struct KvParams {
   const int32_t* q_idx;      // [Hkv, cap]
   const int32_t* slot;       // [Hkv, cap]
   const int32_t* chunk_ptr;  // [Hkv*nrows + 1] exclusive prefix of per-row chunk counts
+  const int4* items;         // [total chunks] (hkv, row, first entry, entry count)
   int B, Sq, Skv, Hq, Hkv, qpk, topk, nblk, nrows;
   long long cap;             // B*Sq*topk
   int chunk_entries;         // CSR entries per work item
   int causal;
   float scale_log2;
-  uint16_t* o_part;          // bf16 [B*Sq][topk][Hq][D]
-  float* lse_part;           // [B*Sq][topk][Hq]
+  uint16_t* o_part;          // bf16 [B*Sq][topk][Hkv][16 dim chunks][qpk][8], unnormalised:
+                             // sum_j e^(s_j - M) V_j
+  float2* lse_part;          // [B*Sq][topk][Hq]: (LSE of the block, reference max M), natural log
 };
+// grid = an upper bound on the item count (workgroups past the count exit)
 hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
+hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
+                           int chunk_entries, int4* items, hipStream_t stream);
+// compute units of the current device (cached per device)
+int device_cu_count();
 
 // combine of slot partials (kv-centric): valid slots are the q2k entries in [0, nblk)
-hipError_t launch_combine_slots(const uint16_t* o_part, const float* lse_part, const int32_t* q2k,
+hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
                                 float* lse, hipStream_t stream);
 // combine of split partials (split-KV q-centric / paged decode)
@@ -143,9 +160,12 @@ struct CsrPlan {
 };
 CsrPlan csr_plan(int B, int Hkv, int Sq, int topk, int nrows);
 size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows);
+// ordered = true: entries of a row ascending in (query, slot), the unique CSR
+// ordered = false: same rows and entry sets, order inside a row unspecified
+// (used internally by the kv-centric path, whose results do not depend on it)
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, bool ordered = true);
 // per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
                                  int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,

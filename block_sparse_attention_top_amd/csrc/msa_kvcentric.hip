@@ -4,19 +4,25 @@
 // This follows the structure of the pages' sparse forward: `sparse_atten_func`
 // on the page "MSA interface.py" consumes the kv-block -> query CSR from
 // `build_k2q_csr`, computes for each (KV block, queries that selected it) a
-// block-local softmax and a normalised partial output plus its LSE, and merges
+// block-local softmax and a partial output plus its LSE, and merges
 // the partials of each query by log-sum-exp in a separate `combine` step (its
 // split-K semantics are the `o_partial_dtype` branch of `sparse_attention_ref`
 // on the page "test_sparse_atten.py"). Partials are bf16 (the pages' default
-// partial dtype) with fp32 LSE, indexed by the slot t of the index row.
+// partial dtype), indexed by the slot t of the index row, and left
+// unnormalised: U = sum_j e^(s_j - M) V_j with the block's reference max M,
+// stored beside (LSE of the block, M); the combine applies e^(M - LSE_total).
 //
-// Layout on gfx950: a work item is (KV head, CSR row = (b, block), a chunk of
-// up to `chunk_entries` CSR entries). The workgroup (4 waves) stages the
-// block's K and V tiles (128 x 128 bf16 each) in LDS once; each wave then
-// takes 32 gathered (query, head) rows at a time as the N = 32 columns of
-// v_mfma_f32_32x32x16_bf16: S^T = K Q^T with K fragments from LDS and Q rows
-// loaded straight from HBM, a block-local softmax per lane column, and
-// O^T = V^T P^T with V fragments from the transposing ds_read_b64_tr_b16.
+// Layout on gfx950. A work item is (KV head, CSR row = (b, block), a chunk of
+// up to `chunk_entries` CSR entries), listed in an item table by the schedule
+// kernel. A workgroup of 4 waves stages the block's K and V tiles
+// (128 x 128 bf16, padded rows) and the chunk's (query, slot) entries in LDS;
+// two workgroups share a CU, so one wave's softmax (VALU) overlaps the other
+// wave's matrix work on each SIMD, and one workgroup's tile load overlaps the
+// other's compute. Each wave takes 32 gathered (query, head) rows at a time as
+// the N = 32 columns of v_mfma_f32_32x32x16_bf16, Q rows loaded from HBM one
+// step ahead: S^T = K Q^T (K fragments by ds_read_b128), a block-local softmax
+// per lane column (two 64-token halves, online), O^T = V^T P^T (V fragments by
+// the transposing ds_read_b64_tr_b16).
 #include "msa_internal.hpp"
 
 #include <math.h>
@@ -26,159 +32,222 @@ namespace msa {
 namespace {
 
 template <int QPK>
-__global__ __launch_bounds__(256) void kvcentric_kernel(KvParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlk * 256];
-  uint8_t* ks = lds;
-  uint8_t* vs = lds + kBlk * 256;
+__global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
+  constexpr int kEnt = kKvChunkRows / QPK < kKvMaxEntries ? kKvChunkRows / QPK : kKvMaxEntries;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[kBlk * kVStride];
+  __shared__ int ent_q[kEnt];
+  __shared__ int ent_t[kEnt];
 
-  const int nitems = p.Hkv * p.nrows;
-  const int total = p.chunk_ptr[nitems];
+  const int total = p.chunk_ptr[p.Hkv * p.nrows];
   const int w = blockIdx.x;
   if (w >= total) return;
-  // the (hkv, row) whose chunk range holds w
-  int lo = 0, hi = nitems;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.chunk_ptr[mid] <= w) lo = mid; else hi = mid;
-  }
-  const int hkv = lo / p.nrows, r = lo % p.nrows;
-  const int* rp = p.row_ptr + static_cast<long long>(hkv) * (p.nrows + 1);
-  const int e0 = rp[r] + (w - p.chunk_ptr[lo]) * p.chunk_entries;
-  const int e1 = min(e0 + p.chunk_entries, rp[r + 1]);
+  const int tid = threadIdx.x;
+  const int4 item = p.items[w];
+  const int hkv = item.x, r = item.y, e0 = item.z, ne = item.w;
   const int b = r / p.nblk, s = r % p.nblk;
 
-  // stage K and V of block s (128 tokens x 256 B each)
+  // stage the chunk's entries and the block's K and V (128 tokens x 256 B each)
+  for (int i = tid; i < ne; i += 256) {
+    ent_q[i] = p.q_idx[hkv * p.cap + e0 + i];
+    ent_t[i] = p.slot[hkv * p.cap + e0 + i];
+  }
   {
-    const int tid = threadIdx.x;
     const long long tok0 = static_cast<long long>(b) * p.Skv + static_cast<long long>(s) * kBlk;
-    u32x4 kr[8], vr[8];
+    u32x4 rk[8], rv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ci = i * 256 + tid;
       const int row = ci >> 4, c = ci & 15;
       const long long off = ((tok0 + row) * p.Hkv + hkv) * kD + c * 8;
-      kr[i] = *reinterpret_cast<const u32x4*>(p.k + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(p.v + off);
+      rk[i] = *reinterpret_cast<const u32x4*>(p.k + off);
+      rv[i] = *reinterpret_cast<const u32x4*>(p.v + off);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ci = i * 256 + tid;
       const int row = ci >> 4, c = ci & 15;
-      *reinterpret_cast<u32x4*>(ks + lds_chunk_off(row, c)) = kr[i];
-      *reinterpret_cast<u32x4*>(vs + lds_chunk_off(row, c)) = vr[i];
+      *reinterpret_cast<u32x4*>(ks + k_off(row, c)) = rk[i];
+      *reinterpret_cast<u32x4*>(vs + v_off(row, c)) = rv[i];
     }
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31;   // row column of the 32x32 MFMA
   const int h = lane >> 5;   // k-half
   constexpr int EPW = 32 / QPK;  // CSR entries per wave step
   const int ent = n / QPK, head_i = n % QPK;
   const int head = hkv * QPK + head_i;
-  const long long cap = p.cap;
   const int j16 = lane >> 4, lq = lane & 15, rr = lq >> 2, cq = lq & 3;
   const long long lim_off = static_cast<long long>(p.Skv) - p.Sq;
   const long long blk0 = static_cast<long long>(s) * kBlk;
+  const int nsteps = (ne + EPW - 1) / EPW;
+  const float c2 = p.scale_log2;
+  // lane offsets inside the tiles: K fragment row n, chunk h; V transposed reads
+  const int kbase0 = n * kKStride + h * 16;
+  const int vbase0 = (4 * h + rr) * kVStride + 32 * (j16 & 1) + 8 * cq;
 
-  for (int eb = e0 + wave * EPW; eb < e1; eb += 4 * EPW) {
-    const int e = eb + ent;
-    const bool ok = e < e1;
-    int gq = 0, t = 0;
-    if (ok) {
-      gq = p.q_idx[hkv * cap + e];
-      t = p.slot[hkv * cap + e];
-    }
-    const int qpos = gq % p.Sq;
-    bf16x8 qf[8];
-    {
-      const uint16_t* qrow = p.q + (static_cast<long long>(gq) * p.Hq + head) * kD + 8 * h;
+  struct Rows {
+    bf16x8 q[8];
+    int gq, t;
+    bool ok;
+  };
+  auto fetch = [&](int step, Rows& R) {
+    const int i = step * EPW + ent;
+    R.ok = i < ne;
+    const int ii = R.ok ? i : 0;
+    R.gq = ent_q[ii];
+    R.t = ent_t[ii];
+    const uint16_t* qrow = p.q + (static_cast<long long>(R.gq) * p.Hq + head) * kD + 8 * h;
 #pragma unroll
-      for (int kq = 0; kq < 8; ++kq) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * kq);
-        if (!ok) v = u32x4{0, 0, 0, 0};
-        qf[kq] = as_bf16x8(v);
-      }
-    }
-    // S^T: 128 tokens (4 M tiles of 32) x 32 rows
-    f32x16 sacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = f32x16{};
-#pragma unroll
-      for (int kq = 0; kq < 8; ++kq) {
-        const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(ks + lds_chunk_off(32 * mt + n, 2 * kq + h)));
-        sacc[mt] = mfma32(a, qf[kq], sacc[mt]);
-      }
-    }
-    // lane (n, h) holds tokens 32*mt + 8*(i/4) + 4*h + i%4 of row n
+    for (int kq = 0; kq < 8; ++kq)
+      R.q[kq] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kq));
+  };
+
+  Rows rc, rn;
+  int step = wave;
+  if (step < nsteps) fetch(step, rc);
+  for (; step < nsteps; step += 4) {
+    if (step + 4 < nsteps) fetch(step + 4, rn);
+    // The tile offsets are made opaque per step so that the K fragments are
+    // re-read from LDS each step instead of being held in registers.
+    int kbase = kbase0, vbase = vbase0;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const int qpos = rc.gq % p.Sq;
     const long long lim = p.causal ? qpos + lim_off : (1LL << 62);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const long long j = blk0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float x = (ok && j <= lim) ? sacc[mt][i] * p.scale_log2 : -INFINITY;
-        sacc[mt][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mref = mx == -INFINITY ? 0.f : mx;
-    float ps = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(sacc[mt][i] - mref);
-        sacc[mt][i] = pv;
-        ps += pv;
-      }
-    ps += __shfl_xor(ps, 32);
-
+    const int vis =
+        rc.ok ? static_cast<int>(min(lim - blk0 + 1, static_cast<long long>(kBlk))) : 0;
+    const bool full = __all(vis >= kBlk);
+    // Block-local softmax in two 64-token halves. The reference max m_ref is the
+    // first half's row max; the second half only rescales (online softmax) when
+    // its max exceeds m_ref by more than 8 in log2 units, so that unnormalised
+    // probabilities stay <= 256. P is rounded to bf16 for the P V product; the
+    // row sum is accumulated in fp32 (summing the bf16-rounded values instead
+    // moves the LSE by up to ~1.4e-3 when a few keys dominate a row).
+    float m_ref = -INFINITY, ps = 0.f;
     f32x16 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int mt = kk >> 1, i0 = 8 * (kk & 1);
-      const u32x4 pw = {pack_bf16x2(sacc[mt][i0 + 0], sacc[mt][i0 + 1]),
-                        pack_bf16x2(sacc[mt][i0 + 2], sacc[mt][i0 + 3]),
-                        pack_bf16x2(sacc[mt][i0 + 4], sacc[mt][i0 + 5]),
-                        pack_bf16x2(sacc[mt][i0 + 6], sacc[mt][i0 + 7])};
-      const bf16x8 pb = as_bf16x8(pw);
-      const int r1 = 16 * kk + 4 * h + rr, r2 = r1 + 8;
+    for (int hf = 0; hf < 2; ++hf) {
+      // S^T half (raw dot products): tokens 64*hf + 32*mt + 8*(i/4) + 4*h + i%4 of row n
+      f32x16 sacc[2];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int c = 4 * dt + 2 * (j16 & 1) + (cq >> 1);
-        const int half = (cq & 1) * 8;
-        const i16x4 lo4 = lds_read_tr16(vs + lds_chunk_off(r1, c) + half);
-        const i16x4 hi4 = lds_read_tr16(vs + lds_chunk_off(r2, c) + half);
-        oacc[dt] = mfma32(cat_tr(lo4, hi4), pb, oacc[dt]);
+      for (int mt = 0; mt < 2; ++mt) {
+        sacc[mt] = f32x16{};
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              ks + kbase + (64 * hf + 32 * mt) * kKStride + 32 * kq));
+          sacc[mt] = mfma32(a, rc.q[kq], sacc[mt]);
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = 64 * hf + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (j >= vis) sacc[mt][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[mt][i], sacc[mt][i + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (hf == 0) {
+        m_ref = mx;
+      } else if (__any((mx - m_ref) * c2 > 8.f)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
+        ps *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+        m_ref = m_new;
+      }
+      const float nmc = -(m_ref == -INFINITY ? 0.f : m_ref) * c2;
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(fmaf(sacc[mt][2 * i], c2, nmc));
+          const float p1 = fast_exp2(fmaf(sacc[mt][2 * i + 1], c2, nmc));
+          pk[mt][i] = pack_bf16x2(p0, p1);
+          ps += p0 + p1;
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int mt = kk >> 1, i0 = 4 * (kk & 1);
+        const u32x4 pw = {pk[mt][i0], pk[mt][i0 + 1], pk[mt][i0 + 2], pk[mt][i0 + 3]};
+        const bf16x8 pb = as_bf16x8(pw);
+        // rows 64*hf + 16*kk + 4*h + rr (+8), columns 32*dt + 16*(j16&1) + 4*cq .. +3
+        const uint8_t* vrow = vs + vbase + (64 * hf + 16 * kk) * kVStride;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i16x4 lo4 = lds_read_tr16(vrow + 64 * dt);
+          const i16x4 hi4 = lds_read_tr16(vrow + 8 * kVStride + 64 * dt);
+          oacc[dt] = mfma32(cat_tr(lo4, hi4), pb, oacc[dt]);
+        }
       }
     }
-    if (!ok) continue;
-    // lane (n, h) holds dims 32*dt + 8*(i/4) + 4*h + i%4 of row n
-    const float inv = ps > 0.f ? 1.f / ps : 0.f;
-    const long long prow = (static_cast<long long>(gq) * p.topk + t) * p.Hq + head;
-    uint16_t* orow = p.o_part + prow * kD + 4 * h;
+    ps += __shfl_xor(ps, 32);
+    if (rc.ok) {
+      // lane (n, h) holds dims 32*dt + 8*(i/4) + 4*h + i%4 of row n (unnormalised).
+      // Partial block of (query, slot, KV head): [dim chunk c = 4*dt + i/4][head][8 dims],
+      // so each store instruction writes QPK * 16 contiguous bytes per query.
+      const long long pblk = ((static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hkv + hkv);
+      uint16_t* ob = p.o_part + pblk * (QPK * kD) + head_i * 8 + 4 * h;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 v2 = {pack_bf16x2(oacc[dt][4 * q4 + 0] * inv, oacc[dt][4 * q4 + 1] * inv),
-                          pack_bf16x2(oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * q4) = v2;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x2 v2 = {pack_bf16x2(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1]),
+                            pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3])};
+          *reinterpret_cast<u32x2*>(ob + (4 * dt + q4) * (QPK * 8)) = v2;
+        }
+      if (h == 0) {
+        const long long prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;
+        const float mnat = (m_ref == -INFINITY ? 0.f : m_ref) * c2 * kLn2;
+        const float lse_b = ps > 0.f ? mnat + fast_log2(ps) * kLn2 : -INFINITY;
+        p.lse_part[prow] = make_float2(lse_b, mnat);
       }
-    if (h == 0) p.lse_part[prow] = ps > 0.f ? (mx + fast_log2(ps)) * kLn2 : -INFINITY;
+    }
+    rc = rn;
   }
+}
+
+// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row
+__global__ void kv_items_kernel(const int32_t* __restrict__ row_ptr,
+                                const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
+                                int chunk_entries, int4* __restrict__ items) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long long>(Hkv) * nrows) return;
+  const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
+  const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
+  const int beg = rp[r], end = rp[r + 1];
+  int c = chunk_ptr[idx];
+  for (int e = beg; e < end; e += chunk_entries, ++c)
+    items[c] = make_int4(hkv, r, e, min(chunk_entries, end - e));
 }
 
 }  // namespace
 
+hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
+                           int chunk_entries, int4* items, hipStream_t stream) {
+  const long long n = static_cast<long long>(Hkv) * nrows;
+  hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items);
+  return hipGetLastError();
+}
+
 hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
+  if (p.chunk_entries * p.qpk > kKvChunkRows || p.chunk_entries > kKvMaxEntries)
+    return hipErrorInvalidValue;
   switch (p.qpk) {
     case 1: hipLaunchKernelGGL(kvcentric_kernel<1>, dim3(grid), dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL(kvcentric_kernel<2>, dim3(grid), dim3(256), 0, stream, p); break;

@@ -10,7 +10,7 @@
 // Layout on gfx950: the qpk heads of one row are the N = 16 columns of
 // v_mfma_f32_16x16x32_bf16 (zero-padded when qpk < 16). Each selected block
 // is streamed as four 32-token sub-tiles: K and V are fetched with 16-byte
-// loads into registers one sub-tile ahead, stored to LDS (XOR-swizzled), and
+// loads into registers one sub-tile ahead, stored to LDS (padded rows), and
 // consumed as S^T = K Q^T (K fragments by ds_read_b128) and
 // O^T += V^T P^T (V fragments by the transposing ds_read_b64_tr_b16), so each
 // head's softmax statistics stay in its own lane column. Online softmax in
@@ -31,9 +31,8 @@ constexpr int kSub = 32;  // tokens per sub-tile
 
 template <bool PAGED>
 __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSub * 256];
-  uint8_t* ks = lds;
-  uint8_t* vs = lds + kSub * 256;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[kSub * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[kSub * kVStride];
 
   const int lane = threadIdx.x;
   const int n = lane & 15;  // head column
@@ -117,8 +116,8 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
       const int row = ci >> 4, c = ci & 15;
       const bool ok = static_cast<long long>(s) * kBlk + kSub * u + row < end;
       const u32x4 z = {0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(ks + lds_chunk_off(row, c)) = ok ? kr[i] : z;
-      *reinterpret_cast<u32x4*>(vs + lds_chunk_off(row, c)) = ok ? vr[i] : z;
+      *reinterpret_cast<u32x4*>(ks + k_off(row, c)) = ok ? kr[i] : z;
+      *reinterpret_cast<u32x4*>(vs + v_off(row, c)) = ok ? vr[i] : z;
     }
   };
 
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
         const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(ks + lds_chunk_off(16 * mt + n, 4 * kq + g)));
+            as_bf16x8(*reinterpret_cast<const u32x4*>(ks + k_off(16 * mt + n, 4 * kq + g)));
         sacc[mt] = mfma16(a, qf[kq], sacc[mt]);
       }
     // lane (n, g) holds tokens 16*mt + 4*g + i of head n
@@ -174,13 +173,12 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     const u32x4 pw = {pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
                       pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
     const bf16x8 pb = as_bf16x8(pw);
-    const int r1 = 4 * g + rr, r2 = 16 + 4 * g + rr;
+    // rows 4g + rr and 16 + 4g + rr, columns 16*dt + 4*cq .. +3
+    const uint8_t* vrow = vs + (4 * g + rr) * kVStride + 8 * cq;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int c = 2 * dt + (cq >> 1);
-      const int half = (cq & 1) * 8;
-      const i16x4 lo = lds_read_tr16(vs + lds_chunk_off(r1, c) + half);
-      const i16x4 hi = lds_read_tr16(vs + lds_chunk_off(r2, c) + half);
+      const i16x4 lo = lds_read_tr16(vrow + 32 * dt);
+      const i16x4 hi = lds_read_tr16(vrow + 16 * kVStride + 32 * dt);
       oacc[dt] = mfma16(cat_tr(lo, hi), pb, oacc[dt]);
     }
   };
