@@ -31,6 +31,54 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense
 HBM_PEAK_GBS = 8000.0
 PATHS = {"auto": 0, "q": 1, "kv": 2}
+PROFILES = os.path.join(ROOT, "profiles")
+SOURCES = [os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", f) for f in
+           ("msa_api.hip", "msa_qcentric.hip", "msa_kvcentric.hip", "msa_combine.hip",
+            "msa_csr.hip", "msa_internal.hpp")]
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources: counter summaries are only reused for the same kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Pairs of hipEvent_t created through the HIP runtime (ctypes), for the
+    library's profiling hook: the library records them around its dominant
+    kernel on the launch stream."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a.value, b.value))
+
+    def mean_ms(self) -> float:
+        tot = 0.0
+        for a, b in self.pairs:
+            ms = self.ct.c_float()
+            assert self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
+            tot += ms.value
+        return tot / len(self.pairs)
+
+    def close(self) -> None:
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
 
 
 def log(msg: str) -> None:
@@ -94,30 +142,75 @@ class Case:
             self.bytes = None
         self.flops = w.effective_flops()
 
-    def time_steps(self, steps: int, warmup: int) -> float:
-        """Mean ms per step over `steps` back-to-back calls (events on the launch stream)."""
+    def time_steps(self, steps: int, warmup: int) -> tuple:
+        """(mean ms per step, mean ms of the dominant kernel) over `steps` back-to-back
+        calls; step time from events on torch's current stream (the launch stream),
+        kernel time from events the library records around its dominant kernel."""
         import torch
+        import block_sparse_attention_top_amd as msa
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
+        ev = HipEvents(steps)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
-        for _ in range(steps):
+        for i in range(steps):
+            msa.msa_set_profiling_events(*ev.pairs[i])
             self.step()
         end.record()
         end.synchronize()
+        msa.msa_set_profiling_events(None, None)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps
+        kernel_ms = ev.mean_ms()
+        ev.close()
+        return start.elapsed_time(end) / steps, kernel_ms
 
-    def metric(self, ms: float) -> dict:
+    def metric(self, ms: float, kernel_ms: float) -> dict:
         if self.w.paged:
             gbs = self.bytes / (ms * 1e-3) / 1e9
             return {"ms": ms, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                    "kernel_ms": kernel_ms,
+                    "kernel_GB_per_s": self.bytes / (kernel_ms * 1e-3) / 1e9,
                     "algorithmic_bytes": self.bytes, "path": self.path_name}
         tf = self.flops / (ms * 1e-3) / 1e12
         return {"ms": ms, "TFLOP_per_s": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                "kernel_ms": kernel_ms,
+                "kernel_TFLOP_per_s": self.flops / (kernel_ms * 1e-3) / 1e12,
                 "effective_flop": self.flops, "path": self.path_name}
+
+    def dominant_kernel(self) -> str:
+        if self.w.paged:
+            return "qcentric_kernel<true>"
+        return {"q-centric": "qcentric_kernel<false>",
+                "kv-centric": f"kvcentric_kernel<{self.w.qpk}>"}[self.path_name]
+
+
+def measured_traffic(case: "Case"):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    profiles/traffic_<workload>_<path>.json (FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy of known size), if it was taken on the current kernel sources."""
+    f = os.path.join(PROFILES, f"traffic_{case.key}_{case.path_name}.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        d = json.load(fh)
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int, reps: int = 3) -> None:
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
 def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
@@ -165,6 +258,8 @@ def main() -> int:
     ap.add_argument("--path", default="auto", choices=sorted(PATHS))
     ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -172,26 +267,34 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
     case = Case(args.workload, args.path)
     log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
         f"({case.path_name})")
-    ms = case.time_steps(args.steps, args.warmup)
-    m = case.metric(ms)
+    ms, kernel_ms = case.time_steps(args.steps, args.warmup)
+    m = case.metric(ms, kernel_ms)
     log(f"[bench] {args.workload}: {m}")
     w = case.w
+    traffic = measured_traffic(case)
     if w.paged:
         value, unit, metric = m["GB_per_s"], "GB/s", "paged sparse decode GB/s"
-        roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": m["hbm_frac"], "traffic": None}
+        ach = m["kernel_GB_per_s"]
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": traffic}
     else:
         value, unit = m["TFLOP_per_s"], "TFLOP/s"
         metric = "sparse-attn fwd effective TFLOP/s"
-        roof = {"bound": "mfma", "achieved": m["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": m["mfma_frac"], "traffic": None}
+        ach = m["kernel_TFLOP_per_s"]
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+    roof["kernel"] = case.dominant_kernel()
+    roof["kernel_ms"] = kernel_ms
     extra = {}
     for key in [k for k in args.extra.split(",") if k]:
         c = Case(key, args.path)
-        extra[key] = c.metric(c.time_steps(args.steps, args.warmup))
+        extra[key] = c.metric(*c.time_steps(args.steps, args.warmup))
         log(f"[bench] {key}: {extra[key]}")
         del c
         torch.cuda.empty_cache()

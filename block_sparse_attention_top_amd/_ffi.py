@@ -60,12 +60,19 @@ def load_library():
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P,
                                          P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
+    lib.msa_set_profiling_events.argtypes = [P, P]
+    lib.msa_set_profiling_events.restype = I
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_version.argtypes = []
     lib.msa_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def msa_set_profiling_events(before=None, after=None) -> None:
+    """Record hipEvent handles (ints) around the dominant kernel of later calls."""
+    _check(load_library().msa_set_profiling_events(before, after))
 
 
 def msa_last_error() -> str:

@@ -15,6 +15,13 @@ using namespace msa;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_prof_before = nullptr;
+thread_local hipEvent_t g_prof_after = nullptr;
+
+// records the caller's profiling event (if set) on the launch stream
+void prof_mark(hipEvent_t ev, hipStream_t st) {
+  if (ev) (void)hipEventRecord(ev, st);
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -123,6 +130,14 @@ extern "C" {
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
+int msa_set_profiling_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(MSA_ERR_INVALID_VALUE, "profiling events must both be set or both be NULL");
+  g_prof_before = static_cast<hipEvent_t>(before);
+  g_prof_after = static_cast<hipEvent_t>(after);
+  return MSA_OK;
+}
+
 const char* msa_version(void) { return "msa-gfx950 0.1.0"; }
 
 size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
@@ -172,7 +187,9 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     p.splits = 1;
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
+    prof_mark(g_prof_before, st);
     hipError_t e = launch_qcentric(p, false, st);
+    prof_mark(g_prof_after, st);
     return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric forward");
   }
 
@@ -224,7 +241,9 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   e = launch_kv_items(row_ptr, chunk_ptr, Hkv, static_cast<int>(nrows), chunk, items, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
   if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
+  prof_mark(g_prof_before, st);
   e = launch_kvcentric(p, static_cast<int>(L.max_items), st);
+  prof_mark(g_prof_after, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
   e = launch_combine_slots(p.o_part, p.lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
                            static_cast<uint16_t*>(o), lse, st);
@@ -315,7 +334,9 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(splits * rows * kD * 4));
   }
+  prof_mark(g_prof_before, st);
   hipError_t e = launch_qcentric(p, true, st);
+  prof_mark(g_prof_after, st);
   if (e != hipSuccess) return hip_fail(e, "paged forward");
   if (splits > 1) {
     e = launch_combine_splits(p.o_part, p.lse_part, B, Sq, Hq, splits, static_cast<uint16_t*>(o), lse, st);

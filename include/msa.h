@@ -20,8 +20,9 @@
  *     Every tensor is dense row-major in the stated shape, 16-byte aligned.
  *   - The caller owns all memory and the stream. The library never allocates
  *     device memory, never synchronises the stream and keeps no state
- *     between calls (beyond the thread-local error text); calls are
- *     asynchronous on `stream` (a hipStream_t, NULL = the default stream).
+ *     between calls beyond the thread-local error text and the optional
+ *     profiling events of msa_set_profiling_events; calls are asynchronous on
+ *     `stream` (a hipStream_t, NULL = the default stream).
  *   - Inputs are read only; outputs are fully overwritten; workspaces are
  *     scratch whose contents on entry do not matter.
  *   - D must be 128 and the block / page size 128; Hq / Hkv must be one of
@@ -53,7 +54,7 @@ enum msa_status {
 };
 
 enum msa_path {
-  MSA_PATH_AUTO = 0,      /* pick by qhead_per_kv */
+  MSA_PATH_AUTO = 0,      /* kv-centric for large problems, else q-centric */
   MSA_PATH_QCENTRIC = 1,  /* one fused pass per (b, hkv, q) index row */
   MSA_PATH_KVCENTRIC = 2  /* CSR-driven per-block partials + LSE merge */
 };
@@ -127,6 +128,17 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          int num_pages, int max_pages, int causal, float softmax_scale,
                          int num_splits, void* o, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling hook (for benchmarks): when both are non-NULL, every later
+ * forward call on this thread records `before` and `after` (hipEvent_t handles
+ * created by the caller) on its stream immediately around the launch of its
+ * dominant kernel -- the kv-centric per-block kernel, the q-centric kernel or
+ * the paged kernel -- so the caller can read that kernel's duration with
+ * hipEventElapsedTime. NULL, NULL switches it off. Returns MSA_OK, or
+ * MSA_ERR_INVALID_VALUE if exactly one is NULL.
+ */
+int msa_set_profiling_events(void* before, void* after);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* msa_last_error(void);

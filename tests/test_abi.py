@@ -100,3 +100,10 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(_ffi, "_LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         _ffi.load_library()
+
+
+def test_profiling_events_must_pair():
+    lib = msa.load_library()
+    assert lib.msa_set_profiling_events(FAKE, None) == 1
+    assert lib.msa_set_profiling_events(None, FAKE) == 1
+    assert lib.msa_set_profiling_events(None, None) == 0
