@@ -129,11 +129,9 @@ class Case:
                 causal=w.causal, o=self.o, lse=self.lse, workspace=ws)
             self.bytes = decode_algorithmic_bytes(w, self.inp)
         else:
-            p = PATHS[path]
+            p = msa.msa_sparse_fwd_path(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.topk, PATHS[path])
             nb = msa.msa_sparse_fwd_workspace_size(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, w.topk,
                                                    w.blk, p)
-            if p == 0:  # the library's automatic choice: kv-centric iff it needs a workspace
-                p = 2 if nb > 0 else 1
             self.path_name = {1: "q-centric", 2: "kv-centric"}[p]
             ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
             self.step = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"],

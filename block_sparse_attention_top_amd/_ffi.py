@@ -48,6 +48,8 @@ def load_library():
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.msa_sparse_fwd_workspace_size.argtypes = [I] * 9
     lib.msa_sparse_fwd_workspace_size.restype = S
+    lib.msa_sparse_fwd_path.argtypes = [I] * 7
+    lib.msa_sparse_fwd_path.restype = I
     lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, P, P,
                                    S, P]
     lib.msa_sparse_fwd.restype = I
@@ -129,6 +131,10 @@ def msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv=128,
                                   path=MSA_PATH_AUTO) -> int:
     return int(load_library().msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv,
                                                             path))
+
+
+def msa_sparse_fwd_path(B, Sq, Skv, Hq, Hkv, topk, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_sparse_fwd_path(B, Sq, Skv, Hq, Hkv, topk, path))
 
 
 def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None, *,

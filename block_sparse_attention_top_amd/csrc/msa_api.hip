@@ -140,6 +140,10 @@ int msa_set_profiling_events(void* before, void* after) {
 
 const char* msa_version(void) { return "msa-gfx950 0.1.0"; }
 
+int msa_sparse_fwd_path(int B, int Sq, int Skv, int Hq, int Hkv, int topk, int path) {
+  return resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
+}
+
 size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
                                      int blk_kv, int path) {
   if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
@@ -238,6 +242,7 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
   int4* items = reinterpret_cast<int4*>(ws + L.items);
   p.items = items;
+
   e = launch_kv_items(row_ptr, chunk_ptr, Hkv, static_cast<int>(nrows), chunk, items, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
   if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");

@@ -195,19 +195,41 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
       }
     }
     ps += __shfl_xor(ps, 32);
+    // lane (n, h) holds dims 32*dt + 8*q4 + 4*h .. +3 of row n (unnormalised) as
+    // bf16 pairs. Swapping the odd-q4 half of lane h=0 with the even-q4 half of
+    // lane h=1 (v_permlane32_swap) leaves each lane 16 contiguous bytes:
+    // dims 32*dt + 16*pp + 8*h .. +7.
+    uint32_t ow[4][4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        ow[dt][q4][0] = pack_bf16x2(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1]);
+        ow[dt][q4][1] = pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
+      }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(ow[dt][2 * pp][w2], ow[dt][2 * pp + 1][w2],
+                                                           false, false);
+          ow[dt][2 * pp][w2] = sw[0];
+          ow[dt][2 * pp + 1][w2] = sw[1];
+        }
     if (rc.ok) {
-      // lane (n, h) holds dims 32*dt + 8*(i/4) + 4*h + i%4 of row n (unnormalised).
-      // Partial block of (query, slot, KV head): [dim chunk c = 4*dt + i/4][head][8 dims],
-      // so each store instruction writes QPK * 16 contiguous bytes per query.
+      // Partial block of (query, slot, KV head): [dim chunk c][head][8 dims] with
+      // c = dims / 8, so one store instruction writes QPK * 32 contiguous bytes per query.
       const long long pblk = ((static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hkv + hkv);
-      uint16_t* ob = p.o_part + pblk * (QPK * kD) + head_i * 8 + 4 * h;
+      uint16_t* ob = p.o_part + pblk * (QPK * kD) + head_i * 8;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const u32x2 v2 = {pack_bf16x2(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1]),
-                            pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3])};
-          *reinterpret_cast<u32x2*>(ob + (4 * dt + q4) * (QPK * 8)) = v2;
+        for (int pp = 0; pp < 2; ++pp) {
+          const u32x4 v4 = {ow[dt][2 * pp][0], ow[dt][2 * pp][1], ow[dt][2 * pp + 1][0],
+                            ow[dt][2 * pp + 1][1]};
+          *reinterpret_cast<u32x4*>(ob + (4 * dt + 2 * pp + h) * (QPK * 8)) = v4;
         }
       if (h == 0) {
         const long long prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;

@@ -56,7 +56,7 @@ enum msa_status {
 enum msa_path {
   MSA_PATH_AUTO = 0,      /* kv-centric for large problems, else q-centric */
   MSA_PATH_QCENTRIC = 1,  /* one fused pass per (b, hkv, q) index row */
-  MSA_PATH_KVCENTRIC = 2  /* CSR-driven per-block partials + LSE merge */
+  MSA_PATH_KVCENTRIC = 2  /* CSR-driven per-block partials + LSE merge kernel */
 };
 
 /*
@@ -77,6 +77,9 @@ enum msa_path {
  */
 size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
                                      int blk_kv, int path);
+/* The path msa_sparse_fwd takes for these sizes when given `path` (resolves
+ * MSA_PATH_AUTO; other values are returned unchanged). */
+int msa_sparse_fwd_path(int B, int Sq, int Skv, int Hq, int Hkv, int topk, int path);
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
                    const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
                    int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,

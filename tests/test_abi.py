@@ -107,3 +107,12 @@ def test_profiling_events_must_pair():
     assert lib.msa_set_profiling_events(FAKE, None) == 1
     assert lib.msa_set_profiling_events(None, FAKE) == 1
     assert lib.msa_set_profiling_events(None, None) == 0
+
+
+def test_auto_path_resolution():
+    # small problems take the q-centric path, large ones the kv-centric path
+    assert msa.msa_sparse_fwd_path(1, 1024, 1024, 2, 1, 4, 0) == 1
+    assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 0) == 2
+    # more CSR rows than the kv-centric passes hold -> q-centric
+    assert msa.msa_sparse_fwd_path(1, 8192, 128 * 20000, 64, 4, 16, 0) == 1
+    assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 1) == 1

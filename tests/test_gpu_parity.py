@@ -11,7 +11,7 @@ from parity_util import (compare, full_compare, run_contiguous, run_paged, sampl
 
 pytestmark = pytest.mark.gpu
 
-Q, KV = 1, 2  # paths
+Q, KV = 1, 2  # paths: q-centric, kv-centric
 
 
 def contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal, mode, seed=42):
