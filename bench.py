@@ -13,7 +13,9 @@ Metrics (the pages' benchmark harness, "test_sparse_atten.py"):
            (sequence, KV head) * 64 KiB + Q + O + LSE + q2k + page table
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
-                       [--path auto|q|kv] [--extra c5,c3u] [--no-cpu-baseline]
+                       [--path auto|q|kv|decode] [--splits N] [--extra c5,c3u]
+                       [--no-cpu-baseline]
+(--extra workloads run with the automatic path)
 """
 from __future__ import annotations
 
@@ -30,11 +32,11 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense
 HBM_PEAK_GBS = 8000.0
-PATHS = {"auto": 0, "q": 1, "kv": 2}
+PATHS = {"auto": 0, "q": 1, "kv": 2, "decode": 3, "tile": 4}
 PROFILES = os.path.join(ROOT, "profiles")
 SOURCES = [os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", f) for f in
            ("msa_api.hip", "msa_qcentric.hip", "msa_kvcentric.hip", "msa_combine.hip",
-            "msa_csr.hip", "msa_internal.hpp")]
+            "msa_csr.hip", "msa_decode.hip", "msa_tile.hip", "msa_internal.hpp")]
 
 
 def source_digest() -> str:
@@ -104,7 +106,7 @@ def decode_algorithmic_bytes(w, inp) -> int:
 class Case:
     """One workload uploaded to the GPU with a callable that runs one step."""
 
-    def __init__(self, key: str, path: str):
+    def __init__(self, key: str, path: str, splits: int = 0):
         import torch
         import block_sparse_attention_top_amd as msa
         import workloads as wl
@@ -120,19 +122,25 @@ class Case:
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
         t = self.t
         if w.paged:
+            p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, PATHS[path])
+            if p not in (1, 3):
+                raise SystemExit(f"path {path} does not apply to the paged workload {key}")
             nb = msa.msa_paged_sparse_fwd_workspace_size(w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk,
-                                                        w.blk, w.max_pages, 0)
+                                                        w.blk, w.max_pages, splits, p)
             ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
-            self.path_name = "paged-split"
+            self.path_name = {1: "paged-qcentric", 3: "paged-decode"}[p]
+            self.splits = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, splits, p)
             self.step = lambda: msa.msa_paged_sparse_fwd(
                 t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"],
-                causal=w.causal, o=self.o, lse=self.lse, workspace=ws)
+                causal=w.causal, num_splits=splits, path=p, o=self.o, lse=self.lse,
+                workspace=ws)
             self.bytes = decode_algorithmic_bytes(w, self.inp)
         else:
             p = msa.msa_sparse_fwd_path(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.topk, PATHS[path])
             nb = msa.msa_sparse_fwd_workspace_size(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, w.topk,
                                                    w.blk, p)
-            self.path_name = {1: "q-centric", 2: "kv-centric"}[p]
+            self.path_name = {1: "q-centric", 2: "kv-centric", 4: "query-tile"}[p]
+            self.splits = 1
             ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
             self.step = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"],
                                                    causal=w.causal, path=p, o=self.o,
@@ -170,7 +178,8 @@ class Case:
             return {"ms": ms, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                     "kernel_ms": kernel_ms,
                     "kernel_GB_per_s": self.bytes / (kernel_ms * 1e-3) / 1e9,
-                    "algorithmic_bytes": self.bytes, "path": self.path_name}
+                    "algorithmic_bytes": self.bytes, "path": self.path_name,
+                    "splits": self.splits}
         tf = self.flops / (ms * 1e-3) / 1e12
         return {"ms": ms, "TFLOP_per_s": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
                 "kernel_ms": kernel_ms,
@@ -179,9 +188,11 @@ class Case:
 
     def dominant_kernel(self) -> str:
         if self.w.paged:
-            return "qcentric_kernel<true>"
+            return {"paged-qcentric": "qcentric_kernel<true>",
+                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}>"}[self.path_name]
         return {"q-centric": "qcentric_kernel<false>",
-                "kv-centric": f"kvcentric_kernel<{self.w.qpk}>"}[self.path_name]
+                "kv-centric": f"kvcentric_kernel<{self.w.qpk}>",
+                "query-tile": "tile_kernel"}[self.path_name]
 
 
 def measured_traffic(case: "Case"):
@@ -254,6 +265,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS))
+    ap.add_argument("--splits", type=int, default=0,
+                    help="KV splits of the paged workload (0 = the library's choice)")
     ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -268,7 +281,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
-    case = Case(args.workload, args.path)
+    case = Case(args.workload, args.path, args.splits)
     log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
         f"({case.path_name})")
     ms, kernel_ms = case.time_steps(args.steps, args.warmup)
@@ -291,7 +304,7 @@ def main() -> int:
     roof["kernel_ms"] = kernel_ms
     extra = {}
     for key in [k for k in args.extra.split(",") if k]:
-        c = Case(key, args.path)
+        c = Case(key, "auto")
         extra[key] = c.metric(*c.time_steps(args.steps, args.warmup))
         log(f"[bench] {key}: {extra[key]}")
         del c
@@ -307,7 +320,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
-                   "causal": w.causal, "path": case.path_name, "parallelism": "none"},
+                   "causal": w.causal, "path": case.path_name, "splits": case.splits,
+                   "parallelism": "none"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -8,17 +8,20 @@ fallback: if libmsa.so is missing or the GPU is absent the calls raise.
 """
 from __future__ import annotations
 
-from ._ffi import (MSA_PATH_AUTO, MSA_PATH_KVCENTRIC, MSA_PATH_QCENTRIC, MsaError,
-                   MsaNotSupportedError, MsaValueError, lib_path, load_library,
+from ._ffi import (MSA_PATH_AUTO, MSA_PATH_DECODE, MSA_PATH_KVCENTRIC, MSA_PATH_QCENTRIC,
+                   MSA_PATH_TILE,
+                   MsaError, MsaNotSupportedError, MsaValueError, lib_path, load_library,
                    msa_build_k2q_csr, msa_build_k2q_csr_workspace_size, msa_last_error,
-                   msa_paged_sparse_fwd, msa_paged_sparse_fwd_workspace_size, msa_sparse_fwd,
-                   msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_set_profiling_events,
-                   msa_version)
+                   msa_paged_sparse_fwd, msa_paged_sparse_fwd_path, msa_paged_sparse_fwd_splits,
+                   msa_paged_sparse_fwd_workspace_size, msa_set_profiling_events, msa_sparse_fwd,
+                   msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_version)
 
 __all__ = [
-    "MSA_PATH_AUTO", "MSA_PATH_QCENTRIC", "MSA_PATH_KVCENTRIC", "MsaError", "MsaValueError",
-    "MsaNotSupportedError", "lib_path", "load_library", "msa_sparse_fwd",
-    "msa_sparse_fwd_path", "msa_sparse_fwd_workspace_size", "msa_build_k2q_csr", "msa_build_k2q_csr_workspace_size",
-    "msa_paged_sparse_fwd", "msa_paged_sparse_fwd_workspace_size", "msa_last_error",
+    "MSA_PATH_AUTO", "MSA_PATH_QCENTRIC", "MSA_PATH_KVCENTRIC", "MSA_PATH_DECODE",
+    "MSA_PATH_TILE", "MsaError",
+    "MsaValueError", "MsaNotSupportedError", "lib_path", "load_library", "msa_sparse_fwd",
+    "msa_sparse_fwd_path", "msa_sparse_fwd_workspace_size", "msa_build_k2q_csr",
+    "msa_build_k2q_csr_workspace_size", "msa_paged_sparse_fwd", "msa_paged_sparse_fwd_path",
+    "msa_paged_sparse_fwd_splits", "msa_paged_sparse_fwd_workspace_size", "msa_last_error",
     "msa_set_profiling_events", "msa_version",
 ]

@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_VALUE, MSA_ERR_NOT_SUPPORTED, MSA_ERR_HIP = 0, 1, 2, 3
-MSA_PATH_AUTO, MSA_PATH_QCENTRIC, MSA_PATH_KVCENTRIC = 0, 1, 2
+MSA_PATH_AUTO, MSA_PATH_QCENTRIC, MSA_PATH_KVCENTRIC, MSA_PATH_DECODE, MSA_PATH_TILE = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -57,10 +57,14 @@ def load_library():
     lib.msa_build_k2q_csr_workspace_size.restype = S
     lib.msa_build_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P, P, S, P]
     lib.msa_build_k2q_csr.restype = I
-    lib.msa_paged_sparse_fwd_workspace_size.argtypes = [I] * 9
+    lib.msa_paged_sparse_fwd_workspace_size.argtypes = [I] * 10
     lib.msa_paged_sparse_fwd_workspace_size.restype = S
-    lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P,
-                                         P, P, S, P]
+    lib.msa_paged_sparse_fwd_path.argtypes = [I] * 5
+    lib.msa_paged_sparse_fwd_path.restype = I
+    lib.msa_paged_sparse_fwd_splits.argtypes = [I] * 6
+    lib.msa_paged_sparse_fwd_splits.restype = I
+    lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
+                                         P, P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
     lib.msa_set_profiling_events.argtypes = [P, P]
     lib.msa_set_profiling_events.restype = I
@@ -191,15 +195,24 @@ def msa_build_k2q_csr(q2k, num_kv_blocks: int, *, row_ptr=None, q_idx=None, slot
 
 
 def msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size, max_pages,
-                                        num_splits=0) -> int:
+                                        num_splits=0, path=MSA_PATH_AUTO) -> int:
     return int(load_library().msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk,
                                                                   page_size, max_pages,
-                                                                  num_splits))
+                                                                  num_splits, path))
+
+
+def msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, path))
+
+
+def msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, num_splits=0, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, num_splits, path))
 
 
 def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,
-                         softmax_scale: float = 0.0, num_splits: int = 0, o=None, lse=None,
-                         workspace=None, stream=None):
+                         softmax_scale: float = 0.0, num_splits: int = 0,
+                         path: int = MSA_PATH_AUTO, o=None, lse=None, workspace=None,
+                         stream=None):
     """Sparse forward through a page table. Returns (O, LSE) as msa_sparse_fwd."""
     lib = load_library()
     _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
@@ -215,12 +228,12 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
     nbytes = int(lib.msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size,
-                                                         max_pages, num_splits))
+                                                         max_pages, num_splits, path))
     ws, wsn = _workspace(nbytes, q.device, workspace)
     rc = lib.msa_paged_sparse_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                                   _ptr(seqused_k), _ptr(q2k), B, Sq, Hq, Hkv, D, topk, page_size,
                                   num_pages, max_pages, int(bool(causal)), float(softmax_scale),
-                                  int(num_splits), _ptr(o), _ptr(lse), _ptr(ws), wsn,
+                                  int(num_splits), int(path), _ptr(o), _ptr(lse), _ptr(ws), wsn,
                                   _stream(stream))
     _check(rc)
     return o, lse

@@ -64,7 +64,7 @@ int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
 // problems with more CSR rows than the LDS-resident CSR passes take the
 // q-centric path.
 int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
-  if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC) return path;
+  if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC || path == MSA_PATH_TILE) return path;
   const long long nrows = static_cast<long long>(B) * (Skv / kBlk);
   const long long work = static_cast<long long>(B) * Sq * Hq * topk;  // (query, head, slot) triples
   if (nrows > kMaxCsrRows || work < (1LL << 20)) return MSA_PATH_QCENTRIC;
@@ -104,11 +104,49 @@ KvLayout kv_layout(int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   return L;
 }
 
-int auto_splits(int B, int Sq, int Hkv, int topk) {
-  const long long rows = static_cast<long long>(B) * Hkv * Sq;
-  long long s = (4096 + rows - 1) / rows;
-  s = std::max<long long>(1, std::min<long long>(s, std::min(topk, 8)));
-  return static_cast<int>(s);
+// Paged plan: which kernel and how many KV splits. MSA_PATH_AUTO takes the
+// q-centric kernel: on the 32 x 8-query decode workload with random per-query
+// blocks it measured faster than the union (decode) kernel, which reads each
+// distinct block of a (b, hkv) once and pays off when the Sq index rows share
+// blocks; the caller asks for it explicitly. The decode kernel splits the union
+// into `splits` contiguous shares; the q-centric kernel splits each index row's
+// slots. Automatic splits aim at about three workgroups per compute unit
+// (decode) or about 1024 single-wave workgroups (q-centric: on the 32 x 8 x 4
+// decode workload one split, 1024 waves, measured fastest; 2, 4 and 8 splits
+// were 5-15% slower and add the combine pass).
+struct PagedPlan {
+  int path;
+  int splits;
+};
+
+PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int num_splits, int path) {
+  PagedPlan pl;
+  if (path == MSA_PATH_AUTO) path = MSA_PATH_QCENTRIC;
+  pl.path = path;
+  if (path == MSA_PATH_DECODE) {
+    const long long cap = std::min<long long>(static_cast<long long>(Sq) * topk, kMaxDecodeSplits);
+    long long s = num_splits;
+    if (s <= 0) {
+      const long long pairs = static_cast<long long>(B) * Hkv;
+      s = (3LL * device_cu_count() + pairs - 1) / pairs;
+    }
+    pl.splits = static_cast<int>(std::max<long long>(1, std::min(s, cap)));
+  } else {
+    long long s = num_splits;
+    if (s <= 0) {
+      const long long rows = static_cast<long long>(B) * Hkv * Sq;
+      s = (1024 + rows - 1) / rows;
+      s = std::min<long long>(s, 8);
+    }
+    pl.splits = static_cast<int>(std::max<long long>(1, std::min<long long>(s, topk)));
+  }
+  return pl;
+}
+
+size_t paged_workspace(int B, int Sq, int Hq, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * Sq * Hq;
+  return align256(splits * rows * kD * 4) + align256(splits * rows * 4);
 }
 
 }  // namespace
@@ -149,7 +187,8 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
   if (B <= 0 || Sq <= 0 || Skv <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
       blk_kv != kBlk || Skv % kBlk || Hq % Hkv)
     return 0;
-  if (resolve_path(path, B, Sq, Skv, Hq, Hkv, topk) == MSA_PATH_QCENTRIC) return 0;
+  const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
+  if (which == MSA_PATH_QCENTRIC || which == MSA_PATH_TILE) return 0;
   return kv_layout(B, Sq, Skv, Hq, Hkv, topk).total;
 }
 
@@ -168,7 +207,8 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(q2k, 4) || !aligned(lse, 4))
     return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
-  if (path < MSA_PATH_AUTO || path > MSA_PATH_KVCENTRIC)
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_KVCENTRIC &&
+      path != MSA_PATH_TILE)
     return fail(MSA_ERR_INVALID_VALUE, "unknown path %d", path);
   const bool have_csr = csr_row_ptr || csr_q_idx || csr_slot;
   if (have_csr && !(csr_row_ptr && csr_q_idx && csr_slot))
@@ -178,6 +218,27 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
+
+  if (which == MSA_PATH_TILE) {
+    if (!tile_supported(qpk, topk))
+      return fail(MSA_ERR_NOT_SUPPORTED,
+                  "query-tile path needs qhead_per_kv 8 or 16 and (256 / qhead_per_kv) * topk "
+                  "<= %d (got qhead_per_kv %d, topk %d)", kTileMaxEntries, qpk, topk);
+    TileParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.q2k = q2k;
+    p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+    p.nblk = nblk; p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    prof_mark(g_prof_before, st);
+    hipError_t e = launch_tile(p, st);
+    prof_mark(g_prof_after, st);
+    return e == hipSuccess ? MSA_OK : hip_fail(e, "query-tile forward");
+  }
 
   if (which == MSA_PATH_QCENTRIC) {
     QcParams p{};
@@ -284,22 +345,31 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
   return e == hipSuccess ? MSA_OK : hip_fail(e, "k2q CSR build");
 }
 
+int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path) {
+  if (path != MSA_PATH_AUTO) return path;
+  return paged_plan(B, Sq, Hkv, topk, 0, path).path;
+}
+
+int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int num_splits, int path) {
+  if (B <= 0 || Sq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < 0) return 0;
+  return paged_plan(B, Sq, Hkv, topk, num_splits, path).splits;
+}
+
 size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
-                                           int page_size, int max_pages, int num_splits) {
+                                           int page_size, int max_pages, int num_splits,
+                                           int path) {
   if (B <= 0 || Sq <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD || page_size != kBlk ||
-      max_pages <= 0 || Hq % Hkv)
+      max_pages <= 0 || Hq % Hkv || num_splits < 0)
     return 0;
-  const int splits = num_splits > 0 ? std::min(num_splits, topk) : auto_splits(B, Sq, Hkv, topk);
-  if (splits <= 1) return 0;
-  const size_t rows = static_cast<size_t>(B) * Sq * Hq;
-  return align256(splits * rows * kD * 4) + align256(splits * rows * 4);
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE) return 0;
+  return paged_workspace(B, Sq, Hq, paged_plan(B, Sq, Hkv, topk, num_splits, path).splits);
 }
 
 int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, void* o, float* lse, void* workspace,
+                         int num_splits, int path, void* o, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_common(B, Sq, Hq, Hkv, D, topk, page_size);
@@ -312,7 +382,14 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
       !aligned(q2k, 4) || !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seqused_k, 4))
     return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
   if (num_splits < 0) return fail(MSA_ERR_INVALID_VALUE, "num_splits must be >= 0");
-  const int splits = num_splits > 0 ? std::min(num_splits, topk) : auto_splits(B, Sq, Hkv, topk);
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE)
+    return fail(MSA_ERR_INVALID_VALUE, "unknown paged path %d", path);
+  if (path == MSA_PATH_DECODE && !paged_decode_supported(Sq, topk))
+    return fail(MSA_ERR_NOT_SUPPORTED,
+                "decode path needs Sq <= %d and Sq * topk <= %d (got Sq %d, topk %d)",
+                4 * kMaxQPerWave, kDecMaxEntries, Sq, topk);
+  const PagedPlan plan = paged_plan(B, Sq, Hkv, topk, num_splits, path);
+  const int splits = plan.splits;
   const int qpk = Hq / Hkv;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -331,16 +408,17 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   if (splits > 1) {
-    const size_t rows = static_cast<size_t>(B) * Sq * Hq;
-    const size_t need = align256(splits * rows * kD * 4) + align256(splits * rows * 4);
+    const size_t need = paged_workspace(B, Sq, Hq, splits);
     if (!workspace || workspace_bytes < need)
       return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+    const size_t rows = static_cast<size_t>(B) * Sq * Hq;
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(splits * rows * kD * 4));
   }
   prof_mark(g_prof_before, st);
-  hipError_t e = launch_qcentric(p, true, st);
+  hipError_t e = plan.path == MSA_PATH_DECODE ? launch_paged_decode(p, st)
+                                              : launch_qcentric(p, true, st);
   prof_mark(g_prof_after, st);
   if (e != hipSuccess) return hip_fail(e, "paged forward");
   if (splits > 1) {

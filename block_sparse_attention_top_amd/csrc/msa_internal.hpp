@@ -13,6 +13,12 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxCsrRows = 16384;  // B * num_kv_blocks: the CSR passes keep one int per row in LDS
 constexpr int kKvChunkRows = 2048;  // (query, head) rows per kv-centric work item
 constexpr int kKvMaxEntries = 512;  // CSR entries per kv-centric work item (LDS bound)
+constexpr int kDecMaxEntries = 512; // Sq * topk index entries per paged decode workgroup
+constexpr int kDecPasses = kDecMaxEntries / 256;
+constexpr int kMaxQPerWave = 4;     // query rows per wave in the paged decode kernel (Sq <= 16)
+constexpr int kMaxDecodeSplits = 64;
+constexpr int kTileMaxQ = 32;       // queries per workgroup in the query-tile kernel (qpk 8)
+constexpr int kTileMaxEntries = 512;  // index entries (queries x topk) per query tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -114,6 +120,27 @@ struct QcParams {
   float* lse_part;           // [splits][B*Sq][Hq]
 };
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream);
+// paged decode over the union of the blocks of each (b, hkv): splits partition that
+// union; needs Sq <= 4 * kMaxQPerWave and Sq * topk <= kDecMaxEntries
+bool paged_decode_supported(int Sq, int topk);
+hipError_t launch_paged_decode(const QcParams& p, hipStream_t stream);
+
+// query-tile kernel (contiguous K/V): a workgroup per 256 / qpk consecutive
+// queries of one (b, hkv), streaming the union of their selected blocks once
+struct TileParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q2k;
+  int B, Sq, Skv, Hq, Hkv, qpk, topk, nblk, causal;
+  float scale_log2;
+  uint16_t* o;
+  float* lse;
+  int ntiles;     // set by the launcher
+  int xcd_pairs;  // set by the launcher: (b, hkv) pairs mapped onto XCD groups
+};
+bool tile_supported(int qpk, int topk);  // qpk 8 or 16, tile queries x topk <= 512
+hipError_t launch_tile(TileParams p, hipStream_t stream);
 
 struct KvParams {
   const uint16_t* q;

@@ -56,7 +56,14 @@ enum msa_status {
 enum msa_path {
   MSA_PATH_AUTO = 0,      /* kv-centric for large problems, else q-centric */
   MSA_PATH_QCENTRIC = 1,  /* one fused pass per (b, hkv, q) index row */
-  MSA_PATH_KVCENTRIC = 2  /* CSR-driven per-block partials + LSE merge kernel */
+  MSA_PATH_KVCENTRIC = 2, /* CSR-driven per-block partials + LSE merge kernel */
+  MSA_PATH_DECODE = 3,    /* paged only: one pass over the union of the blocks that
+                             the Sq index rows of a (b, hkv) select, each block
+                             read once; needs Sq <= 16 and Sq * topk <= 512 */
+  MSA_PATH_TILE = 4       /* contiguous only: a workgroup per tile of consecutive
+                             queries of one (b, hkv) streams the union of their
+                             blocks once (for selections where many nearby queries
+                             share blocks) */
 };
 
 /*
@@ -118,18 +125,32 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
  *               are masked and never influence the result)
  *   q2k         int32 [B, Hkv, Sq, topk], valid ids [0, max_pages)
  *   causal      bottom-right with the limit q + seqused_k[b] - Sq
- *   num_splits  0 = automatic; else split each index row's blocks into that
- *               many partial passes merged by log-sum-exp (1..topk)
+ *   num_splits  0 = automatic; else the number of KV splits, each a partial pass
+ *               merged afterwards by log-sum-exp. q-centric: each index row's
+ *               slots are split (clamped to 1..topk); decode: the union of the
+ *               blocks of a (b, hkv) is split (clamped to 1..min(Sq*topk, 64))
+ *   path        MSA_PATH_AUTO (= MSA_PATH_QCENTRIC), MSA_PATH_QCENTRIC or
+ *               MSA_PATH_DECODE (reads each distinct block of a (b, hkv) once: for
+ *               index rows that share blocks; MSA_ERR_NOT_SUPPORTED when
+ *               Sq > 16 or Sq * topk > 512)
  *   o, lse      as msa_sparse_fwd
- *   workspace   at least msa_paged_sparse_fwd_workspace_size(...)
+ *   workspace   at least msa_paged_sparse_fwd_workspace_size(...) with the same
+ *               num_splits and path (zero when one split results)
+ * Duplicate ids within one index row: the decode path counts each block once;
+ * the q-centric path requires distinct ids.
  */
 size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
-                                           int page_size, int max_pages, int num_splits);
+                                           int page_size, int max_pages, int num_splits,
+                                           int path);
+/* The kernel msa_paged_sparse_fwd runs for these sizes (resolves MSA_PATH_AUTO)
+ * and the number of splits it uses (0 for invalid sizes). */
+int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path);
+int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int num_splits, int path);
 int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, void* o, float* lse, void* workspace,
+                         int num_splits, int path, void* o, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /*
@@ -137,7 +158,7 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
  * forward call on this thread records `before` and `after` (hipEvent_t handles
  * created by the caller) on its stream immediately around the launch of its
  * dominant kernel -- the kv-centric per-block kernel, the q-centric kernel or
- * the paged kernel -- so the caller can read that kernel's duration with
+ * the paged (q-centric or decode) kernel -- so the caller can read that kernel's duration with
  * hipEventElapsedTime. NULL, NULL switches it off. Returns MSA_OK, or
  * MSA_ERR_INVALID_VALUE if exactly one is NULL.
  */

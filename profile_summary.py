@@ -84,10 +84,12 @@ def main() -> int:
     durs = kernel_durations(args.trace)
     w = wl.WORKLOADS[args.workload]
     if w.paged:
-        dom = "qcentric_kernel<true>"
+        dom = {"paged-qcentric": "qcentric_kernel<true>",
+               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}>"}[args.path]
     else:
         dom = {"q-centric": "qcentric_kernel<false>",
-               "kv-centric": f"kvcentric_kernel<{w.qpk}>"}[args.path]
+               "kv-centric": f"kvcentric_kernel<{w.qpk}>",
+               "query-tile": "tile_kernel"}[args.path]
     lines = [f"# Kernel profile: {w.name}, {args.path} path", ""]
     if args.commands:
         lines += ["Commands (run from the repository root on one MI355X):", "", "```"]

@@ -61,12 +61,14 @@ def run_contiguous(inp: dict, causal: bool, path: int, softmax_scale: float = 0.
     return o, lse
 
 
-def run_paged(inp: dict, causal: bool, num_splits: int = 0, softmax_scale: float = 0.0):
+def run_paged(inp: dict, causal: bool, num_splits: int = 0, softmax_scale: float = 0.0,
+              path: int = 0):
     import block_sparse_attention_top_amd as msa
     t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k", "q2k")}
     o, lse = msa.msa_paged_sparse_fwd(t["q"], t["k_pool"], t["v_pool"], t["page_table"],
                                       t["seqused_k"], t["q2k"], causal=causal,
-                                      num_splits=num_splits, softmax_scale=softmax_scale)
+                                      num_splits=num_splits, softmax_scale=softmax_scale,
+                                      path=path)
     torch.cuda.synchronize()
     return o, lse
 

@@ -69,9 +69,18 @@ def test_workspace_queries():
     assert msa.msa_sparse_fwd_workspace_size(1, 1024, 1000, 64, 4, 128, 16, 128, 2) == 0
     assert msa.msa_build_k2q_csr_workspace_size(1, 4, 8192, 16, 64) > 0
     # paged: one split needs no workspace, several need fp32 partials
-    assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 1) == 0
-    assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 4) >= \
-        4 * 32 * 8 * 64 * 128 * 4
+    for path in (0, 1, 3):
+        assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 1,
+                                                       path) == 0
+        assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 4,
+                                                       path) >= 4 * 32 * 8 * 64 * 128 * 4
+    # the decode kernel splits the union of a (b, hkv)'s blocks: up to min(Sq*topk, 64) splits
+    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 100, 3) == 64
+    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 100, 1) == 16
+    assert msa.msa_paged_sparse_fwd_splits(1, 1, 1, 4, 0, 3) == 4
+    assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 64, 3) >= \
+        64 * 8 * 16 * 128 * 4
+    assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 4, 2) == 0
 
 
 def test_csr_and_paged_reject():
@@ -81,17 +90,23 @@ def test_csr_and_paged_reject():
     assert lib.msa_build_k2q_csr(FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, None, None, 0, None) == 1
     assert lib.msa_build_k2q_csr(None, 1, 1, 16, 4, 8, FAKE, FAKE, None, FAKE, 1 << 20,
                                  None) == 1
-    # paged: page_size != 128, missing seqused_k, forced splits without workspace
-    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, FAKE, FAKE, None, 0,
-                         None]
+    # paged: page_size != 128, missing seqused_k, forced splits without workspace,
+    # negative splits, unknown or kv-centric path, decode path with Sq > 16
+    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, 0, FAKE, FAKE, None,
+                         0, None]
     a = list(args); a[12] = 64
     assert lib.msa_paged_sparse_fwd(*a) == 2
     a = list(args); a[4] = None
     assert lib.msa_paged_sparse_fwd(*a) == 1
-    a = list(args); a[17] = 4
-    assert lib.msa_paged_sparse_fwd(*a) == 1
+    for path in (0, 1, 3):
+        a = list(args); a[17] = 4; a[18] = path
+        assert lib.msa_paged_sparse_fwd(*a) == 1
     a = list(args); a[17] = -1
     assert lib.msa_paged_sparse_fwd(*a) == 1
+    a = list(args); a[18] = 2
+    assert lib.msa_paged_sparse_fwd(*a) == 1
+    a = list(args); a[18] = 3; a[7] = 17
+    assert lib.msa_paged_sparse_fwd(*a) == 2
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):
@@ -116,3 +131,9 @@ def test_auto_path_resolution():
     # more CSR rows than the kv-centric passes hold -> q-centric
     assert msa.msa_sparse_fwd_path(1, 8192, 128 * 20000, 64, 4, 16, 0) == 1
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 1) == 1
+    # paged: automatic is the q-centric kernel; the decode kernel is asked for
+    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16, 3) == msa.MSA_PATH_DECODE
+    assert msa.msa_paged_sparse_fwd_splits(32, 8, 4, 16) == 1
+    # contiguous: the query tile is asked for
+    assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 4) == msa.MSA_PATH_TILE

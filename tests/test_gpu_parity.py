@@ -11,13 +11,24 @@ from parity_util import (compare, full_compare, run_contiguous, run_paged, sampl
 
 pytestmark = pytest.mark.gpu
 
-Q, KV = 1, 2  # paths: q-centric, kv-centric
+Q, KV, TILE = 1, 2, 4  # paths: q-centric, kv-centric, query-tile
 
 
 def contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal, mode, seed=42):
     w = wl.Workload("case", B=B, Sq=Sq, Skv=Skv, Hkv=Hkv, qpk=qpk, topk=topk, causal=causal,
                     mode=mode, seed=seed)
     return w, wl.make_inputs(w)
+
+
+def tile_ok(qpk, topk):
+    """Shapes the query-tile kernel takes: qpk 8 or 16, (256 / qpk) * topk <= 512."""
+    return qpk in (8, 16) and (256 // qpk) * topk <= 512
+
+
+def expect_not_supported(inp, causal, path):
+    import block_sparse_attention_top_amd as msa
+    with pytest.raises(msa.MsaNotSupportedError):
+        run_contiguous(inp, causal, path)
 
 
 def check_contiguous(w, inp, path, label, softmax_scale=0.0):
@@ -30,7 +41,7 @@ def check_contiguous(w, inp, path, label, softmax_scale=0.0):
     return full_compare(o, lse, o_ref, lse_ref, label), (o, lse)
 
 
-@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("path", [Q, KV, TILE])
 @pytest.mark.parametrize("name,B,Sq,Skv,Hkv,qpk,topk,causal,mode", [
     ("c1-full", 1, 1024, 1024, 1, 2, 4, False, wl.MODE_PERM),
     ("c2-small", 1, 1152, 1152, 2, 16, 8, True, wl.MODE_CAUSAL),
@@ -45,17 +56,23 @@ def check_contiguous(w, inp, path, label, softmax_scale=0.0):
 ])
 def test_contiguous_small(path, name, B, Sq, Skv, Hkv, qpk, topk, causal, mode):
     w, inp = contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal, mode)
+    if path == TILE and not tile_ok(qpk, topk):
+        expect_not_supported(inp, causal, path)
+        return
     check_contiguous(w, inp, path, name)
 
 
-@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("path", [Q, KV, TILE])
 @pytest.mark.parametrize("qpk", [1, 2, 4, 8, 16])
 def test_qhead_per_kv_sweep(path, qpk):
     w, inp = contiguous_case(2, 300, 640, 2, qpk, 3, True, wl.MODE_CAUSAL, seed=7)
+    if path == TILE and not tile_ok(qpk, 3):
+        expect_not_supported(inp, True, path)
+        return
     check_contiguous(w, inp, path, f"qpk{qpk}")
 
 
-@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("path", [Q, KV, TILE])
 def test_unused_slots_invalid_ids_and_empty_blocks(path):
     """-1 rows, ids outside [0, nblk), a block nobody selects, and a custom scale."""
     w, inp = contiguous_case(1, 256, 1024, 2, 8, 4, False, wl.MODE_PERM, seed=3)
@@ -69,7 +86,7 @@ def test_unused_slots_invalid_ids_and_empty_blocks(path):
     check_contiguous(w, inp, path, "edge-ids", softmax_scale=0.05)
 
 
-@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("path", [Q, KV, TILE])
 def test_deterministic(path):
     w, inp = contiguous_case(1, 512, 1024, 2, 16, 4, True, wl.MODE_CAUSAL, seed=5)
     o1, l1 = run_contiguous(inp, True, path)
@@ -77,14 +94,42 @@ def test_deterministic(path):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_paths_agree():
+@pytest.mark.parametrize("other", [KV, TILE])
+def test_paths_agree(other):
     w, inp = contiguous_case(1, 640, 1024, 2, 16, 8, True, wl.MODE_CAUSAL, seed=9)
     oq, lq = run_contiguous(inp, True, Q)
-    ok, lk = run_contiguous(inp, True, KV)
+    ok, lk = run_contiguous(inp, True, other)
     assert (oq.float() - ok.float()).abs().max().item() <= 2e-2
     fin = torch.isfinite(lq)
     assert torch.equal(fin, torch.isfinite(lk))
     assert (lq[fin] - lk[fin]).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hkv,qpk,topk,causal", [
+    (1, 200, 4096, 1, 16, 32, True),   # 16 x 32 = 512 index entries per tile, ragged tail
+    (1, 100, 2048, 2, 8, 16, False),   # 32-query tiles, 512 entries
+    (3, 77, 1024, 3, 16, 4, True),     # 9 (b, hkv) pairs: plain placement
+    (2, 130, 640, 1, 8, 5, True),      # 2 pairs over XCD groups of 4, Sq > Skv
+    (1, 16, 128, 1, 16, 1, True),      # one tile, one block
+])
+def test_tile_shapes(B, Sq, Skv, Hkv, qpk, topk, causal):
+    w, inp = contiguous_case(B, Sq, Skv, Hkv, qpk, topk, causal,
+                             wl.MODE_CAUSAL if causal else wl.MODE_PERM, seed=31)
+    check_contiguous(w, inp, TILE, f"tile-B{B}-Sq{Sq}-qpk{qpk}-k{topk}")
+
+
+def test_tile_rejects_large_index_sets():
+    w, inp = contiguous_case(1, 64, 4096, 1, 8, 17, False, wl.MODE_PERM, seed=2)
+    expect_not_supported(inp, False, TILE)
+
+
+def test_tile_duplicate_ids_count_once():
+    """The query-tile path takes each selected block once per row (set semantics,
+    as the oracle): a row listing a block twice equals the row listing it once."""
+    w, inp = contiguous_case(1, 256, 1024, 2, 16, 6, True, wl.MODE_CAUSAL, seed=12)
+    q2k = inp["q2k"].copy()
+    q2k[:, :, :, -1] = q2k[:, :, :, 0]
+    check_contiguous(w, dict(inp, q2k=q2k), TILE, "tile-duplicates")
 
 
 # ---------------------------------------------------------------------------
@@ -156,10 +201,10 @@ def paged_case(B, Sq, Skv, Hkv, qpk, topk, causal, trims, seed=42, shuffle=True)
     return w, inp
 
 
-def check_paged(w, inp, splits, label):
-    say(f"[paged] {label} splits={splits} B={w.B} Sq={w.Sq} Skv={w.Skv} qpk={w.qpk} "
-        f"topk={w.topk} causal={w.causal}")
-    o, lse = run_paged(inp, w.causal, num_splits=splits)
+def check_paged(w, inp, splits, label, path=0):
+    say(f"[paged] {label} path={path} splits={splits} B={w.B} Sq={w.Sq} Skv={w.Skv} "
+        f"qpk={w.qpk} topk={w.topk} causal={w.causal}")
+    o, lse = run_paged(inp, w.causal, num_splits=splits, path=path)
     o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
                                                    inp["page_table"], inp["seqused_k"],
                                                    inp["q2k"], causal=w.causal)
@@ -167,11 +212,52 @@ def check_paged(w, inp, splits, label):
     return o, lse
 
 
-@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+PQ, PD = 1, 3  # paged q-centric and decode (union of blocks) kernels
+
+
+@pytest.mark.parametrize("path,splits", [(PQ, 0), (PQ, 1), (PQ, 3), (PQ, 8),
+                                         (PD, 0), (PD, 1), (PD, 3), (PD, 8), (PD, 64)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_paged_small(splits, causal):
+def test_paged_small(path, splits, causal):
     w, inp = paged_case(4, 8, 2048, 2, 16, 8, causal, trims=[17, 0, 1000, 2047])
-    check_paged(w, inp, splits, "c5-small")
+    check_paged(w, inp, splits, "c5-small", path)
+
+
+@pytest.mark.parametrize("Sq,topk,qpk,causal", [
+    (1, 16, 16, True),    # one query: three of four waves idle
+    (1, 32, 8, False),
+    (5, 12, 4, True),     # ragged query count per wave
+    (13, 8, 1, True),
+    (16, 32, 2, True),    # the largest index set one workgroup holds (512 entries)
+    (16, 4, 16, False),
+])
+def test_paged_decode_shapes(Sq, topk, qpk, causal):
+    w, inp = paged_case(3, Sq, 4096, 2, qpk, topk, causal, trims=[0, 77, 2500], seed=5 + Sq)
+    check_paged(w, inp, 0, f"decode-Sq{Sq}-topk{topk}", PD)
+    check_paged(w, inp, 2, f"decode-Sq{Sq}-topk{topk}-2split", PD)
+
+
+def test_paged_decode_shared_blocks():
+    """Every query selects the same blocks (the sink/recent pattern of decode):
+    the union holds topk blocks, each read once for all Sq queries, and duplicate
+    ids inside a row count once, as in the oracle's set semantics."""
+    B, Sq, Skv, Hkv, qpk, topk = 2, 8, 2048, 2, 16, 8
+    w, inp = paged_case(B, Sq, Skv, Hkv, qpk, topk, True, trims=[0, 3], seed=7)
+    q2k = inp["q2k"].copy()
+    q2k[:, :, :, :] = q2k[:, :, -1:, :]  # the last query's row for every query
+    q2k[:, :, :, -1] = q2k[:, :, :, 0]   # one duplicate id per row
+    inp = dict(inp, q2k=q2k)
+    for splits in (0, 1, 5):
+        check_paged(w, inp, splits, "decode-shared", PD)
+
+
+def test_paged_decode_rejects_long_query_sets():
+    import block_sparse_attention_top_amd as msa
+    w, inp = paged_case(1, 17, 1024, 1, 16, 4, True, trims=[0])
+    with pytest.raises(msa.MsaNotSupportedError):
+        run_paged(inp, True, path=PD)
+    assert msa.msa_paged_sparse_fwd_path(1, 17, 1, 4) == PQ
+    assert msa.msa_paged_sparse_fwd_path(1, 16, 1, 4, PD) == PD
 
 
 @pytest.mark.parametrize("qpk", [1, 4, 16])
@@ -180,11 +266,12 @@ def test_paged_prefill_ragged(qpk):
     check_paged(w, inp, 0, f"paged-prefill-qpk{qpk}")
 
 
-def test_paged_tail_poison_and_bad_page():
+@pytest.mark.parametrize("path", [PQ, PD])
+def test_paged_tail_poison_and_bad_page(path):
     """NaN and huge values past seqused_k change nothing; an out-of-range page id
     drops that block (as the oracle does)."""
     w, inp = paged_case(2, 8, 1024, 1, 16, 4, True, trims=[17, 300], seed=11)
-    o0, l0 = check_paged(w, inp, 0, "tail-clean")
+    o0, l0 = check_paged(w, inp, 0, "tail-clean", path)
     kp, vp, pt = inp["k_pool"].copy(), inp["v_pool"].copy(), inp["page_table"]
     for b in range(w.B):
         used = int(inp["seqused_k"][b])
@@ -194,14 +281,15 @@ def test_paged_tail_poison_and_bad_page():
                 kp[pt[b, s], :, lo:] = 0x7FC0  # NaN
                 vp[pt[b, s], :, lo:] = 0x7F80  # +inf
     inp2 = dict(inp, k_pool=kp, v_pool=vp)
-    o1, l1 = run_paged(inp2, True)
+    o1, l1 = run_paged(inp2, True, path=path)
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     bad = pt.copy()
     bad[0, int(inp["q2k"][0, 0, 0, 0])] = 1 << 20
-    check_paged(w, dict(inp, page_table=bad), 0, "bad-page")
+    check_paged(w, dict(inp, page_table=bad), 0, "bad-page", path)
 
 
-def test_paged_shuffled_equals_identity_bitwise():
+@pytest.mark.parametrize("path", [PQ, PD])
+def test_paged_shuffled_equals_identity_bitwise(path):
     """The same logical K/V through a shuffled and through an identity page table."""
     B, Sq, Skv, Hkv, qpk, topk = 3, 8, 1024, 2, 16, 6
     w, inp = paged_case(B, Sq, Skv, Hkv, qpk, topk, True, trims=[5, 0, 200], seed=13)
@@ -211,8 +299,8 @@ def test_paged_shuffled_equals_identity_bitwise():
     v2 = np.empty_like(inp["v_pool"])
     k2[ident.reshape(-1)] = inp["k_pool"][pt.reshape(-1)]
     v2[ident.reshape(-1)] = inp["v_pool"][pt.reshape(-1)]
-    o1, l1 = run_paged(inp, True)
-    o2, l2 = run_paged(dict(inp, k_pool=k2, v_pool=v2, page_table=ident), True)
+    o1, l1 = run_paged(inp, True, path=path)
+    o2, l2 = run_paged(dict(inp, k_pool=k2, v_pool=v2, page_table=ident), True, path=path)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
@@ -228,7 +316,7 @@ def test_paged_equals_contiguous():
     pin = dict(q=inp["q"], k_pool=pool_k, v_pool=pool_v, q2k=inp["q2k"],
                page_table=np.arange(B * mp, dtype=np.int32).reshape(B, mp),
                seqused_k=np.full(B, Skv, dtype=np.int32))
-    op, lp = run_paged(pin, True, num_splits=1)
+    op, lp = run_paged(pin, True, num_splits=1, path=PQ)
     oc, lc = run_contiguous(inp, True, Q)
     assert torch.equal(op, oc) and torch.equal(lp, lc)
 
@@ -252,12 +340,13 @@ def test_full_size_sampled(key):
     say(f"[full] {key}: {stats}")
 
 
-def test_full_size_paged_decode():
+@pytest.mark.parametrize("path", [0, PQ])
+def test_full_size_paged_decode(path):
     w = wl.WORKLOADS["c5"]
     say(f"[full] c5 {w.name}: generating inputs")
     inp = wl.make_inputs(w)
-    say("[full] c5: running GPU (auto splits)")
-    o, lse = run_paged(inp, True)
+    say(f"[full] c5: running GPU (path {path}, auto splits)")
+    o, lse = run_paged(inp, True, path=path)
     rows = sample_rows(w.B, w.Sq, 64, seed=2)
     o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
                                                    inp["page_table"], inp["seqused_k"],
