@@ -21,54 +21,62 @@ namespace {
 // [16 dim chunks][qpk heads][8 dims], with (LSE_t, M_t) [B*Sq][topk][Hq], so
 // that O = sum_t e^(M_t - L) U_t; slot t of (b, q, h) exists iff
 // q2k[b][h/qpk][q][t] is a valid block id. A block of 256 threads merges 16
-// consecutive (query, head) rows: the slot weights are formed once per row in
-// LDS, then every thread streams its 16-byte chunk of each weighted partial
-// (thread = dim chunk * 16 + row, so a wave reads whole runs of heads).
+// consecutive (query, head) rows. Weights: thread (row, t % 16) takes slots t
+// and t + 16, the row's max and sum of e^(LSE_t) come from shuffles inside its
+// 16-lane group, and e^(M_t - L) goes to LDS. Sums: thread = dim chunk * 16 +
+// row streams its 16-byte chunk of every weighted partial (all loads issued
+// together), so a wave reads whole runs of heads.
 __global__ __launch_bounds__(256) void combine_slots_kernel(
     const uint16_t* __restrict__ o_part, const float2* __restrict__ lse_part,
     const int32_t* __restrict__ q2k, int B, int Sq, int Hq, int Hkv, int topk, int nblk,
     uint16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ float wts[16][kMaxTopk];
-  __shared__ float refm[16][kMaxTopk];
   __shared__ float row_lse[16];
   const long long rows = static_cast<long long>(B) * Sq * Hq;
   const long long rh0 = static_cast<long long>(blockIdx.x) * 16;
   const int tid = threadIdx.x;
   const int qpk = Hq / Hkv;
-  for (int idx = tid; idx < 16 * topk; idx += 256) {
-    const int rl = idx / topk, t = idx % topk;
+  {
+    const int rl = tid >> 4, t0 = tid & 15;
     const long long rh = rh0 + rl;
-    float l = -INFINITY, mref = 0.f;
+    float l[2] = {-INFINITY, -INFINITY}, mr[2] = {0.f, 0.f};
     if (rh < rows) {
       const long long gq = rh / Hq;
       const int head = static_cast<int>(rh % Hq);
       const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-      const int sblk = q2k[((static_cast<long long>(b) * Hkv + head / qpk) * Sq + qpos) * topk + t];
-      if (sblk >= 0 && sblk < nblk) {
-        const float2 lm = lse_part[(gq * topk + t) * Hq + head];
-        l = lm.x;
-        mref = lm.y;
+      const int32_t* row = q2k + ((static_cast<long long>(b) * Hkv + head / qpk) * Sq + qpos) * topk;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int t = t0 + 16 * k;
+        if (t < topk) {
+          const int sblk = row[t];
+          if (sblk >= 0 && sblk < nblk) {
+            const float2 lm = lse_part[(gq * topk + t) * Hq + head];
+            l[k] = lm.x;
+            mr[k] = lm.y;
+          }
+        }
       }
     }
-    wts[rl][t] = l;
-    refm[rl][t] = mref;
-  }
-  __syncthreads();
-  if (tid < 16) {
-    float m = -INFINITY;
-    for (int t = 0; t < topk; ++t) m = fmaxf(m, wts[tid][t]);
-    float L = -INFINITY;
+    float m = fmaxf(l[0], l[1]);
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+    float sum = 0.f;
     if (m != -INFINITY) {
-      float sum = 0.f;
-      for (int t = 0; t < topk; ++t) sum += expf(wts[tid][t] - m);
-      L = m + logf(sum);
-      // partials are unnormalised relative to their reference max
-      for (int t = 0; t < topk; ++t)
-        wts[tid][t] = wts[tid][t] == -INFINITY ? 0.f : expf(refm[tid][t] - L);
-    } else {
-      for (int t = 0; t < topk; ++t) wts[tid][t] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (l[k] != -INFINITY) sum += fast_exp2((l[k] - m) * kLog2e);
     }
-    row_lse[tid] = L;
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 16);
+    const float L = m == -INFINITY ? -INFINITY : m + fast_log2(sum) * kLn2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = t0 + 16 * k;
+      if (t < topk)
+        wts[rl][t] = (l[k] == -INFINITY || L == -INFINITY) ? 0.f : fast_exp2((mr[k] - L) * kLog2e);
+    }
+    if (t0 == 0) row_lse[rl] = L;
   }
   __syncthreads();
   const int rl = tid & 15, dc = tid >> 4;
@@ -77,21 +85,22 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
   const long long gq = rh / Hq;
   const int head = static_cast<int>(rh % Hq);
   const int hkv = head / qpk, head_i = head % qpk;
+  const uint16_t* base = o_part + (dc * qpk + head_i) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t0 = 0; t0 < topk; t0 += 8) {
-    u32x4 raw[8];
-    float wgt[8];
+  for (int t0 = 0; t0 < topk; t0 += 16) {
+    u32x4 raw[16];
+    float wgt[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 16; ++k) {
       const int t = t0 + k;
       wgt[k] = t < topk ? wts[rl][t] : 0.f;
       const long long blk = (gq * topk + t) * Hkv + hkv;
-      raw[k] = wgt[k] > 0.f ? *reinterpret_cast<const u32x4*>(
-                                  o_part + blk * (qpk * kD) + (dc * qpk + head_i) * 8)
+      raw[k] = wgt[k] > 0.f ? __builtin_nontemporal_load(
+                                  reinterpret_cast<const u32x4*>(base + blk * (qpk * kD)))
                             : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < 16; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += wgt[k] * __uint_as_float(raw[k][i] << 16);

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
         for (int pp = 0; pp < 2; ++pp) {
           const u32x4 v4 = {ow[dt][2 * pp][0], ow[dt][2 * pp][1], ow[dt][2 * pp + 1][0],
                             ow[dt][2 * pp + 1][1]};
-          *reinterpret_cast<u32x4*>(ob + (4 * dt + 2 * pp + h) * (QPK * 8)) = v4;
+          // written once, read once by the combine: non-temporal
+          __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(ob + (4 * dt + 2 * pp + h) * (QPK * 8)));
         }
       if (h == 0) {
         const long long prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;
