@@ -172,6 +172,38 @@ class Case:
         ev.close()
         return start.elapsed_time(end) / steps, kernel_ms
 
+    def breakdown(self, steps: int, warmup: int):
+        """kv-centric only: mean ms of the k2q CSR build alone, of the forward given a
+        prebuilt CSR, and of the two together (the timed step)."""
+        if self.w.paged or self.path_name != "kv-centric":
+            return None
+        import torch
+        import block_sparse_attention_top_amd as msa
+        w, t = self.w, self.t
+        nblk = w.Skv // w.blk
+        csr = msa.msa_build_k2q_csr(t["q2k"], nblk)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            b.synchronize()
+            return a.elapsed_time(b) / steps
+
+        csr_ms = timed(lambda: msa.msa_build_k2q_csr(t["q2k"], nblk, row_ptr=csr[0], q_idx=csr[1],
+                                                     slot=csr[2]))
+        fwd_ms = timed(lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"], *csr,
+                                                  causal=w.causal, path=2, o=self.o,
+                                                  lse=self.lse))
+        both_ms = timed(self.step)
+        return {"csr_ms": csr_ms, "fwd_ms": fwd_ms, "csr_plus_fwd_ms": both_ms,
+                "fwd_TFLOP_per_s": self.flops / (fwd_ms * 1e-3) / 1e12}
+
     def metric(self, ms: float, kernel_ms: float) -> dict:
         if self.w.paged:
             gbs = self.bytes / (ms * 1e-3) / 1e9
@@ -242,10 +274,14 @@ def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
                                     rows=rows, nthreads=threads)
         return rows.size, time.perf_counter() - t0
 
+    # grow the probe until it takes a quarter of the budget (small probes overstate
+    # the per-row cost: thread start-up), then size the timed sample from it
     n, dt = run(max(threads, 16))
-    per_row = dt / n
-    n_target = int(min(total_rows, max(n, budget_s / max(per_row, 1e-9))))
-    n, dt = run(n_target)
+    while dt < budget_s / 4 and n < total_rows:
+        n, dt = run(min(total_rows, n * 4))
+    n_target = int(min(total_rows, max(n, n * budget_s / max(dt, 1e-9))))
+    if n_target > n:
+        n, dt = run(n_target)
     frac = n / total_rows
     if w.paged:
         value = case.bytes * frac / dt / 1e9
@@ -302,6 +338,9 @@ def main() -> int:
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     roof["kernel"] = case.dominant_kernel()
     roof["kernel_ms"] = kernel_ms
+    brk = case.breakdown(args.steps, args.warmup)
+    if brk is not None:
+        log(f"[bench] {args.workload}: breakdown {brk}")
     extra = {}
     for key in [k for k in args.extra.split(",") if k]:
         c = Case(key, "auto")
@@ -325,6 +364,8 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if brk is not None:
+        line["breakdown"] = brk
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)

@@ -143,6 +143,11 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restric
     counts[(static_cast<long long>(hkv) * nrows + r) * ntiles + tile] = cnt[r];
 }
 
+// Stable scatter, one wave per (tile, KV head): the tile's entries are taken in
+// rounds of 64 x 16 (all loads of a round issued together), then in order in
+// batches of 64 consecutive entries; a lane's rank among the lower lanes holding
+// the same row comes from ballots (one pass per distinct row in the batch), so
+// entries of a row keep ascending (query, slot) order.
 __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ q2k, int B,
                                                          int Hkv, int Sq, int topk, int nblk,
                                                          int tile_q, int ntiles,
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ q_idx,
                                                          int32_t* __restrict__ slot) {
   extern __shared__ int cursor[];
+  constexpr int kPer = 16;  // entries per lane per round
   const int tile = blockIdx.x, hkv = blockIdx.y;
   const int lane = threadIdx.x;
   const int nrows = B * nblk;
@@ -162,42 +168,49 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
   const long long nq = static_cast<long long>(B) * Sq;
   const long long g0 = static_cast<long long>(tile) * tile_q;
   const long long g1 = std::min<long long>(nq, g0 + tile_q);
+  const long long e_end = g1 * topk;
   int32_t* qi = q_idx + hkv * cap;
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
-  for (long long eb = g0 * topk; eb < g1 * topk; eb += 64) {
-    const long long e = eb + lane;
-    int row = -1;
-    long long gq = 0;
-    int t = 0;
-    if (e < g1 * topk) {
-      gq = e / topk;
-      t = static_cast<int>(e % topk);
-      const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-      const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
-      if (s >= 0 && s < nblk) row = b * nblk + s;
-    }
-    // rank among lower lanes with the same row
-    unsigned long long pending = __ballot(row >= 0);
-    int rank = 0, cnt = 0;
-    while (pending) {
-      const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-      const int lrow = __shfl(row, leader);
-      const unsigned long long peers = __ballot(row == lrow);
-      if (row == lrow) {
-        rank = __popcll(peers & __lanemask_lt());
-        cnt = __popcll(peers);
+  for (long long rb = g0 * topk; rb < e_end; rb += 64 * kPer) {
+    int rows[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long e = rb + 64 * k + lane;
+      rows[k] = -1;
+      if (e < e_end) {
+        const long long gq = e / topk;
+        const int t = static_cast<int>(e % topk);
+        const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+        const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
+        if (s >= 0 && s < nblk) rows[k] = b * nblk + s;
       }
-      pending &= ~peers;
     }
-    int pos = 0;
-    if (row >= 0) pos = cursor[row] + rank;
-    __syncthreads();
-    if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
-    if (row >= 0) {
-      qi[pos] = static_cast<int32_t>(gq);
-      if (sl) sl[pos] = t;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long e = rb + 64 * k + lane;
+      const int row = rows[k];
+      unsigned long long pending = __ballot(row >= 0);
+      int rank = 0, cnt = 0;
+      while (pending) {
+        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+        const int lrow = __shfl(row, leader);
+        const unsigned long long peers = __ballot(row == lrow);
+        if (row == lrow) {
+          rank = __popcll(peers & __lanemask_lt());
+          cnt = __popcll(peers);
+        }
+        pending &= ~peers;
+      }
+      int pos = 0;
+      if (row >= 0) pos = cursor[row] + rank;
+      __syncthreads();
+      if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
+      if (row >= 0) {
+        qi[pos] = static_cast<int32_t>(e / topk);
+        if (sl) sl[pos] = static_cast<int32_t>(e % topk);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -275,7 +288,7 @@ hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, long long n, i
 CsrPlan csr_plan(int B, int Hkv, int Sq, int topk, int nrows) {
   (void)topk;
   const long long nq = static_cast<long long>(B) * Sq;
-  long long ntiles = (nq + 255) / 256;  // ~256 queries per tile
+  long long ntiles = (nq + 63) / 64;  // ~64 queries per tile
   const long long max_counts = 4LL << 20;
   const long long cap_tiles = std::max<long long>(1, max_counts / (static_cast<long long>(Hkv) * nrows));
   ntiles = std::max<long long>(1, std::min(ntiles, cap_tiles));
