@@ -34,17 +34,24 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense
 HBM_PEAK_GBS = 8000.0
 PATHS = {"auto": 0, "q": 1, "kv": 2, "decode": 3, "tile": 4}
 PROFILES = os.path.join(ROOT, "profiles")
-SOURCES = [os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", f) for f in
-           ("msa_api.hip", "msa_qcentric.hip", "msa_kvcentric.hip", "msa_combine.hip",
-            "msa_csr.hip", "msa_decode.hip", "msa_tile.hip", "msa_internal.hpp")]
+CSRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc")
+# the source file of each dominant kernel (with the shared header)
+KERNEL_SOURCES = {
+    "qcentric_kernel": "msa_qcentric.hip",
+    "kvcentric_kernel": "msa_kvcentric.hip",
+    "paged_decode_kernel": "msa_decode.hip",
+    "tile_kernel": "msa_tile.hip",
+}
 
 
-def source_digest() -> str:
-    """Hash of the HIP sources: counter summaries are only reused for the same kernels."""
+def source_digest(kernel: str) -> str:
+    """Hash of a kernel's source and the shared header: a counter summary is reused
+    only while the kernel it measured is unchanged."""
     import hashlib
+    src = next(f for k, f in KERNEL_SOURCES.items() if kernel.startswith(k))
     h = hashlib.sha256()
-    for f in SOURCES:
-        with open(f, "rb") as fh:
+    for f in (src, "msa_internal.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -236,7 +243,7 @@ def measured_traffic(case: "Case"):
         return None
     with open(f) as fh:
         d = json.load(fh)
-    if d.get("source_digest") != source_digest():
+    if d.get("source_digest") != source_digest(case.dominant_kernel()):
         return None
     return d.get("hbm_bytes_per_launch")
 

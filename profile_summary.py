@@ -140,7 +140,7 @@ def main() -> int:
         with open(js, "w") as fh:
             json.dump({"workload": w.name, "path": args.path, "kernel": dom,
                        "hbm_bytes_per_launch": traffic, "kernel_avg_us": dom_avg,
-                       "source_digest": bench.source_digest()}, fh, indent=1)
+                       "source_digest": bench.source_digest(dom)}, fh, indent=1)
             fh.write("\n")
         print("wrote", js)
     return 0
