@@ -21,6 +21,10 @@ SOURCES = ["msa_api.hip", "msa_qcentric.hip", "msa_kvcentric.hip", "msa_combine.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms are kept out of the generated code on purpose
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # no kernel computes on NaN (masked or out-of-range keys are zeroed or replaced
+         # before any arithmetic), so fmaxf needs no NaN-quieting of its MFMA inputs;
+         # infinities are still honoured (masking uses -inf)
+         "-fno-honor-nans",
          "-Wall", "-Wno-unused-function"]
 
 
