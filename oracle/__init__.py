@@ -47,6 +47,11 @@ def _load():
         lib.oracle_paged_sparse_attention.restype = I
         lib.oracle_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P]
         lib.oracle_k2q_csr.restype = I
+        lib.oracle_sparse_attention_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, D,
+                                                       P, I64, P, P, I]
+        lib.oracle_sparse_attention_varlen.restype = I
+        lib.oracle_k2q_csr_varlen.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
+        lib.oracle_k2q_csr_varlen.restype = I
         _lib = lib
     return _lib
 
@@ -134,6 +139,64 @@ def k2q_csr(q2k, nblk: int, with_slot: bool = True):
                                 _ptr(slot))
     if rc != 0:
         raise ValueError("oracle_k2q_csr: invalid arguments")
+    return row_ptr, q_idx, slot
+
+
+def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal: bool,
+                            blk: int = 128, softmax_scale: Optional[float] = None, rows=None,
+                            nthreads: int = 0):
+    """Oracle forward of a variable-length batch.
+
+    q [total_q,Hq,D], k/v [total_k,Hkv,D] (uint16 bf16 bits), q2k [Hkv,total_q,topk],
+    cu_seqlens_q / cu_seqlens_k [B+1]. rows=None: O [total_q,Hq,D] and LSE [Hq,total_q];
+    else O [n,Hq,D] and LSE [n,Hq] for the given global rows.
+    """
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    q2k, cq, ck = _c(q2k, np.int32), _c(cu_seqlens_q, np.int32), _c(cu_seqlens_k, np.int32)
+    total_q, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    topk = q2k.shape[-1]
+    B = cq.size - 1
+    assert q2k.shape == (Hkv, total_q, topk) and ck.size == B + 1 and cq[-1] == total_q
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    rws = _c(rows, np.int64)
+    n = total_q if rws is None else rws.size
+    o = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    rc = _load().oracle_sparse_attention_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cq),
+                                                _ptr(ck), B, Hq, Hkv, D, topk, blk, int(causal),
+                                                scale, _ptr(rws), n, _ptr(o), _ptr(lse),
+                                                nthreads)
+    if rc != 0:
+        raise ValueError("oracle_sparse_attention_varlen: invalid arguments")
+    if rws is None:
+        return o, lse.T.copy()
+    return o, lse
+
+
+def varlen_total_rows(cu_seqlens_k, blk: int = 128) -> int:
+    """Number of CSR rows of a variable-length batch: sum of ceil(Skv_b / blk)."""
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    return int(((np.diff(ck) + blk - 1) // blk).sum())
+
+
+def k2q_csr_varlen(q2k, cu_seqlens_q, cu_seqlens_k, *, blk: int = 128, with_slot: bool = True):
+    """Oracle CSR of a variable-length batch (q2k [Hkv,total_q,topk]).
+
+    Returns (row_ptr [Hkv, total_rows+1], q_idx [Hkv, total_q*topk], slot or None);
+    entries past row_ptr[h, -1] are -1.
+    """
+    q2k, cq, ck = _c(q2k, np.int32), _c(cu_seqlens_q, np.int32), _c(cu_seqlens_k, np.int32)
+    Hkv, total_q, topk = q2k.shape
+    B = cq.size - 1
+    rows = varlen_total_rows(ck, blk)
+    row_ptr = np.empty((Hkv, rows + 1), dtype=np.int32)
+    q_idx = np.full((Hkv, total_q * topk), -1, dtype=np.int32)
+    slot = np.full((Hkv, total_q * topk), -1, dtype=np.int32) if with_slot else None
+    rc = _load().oracle_k2q_csr_varlen(_ptr(q2k), _ptr(cq), _ptr(ck), B, Hkv, topk, blk, rows,
+                                       _ptr(row_ptr), _ptr(q_idx), _ptr(slot))
+    if rc != 0:
+        raise ValueError("oracle_k2q_csr_varlen: invalid arguments")
     return row_ptr, q_idx, slot
 
 

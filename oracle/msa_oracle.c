@@ -41,26 +41,32 @@ static int64_t kv_offset(const kv_source* s, int b, int hkv, int64_t j) {
 }
 
 /*
- * One query row (b, qpos): all Hq heads.
- *   nblk   valid block ids are [0, nblk)
- *   kvlen  keys j >= kvlen are masked
+ * One query row: all Hq heads.
+ *   qrow       the row's Q, [Hq, D]
+ *   sel0       the row's index slots for KV head 0; KV head hkv's slots are at
+ *              sel0 + hkv * sel_stride
+ *   b          the sequence (K/V source coordinate)
+ *   qpos, Sq   position of the row in its sequence and the sequence's length
+ *   nblk       valid block ids are [0, nblk)
+ *   kvlen      keys j >= kvlen are masked
  *   The causal limit is qpos + kvlen - Sq (bottom-right alignment).
  */
-static void attend_row(const kv_source* src, const uint16_t* q, const int32_t* q2k, int b, int qpos,
-                       int Sq, int Hq, int Hkv, int D, int topk, int blk, int nblk, int64_t kvlen,
-                       int causal, double scale, unsigned char* mark, double* score, double* acc,
-                       double* o_row, double* lse_row) {
+static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t* sel0,
+                       int64_t sel_stride, int b, int qpos, int Sq, int Hq, int Hkv, int D,
+                       int topk, int blk, int nblk, int64_t kvlen, int causal, double scale,
+                       unsigned char* mark, double* score, double* acc, double* o_row,
+                       double* lse_row) {
   const int qpk = Hq / Hkv;
   const int64_t limit = causal ? (int64_t)qpos + kvlen - Sq : INT64_MAX;
   for (int hkv = 0; hkv < Hkv; ++hkv) {
     /* selected set: each valid block id once */
-    memset(mark, 0, (size_t)nblk);
-    const int32_t* sel = q2k + (((int64_t)b * Hkv + hkv) * Sq + qpos) * topk;
+    if (nblk > 0) memset(mark, 0, (size_t)nblk);
+    const int32_t* sel = sel0 + hkv * sel_stride;
     for (int t = 0; t < topk; ++t)
       if (sel[t] >= 0 && sel[t] < nblk) mark[sel[t]] = 1;
 
     for (int h = hkv * qpk; h < (hkv + 1) * qpk; ++h) {
-      const uint16_t* qh = q + (((int64_t)b * Sq + qpos) * Hq + h) * D;
+      const uint16_t* qh = qrow + (int64_t)h * D;
       double* oh = o_row + (int64_t)h * D;
       /* scores of the visible keys, in ascending key order */
       int64_t n = 0;
@@ -114,7 +120,7 @@ static int run_rows(const kv_source* src, const uint16_t* q, const int32_t* q2k,
   const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #pragma omp parallel num_threads(nt)
   {
-    unsigned char* mark = (unsigned char*)malloc((size_t)nblk);
+    unsigned char* mark = (unsigned char*)malloc((size_t)(nblk > 0 ? nblk : 1));
     double* score = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)blk);
     double* acc = (double*)malloc(sizeof(double) * (size_t)D);
     if (!mark || !score || !acc) {
@@ -133,8 +139,9 @@ static int run_rows(const kv_source* src, const uint16_t* q, const int32_t* q2k,
         int64_t kvlen = full_len;
         if (seqused_k && seqused_k[b] < kvlen) kvlen = seqused_k[b];
         if (kvlen < 0) kvlen = 0;
-        attend_row(src, q, q2k, b, qpos, Sq, Hq, Hkv, D, topk, blk, nblk, kvlen, causal, scale,
-                   mark, score, acc, o + i * Hq * D, lse + i * Hq);
+        attend_row(src, q + g * Hq * D, q2k + (((int64_t)b * Hkv) * Sq + qpos) * topk,
+                   (int64_t)Sq * topk, b, qpos, Sq, Hq, Hkv, D, topk, blk, nblk, kvlen, causal,
+                   scale, mark, score, acc, o + i * Hq * D, lse + i * Hq);
       }
     }
     free(mark);
@@ -206,5 +213,134 @@ int oracle_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nbl
       }
   }
   free(cursor);
+  return 0;
+}
+
+/* Sequence of global query row g: the b with cu_q[b] <= g < cu_q[b + 1]. */
+static int sequence_of(const int32_t* cu_q, int B, int64_t g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (cu_q[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+static int varlen_args_ok(const int32_t* cu_q, const int32_t* cu_k, int B) {
+  if (!cu_q || !cu_k || B <= 0 || cu_q[0] != 0 || cu_k[0] != 0) return 0;
+  for (int b = 0; b < B; ++b)
+    if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return 0;
+  return 1;
+}
+
+int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* q2k, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
+                                   int topk, int blk, int causal, double scale,
+                                   const int64_t* rows, int64_t nrows, double* o, double* lse,
+                                   int nthreads) {
+  if (!q || !k || !v || !q2k || !o || !lse || Hkv <= 0 || Hq <= 0 || Hq % Hkv || D <= 0 ||
+      topk <= 0 || blk <= 0 || !varlen_args_ok(cu_seqlens_q, cu_seqlens_k, B))
+    return -1;
+  const int64_t total_q = cu_seqlens_q[B];
+  int max_nblk = 1;
+  for (int b = 0; b < B; ++b) {
+    const int nb = (cu_seqlens_k[b + 1] - cu_seqlens_k[b] + blk - 1) / blk;
+    if (nb > max_nblk) max_nblk = nb;
+  }
+  if (!rows) nrows = total_q;
+  int failed = 0;
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+  {
+    unsigned char* mark = (unsigned char*)malloc((size_t)max_nblk);
+    double* score = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)blk);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!mark || !score || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t g = rows ? rows[i] : i;
+        if (g < 0 || g >= total_q) {
+#pragma omp atomic write
+          failed = 1;
+          continue;
+        }
+        /* the row's sequence: its keys are tokens cu_k[b] .. cu_k[b+1]-1 of k/v, its
+         * block ids count from that sequence's first token */
+        const int b = sequence_of(cu_seqlens_q, B, g);
+        const int Sq_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        const int Skv_b = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+        const int nblk_b = (Skv_b + blk - 1) / blk;
+        const kv_source src = {k + (int64_t)cu_seqlens_k[b] * Hkv * D,
+                               v + (int64_t)cu_seqlens_k[b] * Hkv * D, NULL, Skv_b, Hkv, D,
+                               blk, 0, 0};
+        attend_row(&src, q + g * Hq * D, q2k + g * topk, total_q * topk, 0,
+                   (int)(g - cu_seqlens_q[b]), Sq_b, Hq, Hkv, D, topk, blk, nblk_b, Skv_b,
+                   causal, scale, mark, score, acc, o + i * Hq * D, lse + i * Hq);
+      }
+    }
+    free(mark);
+    free(score);
+    free(acc);
+  }
+  return failed ? -1 : 0;
+}
+
+int oracle_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int B, int Hkv, int topk, int blk,
+                          int total_rows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot) {
+  if (!q2k || !row_ptr || !q_idx || Hkv <= 0 || topk <= 0 || blk <= 0 ||
+      !varlen_args_ok(cu_seqlens_q, cu_seqlens_k, B))
+    return -1;
+  /* row r = rowbase[b] + s for block s of sequence b */
+  int64_t* rowbase = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B + 1));
+  if (!rowbase) return -1;
+  rowbase[0] = 0;
+  for (int b = 0; b < B; ++b)
+    rowbase[b + 1] = rowbase[b] + (cu_seqlens_k[b + 1] - cu_seqlens_k[b] + blk - 1) / blk;
+  if (rowbase[B] != total_rows) {
+    free(rowbase);
+    return -1;
+  }
+  const int64_t total_q = cu_seqlens_q[B];
+  const int64_t cap = total_q * topk;
+  int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)(total_rows > 0 ? total_rows : 1));
+  if (!cursor) {
+    free(rowbase);
+    return -1;
+  }
+  for (int hkv = 0; hkv < Hkv; ++hkv) {
+    int32_t* rp = row_ptr + (int64_t)hkv * (total_rows + 1);
+    for (int64_t r = 0; r <= total_rows; ++r) rp[r] = 0;
+    /* count, then place in ascending (global query, slot) order */
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1) {
+        for (int64_t r = 0; r < total_rows; ++r) rp[r + 1] += rp[r];
+        for (int64_t r = 0; r < total_rows; ++r) cursor[r] = rp[r];
+      }
+      for (int b = 0; b < B; ++b) {
+        const int nblk_b = (int)(rowbase[b + 1] - rowbase[b]);
+        for (int64_t g = cu_seqlens_q[b]; g < cu_seqlens_q[b + 1]; ++g) {
+          const int32_t* sel = q2k + ((int64_t)hkv * total_q + g) * topk;
+          for (int t = 0; t < topk; ++t) {
+            if (sel[t] < 0 || sel[t] >= nblk_b) continue;
+            const int64_t r = rowbase[b] + sel[t];
+            if (pass == 0) {
+              rp[r + 1] += 1;
+            } else {
+              const int64_t pos = cursor[r]++;
+              q_idx[hkv * cap + pos] = (int32_t)g;
+              if (slot) slot[hkv * cap + pos] = t;
+            }
+          }
+        }
+      }
+    }
+  }
+  free(cursor);
+  free(rowbase);
   return 0;
 }

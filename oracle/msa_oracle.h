@@ -68,6 +68,38 @@ int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
 int oracle_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                    int32_t* row_ptr, int32_t* q_idx, int32_t* slot);
 
+/*
+ * Variable-length batches (the packed form of `sparse_atten_func` on the page
+ * "MSA interface.py": cu_seqlens_q / cu_seqlens_k prefix sums, q2k
+ * [Hkv, total_q, topK]). Sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and
+ * keys cu_k[b] .. cu_k[b+1]-1; its block ids s count from its first key
+ * (keys 128 s .. 128 s + 127 of the sequence, those >= its length masked),
+ * valid ids are [0, ceil(Skv_b / blk)), and the causal limit is
+ * q + Skv_b - Sq_b with q the row's position in its sequence. Each sequence is
+ * the batched definition above with B = 1 (the page's varlen tests compare each
+ * sequence against `sparse_attention_ref` that way).
+ *   q     [total_q, Hq, D]; k, v [total_k, Hkv, D]; q2k [Hkv, total_q, topk]
+ *   rows  NULL (all total_q rows) or nrows global row ids
+ *   o     [nrows, Hq, D] double; lse [nrows, Hq] double
+ */
+int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* q2k, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
+                                   int topk, int blk, int causal, double scale,
+                                   const int64_t* rows, int64_t nrows, double* o, double* lse,
+                                   int nthreads);
+
+/*
+ * k2q CSR of a variable-length batch (`build_k2q_csr` with cu_seqlens and
+ * total_rows on the page "MSA interface.py"): row r = rowbase[b] + s with
+ * rowbase[b] = sum over b' < b of ceil(Skv_b' / blk); total_rows must equal
+ * rowbase[B]. Entries of a row are global query ids g ascending, then slot t.
+ *   row_ptr [Hkv, total_rows + 1]; q_idx, slot [Hkv, total_q * topk]
+ */
+int oracle_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int B, int Hkv, int topk, int blk,
+                          int total_rows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot);
+
 #ifdef __cplusplus
 }
 #endif

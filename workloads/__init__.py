@@ -178,3 +178,52 @@ def make_inputs(w: Workload, q2k: Optional[np.ndarray] = None) -> dict:
         q2k = q2k_table(w.seed, w.mode, w.B, w.Hkv, w.Sq, w.kvlen, w.blk, w.topk)
     out["q2k"] = q2k
     return out
+
+
+# ---------------------------------------------------------------------------
+# Variable-length batches (the packed form: q [total_q,Hq,D], k/v [total_k,Hkv,D],
+# q2k [Hkv,total_q,topk], cu_seqlens [B+1])
+# ---------------------------------------------------------------------------
+def varlen_lengths(seed: int, B: int, max_q: int, max_k: int, blk: int = 128,
+                   k_multiple: bool = True):
+    """Ragged lengths in the manner of the test page's samplers: q lengths uniform in
+    [1, max_q] and K lengths uniform in [1, max_k] (whole blocks when k_multiple),
+    the first sequence at the maximum of each. Uses numpy's PCG64 seeded generator."""
+    rng = np.random.default_rng(seed)
+    q_lens = rng.integers(1, max_q + 1, size=B)
+    q_lens[0] = max_q
+    if k_multiple:
+        k_lens = rng.integers(1, max_k // blk + 1, size=B) * blk
+    else:
+        k_lens = rng.integers(1, max_k + 1, size=B)
+    k_lens[0] = max_k
+    return [int(x) for x in q_lens], [int(x) for x in k_lens]
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_varlen_inputs(seed: int, q_lens, k_lens, Hkv: int, qpk: int, topk: int, mode: int,
+                       D: int = 128, blk: int = 128) -> dict:
+    """Host inputs of a variable-length batch; sequence b's index rows come from the
+    same recipes as the batched workloads (seed + 1000 + b), block ids local to b."""
+    q_lens, k_lens = list(q_lens), list(k_lens)
+    total_q, total_k = sum(q_lens), sum(k_lens)
+    Hq = Hkv * qpk
+    out = {"q": normal_bf16(seed, STREAM_Q, (total_q, Hq, D)),
+           "k": normal_bf16(seed, STREAM_K, (total_k, Hkv, D)),
+           "v": normal_bf16(seed, STREAM_V, (total_k, Hkv, D)),
+           "cu_seqlens_q": cu_seqlens(q_lens), "cu_seqlens_k": cu_seqlens(k_lens)}
+    q2k = np.full((Hkv, total_q, topk), -1, dtype=np.int32)
+    g = 0
+    for b, (sq, sk) in enumerate(zip(q_lens, k_lens)):
+        if sq > 0 and sk > 0:
+            q2k[:, g:g + sq] = q2k_table(seed + 1000 + b, mode, 1, Hkv, sq, sk, blk, topk)[0]
+        g += sq
+    out["q2k"] = q2k
+    return out
+
+
+def varlen_effective_flops(q_lens, Hq: int, topk: int, D: int = 128, blk: int = 128) -> float:
+    return 4.0 * sum(q_lens) * Hq * topk * blk * D
