@@ -14,7 +14,9 @@ from ._ffi import (MSA_PATH_AUTO, MSA_PATH_DECODE, MSA_PATH_KVCENTRIC, MSA_PATH_
                    msa_build_k2q_csr, msa_build_k2q_csr_workspace_size, msa_last_error,
                    msa_paged_sparse_fwd, msa_paged_sparse_fwd_path, msa_paged_sparse_fwd_splits,
                    msa_paged_sparse_fwd_workspace_size, msa_set_profiling_events, msa_sparse_fwd,
-                   msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_version)
+                   msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_sparse_fwd_varlen,
+                   msa_sparse_fwd_varlen_path, msa_sparse_fwd_varlen_workspace_size,
+                   msa_build_k2q_csr_varlen, msa_build_k2q_csr_varlen_workspace_size, msa_version)
 
 __all__ = [
     "MSA_PATH_AUTO", "MSA_PATH_QCENTRIC", "MSA_PATH_KVCENTRIC", "MSA_PATH_DECODE",
@@ -23,5 +25,7 @@ __all__ = [
     "msa_sparse_fwd_path", "msa_sparse_fwd_workspace_size", "msa_build_k2q_csr",
     "msa_build_k2q_csr_workspace_size", "msa_paged_sparse_fwd", "msa_paged_sparse_fwd_path",
     "msa_paged_sparse_fwd_splits", "msa_paged_sparse_fwd_workspace_size", "msa_last_error",
-    "msa_set_profiling_events", "msa_version",
+    "msa_set_profiling_events", "msa_version", "msa_sparse_fwd_varlen",
+    "msa_sparse_fwd_varlen_path", "msa_sparse_fwd_varlen_workspace_size",
+    "msa_build_k2q_csr_varlen", "msa_build_k2q_csr_varlen_workspace_size",
 ]

@@ -57,6 +57,17 @@ def load_library():
     lib.msa_build_k2q_csr_workspace_size.restype = S
     lib.msa_build_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P, P, S, P]
     lib.msa_build_k2q_csr.restype = I
+    lib.msa_sparse_fwd_varlen_workspace_size.argtypes = [I] * 9
+    lib.msa_sparse_fwd_varlen_workspace_size.restype = S
+    lib.msa_sparse_fwd_varlen_path.argtypes = [I] * 7
+    lib.msa_sparse_fwd_varlen_path.restype = I
+    lib.msa_sparse_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                          I, F, I, P, P, P, S, P]
+    lib.msa_sparse_fwd_varlen.restype = I
+    lib.msa_build_k2q_csr_varlen_workspace_size.argtypes = [I] * 5
+    lib.msa_build_k2q_csr_varlen_workspace_size.restype = S
+    lib.msa_build_k2q_csr_varlen.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, S, P]
+    lib.msa_build_k2q_csr_varlen.restype = I
     lib.msa_paged_sparse_fwd_workspace_size.argtypes = [I] * 10
     lib.msa_paged_sparse_fwd_workspace_size.restype = S
     lib.msa_paged_sparse_fwd_path.argtypes = [I] * 5
@@ -190,6 +201,88 @@ def msa_build_k2q_csr(q2k, num_kv_blocks: int, *, row_ptr=None, q_idx=None, slot
     ws, wsn = _workspace(nbytes, dev, workspace)
     rc = lib.msa_build_k2q_csr(_ptr(q2k), B, Hkv, Sq, topk, num_kv_blocks, _ptr(row_ptr),
                                _ptr(q_idx), _ptr(slot), _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    return row_ptr, q_idx, slot
+
+
+def msa_sparse_fwd_varlen_workspace_size(B, total_q, total_k, Hq, Hkv, D, topk, blk_kv=128,
+                                         path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_sparse_fwd_varlen_workspace_size(B, total_q, total_k, Hq, Hkv, D,
+                                                                   topk, blk_kv, path))
+
+
+def msa_sparse_fwd_varlen_path(B, total_q, total_k, Hq, Hkv, topk, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_sparse_fwd_varlen_path(B, total_q, total_k, Hq, Hkv, topk, path))
+
+
+def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=None,
+                          csr_q_idx=None, csr_slot=None, csr_total_rows: int = 0, *, causal: bool,
+                          softmax_scale: float = 0.0, path: int = MSA_PATH_AUTO, blk_kv: int = 128,
+                          o=None, lse=None, workspace=None, stream=None):
+    """Sparse forward of a variable-length batch (packed q [total_q,Hq,D], k/v
+    [total_k,Hkv,D], q2k [Hkv,total_q,topk], cu_seqlens [B+1] on the device).
+    Returns (O bf16 [total_q,Hq,D], LSE fp32 [total_q,Hq])."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
+    _dev(q2k, "q2k", torch.int32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    topk = q2k.shape[-1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if tuple(q2k.shape) != (Hkv, total_q, topk):
+        raise ValueError("q2k must have shape [Hkv, total_q, topk]")
+    for t, nm in ((csr_row_ptr, "csr_row_ptr"), (csr_q_idx, "csr_q_idx"), (csr_slot, "csr_slot")):
+        if t is not None:
+            _dev(t, nm, torch.int32)
+    if o is None:
+        o = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    nbytes = int(lib.msa_sparse_fwd_varlen_workspace_size(B, total_q, total_k, Hq, Hkv, D, topk,
+                                                          blk_kv, path))
+    ws, wsn = _workspace(nbytes, q.device, workspace)
+    rc = lib.msa_sparse_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        _ptr(csr_row_ptr), _ptr(csr_q_idx), _ptr(csr_slot), int(csr_total_rows), B, total_q,
+        total_k, Hq, Hkv, D, topk, blk_kv, int(bool(causal)), float(softmax_scale), int(path),
+        _ptr(o), _ptr(lse), _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    return o, lse
+
+
+def msa_build_k2q_csr_varlen_workspace_size(B, Hkv, total_q, topk, total_rows) -> int:
+    return int(load_library().msa_build_k2q_csr_varlen_workspace_size(B, Hkv, total_q, topk,
+                                                                      total_rows))
+
+
+def msa_build_k2q_csr_varlen(q2k, cu_seqlens_q, cu_seqlens_k, total_k: int, total_rows: int, *,
+                             row_ptr=None, q_idx=None, slot=None, with_slot: bool = True,
+                             workspace=None, stream=None):
+    """kv-block -> query CSR of a variable-length batch (q2k [Hkv,total_q,topk]) over
+    total_rows = sum_b ceil(Skv_b / 128) rows. Returns (row_ptr, q_idx, slot or None)."""
+    lib = load_library()
+    _dev(q2k, "q2k", torch.int32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    Hkv, total_q, topk = q2k.shape
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    dev = q2k.device
+    if row_ptr is None:
+        row_ptr = torch.empty((Hkv, total_rows + 1), dtype=torch.int32, device=dev)
+    if q_idx is None:
+        q_idx = torch.empty((Hkv, total_q * topk), dtype=torch.int32, device=dev)
+    if slot is None and with_slot:
+        slot = torch.empty((Hkv, total_q * topk), dtype=torch.int32, device=dev)
+    nbytes = int(lib.msa_build_k2q_csr_varlen_workspace_size(B, Hkv, total_q, topk, total_rows))
+    ws, wsn = _workspace(nbytes, dev, workspace)
+    rc = lib.msa_build_k2q_csr_varlen(_ptr(q2k), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hkv,
+                                      total_q, int(total_k), topk, int(total_rows), _ptr(row_ptr),
+                                      _ptr(q_idx), _ptr(slot), _ptr(ws), wsn, _stream(stream))
     _check(rc)
     return row_ptr, q_idx, slot
 

@@ -72,6 +72,18 @@ int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   return MSA_PATH_KVCENTRIC;
 }
 
+// Varlen batches: the same rule with the packed sizes; the CSR row count is
+// bounded on the host by floor(total_k / 128) + B (each sequence adds at most
+// one partial block), since the lengths themselves are on the device.
+long long varlen_rows_bound(int B, long long total_k) { return total_k / kBlk + B; }
+int resolve_varlen_path(int path, int B, long long total_q, long long total_k, int Hq, int topk) {
+  if (path != MSA_PATH_AUTO) return path;
+  const long long work = total_q * Hq * topk;
+  if (total_k == 0 || varlen_rows_bound(B, total_k) > kMaxCsrRows || work < (1LL << 20))
+    return MSA_PATH_QCENTRIC;
+  return MSA_PATH_KVCENTRIC;
+}
+
 // Entries per kv-centric work item: kKvChunkRows (query, head) rows.
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
@@ -81,17 +93,17 @@ struct KvLayout {
   long long max_items;
 };
 
-KvLayout kv_layout(int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
-  const int nblk = Skv / kBlk;
-  const long long nrows = static_cast<long long>(B) * nblk;
-  const long long cap = static_cast<long long>(B) * Sq * topk;
+// nq query rows (B * Sq, or total_q), nrows CSR rows
+KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
+  const long long cap = nq * topk;
   const long long nchunk = static_cast<long long>(Hkv) * nrows;
   KvLayout L;
   size_t off = 0;
   L.row_ptr = off; off += align256(Hkv * (nrows + 1) * 4);
   L.q_idx = off; off += align256(Hkv * cap * 4);
   L.slot = off; off += align256(Hkv * cap * 4);
-  L.csr_ws = off; off += align256(csr_workspace_bytes(B, Hkv, Sq, topk, static_cast<int>(nrows)));
+  L.csr_ws = off;
+  off += align256(csr_workspace_bytes(1, Hkv, static_cast<int>(nq), topk, static_cast<int>(nrows)));
   L.chunk_counts = off; off += align256(nchunk * 4);
   L.chunk_ptr = off; off += align256((nchunk + 1) * 4);
   L.scan_tmp = off; off += align256(scan_tmp_ints(nchunk) * 4);
@@ -149,6 +161,66 @@ size_t paged_workspace(int B, int Sq, int Hq, int splits) {
   return align256(splits * rows * kD * 4) + align256(splits * rows * 4);
 }
 
+// The kv-centric pipeline: k2q CSR (unless given), chunk schedule, item table,
+// per-block partials, slot combine. `p` carries the problem (and, for a varlen
+// batch, cu_q / cu_k / total sizes); vt != nullptr selects the varlen layout,
+// its tables already built on the stream.
+int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
+                  const int32_t* csr_q_idx, const int32_t* csr_slot, const KvLayout& L, char* ws,
+                  const VarlenTables* vt, uint16_t* o, float* lse, hipStream_t st) {
+  const int nrows = p.nrows;
+  const long long nq = vt ? p.total_q : static_cast<long long>(p.B) * p.Sq;
+  const int32_t* row_ptr = csr_row_ptr;
+  const int32_t* q_idx = csr_q_idx;
+  const int32_t* slot = csr_slot;
+  hipError_t e;
+  if (!row_ptr) {
+    int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
+    int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
+    int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
+    if (vt)
+      e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi, sl,
+                                  ws + L.csr_ws, st, /*ordered=*/false);
+    else
+      e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, sl, ws + L.csr_ws, st,
+                           /*ordered=*/false);
+    if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
+    row_ptr = rp; q_idx = qi; slot = sl;
+  }
+  const int chunk = chunk_entries_for(p.qpk);
+  int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
+  e = launch_chunk_schedule(row_ptr, p.Hkv, nrows, chunk,
+                            reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
+                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
+  p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot; p.chunk_ptr = chunk_ptr;
+  p.chunk_entries = chunk;
+  p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
+  p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
+  if (vt) {
+    p.rowbase = vt->rowbase;
+    p.row_seq = vt->row_seq;
+  }
+  int4* items = reinterpret_cast<int4*>(ws + L.items);
+  p.items = items;
+  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
+  if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
+  prof_mark(g_prof_before, st);
+  e = launch_kvcentric(p, static_cast<int>(L.max_items), st);
+  prof_mark(g_prof_after, st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
+  if (vt) {
+    const CombineVarlen cv{vt->q_rows};
+    e = launch_combine_slots(p.o_part, p.lse_part, q2k, 1, static_cast<int>(nq), p.Hq, p.Hkv,
+                             p.topk, 0, o, lse, st, &cv);
+  } else {
+    e = launch_combine_slots(p.o_part, p.lse_part, q2k, p.B, p.Sq, p.Hq, p.Hkv, p.topk, p.nblk, o,
+                             lse, st);
+  }
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "combine");
+}
+
 }  // namespace
 
 int msa::device_cu_count() {
@@ -189,7 +261,8 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
     return 0;
   const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
   if (which == MSA_PATH_QCENTRIC || which == MSA_PATH_TILE) return 0;
-  return kv_layout(B, Sq, Skv, Hq, Hkv, topk).total;
+  return kv_layout(static_cast<long long>(B) * Sq, static_cast<long long>(B) * (Skv / kBlk), Hq, Hkv,
+                   topk).total;
 }
 
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
@@ -263,57 +336,22 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   if (nrows > kMaxCsrRows)
     return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: B*Skv/128 = %lld exceeds %d", nrows,
                 kMaxCsrRows);
-  const KvLayout L = kv_layout(B, Sq, Skv, Hq, Hkv, topk);
+  const KvLayout L = kv_layout(static_cast<long long>(B) * Sq, nrows, Hq, Hkv, topk);
   if (!workspace || workspace_bytes < L.total)
     return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu", L.total,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
   if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
-  const int32_t* row_ptr = csr_row_ptr;
-  const int32_t* q_idx = csr_q_idx;
-  const int32_t* slot = csr_slot;
-  hipError_t e;
-  if (!have_csr) {
-    int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
-    int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
-    int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
-    e = launch_build_csr(q2k, B, Hkv, Sq, topk, nblk, rp, qi, sl, ws + L.csr_ws, st,
-                         /*ordered=*/false);
-    if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
-    row_ptr = rp; q_idx = qi; slot = sl;
-  }
-  const int chunk = chunk_entries_for(qpk);
-  int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
-  e = launch_chunk_schedule(row_ptr, Hkv, static_cast<int>(nrows), chunk,
-                            reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
-                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st);
-  if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
   KvParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
-  p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot; p.chunk_ptr = chunk_ptr;
   p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
   p.nblk = nblk; p.nrows = static_cast<int>(nrows);
   p.cap = static_cast<long long>(B) * Sq * topk;
-  p.chunk_entries = chunk;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
-  p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
-  p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
-  int4* items = reinterpret_cast<int4*>(ws + L.items);
-  p.items = items;
-
-  e = launch_kv_items(row_ptr, chunk_ptr, Hkv, static_cast<int>(nrows), chunk, items, st);
-  if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
-  if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
-  prof_mark(g_prof_before, st);
-  e = launch_kvcentric(p, static_cast<int>(L.max_items), st);
-  prof_mark(g_prof_after, st);
-  if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
-  e = launch_combine_slots(p.o_part, p.lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
-                           static_cast<uint16_t*>(o), lse, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e, "combine");
+  return run_kvcentric(p, q2k, have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
+                       static_cast<char*>(workspace), nullptr, static_cast<uint16_t*>(o), lse, st);
 }
 
 size_t msa_build_k2q_csr_workspace_size(int B, int Hkv, int Sq, int topk, int num_kv_blocks) {
@@ -343,6 +381,166 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
   hipError_t e = launch_build_csr(q2k, B, Hkv, Sq, topk, num_kv_blocks, row_ptr, q_idx, slot,
                                   workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "k2q CSR build");
+}
+
+// ---------------------------------------------------------------------------
+// Variable-length batches
+// ---------------------------------------------------------------------------
+int msa_sparse_fwd_varlen_path(int B, int total_q, int total_k, int Hq, int Hkv, int topk,
+                               int path) {
+  (void)Hkv;
+  return resolve_varlen_path(path, B, total_q, total_k, Hq, topk);
+}
+
+static bool varlen_sizes_ok(int B, int total_q, int total_k, int Hq, int Hkv, int D, int topk,
+                            int blk_kv) {
+  return B > 0 && total_q >= 0 && total_k >= 0 && Hq > 0 && Hkv > 0 && topk > 0 && D == kD &&
+         blk_kv == kBlk && Hq % Hkv == 0;
+}
+
+size_t msa_sparse_fwd_varlen_workspace_size(int B, int total_q, int total_k, int Hq, int Hkv,
+                                            int D, int topk, int blk_kv, int path) {
+  if (!varlen_sizes_ok(B, total_q, total_k, Hq, Hkv, D, topk, blk_kv) || total_k == 0) return 0;
+  if (resolve_varlen_path(path, B, total_q, total_k, Hq, topk) != MSA_PATH_KVCENTRIC) return 0;
+  const long long nrows = varlen_rows_bound(B, total_k);
+  return align256(varlen_tables_bytes(B, total_q, nrows)) +
+         kv_layout(total_q, nrows, Hq, Hkv, topk).total;
+}
+
+int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* q2k,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
+                          const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
+                          int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
+                          float softmax_scale, int path, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || total_q < 0 || total_k < 0)
+    return fail(MSA_ERR_INVALID_VALUE, "B must be positive, total_q and total_k non-negative");
+  int rc = check_common(B, 1, Hq, Hkv, D, topk, blk_kv);
+  if (rc) return rc;
+  if (static_cast<long long>(total_q) * topk > 0x7FFFFFFFLL)
+    return fail(MSA_ERR_INVALID_VALUE, "total_q*topk exceeds the int32 index range");
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_KVCENTRIC)
+    return fail(path == MSA_PATH_TILE || path == MSA_PATH_DECODE ? MSA_ERR_NOT_SUPPORTED
+                                                                 : MSA_ERR_INVALID_VALUE,
+                "path %d not available for variable-length batches", path);
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(MSA_ERR_INVALID_VALUE, "null cu_seqlens pointer");
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned cu_seqlens pointer");
+  const bool have_csr = csr_row_ptr || csr_q_idx || csr_slot;
+  if (have_csr && !(csr_row_ptr && csr_q_idx && csr_slot))
+    return fail(MSA_ERR_INVALID_VALUE, "csr_row_ptr, csr_q_idx and csr_slot go together");
+  if (total_q == 0) return MSA_OK;  // nothing to compute or write
+  if (!q || !q2k || !o || !lse || (total_k > 0 && (!k || !v)))
+    return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(q2k, 4) || !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
+  const long long nrows_bound = varlen_rows_bound(B, total_k);
+  if (have_csr && (csr_total_rows <= 0 || csr_total_rows > nrows_bound))
+    return fail(MSA_ERR_INVALID_VALUE,
+                "csr_total_rows (%d) must be in [1, floor(total_k / 128) + B = %lld]",
+                csr_total_rows, nrows_bound);
+  const int qpk = Hq / Hkv;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int which = resolve_varlen_path(path, B, total_q, total_k, Hq, topk);
+  if (total_k == 0) which = MSA_PATH_QCENTRIC;  // no keys: every row is empty
+
+  if (which == MSA_PATH_QCENTRIC) {
+    QcParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.q2k = q2k;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.splits = 1;
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    prof_mark(g_prof_before, st);
+    hipError_t e = launch_qcentric(p, false, st);
+    prof_mark(g_prof_after, st);
+    return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric varlen forward");
+  }
+
+  // kv-centric
+  if (nrows_bound > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED,
+                "kv-centric path: floor(total_k/128) + B = %lld CSR rows exceed %d", nrows_bound,
+                kMaxCsrRows);
+  const long long nrows = have_csr ? csr_total_rows : nrows_bound;
+  const size_t tbytes = align256(varlen_tables_bytes(B, total_q, nrows_bound));
+  const KvLayout L = kv_layout(total_q, nrows_bound, Hq, Hkv, topk);
+  if (!workspace || workspace_bytes < tbytes + L.total)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu",
+                tbytes + L.total, workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const VarlenTables vt = varlen_tables_at(ws, B, total_q, nrows);
+  hipError_t e = launch_varlen_tables(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, nrows, vt, st);
+  if (e != hipSuccess) return hip_fail(e, "varlen tables");
+  KvParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.B = 1; p.Sq = total_q; p.Skv = 0; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+  p.nblk = 0; p.nrows = static_cast<int>(nrows);
+  p.cap = static_cast<long long>(total_q) * topk;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  return run_kvcentric(p, q2k, have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
+                       ws + tbytes, &vt, static_cast<uint16_t*>(o), lse, st);
+}
+
+size_t msa_build_k2q_csr_varlen_workspace_size(int B, int Hkv, int total_q, int topk,
+                                               int total_rows) {
+  if (B <= 0 || Hkv <= 0 || total_q <= 0 || topk <= 0 || total_rows <= 0) return 0;
+  return align256(varlen_tables_bytes(B, total_q, 0)) +
+         csr_workspace_bytes(1, Hkv, total_q, topk, total_rows);
+}
+
+int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, int B, int Hkv, int total_q, int total_k,
+                             int topk, int total_rows, int32_t* row_ptr, int32_t* q_idx,
+                             int32_t* slot, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || Hkv <= 0 || total_q <= 0 || total_k < 0 || topk <= 0 || total_rows <= 0)
+    return fail(MSA_ERR_INVALID_VALUE,
+                "B, Hkv, total_q, topk and total_rows must be positive, total_k non-negative");
+  if (topk > kMaxTopk) return fail(MSA_ERR_NOT_SUPPORTED, "topk %d not supported (1..32)", topk);
+  if (static_cast<long long>(total_q) * topk > 0x7FFFFFFFLL)
+    return fail(MSA_ERR_INVALID_VALUE, "total_q*topk exceeds the int32 index range");
+  if (total_rows > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED, "total_rows = %d exceeds %d", total_rows, kMaxCsrRows);
+  if (!q2k || !cu_seqlens_q || !cu_seqlens_k || !row_ptr || !q_idx)
+    return fail(MSA_ERR_INVALID_VALUE, "null pointer");
+  if (!aligned(q2k, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) ||
+      !aligned(row_ptr, 4) || !aligned(q_idx, 4) || (slot && !aligned(slot, 4)))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned int32 pointer");
+  const size_t tbytes = align256(varlen_tables_bytes(B, total_q, 0));
+  const size_t need = tbytes + csr_workspace_bytes(1, Hkv, total_q, topk, total_rows);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const VarlenTables vt = varlen_tables_at(ws, B, total_q, 0);
+  hipError_t e = launch_varlen_tables(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, 0, vt, st);
+  if (e != hipSuccess) return hip_fail(e, "varlen tables");
+  e = launch_build_csr_varlen(q2k, vt, Hkv, total_q, topk, total_rows, row_ptr, q_idx, slot,
+                              ws + tbytes, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "k2q CSR build (varlen)");
 }
 
 int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path) {

@@ -29,10 +29,10 @@ namespace {
 __global__ __launch_bounds__(256) void combine_slots_kernel(
     const uint16_t* __restrict__ o_part, const float2* __restrict__ lse_part,
     const int32_t* __restrict__ q2k, int B, int Sq, int Hq, int Hkv, int topk, int nblk,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const int2* __restrict__ q_rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ float wts[16][kMaxTopk];
   __shared__ float row_lse[16];
-  const long long rows = static_cast<long long>(B) * Sq * Hq;
+  const long long rows = static_cast<long long>(B) * Sq * Hq;  // varlen: B = 1, Sq = total_q
   const long long rh0 = static_cast<long long>(blockIdx.x) * 16;
   const int tid = threadIdx.x;
   const int qpk = Hq / Hkv;
@@ -44,13 +44,15 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
       const long long gq = rh / Hq;
       const int head = static_cast<int>(rh % Hq);
       const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+      // varlen (q_rows set): q2k [Hkv][total_q][topk], valid ids below the sequence's block count
       const int32_t* row = q2k + ((static_cast<long long>(b) * Hkv + head / qpk) * Sq + qpos) * topk;
+      const int nb = q_rows ? q_rows[gq].y : nblk;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int t = t0 + 16 * k;
         if (t < topk) {
           const int sblk = row[t];
-          if (sblk >= 0 && sblk < nblk) {
+          if (sblk >= 0 && sblk < nb) {
             const float2 lm = lse_part[(gq * topk + t) * Hq + head];
             l[k] = lm.x;
             mr[k] = lm.y;
@@ -111,8 +113,12 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   *reinterpret_cast<u32x4*>(o + rh * kD + 8 * dc) = out;
   if (dc == 0) {
-    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-    lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = row_lse[rl];
+    if (q_rows) {
+      lse[rh] = row_lse[rl];  // [total_q][Hq]
+    } else {
+      const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
+      lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = row_lse[rl];
+    }
   }
 }
 
@@ -162,12 +168,14 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(
 
 hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
-                                float* lse, hipStream_t stream) {
+                                float* lse, hipStream_t stream, const CombineVarlen* v) {
   const long long total = static_cast<long long>(B) * Sq * Hq * 16;
   const long long blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (v && B != 1) return hipErrorInvalidValue;  // a varlen batch passes B = 1, Sq = total_q
   hipLaunchKernelGGL(combine_slots_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, o_part, lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk, o, lse);
+                     stream, o_part, lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
+                     v ? v->q_rows : nullptr, o, lse);
   return hipGetLastError();
 }
 

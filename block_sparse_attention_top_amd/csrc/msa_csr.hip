@@ -7,6 +7,11 @@
 // bit-exact against a reference). Entries are ordered by query, then slot, so
 // the result is unique and every call writes the same bits.
 //
+// A variable-length batch (q2k [Hkv, total_q, topk], `build_k2q_csr` with
+// cu_seqlens and total_rows) has the same passes: query g of sequence b maps
+// slot value s in [0, ceil(Skv_b / 128)) to row rowbase[b] + s, read from the
+// per-query table of (rowbase[b], block count).
+//
 // Method (a stable counting sort, no order-dependent atomics):
 //   1. count:   the entry sequence of each KV head, in (query, slot) order, is
 //               cut into tiles of whole queries; each tile histograms its rows
@@ -117,26 +122,46 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply(const int32_t* in, lo
 
 // ---------------------------------------------------------------------------
 // CSR passes. Grid (ntiles, Hkv). Tile `tile` of KV head hkv covers global
-// queries [tile * tile_q, min(B*Sq, (tile+1) * tile_q)).
+// queries [tile * tile_q, min(nq, (tile+1) * tile_q)).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restrict__ q2k, int B,
-                                                        int Hkv, int Sq, int topk, int nblk,
-                                                        int tile_q, int ntiles,
+struct CsrSrc {
+  const int32_t* q2k;
+  const int2* q_rows;  // varlen: (first row, block count) of each query's sequence
+  int Hkv, Sq, topk, nblk, nrows;
+  long long nq;        // B * Sq, or total_q
+};
+
+// CSR row of entry e = (query, slot) of KV head hkv, or -1 when its slot is unused
+template <bool VARLEN>
+__device__ __forceinline__ int entry_row(const CsrSrc& a, int hkv, long long e) {
+  const long long gq = e / a.topk;
+  if (VARLEN) {
+    const int s = a.q2k[static_cast<long long>(hkv) * a.nq * a.topk + e];
+    const int2 qr = a.q_rows[gq];
+    if (s < 0 || s >= qr.y) return -1;
+    const long long r = static_cast<long long>(qr.x) + s;
+    return r < a.nrows ? static_cast<int>(r) : -1;
+  } else {
+    const int t = static_cast<int>(e - gq * a.topk);
+    const int b = static_cast<int>(gq / a.Sq), qpos = static_cast<int>(gq - static_cast<long long>(b) * a.Sq);
+    const int s = a.q2k[((static_cast<long long>(b) * a.Hkv + hkv) * a.Sq + qpos) * a.topk + t];
+    return (s >= 0 && s < a.nblk) ? b * a.nblk + s : -1;
+  }
+}
+
+template <bool VARLEN>
+__global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
                                                         int32_t* __restrict__ counts) {
   extern __shared__ int cnt[];
   const int tile = blockIdx.x, hkv = blockIdx.y;
-  const int nrows = B * nblk;
+  const int nrows = a.nrows;
   for (int r = threadIdx.x; r < nrows; r += blockDim.x) cnt[r] = 0;
   __syncthreads();
-  const long long nq = static_cast<long long>(B) * Sq;
   const long long g0 = static_cast<long long>(tile) * tile_q;
-  const long long g1 = std::min<long long>(nq, g0 + tile_q);
-  for (long long e = g0 * topk + threadIdx.x; e < g1 * topk; e += blockDim.x) {
-    const long long gq = e / topk;
-    const int t = static_cast<int>(e % topk);
-    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-    const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
-    if (s >= 0 && s < nblk) atomicAdd(&cnt[b * nblk + s], 1);
+  const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
+  for (long long e = g0 * a.topk + threadIdx.x; e < g1 * a.topk; e += blockDim.x) {
+    const int row = entry_row<VARLEN>(a, hkv, e);
+    if (row >= 0) atomicAdd(&cnt[row], 1);
   }
   __syncthreads();
   for (int r = threadIdx.x; r < nrows; r += blockDim.x)
@@ -148,9 +173,8 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const int32_t* __restric
 // batches of 64 consecutive entries; a lane's rank among the lower lanes holding
 // the same row comes from ballots (one pass per distinct row in the batch), so
 // entries of a row keep ascending (query, slot) order.
-__global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ q2k, int B,
-                                                         int Hkv, int Sq, int topk, int nblk,
-                                                         int tile_q, int ntiles,
+template <bool VARLEN>
+__global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, int ntiles,
                                                          const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ q_idx,
                                                          int32_t* __restrict__ slot) {
@@ -158,32 +182,24 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
   constexpr int kPer = 16;  // entries per lane per round
   const int tile = blockIdx.x, hkv = blockIdx.y;
   const int lane = threadIdx.x;
-  const int nrows = B * nblk;
-  const long long cap = static_cast<long long>(B) * Sq * topk;
+  const int nrows = a.nrows;
+  const long long cap = a.nq * a.topk;
   const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
   const int base_h = offsets[seg];
   for (int r = lane; r < nrows; r += 64)
     cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
   __syncthreads();
-  const long long nq = static_cast<long long>(B) * Sq;
   const long long g0 = static_cast<long long>(tile) * tile_q;
-  const long long g1 = std::min<long long>(nq, g0 + tile_q);
-  const long long e_end = g1 * topk;
+  const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
+  const long long e_end = g1 * a.topk;
   int32_t* qi = q_idx + hkv * cap;
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
-  for (long long rb = g0 * topk; rb < e_end; rb += 64 * kPer) {
+  for (long long rb = g0 * a.topk; rb < e_end; rb += 64 * kPer) {
     int rows[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
-      rows[k] = -1;
-      if (e < e_end) {
-        const long long gq = e / topk;
-        const int t = static_cast<int>(e % topk);
-        const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-        const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
-        if (s >= 0 && s < nblk) rows[k] = b * nblk + s;
-      }
+      rows[k] = e < e_end ? entry_row<VARLEN>(a, hkv, e) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -206,8 +222,8 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
       __syncthreads();
       if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
       if (row >= 0) {
-        qi[pos] = static_cast<int32_t>(e / topk);
-        if (sl) sl[pos] = static_cast<int32_t>(e % topk);
+        qi[pos] = static_cast<int32_t>(e / a.topk);
+        if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
       }
       __syncthreads();
     }
@@ -216,33 +232,29 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restri
 
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
+template <bool VARLEN>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
-    const int32_t* __restrict__ q2k, int B, int Hkv, int Sq, int topk, int nblk, int tile_q,
-    int ntiles, const int32_t* __restrict__ offsets, int32_t* __restrict__ q_idx,
-    int32_t* __restrict__ slot) {
+    CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ q_idx, int32_t* __restrict__ slot) {
   extern __shared__ int cursor[];
   const int tile = blockIdx.x, hkv = blockIdx.y;
-  const int nrows = B * nblk;
-  const long long cap = static_cast<long long>(B) * Sq * topk;
+  const int nrows = a.nrows;
+  const long long cap = a.nq * a.topk;
   const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
   const int base_h = offsets[seg];
   for (int r = threadIdx.x; r < nrows; r += blockDim.x)
     cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
   __syncthreads();
-  const long long nq = static_cast<long long>(B) * Sq;
   const long long g0 = static_cast<long long>(tile) * tile_q;
-  const long long g1 = std::min<long long>(nq, g0 + tile_q);
+  const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
   int32_t* qi = q_idx + hkv * cap;
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
-  for (long long e = g0 * topk + threadIdx.x; e < g1 * topk; e += blockDim.x) {
-    const long long gq = e / topk;
-    const int t = static_cast<int>(e % topk);
-    const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-    const int s = q2k[((static_cast<long long>(b) * Hkv + hkv) * Sq + qpos) * topk + t];
-    if (s < 0 || s >= nblk) continue;
-    const int pos = atomicAdd(&cursor[b * nblk + s], 1);
-    qi[pos] = static_cast<int32_t>(gq);
-    if (sl) sl[pos] = t;
+  for (long long e = g0 * a.topk + threadIdx.x; e < g1 * a.topk; e += blockDim.x) {
+    const int row = entry_row<VARLEN>(a, hkv, e);
+    if (row < 0) continue;
+    const int pos = atomicAdd(&cursor[row], 1);
+    qi[pos] = static_cast<int32_t>(e / a.topk);
+    if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
   }
 }
 
@@ -307,11 +319,14 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows) {
          align256(scan_tmp_ints(plan.counts) * 4);
 }
 
-hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
-                            int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream, bool ordered) {
-  const int nrows = B * nblk;
-  const CsrPlan plan = csr_plan(B, Hkv, Sq, topk, nrows);
+namespace {
+
+template <bool VARLEN>
+hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
+                     hipStream_t stream, bool ordered) {
+  const int nrows = a.nrows;
+  // the plan depends on the query count and the rows only: B * Sq == nq
+  const CsrPlan plan = csr_plan(1, a.Hkv, static_cast<int>(a.nq), a.topk, nrows);
   char* base = static_cast<char*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(base);
   base += align256(plan.counts * 4);
@@ -319,23 +334,49 @@ hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk
   base += align256((plan.counts + 1) * 4);
   int32_t* tmp = reinterpret_cast<int32_t*>(base);
   const size_t lds = static_cast<size_t>(nrows) * sizeof(int);
-  const dim3 grid(plan.ntiles, Hkv);
-  hipLaunchKernelGGL(csr_count_kernel, grid, dim3(256), lds, stream, q2k, B, Hkv, Sq, topk, nblk,
-                     plan.tile_q, plan.ntiles, counts);
+  const dim3 grid(plan.ntiles, a.Hkv);
+  hipLaunchKernelGGL(csr_count_kernel<VARLEN>, grid, dim3(256), lds, stream, a, plan.tile_q,
+                     plan.ntiles, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
   if (ordered)
-    hipLaunchKernelGGL(csr_scatter_kernel, grid, dim3(64), lds, stream, q2k, B, Hkv, Sq, topk,
-                       nblk, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+    hipLaunchKernelGGL(csr_scatter_kernel<VARLEN>, grid, dim3(64), lds, stream, a, plan.tile_q,
+                       plan.ntiles, offsets, q_idx, slot);
   else
-    hipLaunchKernelGGL(csr_scatter_unordered_kernel, grid, dim3(256), lds, stream, q2k, B, Hkv,
-                       Sq, topk, nblk, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
-  const long long nrp = static_cast<long long>(Hkv) * (nrows + 1);
+    hipLaunchKernelGGL(csr_scatter_unordered_kernel<VARLEN>, grid, dim3(256), lds, stream, a,
+                       plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
   hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
-                     offsets, Hkv, nrows, plan.ntiles, row_ptr);
+                     offsets, a.Hkv, nrows, plan.ntiles, row_ptr);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
+                            int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
+                            hipStream_t stream, bool ordered) {
+  CsrSrc a{};
+  a.q2k = q2k;
+  a.Hkv = Hkv; a.Sq = Sq; a.topk = topk; a.nblk = nblk;
+  a.nrows = B * nblk;
+  a.nq = static_cast<long long>(B) * Sq;
+  return build_csr<false>(a, row_ptr, q_idx, slot, ws, stream, ordered);
+}
+
+hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, int Hkv,
+                                   int total_q, int topk, int nrows, int32_t* row_ptr,
+                                   int32_t* q_idx, int32_t* slot, void* ws, hipStream_t stream,
+                                   bool ordered) {
+  CsrSrc a{};
+  a.q2k = q2k;
+  a.q_rows = t.q_rows;
+  a.Hkv = Hkv; a.Sq = total_q; a.topk = topk; a.nblk = 0;
+  a.nrows = nrows;
+  a.nq = total_q;
+  return build_csr<true>(a, row_ptr, q_idx, slot, ws, stream, ordered);
 }
 
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,

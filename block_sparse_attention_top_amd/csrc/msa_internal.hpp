@@ -99,6 +99,49 @@ __host__ __device__ __forceinline__ long long floor_div(long long a, long long b
 }
 
 // ---------------------------------------------------------------------------
+// Variable-length batches. cu_q / cu_k are prefix sums over the B sequences
+// (cu[0] = 0, cu[B] = total); sequence b owns the packed query rows
+// [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]). Offsets read from
+// them are clamped into [0, total] so that malformed prefix sums give
+// unspecified values but never an access outside the packed tensors.
+// ---------------------------------------------------------------------------
+// largest b in [0, n) with cu[b] <= g (binary search; n >= 1)
+__device__ __forceinline__ int seq_search(const int32_t* cu, int n, long long g) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+// first row and length of sequence b in a packed dimension of `total` rows
+__device__ __forceinline__ void seq_range(const int32_t* cu, int b, long long total,
+                                          long long& beg, long long& len) {
+  long long a = cu[b], e = cu[b + 1];
+  a = a < 0 ? 0 : (a > total ? total : a);
+  e = e < a ? a : (e > total ? total : e);
+  beg = a;
+  len = e - a;
+}
+
+// Per-sequence tables of a varlen batch, built on the device (msa_varlen.hip):
+//   rowbase [B+1]      first k2q CSR row of each sequence: prefix sum of ceil(Skv_b / 128)
+//   q_rows  [total_q]  (rowbase[b], ceil(Skv_b / 128)) of the sequence b of each query
+//   row_seq [nrows]    sequence of each CSR row, -1 past rowbase[B]
+struct VarlenTables {
+  int32_t* rowbase;
+  int2* q_rows;
+  int32_t* row_seq;
+};
+size_t varlen_tables_bytes(int B, long long total_q, long long nrows);
+// carves the tables out of ws (varlen_tables_bytes(...) bytes, 256-byte aligned)
+VarlenTables varlen_tables_at(void* ws, int B, long long total_q, long long nrows);
+hipError_t launch_varlen_tables(const int32_t* cu_q, const int32_t* cu_k, int B, long long total_q,
+                                long long total_k, long long nrows, const VarlenTables& t,
+                                hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() after its launches).
 // ---------------------------------------------------------------------------
 struct QcParams {
@@ -118,6 +161,12 @@ struct QcParams {
   float* lse;                // [B,Hq,Sq]
   float* o_part;             // [splits][B*Sq][Hq][D]
   float* lse_part;           // [splits][B*Sq][Hq]
+  // variable-length batch (contiguous K/V only): cu_q != nullptr. Then q is
+  // [total_q,Hq,D], k/v [total_k,Hkv,D], q2k [Hkv,total_q,topk], o [total_q,Hq,D],
+  // lse [total_q,Hq]; B is the sequence count and Sq, Skv, nblk are unused.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  long long total_q, total_k;
 };
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream);
 // paged decode over the union of the blocks of each (b, hkv): splits partition that
@@ -159,6 +208,13 @@ struct KvParams {
   uint16_t* o_part;          // bf16 [B*Sq][topk][Hkv][16 dim chunks][qpk][8], unnormalised:
                              // sum_j e^(s_j - M) V_j
   float2* lse_part;          // [B*Sq][topk][Hq]: (LSE of the block, reference max M), natural log
+  // variable-length batch: cu_q != nullptr, rows r of sequence row_seq[r] hold its
+  // block r - rowbase[b]; B*Sq above reads total_q (cap = total_q * topk)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* rowbase;
+  const int32_t* row_seq;
+  long long total_q, total_k;
 };
 // grid = an upper bound on the item count (workgroups past the count exit)
 hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
@@ -168,9 +224,13 @@ hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int
 int device_cu_count();
 
 // combine of slot partials (kv-centric): valid slots are the q2k entries in [0, nblk)
+// (uniform batch), or in [0, ceil(Skv_b / 128)) for a varlen batch (v != nullptr)
+struct CombineVarlen {
+  const int2* q_rows;  // VarlenTables::q_rows
+};
 hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
-                                float* lse, hipStream_t stream);
+                                float* lse, hipStream_t stream, const CombineVarlen* v = nullptr);
 // combine of split partials (split-KV q-centric / paged decode)
 hipError_t launch_combine_splits(const float* o_part, const float* lse_part, int B, int Sq, int Hq,
                                  int splits, uint16_t* o, float* lse, hipStream_t stream);
@@ -193,6 +253,13 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows);
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
                             hipStream_t stream, bool ordered = true);
+// varlen CSR over nrows rows (q2k [Hkv,total_q,topk]); the tables come from
+// launch_varlen_tables; entries whose row is >= nrows are dropped. Workspace:
+// csr_workspace_bytes(1, Hkv, total_q, topk, nrows).
+hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, int Hkv,
+                                   int total_q, int topk,
+                                   int nrows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
+                                   void* ws, hipStream_t stream, bool ordered = true);
 // per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
                                  int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,

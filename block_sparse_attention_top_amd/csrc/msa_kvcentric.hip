@@ -12,6 +12,11 @@
 // unnormalised: U = sum_j e^(s_j - M) V_j with the block's reference max M,
 // stored beside (LSE of the block, M); the combine applies e^(M - LSE_total).
 //
+// A variable-length batch (packed Q/K/V with cu_seqlens) differs only in where
+// a row's keys and queries live: row r is block r - rowbase[b] of sequence b
+// (from the per-row sequence table), the block's keys start at cu_seqlens_k[b]
+// and may end inside it, and the causal limit uses the sequence's own lengths.
+//
 // Layout on gfx950. A work item is (KV head, CSR row = (b, block), a chunk of
 // up to `chunk_entries` CSR entries), listed in an item table by the schedule
 // kernel. A workgroup of 4 waves stages the block's K and V tiles
@@ -45,7 +50,25 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   const int tid = threadIdx.x;
   const int4 item = p.items[w];
   const int hkv = item.x, r = item.y, e0 = item.z, ne = item.w;
-  const int b = r / p.nblk, s = r % p.nblk;
+  // the row's sequence b and block s; the sequence's first query and query
+  // count, first key and key count
+  int s;
+  long long qbeg, sq_b, kbeg, kvlen;
+  if (p.cu_q) {
+    const int b = p.row_seq[r];
+    if (b < 0) return;  // a row past the last sequence holds no entries
+    s = r - p.rowbase[b];
+    seq_range(p.cu_q, b, p.total_q, qbeg, sq_b);
+    seq_range(p.cu_k, b, p.total_k, kbeg, kvlen);
+  } else {
+    const int b = r / p.nblk;
+    s = r % p.nblk;
+    qbeg = static_cast<long long>(b) * p.Sq;
+    sq_b = p.Sq;
+    kbeg = static_cast<long long>(b) * p.Skv;
+    kvlen = p.Skv;
+  }
+  const long long blk0 = static_cast<long long>(s) * kBlk;
 
   // stage the chunk's entries and the block's K and V (128 tokens x 256 B each)
   for (int i = tid; i < ne; i += 256) {
@@ -53,13 +76,14 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
     ent_t[i] = p.slot[hkv * p.cap + e0 + i];
   }
   {
-    const long long tok0 = static_cast<long long>(b) * p.Skv + static_cast<long long>(s) * kBlk;
+    // rows past the sequence's last key re-read that key; they are masked out of S
     u32x4 rk[8], rv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ci = i * 256 + tid;
       const int row = ci >> 4, c = ci & 15;
-      const long long off = ((tok0 + row) * p.Hkv + hkv) * kD + c * 8;
+      const long long tok = kbeg + min(blk0 + row, kvlen - 1);
+      const long long off = (tok * p.Hkv + hkv) * kD + c * 8;
       rk[i] = *reinterpret_cast<const u32x4*>(p.k + off);
       rv[i] = *reinterpret_cast<const u32x4*>(p.v + off);
     }
@@ -80,8 +104,8 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   const int ent = n / QPK, head_i = n % QPK;
   const int head = hkv * QPK + head_i;
   const int j16 = lane >> 4, lq = lane & 15, rr = lq >> 2, cq = lq & 3;
-  const long long lim_off = static_cast<long long>(p.Skv) - p.Sq;
-  const long long blk0 = static_cast<long long>(s) * kBlk;
+  const long long lim_off = kvlen - sq_b;
+  const long long kend = min(kvlen - blk0, static_cast<long long>(kBlk));  // keys of the block
   const int nsteps = (ne + EPW - 1) / EPW;
   const float c2 = p.scale_log2;
   // lane offsets inside the tiles: K fragment row n, chunk h; V transposed reads
@@ -114,10 +138,9 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
     // re-read from LDS each step instead of being held in registers.
     int kbase = kbase0, vbase = vbase0;
     asm volatile("" : "+v"(kbase), "+v"(vbase));
-    const int qpos = rc.gq % p.Sq;
+    const long long qpos = rc.gq - qbeg;
     const long long lim = p.causal ? qpos + lim_off : (1LL << 62);
-    const int vis =
-        rc.ok ? static_cast<int>(min(lim - blk0 + 1, static_cast<long long>(kBlk))) : 0;
+    const int vis = rc.ok ? static_cast<int>(max(min(lim - blk0 + 1, kend), -1LL)) : 0;
     const bool full = __all(vis >= kBlk);
     // Block-local softmax in two 64-token halves. The reference max m_ref is the
     // first half's row max; the second half only rescales (online softmax) when

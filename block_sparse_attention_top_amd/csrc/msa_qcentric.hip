@@ -19,6 +19,11 @@
 // With splits > 1 a wave handles a contiguous share of the slots and writes a
 // normalised fp32 partial (O, LSE) that the split combine merges (the
 // split-KV decode of `sparse_decode_atten_func` on the page "MSA interface.py").
+//
+// Variable-length batches (packed Q/K/V with cu_seqlens, contiguous K/V): a
+// wave finds the sequence of its query row by binary search over
+// cu_seqlens_q; block ids count from the sequence's first key and the causal
+// limit uses the sequence's own lengths.
 #include "msa_internal.hpp"
 
 #include <math.h>
@@ -41,14 +46,35 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   long long item = blockIdx.x;
   const int sp = static_cast<int>(item % p.splits);
   item /= p.splits;
-  const int qpos = static_cast<int>(item % p.Sq);
-  item /= p.Sq;
-  const int hkv = static_cast<int>(item % p.Hkv);
-  const int b = static_cast<int>(item / p.Hkv);
+  // the row's sequence b: its query position and count, its first key and key count
+  int b, hkv;
+  long long grow, qpos, sq_b, kbeg, kvlen;
+  const int32_t* sel;
+  if (!PAGED && p.cu_q) {
+    grow = item % p.total_q;
+    hkv = static_cast<int>(item / p.total_q);
+    b = seq_search(p.cu_q, p.B, grow);
+    long long qbeg;
+    seq_range(p.cu_q, b, p.total_q, qbeg, sq_b);
+    qpos = grow - qbeg;
+    seq_range(p.cu_k, b, p.total_k, kbeg, kvlen);
+    sel = p.q2k + (static_cast<long long>(hkv) * p.total_q + grow) * p.topk;
+  } else {
+    qpos = item % p.Sq;
+    item /= p.Sq;
+    hkv = static_cast<int>(item % p.Hkv);
+    b = static_cast<int>(item / p.Hkv);
+    grow = static_cast<long long>(b) * p.Sq + qpos;
+    sq_b = p.Sq;
+    kbeg = static_cast<long long>(b) * p.Skv;
+    kvlen = PAGED ? static_cast<long long>(p.seqused[b]) : p.Skv;
+    sel = p.q2k + ((static_cast<long long>(b) * p.Hkv + hkv) * p.Sq + qpos) * p.topk;
+  }
+  // valid block ids: [0, nblk) (uniform or paged) or the blocks of the sequence (varlen)
+  const long long nblk_b = (!PAGED && p.cu_q) ? (kvlen + kBlk - 1) / kBlk : p.nblk;
 
   const int head = hkv * p.qpk + n;
   const bool head_ok = n < p.qpk;
-  const long long grow = static_cast<long long>(b) * p.Sq + qpos;
 
   // Q fragments: lane (n, g) holds dims 32*kq + 8*g .. +7 of head n.
   bf16x8 qf[4];
@@ -62,14 +88,12 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     }
   }
 
-  const long long kvlen = PAGED ? static_cast<long long>(p.seqused[b]) : p.Skv;
-  long long end = kvlen;  // keys [0, end) are visible
+  long long end = kvlen;  // keys [0, end) of the sequence are visible
   if (p.causal) {
-    const long long lim = qpos + kvlen - p.Sq;
+    const long long lim = qpos + kvlen - sq_b;
     if (lim + 1 < end) end = lim + 1;
   }
 
-  const int32_t* sel = p.q2k + ((static_cast<long long>(b) * p.Hkv + hkv) * p.Sq + qpos) * p.topk;
   const int per = (p.topk + p.splits - 1) / p.splits;
   const int t0 = sp * per;
   const int t1 = min(p.topk, t0 + per);
@@ -79,7 +103,7 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     while (t < t1) {
       if (u < 4) {
         s = sel[t];
-        bool ok = s >= 0 && s < p.nblk &&
+        bool ok = s >= 0 && s < nblk_b &&
                   static_cast<long long>(s) * kBlk + kSub * u < end;
         if (ok && PAGED) {
           pg = p.page_table[static_cast<long long>(b) * p.max_pages + s];
@@ -101,9 +125,9 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
       long long off;
       if (PAGED)
         off = ((static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * u + row) * kD + c * 8;
-      else
-        off = ((static_cast<long long>(b) * p.Skv + static_cast<long long>(s) * kBlk + kSub * u + row) *
-                   p.Hkv + hkv) * kD + c * 8;
+      else  // rows past the sequence's last key re-read that key (stored as zeros)
+        off = ((kbeg + min(static_cast<long long>(s) * kBlk + kSub * u + row, kvlen - 1)) * p.Hkv +
+               hkv) * kD + c * 8;
       kr[i] = *reinterpret_cast<const u32x4*>(p.k + off);
       vr[i] = *reinterpret_cast<const u32x4*>(p.v + off);
     }
@@ -213,9 +237,14 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
                        pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
       *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
     }
-    if (g == 0) p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos] = lse_v;
+    if (g == 0) {
+      if (!PAGED && p.cu_q)
+        p.lse[grow * p.Hq + head] = lse_v;
+      else
+        p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos] = lse_v;
+    }
   } else {
-    const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;
+    const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;  // paged
     float* orow = p.o_part + prow * kD + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = oacc[dt] * inv;
@@ -226,7 +255,9 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
 }  // namespace
 
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
-  const long long items = static_cast<long long>(p.B) * p.Hkv * p.Sq * p.splits;
+  const long long rows = (!paged && p.cu_q) ? p.total_q : static_cast<long long>(p.B) * p.Sq;
+  const long long items = rows * p.Hkv * p.splits;
+  if (!paged && p.cu_q && p.splits != 1) return hipErrorInvalidValue;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));

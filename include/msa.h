@@ -113,6 +113,69 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Variable-length batches: the packed form of sparse_atten_func and
+ * build_k2q_csr on the page "MSA interface.py" (cu_seqlens_q / cu_seqlens_k).
+ * Sequence b owns the query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and the
+ * key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1. Its block ids count from its
+ * first key (block s = its keys 128 s .. 128 s + 127; the last block may be
+ * partial), valid ids are [0, ceil(Skv_b / 128)), and the causal limit is
+ * q + Skv_b - Sq_b with q the row's position inside its sequence: each sequence
+ * is the definition at the top of this file with B = 1. Sequences may be empty.
+ *   q             bf16 [total_q, Hq, D]
+ *   k, v          bf16 [total_k, Hkv, D]   (may be NULL when total_k == 0)
+ *   q2k           int32 [Hkv, total_q, topk]
+ *   cu_seqlens_q  int32 [B + 1] (device): 0 = cu[0] <= cu[1] <= ... <= cu[B] = total_q
+ *   cu_seqlens_k  int32 [B + 1] (device): likewise, ending at total_k. Prefix sums
+ *                 that break these rules give unspecified results, but every
+ *                 access stays inside the tensors.
+ *   csr_row_ptr, csr_q_idx, csr_slot, csr_total_rows
+ *                 optional prebuilt CSR from msa_build_k2q_csr_varlen over
+ *                 csr_total_rows rows (the three pointers all or none;
+ *                 1 <= csr_total_rows <= floor(total_k / 128) + B); used by the
+ *                 kv-centric path only
+ *   path          MSA_PATH_AUTO, MSA_PATH_QCENTRIC or MSA_PATH_KVCENTRIC
+ *                 (MSA_ERR_NOT_SUPPORTED for the tile and decode paths)
+ *   o             bf16 [total_q, Hq, D]   (out)
+ *   lse           fp32 [total_q, Hq]      (out; the packed layout of the page)
+ *   workspace     at least msa_sparse_fwd_varlen_workspace_size(...)
+ * total_q == 0 returns MSA_OK without touching anything.
+ */
+size_t msa_sparse_fwd_varlen_workspace_size(int B, int total_q, int total_k, int Hq, int Hkv,
+                                            int D, int topk, int blk_kv, int path);
+int msa_sparse_fwd_varlen_path(int B, int total_q, int total_k, int Hq, int Hkv, int topk,
+                               int path);
+int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* q2k,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
+                          const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
+                          int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
+                          float softmax_scale, int path, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * k2q CSR of a variable-length batch (build_k2q_csr with cu_seqlens and
+ * total_rows). Row rowbase[b] + s, with rowbase[b] the sum over b' < b of
+ * ceil(Skv_b' / 128), lists for KV head hkv the global query ids g of sequence
+ * b whose index row q2k[hkv][g][:] holds block s, ascending in g and then in
+ * slot t; slot holds that t.
+ *   q2k          int32 [Hkv, total_q, topk]
+ *   cu_seqlens_q, cu_seqlens_k   as msa_sparse_fwd_varlen
+ *   total_rows   sum over b of ceil(Skv_b / 128), computed by the caller from its
+ *                lengths (entries of rows >= total_rows are dropped, rows past
+ *                the true count stay empty)
+ *   row_ptr      int32 [Hkv, total_rows + 1]   (out)
+ *   q_idx, slot  int32 [Hkv, total_q * topk]   (out; slot may be NULL)
+ *   workspace    at least msa_build_k2q_csr_varlen_workspace_size(...)
+ * Deterministic: every call writes the same bits.
+ */
+size_t msa_build_k2q_csr_varlen_workspace_size(int B, int Hkv, int total_q, int topk,
+                                               int total_rows);
+int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, int B, int Hkv, int total_q, int total_k,
+                             int topk, int total_rows, int32_t* row_ptr, int32_t* q_idx,
+                             int32_t* slot, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sparse forward, paged K/V (sparse_atten_func with page_table / seqused_k,
  * and the split-KV decode of sparse_decode_atten_func on the page
  * "MSA interface.py"; paging as in pack_paged_kv on the test page).

@@ -137,3 +137,68 @@ def test_auto_path_resolution():
     assert msa.msa_paged_sparse_fwd_splits(32, 8, 4, 16) == 1
     # contiguous: the query tile is asked for
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 4) == msa.MSA_PATH_TILE
+
+
+def fwd_varlen(**kw):
+    lib = msa.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, cuq=FAKE, cuk=FAKE, rp=None, qi=None, sl=None,
+             rows=0, B=3, tq=300, tk=900, Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1,
+             scale=0.0, path=0, o=FAKE, lse=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return lib.msa_sparse_fwd_varlen(a["q"], a["k"], a["v"], a["q2k"], a["cuq"], a["cuk"],
+                                     a["rp"], a["qi"], a["sl"], a["rows"], a["B"], a["tq"],
+                                     a["tk"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
+                                     a["causal"], a["scale"], a["path"], a["o"], a["lse"],
+                                     a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), 2), (dict(blk=64), 2), (dict(Hq=3), 2), (dict(topk=33), 2), (dict(B=0), 1),
+    (dict(tq=-1), 1), (dict(tk=-1), 1), (dict(cuq=None), 1), (dict(cuk=FAKE + 2), 1),
+    (dict(q=None), 1), (dict(o=FAKE + 8), 1), (dict(path=4), 2), (dict(path=3), 2),
+    (dict(path=9), 1), (dict(rp=FAKE), 1),
+    # a prebuilt CSR needs its row count, at most floor(total_k / 128) + B
+    (dict(rp=FAKE, qi=FAKE, sl=FAKE, rows=0, path=2), 1),
+    (dict(rp=FAKE, qi=FAKE, sl=FAKE, rows=7 + 3 + 1, path=2), 1),
+    # kv-centric without workspace / with too many CSR rows
+    (dict(path=2), 1), (dict(path=2, tk=128 * 20000), 2),
+    # keys may be absent only when total_k == 0
+    (dict(k=None), 1),
+])
+def test_sparse_fwd_varlen_rejects(kw, code):
+    assert fwd_varlen(**kw) == code
+    assert msa.msa_last_error() != ""
+
+
+def test_sparse_fwd_varlen_empty_batch_is_a_no_op():
+    # total_q == 0: nothing to compute, no pointer is needed
+    assert fwd_varlen(q=None, o=None, lse=None, q2k=None, tq=0) == 0
+
+
+def test_varlen_workspace_and_paths():
+    # small batches run q-centric (no workspace), large ones kv-centric
+    assert msa.msa_sparse_fwd_varlen_path(3, 300, 900, 16, 1, 4) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(4, 32768, 32768, 64, 4, 16) == msa.MSA_PATH_KVCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(4, 32768, 0, 64, 4, 16) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(2, 8192, 128 * 20000, 64, 4, 16) == \
+        msa.MSA_PATH_QCENTRIC
+    assert msa.msa_sparse_fwd_varlen_workspace_size(3, 300, 900, 16, 1, 128, 4, 128, 1) == 0
+    n = msa.msa_sparse_fwd_varlen_workspace_size(3, 300, 900, 16, 1, 128, 4, 128, 2)
+    assert n >= 300 * 4 * 16 * 128 * 2
+    # the varlen CSR workspace holds the per-sequence tables and the count passes
+    assert msa.msa_build_k2q_csr_varlen_workspace_size(3, 2, 300, 4, 9) > 300 * 8
+
+
+def test_csr_varlen_rejects():
+    lib = msa.load_library()
+    base = [FAKE, FAKE, FAKE, 3, 2, 300, 900, 4, 9, FAKE, FAKE, None, FAKE, 1 << 20, None]
+    a = list(base); a[8] = 0  # total_rows
+    assert lib.msa_build_k2q_csr_varlen(*a) == 1
+    a = list(base); a[8] = 20000
+    assert lib.msa_build_k2q_csr_varlen(*a) == 2
+    a = list(base); a[7] = 33
+    assert lib.msa_build_k2q_csr_varlen(*a) == 2
+    a = list(base); a[1] = None
+    assert lib.msa_build_k2q_csr_varlen(*a) == 1
+    a = list(base); a[12] = None; a[13] = 0
+    assert lib.msa_build_k2q_csr_varlen(*a) == 1
