@@ -148,8 +148,8 @@ def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal:
     """Oracle forward of a variable-length batch.
 
     q [total_q,Hq,D], k/v [total_k,Hkv,D] (uint16 bf16 bits), q2k [Hkv,total_q,topk],
-    cu_seqlens_q / cu_seqlens_k [B+1]. rows=None: O [total_q,Hq,D] and LSE [Hq,total_q];
-    else O [n,Hq,D] and LSE [n,Hq] for the given global rows.
+    cu_seqlens_q / cu_seqlens_k [B+1]. Returns O [n,Hq,D] and LSE [n,Hq] (the packed
+    layout of the interface page) for the given global rows, n = total_q when rows=None.
     """
     q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
     q2k, cq, ck = _c(q2k, np.int32), _c(cu_seqlens_q, np.int32), _c(cu_seqlens_k, np.int32)
@@ -169,8 +169,6 @@ def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal:
                                                 nthreads)
     if rc != 0:
         raise ValueError("oracle_sparse_attention_varlen: invalid arguments")
-    if rws is None:
-        return o, lse.T.copy()
     return o, lse
 
 
