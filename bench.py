@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the top-k block-sparse GQA attention forward on one MI355X.
 
-A step is one full forward call (msa_sparse_fwd, or msa_paged_sparse_fwd for the
-paged decode workload) over one batch of seeded synthetic inputs already
+A step is one full forward call (msa_sparse_fwd, msa_sparse_fwd_varlen for the
+ragged-batch workload, or msa_paged_sparse_fwd for the paged decode workload)
+over one batch of seeded synthetic inputs already
 resident in HBM: for the kv-centric path that includes the k2q CSR build, the
 schedule, the per-block kernel and the combine. Prints one JSON line.
 
@@ -12,7 +13,7 @@ Metrics (the pages' benchmark harness, "test_sparse_atten.py"):
   decode:  GB/s of algorithmic bytes = distinct selected K/V blocks of each
            (sequence, KV head) * 64 KiB + Q + O + LSE + q2k + page table
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2|vmix|...]
                        [--path auto|q|kv|decode] [--splits N] [--extra c5,c3u]
                        [--no-cpu-baseline]
 (--extra workloads run with the automatic path)
@@ -117,17 +118,37 @@ class Case:
         import torch
         import block_sparse_attention_top_amd as msa
         import workloads as wl
-        self.key, self.w = key, wl.WORKLOADS[key]
+        self.varlen = key in wl.VARLEN_WORKLOADS
+        self.key = key
+        self.w = wl.VARLEN_WORKLOADS[key] if self.varlen else wl.WORKLOADS[key]
         w = self.w
         t0 = time.time()
-        self.inp = wl.make_inputs(w)
+        self.inp = wl.make_varlen_workload_inputs(w) if self.varlen else wl.make_inputs(w)
         log(f"[bench] {key}: inputs generated in {time.time() - t0:.1f}s")
         dev = lambda x: (torch.from_numpy(x).view(torch.bfloat16) if x.dtype == np.uint16
                          else torch.from_numpy(x)).to("cuda")
         self.t = {k: dev(v) for k, v in self.inp.items()}
+        t = self.t
+        if self.varlen:
+            self.o = torch.empty((w.total_q, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+            self.lse = torch.empty((w.total_q, w.Hq), dtype=torch.float32, device="cuda")
+            p = msa.msa_sparse_fwd_varlen_path(w.B, w.total_q, w.total_k, w.Hq, w.Hkv, w.topk,
+                                               PATHS[path])
+            if p not in (1, 2):
+                raise SystemExit(f"path {path} does not apply to the varlen workload {key}")
+            nb = msa.msa_sparse_fwd_varlen_workspace_size(w.B, w.total_q, w.total_k, w.Hq, w.Hkv,
+                                                          w.D, w.topk, w.blk, p)
+            ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+            self.path_name = {1: "q-centric", 2: "kv-centric"}[p]
+            self.splits = 1
+            self.step = lambda: msa.msa_sparse_fwd_varlen(
+                t["q"], t["k"], t["v"], t["q2k"], t["cu_seqlens_q"], t["cu_seqlens_k"],
+                causal=w.causal, path=p, o=self.o, lse=self.lse, workspace=ws)
+            self.bytes = None
+            self.flops = w.effective_flops()
+            return
         self.o = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
-        t = self.t
         if w.paged:
             p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, PATHS[path])
             if p not in (1, 3):
@@ -187,8 +208,23 @@ class Case:
         import torch
         import block_sparse_attention_top_amd as msa
         w, t = self.w, self.t
-        nblk = w.Skv // w.blk
-        csr = msa.msa_build_k2q_csr(t["q2k"], nblk)
+        if self.varlen:
+            rows = int(sum((k + w.blk - 1) // w.blk for k in w.k_lens))
+            cuq, cuk = t["cu_seqlens_q"], t["cu_seqlens_k"]
+            csr = msa.msa_build_k2q_csr_varlen(t["q2k"], cuq, cuk, w.total_k, rows)
+            build = lambda: msa.msa_build_k2q_csr_varlen(t["q2k"], cuq, cuk, w.total_k, rows,
+                                                         row_ptr=csr[0], q_idx=csr[1],
+                                                         slot=csr[2])
+            fwd = lambda: msa.msa_sparse_fwd_varlen(t["q"], t["k"], t["v"], t["q2k"], cuq, cuk,
+                                                    *csr, rows, causal=w.causal, path=2,
+                                                    o=self.o, lse=self.lse)
+        else:
+            nblk = w.Skv // w.blk
+            csr = msa.msa_build_k2q_csr(t["q2k"], nblk)
+            build = lambda: msa.msa_build_k2q_csr(t["q2k"], nblk, row_ptr=csr[0], q_idx=csr[1],
+                                                  slot=csr[2])
+            fwd = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"], *csr,
+                                             causal=w.causal, path=2, o=self.o, lse=self.lse)
 
         def timed(fn):
             for _ in range(warmup):
@@ -202,11 +238,8 @@ class Case:
             b.synchronize()
             return a.elapsed_time(b) / steps
 
-        csr_ms = timed(lambda: msa.msa_build_k2q_csr(t["q2k"], nblk, row_ptr=csr[0], q_idx=csr[1],
-                                                     slot=csr[2]))
-        fwd_ms = timed(lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"], *csr,
-                                                  causal=w.causal, path=2, o=self.o,
-                                                  lse=self.lse))
+        csr_ms = timed(build)
+        fwd_ms = timed(fwd)
         both_ms = timed(self.step)
         return {"csr_ms": csr_ms, "fwd_ms": fwd_ms, "csr_plus_fwd_ms": both_ms,
                 "fwd_TFLOP_per_s": self.flops / (fwd_ms * 1e-3) / 1e12}
@@ -267,12 +300,16 @@ def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
     w, inp = case.w, case.inp
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     rng = np.random.default_rng(0)
-    total_rows = w.B * w.Sq
+    total_rows = w.total_q if case.varlen else w.B * w.Sq
 
     def run(n):
         rows = np.sort(rng.choice(total_rows, size=min(n, total_rows), replace=False))
         t0 = time.perf_counter()
-        if w.paged:
+        if case.varlen:
+            oracle.sparse_attention_varlen(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                           inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                                           causal=w.causal, rows=rows, nthreads=threads)
+        elif w.paged:
             oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
                                           inp["page_table"], inp["seqused_k"], inp["q2k"],
                                           causal=w.causal, rows=rows, nthreads=threads)
@@ -364,10 +401,15 @@ def main() -> int:
         "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
-                   "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
-                   "causal": w.causal, "path": case.path_name, "splits": case.splits,
-                   "parallelism": "none"},
+        "config": ({"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
+                    "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
+                    "causal": w.causal, "path": case.path_name, "splits": case.splits,
+                    "parallelism": "none"} if not case.varlen else
+                   {"workload": w.name, "B": w.B, "varlen": True, "total_q": w.total_q,
+                    "total_k": w.total_k, "q_lens": list(w.q_lens), "k_lens": list(w.k_lens),
+                    "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
+                    "causal": w.causal, "path": case.path_name, "splits": 1,
+                    "parallelism": "none"}),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -82,7 +82,8 @@ def main() -> int:
     import workloads as wl
 
     durs = kernel_durations(args.trace)
-    w = wl.WORKLOADS[args.workload]
+    w = (wl.VARLEN_WORKLOADS[args.workload] if args.workload in wl.VARLEN_WORKLOADS
+         else wl.WORKLOADS[args.workload])
     if w.paged:
         dom = {"paged-qcentric": "qcentric_kernel<true>",
                "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}>"}[args.path]

@@ -227,3 +227,56 @@ def make_varlen_inputs(seed: int, q_lens, k_lens, Hkv: int, qpk: int, topk: int,
 
 def varlen_effective_flops(q_lens, Hq: int, topk: int, D: int = 128, blk: int = 128) -> float:
     return 4.0 * sum(q_lens) * Hq * topk * blk * D
+
+
+@dataclass
+class VarlenWorkload:
+    """A variable-length batch: per-sequence query and key lengths, shared heads and
+    index recipe (each sequence's index rows as in the uniform workloads)."""
+    name: str
+    q_lens: tuple
+    k_lens: tuple
+    Hkv: int
+    qpk: int
+    topk: int
+    causal: bool
+    mode: int
+    D: int = 128
+    blk: int = 128
+    seed: int = DEFAULT_SEED
+    paged = False  # contiguous K/V only (class attribute, not a field)
+
+    @property
+    def Hq(self) -> int:
+        return self.Hkv * self.qpk
+
+    @property
+    def B(self) -> int:
+        return len(self.q_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(self.k_lens))
+
+    def effective_flops(self) -> int:
+        """4 * total_q * Hq * (topk * blk) * D: every slot counted as a full block."""
+        return 4 * self.total_q * self.Hq * self.topk * self.blk * self.D
+
+
+# A ragged prefill batch with the heads and index rule of the 8K causal workload:
+# eight sequences of 32 768 tokens in all, five of them ending inside a block.
+VARLEN_WORKLOADS = {
+    "vmix": VarlenWorkload("vmix_b8_t32k_hq64_hkv4_top16_causal",
+                           q_lens=(8192, 7000, 5000, 4096, 3500, 2500, 1500, 980),
+                           k_lens=(8192, 7000, 5000, 4096, 3500, 2500, 1500, 980),
+                           Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL),
+}
+
+
+def make_varlen_workload_inputs(w: VarlenWorkload) -> dict:
+    return make_varlen_inputs(w.seed, w.q_lens, w.k_lens, w.Hkv, w.qpk, w.topk, w.mode, w.D,
+                              w.blk)
