@@ -40,15 +40,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, D, P,
-                                                I64, P, P, I]
+                                                I64, P, P, D, P, I]
         lib.oracle_sparse_attention.restype = I
         lib.oracle_paged_sparse_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I,
-                                                      I, I, D, P, I64, P, P, I]
+                                                      I, I, D, P, I64, P, P, D, P, I]
         lib.oracle_paged_sparse_attention.restype = I
         lib.oracle_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P]
         lib.oracle_k2q_csr.restype = I
         lib.oracle_sparse_attention_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, D,
-                                                       P, I64, P, P, I]
+                                                       P, I64, P, P, D, P, I]
         lib.oracle_sparse_attention_varlen.restype = I
         lib.oracle_k2q_csr_varlen.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
         lib.oracle_k2q_csr_varlen.restype = I
@@ -64,20 +64,33 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
-def _shape_out(o, lse, rows, B, Sq, Hq, D):
+def _shape_out(o, lse, rows, B, Sq, Hq, D, lse_t=None):
     if rows is None:
-        return o.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
-    return o, lse
+        o = o.reshape(B, Sq, Hq, D)
+        lse = lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
+        if lse_t is not None:
+            lse_t = lse_t.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
+    return (o, lse) if lse_t is None else (o, lse, lse_t)
+
+
+def _temperature_out(n, Hq, temperature):
+    """(temp, buffer) for the C call: no buffer unless a temperature is asked for."""
+    if temperature is None:
+        return 1.0, None
+    if not temperature > 0:
+        raise ValueError("temperature must be positive")
+    return float(temperature), np.empty((n, Hq), dtype=np.float64)
 
 
 def sparse_attention(q, k, v, q2k, *, causal: bool, blk: int = 128,
                      softmax_scale: Optional[float] = None, seqused_k=None, rows=None,
-                     nthreads: int = 0):
+                     temperature: Optional[float] = None, nthreads: int = 0):
     """Oracle forward, contiguous K/V.
 
     q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] as uint16 bf16 bits; q2k [B,Hkv,Sq,topk].
     rows=None: returns O [B,Sq,Hq,D] and LSE [B,Hq,Sq] (float64).
     rows = array of b*Sq+q ids: returns O [n,Hq,D] and LSE [n,Hq].
+    temperature: also return the temperature-scaled LSE (same layout as LSE).
     """
     q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
     q2k = _c(q2k, np.int32)
@@ -91,16 +104,19 @@ def sparse_attention(q, k, v, q2k, *, causal: bool, blk: int = 128,
     n = B * Sq if rws is None else rws.size
     o = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
+    temp, lse_t = _temperature_out(n, Hq, temperature)
     rc = _load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(seq), B, Sq,
                                          Skv, Hq, Hkv, D, topk, blk, int(causal), scale,
-                                         _ptr(rws), n, _ptr(o), _ptr(lse), nthreads)
+                                         _ptr(rws), n, _ptr(o), _ptr(lse), temp, _ptr(lse_t),
+                                         nthreads)
     if rc != 0:
         raise ValueError("oracle_sparse_attention: invalid arguments")
-    return _shape_out(o, lse, rws, B, Sq, Hq, D)
+    return _shape_out(o, lse, rws, B, Sq, Hq, D, lse_t)
 
 
 def paged_sparse_attention(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,
-                           softmax_scale: Optional[float] = None, rows=None, nthreads: int = 0):
+                           softmax_scale: Optional[float] = None, rows=None,
+                           temperature: Optional[float] = None, nthreads: int = 0):
     """Oracle forward, paged K/V pool [num_pages,Hkv,page_size,D], page_table [B,max_pages]."""
     q, k_pool, v_pool = _c(q, np.uint16), _c(k_pool, np.uint16), _c(v_pool, np.uint16)
     page_table, seqused_k, q2k = (_c(page_table, np.int32), _c(seqused_k, np.int32),
@@ -115,13 +131,14 @@ def paged_sparse_attention(q, k_pool, v_pool, page_table, seqused_k, q2k, *, cau
     n = B * Sq if rws is None else rws.size
     o = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
+    temp, lse_t = _temperature_out(n, Hq, temperature)
     rc = _load().oracle_paged_sparse_attention(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seqused_k), _ptr(q2k), B, Sq,
         Hq, Hkv, D, topk, page_size, num_pages, max_pages, int(causal), scale, _ptr(rws), n,
-        _ptr(o), _ptr(lse), nthreads)
+        _ptr(o), _ptr(lse), temp, _ptr(lse_t), nthreads)
     if rc != 0:
         raise ValueError("oracle_paged_sparse_attention: invalid arguments")
-    return _shape_out(o, lse, rws, B, Sq, Hq, D)
+    return _shape_out(o, lse, rws, B, Sq, Hq, D, lse_t)
 
 
 def k2q_csr(q2k, nblk: int, with_slot: bool = True):
@@ -144,12 +161,13 @@ def k2q_csr(q2k, nblk: int, with_slot: bool = True):
 
 def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal: bool,
                             blk: int = 128, softmax_scale: Optional[float] = None, rows=None,
-                            nthreads: int = 0):
+                            temperature: Optional[float] = None, nthreads: int = 0):
     """Oracle forward of a variable-length batch.
 
     q [total_q,Hq,D], k/v [total_k,Hkv,D] (uint16 bf16 bits), q2k [Hkv,total_q,topk],
     cu_seqlens_q / cu_seqlens_k [B+1]. Returns O [n,Hq,D] and LSE [n,Hq] (the packed
-    layout of the interface page) for the given global rows, n = total_q when rows=None.
+    layout of the interface page) for the given global rows, n = total_q when rows=None;
+    with a temperature, also the temperature-scaled LSE [n,Hq].
     """
     q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
     q2k, cq, ck = _c(q2k, np.int32), _c(cu_seqlens_q, np.int32), _c(cu_seqlens_k, np.int32)
@@ -163,13 +181,14 @@ def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal:
     n = total_q if rws is None else rws.size
     o = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
+    temp, lse_t = _temperature_out(n, Hq, temperature)
     rc = _load().oracle_sparse_attention_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cq),
                                                 _ptr(ck), B, Hq, Hkv, D, topk, blk, int(causal),
-                                                scale, _ptr(rws), n, _ptr(o), _ptr(lse),
-                                                nthreads)
+                                                scale, _ptr(rws), n, _ptr(o), _ptr(lse), temp,
+                                                _ptr(lse_t), nthreads)
     if rc != 0:
         raise ValueError("oracle_sparse_attention_varlen: invalid arguments")
-    return o, lse
+    return (o, lse) if lse_t is None else (o, lse, lse_t)
 
 
 def varlen_total_rows(cu_seqlens_k, blk: int = 128) -> int:

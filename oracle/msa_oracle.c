@@ -49,13 +49,15 @@ static int64_t kv_offset(const kv_source* s, int b, int hkv, int64_t j) {
  *   qpos, Sq   position of the row in its sequence and the sequence's length
  *   nblk       valid block ids are [0, nblk)
  *   kvlen      keys j >= kvlen are masked
+ *   temp, lset_row  when lset_row is not NULL it receives, per head, the log-sum-exp
+ *              of the same masked scores divided by temp (the temperature-scaled LSE)
  *   The causal limit is qpos + kvlen - Sq (bottom-right alignment).
  */
 static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t* sel0,
                        int64_t sel_stride, int b, int qpos, int Sq, int Hq, int Hkv, int D,
                        int topk, int blk, int nblk, int64_t kvlen, int causal, double scale,
                        unsigned char* mark, double* score, double* acc, double* o_row,
-                       double* lse_row) {
+                       double* lse_row, double temp, double* lset_row) {
   const int qpk = Hq / Hkv;
   const int64_t limit = causal ? (int64_t)qpos + kvlen - Sq : INT64_MAX;
   for (int hkv = 0; hkv < Hkv; ++hkv) {
@@ -87,7 +89,14 @@ static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t
       if (n == 0) {
         for (int d = 0; d < D; ++d) oh[d] = 0.0;
         lse_row[h] = -INFINITY;
+        if (lset_row) lset_row[h] = -INFINITY;
         continue;
+      }
+      /* log sum_j exp(s_j / temp) = m / temp + log sum_j exp((s_j - m) / temp), temp > 0 */
+      if (lset_row) {
+        double lt = 0.0;
+        for (int64_t i2 = 0; i2 < n; ++i2) lt += exp((score[i2] - m) / temp);
+        lset_row[h] = m / temp + log(lt);
       }
       /* softmax-weighted sum of the values, same key order */
       for (int d = 0; d < D; ++d) acc[d] = 0.0;
@@ -114,7 +123,8 @@ static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t
 static int run_rows(const kv_source* src, const uint16_t* q, const int32_t* q2k,
                     const int32_t* seqused_k, int B, int Sq, int Hq, int Hkv, int D, int topk,
                     int blk, int nblk, int64_t full_len, int causal, double scale,
-                    const int64_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
+                    const int64_t* rows, int64_t nrows, double* o, double* lse, double temp,
+                    double* lse_t, int nthreads) {
   if (!rows) nrows = (int64_t)B * Sq;
   int failed = 0;
   const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
@@ -141,7 +151,8 @@ static int run_rows(const kv_source* src, const uint16_t* q, const int32_t* q2k,
         if (kvlen < 0) kvlen = 0;
         attend_row(src, q + g * Hq * D, q2k + (((int64_t)b * Hkv) * Sq + qpos) * topk,
                    (int64_t)Sq * topk, b, qpos, Sq, Hq, Hkv, D, topk, blk, nblk, kvlen, causal,
-                   scale, mark, score, acc, o + i * Hq * D, lse + i * Hq);
+                   scale, mark, score, acc, o + i * Hq * D, lse + i * Hq, temp,
+                   lse_t ? lse_t + i * Hq : NULL);
       }
     }
     free(mark);
@@ -155,13 +166,14 @@ int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* q2k, const int32_t* seqused_k, int B, int Sq, int Skv,
                             int Hq, int Hkv, int D, int topk, int blk, int causal, double scale,
                             const int64_t* rows, int64_t nrows, double* o, double* lse,
-                            int nthreads) {
+                            double temp, double* lse_t, int nthreads) {
   if (!q || !k || !v || !q2k || !o || !lse || B <= 0 || Sq <= 0 || Skv <= 0 || Hkv <= 0 ||
-      Hq <= 0 || Hq % Hkv || D <= 0 || topk <= 0 || blk <= 0 || Skv % blk)
+      Hq <= 0 || Hq % Hkv || D <= 0 || topk <= 0 || blk <= 0 || Skv % blk ||
+      (lse_t && !(temp > 0.0)))
     return -1;
   kv_source src = {k, v, NULL, Skv, Hkv, D, blk, 0, 0};
   return run_rows(&src, q, q2k, seqused_k, B, Sq, Hq, Hkv, D, topk, blk, Skv / blk, Skv, causal,
-                  scale, rows, nrows, o, lse, nthreads);
+                  scale, rows, nrows, o, lse, temp, lse_t, nthreads);
 }
 
 int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
@@ -169,14 +181,16 @@ int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
                                   const int32_t* seqused_k, const int32_t* q2k, int B, int Sq,
                                   int Hq, int Hkv, int D, int topk, int page_size, int num_pages,
                                   int max_pages, int causal, double scale, const int64_t* rows,
-                                  int64_t nrows, double* o, double* lse, int nthreads) {
+                                  int64_t nrows, double* o, double* lse, double temp,
+                                  double* lse_t, int nthreads) {
   if (!q || !k_pool || !v_pool || !page_table || !seqused_k || !q2k || !o || !lse || B <= 0 ||
       Sq <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || D <= 0 || topk <= 0 || page_size <= 0 ||
-      num_pages <= 0 || max_pages <= 0)
+      num_pages <= 0 || max_pages <= 0 || (lse_t && !(temp > 0.0)))
     return -1;
   kv_source src = {k_pool, v_pool, page_table, 0, Hkv, D, page_size, num_pages, max_pages};
   return run_rows(&src, q, q2k, seqused_k, B, Sq, Hq, Hkv, D, topk, page_size, max_pages,
-                  (int64_t)max_pages * page_size, causal, scale, rows, nrows, o, lse, nthreads);
+                  (int64_t)max_pages * page_size, causal, scale, rows, nrows, o, lse, temp,
+                  lse_t, nthreads);
 }
 
 int oracle_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
@@ -238,9 +252,10 @@ int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const u
                                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                    int topk, int blk, int causal, double scale,
                                    const int64_t* rows, int64_t nrows, double* o, double* lse,
-                                   int nthreads) {
+                                   double temp, double* lse_t, int nthreads) {
   if (!q || !k || !v || !q2k || !o || !lse || Hkv <= 0 || Hq <= 0 || Hq % Hkv || D <= 0 ||
-      topk <= 0 || blk <= 0 || !varlen_args_ok(cu_seqlens_q, cu_seqlens_k, B))
+      topk <= 0 || blk <= 0 || !varlen_args_ok(cu_seqlens_q, cu_seqlens_k, B) ||
+      (lse_t && !(temp > 0.0)))
     return -1;
   const int64_t total_q = cu_seqlens_q[B];
   int max_nblk = 1;
@@ -279,7 +294,8 @@ int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const u
                                blk, 0, 0};
         attend_row(&src, q + g * Hq * D, q2k + g * topk, total_q * topk, 0,
                    (int)(g - cu_seqlens_q[b]), Sq_b, Hq, Hkv, D, topk, blk, nblk_b, Skv_b,
-                   causal, scale, mark, score, acc, o + i * Hq * D, lse + i * Hq);
+                   causal, scale, mark, score, acc, o + i * Hq * D, lse + i * Hq, temp,
+                   lse_t ? lse_t + i * Hq : NULL);
       }
     }
     free(mark);

@@ -35,13 +35,17 @@ extern "C" {
  *            limit uses seqused_k[b] in place of Skv
  *   rows     NULL (all B*Sq rows, in order) or nrows global row ids b*Sq+q
  *   o        [nrows, Hq, D] double;  lse [nrows, Hq] double (natural log)
+ *   temp, lse_t  lse_t NULL, or [nrows, Hq]: the temperature-scaled LSE, the
+ *            log-sum-exp of the same masked scores divided by temp > 0
+ *            (`lse_temperature_scale` of `sparse_attention_ref` on the test
+ *            page and of `sparse_atten_func` on the interface page)
  * Returns 0, or -1 on invalid arguments.
  */
 int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* q2k, const int32_t* seqused_k, int B, int Sq, int Skv,
                             int Hq, int Hkv, int D, int topk, int blk, int causal, double scale,
                             const int64_t* rows, int64_t nrows, double* o, double* lse,
-                            int nthreads);
+                            double temp, double* lse_t, int nthreads);
 
 /*
  * Sparse attention, paged K/V. Logical block s of sequence b is physical page
@@ -55,7 +59,8 @@ int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
                                   const int32_t* seqused_k, const int32_t* q2k, int B, int Sq,
                                   int Hq, int Hkv, int D, int topk, int page_size, int num_pages,
                                   int max_pages, int causal, double scale, const int64_t* rows,
-                                  int64_t nrows, double* o, double* lse, int nthreads);
+                                  int64_t nrows, double* o, double* lse, double temp,
+                                  double* lse_t, int nthreads);
 
 /*
  * kv-block -> query CSR of a [B, Hkv, Sq, topk] index table.
@@ -87,7 +92,7 @@ int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const u
                                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                    int topk, int blk, int causal, double scale,
                                    const int64_t* rows, int64_t nrows, double* o, double* lse,
-                                   int nthreads);
+                                   double temp, double* lse_t, int nthreads);
 
 /*
  * k2q CSR of a variable-length batch (`build_k2q_csr` with cu_seqlens and
