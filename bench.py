@@ -15,7 +15,7 @@ Metrics (the pages' benchmark harness, "test_sparse_atten.py"):
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2|vmix|...]
                        [--path auto|q|kv|decode] [--splits N] [--extra c5,c3u]
-                       [--no-cpu-baseline]
+                       [--lse-temperature T] [--no-cpu-baseline]
 (--extra workloads run with the automatic path)
 """
 from __future__ import annotations
@@ -114,12 +114,17 @@ def decode_algorithmic_bytes(w, inp) -> int:
 class Case:
     """One workload uploaded to the GPU with a callable that runs one step."""
 
-    def __init__(self, key: str, path: str, splits: int = 0):
+    def __init__(self, key: str, path: str, splits: int = 0, temperature=None):
         import torch
         import block_sparse_attention_top_amd as msa
         import workloads as wl
         self.varlen = key in wl.VARLEN_WORKLOADS
         self.key = key
+        self.temperature = temperature
+        # the temperature-scaled LSE as an extra output (computed by the kernels)
+        tk = ({} if temperature is None else
+              {"return_temperature_lse": True, "lse_temperature_scale": float(temperature),
+               "temperature_fast_path": False})
         self.w = wl.VARLEN_WORKLOADS[key] if self.varlen else wl.WORKLOADS[key]
         w = self.w
         t0 = time.time()
@@ -143,7 +148,7 @@ class Case:
             self.splits = 1
             self.step = lambda: msa.msa_sparse_fwd_varlen(
                 t["q"], t["k"], t["v"], t["q2k"], t["cu_seqlens_q"], t["cu_seqlens_k"],
-                causal=w.causal, path=p, o=self.o, lse=self.lse, workspace=ws)
+                causal=w.causal, path=p, o=self.o, lse=self.lse, workspace=ws, **tk)
             self.bytes = None
             self.flops = w.effective_flops()
             return
@@ -161,7 +166,7 @@ class Case:
             self.step = lambda: msa.msa_paged_sparse_fwd(
                 t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"],
                 causal=w.causal, num_splits=splits, path=p, o=self.o, lse=self.lse,
-                workspace=ws)
+                workspace=ws, **tk)
             self.bytes = decode_algorithmic_bytes(w, self.inp)
         else:
             p = msa.msa_sparse_fwd_path(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.topk, PATHS[path])
@@ -172,7 +177,7 @@ class Case:
             ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
             self.step = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"],
                                                    causal=w.causal, path=p, o=self.o,
-                                                   lse=self.lse, workspace=ws)
+                                                   lse=self.lse, workspace=ws, **tk)
             self.bytes = None
         self.flops = w.effective_flops()
 
@@ -203,7 +208,7 @@ class Case:
     def breakdown(self, steps: int, warmup: int):
         """kv-centric only: mean ms of the k2q CSR build alone, of the forward given a
         prebuilt CSR, and of the two together (the timed step)."""
-        if self.w.paged or self.path_name != "kv-centric":
+        if self.w.paged or self.path_name != "kv-centric" or self.temperature is not None:
             return None
         import torch
         import block_sparse_attention_top_amd as msa
@@ -260,10 +265,10 @@ class Case:
 
     def dominant_kernel(self) -> str:
         if self.w.paged:
-            return {"paged-qcentric": "qcentric_kernel<true>",
-                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}>"}[self.path_name]
-        return {"q-centric": "qcentric_kernel<false>",
-                "kv-centric": f"kvcentric_kernel<{self.w.qpk}>",
+            return {"paged-qcentric": "qcentric_kernel<true, false>",
+                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}, false>"}[self.path_name]
+        return {"q-centric": "qcentric_kernel<false, false>",
+                "kv-centric": f"kvcentric_kernel<{self.w.qpk}, false>",
                 "query-tile": "tile_kernel"}[self.path_name]
 
 
@@ -349,6 +354,8 @@ def main() -> int:
                     help="KV splits of the paged workload (0 = the library's choice)")
     ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lse-temperature", type=float, default=None, metavar="T",
+                    help="also compute the temperature-scaled LSE with this T")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -361,14 +368,14 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
-    case = Case(args.workload, args.path, args.splits)
+    case = Case(args.workload, args.path, args.splits, args.lse_temperature)
     log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
         f"({case.path_name})")
     ms, kernel_ms = case.time_steps(args.steps, args.warmup)
     m = case.metric(ms, kernel_ms)
     log(f"[bench] {args.workload}: {m}")
     w = case.w
-    traffic = measured_traffic(case)
+    traffic = measured_traffic(case) if args.lse_temperature is None else None
     if w.paged:
         value, unit, metric = m["GB_per_s"], "GB/s", "paged sparse decode GB/s"
         ach = m["kernel_GB_per_s"]
@@ -381,6 +388,8 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     roof["kernel"] = case.dominant_kernel()
+    if args.lse_temperature is not None:  # the kernels' temperature variants
+        roof["kernel"] = roof["kernel"].replace(", false>", ", true>")
     roof["kernel_ms"] = kernel_ms
     brk = case.breakdown(args.steps, args.warmup)
     if brk is not None:
@@ -404,12 +413,13 @@ def main() -> int:
         "config": ({"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
                     "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": case.splits,
+                    "lse_temperature": args.lse_temperature,
                     "parallelism": "none"} if not case.varlen else
                    {"workload": w.name, "B": w.B, "varlen": True, "total_q": w.total_q,
                     "total_k": w.total_k, "q_lens": list(w.q_lens), "k_lens": list(w.k_lens),
                     "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": 1,
-                    "parallelism": "none"}),
+                    "lse_temperature": args.lse_temperature, "parallelism": "none"}),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -50,8 +50,8 @@ def load_library():
     lib.msa_sparse_fwd_workspace_size.restype = S
     lib.msa_sparse_fwd_path.argtypes = [I] * 7
     lib.msa_sparse_fwd_path.restype = I
-    lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, P, P,
-                                   S, P]
+    lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, P, F,
+                                   P, P, S, P]
     lib.msa_sparse_fwd.restype = I
     lib.msa_build_k2q_csr_workspace_size.argtypes = [I] * 5
     lib.msa_build_k2q_csr_workspace_size.restype = S
@@ -62,7 +62,7 @@ def load_library():
     lib.msa_sparse_fwd_varlen_path.argtypes = [I] * 7
     lib.msa_sparse_fwd_varlen_path.restype = I
     lib.msa_sparse_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
-                                          I, F, I, P, P, P, S, P]
+                                          I, F, I, P, P, F, P, P, S, P]
     lib.msa_sparse_fwd_varlen.restype = I
     lib.msa_build_k2q_csr_varlen_workspace_size.argtypes = [I] * 5
     lib.msa_build_k2q_csr_varlen_workspace_size.restype = S
@@ -75,7 +75,7 @@ def load_library():
     lib.msa_paged_sparse_fwd_splits.argtypes = [I] * 6
     lib.msa_paged_sparse_fwd_splits.restype = I
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
-                                         P, P, P, S, P]
+                                         P, P, F, P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
     lib.msa_set_profiling_events.argtypes = [P, P]
     lib.msa_set_profiling_events.restype = I
@@ -133,6 +133,26 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+# |T - 1| at or below this returns the LSE itself as the temperature-scaled LSE,
+# as the interface page's binding does
+TEMPERATURE_FAST_PATH_ABS_TOL = 1e-12
+
+
+def _temperature(lse: torch.Tensor, return_temperature_lse: bool, scale, out, fast_path: bool):
+    """(T, buffer or None, alias): alias means the LSE itself is the answer (T = 1)."""
+    if not return_temperature_lse:
+        return 1.0, None, False
+    t = 1.0 if scale is None else float(scale)
+    if fast_path and abs(t - 1.0) <= TEMPERATURE_FAST_PATH_ABS_TOL and out is None:
+        return t, None, True
+    if out is None:
+        out = torch.empty_like(lse)
+    _dev(out, "lse_temperature", torch.float32)
+    if tuple(out.shape) != tuple(lse.shape):
+        raise ValueError("lse_temperature must have the shape of lse")
+    return t, out, False
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
@@ -154,8 +174,11 @@ def msa_sparse_fwd_path(B, Sq, Skv, Hq, Hkv, topk, path=MSA_PATH_AUTO) -> int:
 
 def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None, *,
                    causal: bool, softmax_scale: float = 0.0, path: int = MSA_PATH_AUTO,
-                   blk_kv: int = 128, o=None, lse=None, workspace=None, stream=None):
-    """Sparse forward with contiguous K/V. Returns (O bf16 [B,Sq,Hq,D], LSE fp32 [B,Hq,Sq])."""
+                   blk_kv: int = 128, o=None, lse=None, return_temperature_lse: bool = False,
+                   lse_temperature_scale: Optional[float] = None, lse_temperature=None,
+                   temperature_fast_path: bool = True, workspace=None, stream=None):
+    """Sparse forward with contiguous K/V. Returns (O bf16 [B,Sq,Hq,D], LSE fp32 [B,Hq,Sq]),
+    plus the temperature-scaled LSE (same layout) when return_temperature_lse."""
     lib = load_library()
     _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
     _dev(q2k, "q2k", torch.int32)
@@ -170,13 +193,17 @@ def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
     nbytes = int(lib.msa_sparse_fwd_workspace_size(B, Sq, Skv, Hq, Hkv, D, topk, blk_kv, path))
     ws, wsn = _workspace(nbytes, q.device, workspace)
     rc = lib.msa_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(csr_row_ptr),
                             _ptr(csr_q_idx), _ptr(csr_slot), B, Sq, Skv, Hq, Hkv, D, topk, blk_kv,
                             int(bool(causal)), float(softmax_scale), int(path), _ptr(o), _ptr(lse),
-                            _ptr(ws), wsn, _stream(stream))
+                            temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
     return o, lse
 
 
@@ -218,7 +245,9 @@ def msa_sparse_fwd_varlen_path(B, total_q, total_k, Hq, Hkv, topk, path=MSA_PATH
 def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=None,
                           csr_q_idx=None, csr_slot=None, csr_total_rows: int = 0, *, causal: bool,
                           softmax_scale: float = 0.0, path: int = MSA_PATH_AUTO, blk_kv: int = 128,
-                          o=None, lse=None, workspace=None, stream=None):
+                          o=None, lse=None, return_temperature_lse: bool = False,
+                          lse_temperature_scale: Optional[float] = None, lse_temperature=None,
+                          temperature_fast_path: bool = True, workspace=None, stream=None):
     """Sparse forward of a variable-length batch (packed q [total_q,Hq,D], k/v
     [total_k,Hkv,D], q2k [Hkv,total_q,topk], cu_seqlens [B+1] on the device).
     Returns (O bf16 [total_q,Hq,D], LSE fp32 [total_q,Hq])."""
@@ -242,6 +271,8 @@ def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=
     if lse is None:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
     _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
     nbytes = int(lib.msa_sparse_fwd_varlen_workspace_size(B, total_q, total_k, Hq, Hkv, D, topk,
                                                           blk_kv, path))
     ws, wsn = _workspace(nbytes, q.device, workspace)
@@ -249,8 +280,10 @@ def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=
         _ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         _ptr(csr_row_ptr), _ptr(csr_q_idx), _ptr(csr_slot), int(csr_total_rows), B, total_q,
         total_k, Hq, Hkv, D, topk, blk_kv, int(bool(causal)), float(softmax_scale), int(path),
-        _ptr(o), _ptr(lse), _ptr(ws), wsn, _stream(stream))
+        _ptr(o), _ptr(lse), temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
     return o, lse
 
 
@@ -304,9 +337,11 @@ def msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, num_splits=0, path=MSA_PATH_AU
 
 def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,
                          softmax_scale: float = 0.0, num_splits: int = 0,
-                         path: int = MSA_PATH_AUTO, o=None, lse=None, workspace=None,
-                         stream=None):
-    """Sparse forward through a page table. Returns (O, LSE) as msa_sparse_fwd."""
+                         path: int = MSA_PATH_AUTO, o=None, lse=None,
+                         return_temperature_lse: bool = False,
+                         lse_temperature_scale: Optional[float] = None, lse_temperature=None,
+                         temperature_fast_path: bool = True, workspace=None, stream=None):
+    """Sparse forward through a page table. Returns (O, LSE[, LSE_T]) as msa_sparse_fwd."""
     lib = load_library()
     _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
     _dev(v_pool, "v_pool", torch.bfloat16), _dev(page_table, "page_table", torch.int32)
@@ -320,13 +355,17 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
     nbytes = int(lib.msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size,
                                                          max_pages, num_splits, path))
     ws, wsn = _workspace(nbytes, q.device, workspace)
     rc = lib.msa_paged_sparse_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                                   _ptr(seqused_k), _ptr(q2k), B, Sq, Hq, Hkv, D, topk, page_size,
                                   num_pages, max_pages, int(bool(causal)), float(softmax_scale),
-                                  int(num_splits), int(path), _ptr(o), _ptr(lse), _ptr(ws), wsn,
-                                  _stream(stream))
+                                  int(num_splits), int(path), _ptr(o), _ptr(lse), temp,
+                                  _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
     return o, lse

@@ -84,12 +84,21 @@ int resolve_varlen_path(int path, int B, long long total_q, long long total_k, i
   return MSA_PATH_KVCENTRIC;
 }
 
+// Temperature-scaled LSE request: no buffer = off; else T must be positive and finite.
+int check_temperature(float scale, const float* lse_t) {
+  if (!lse_t) return MSA_OK;
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(MSA_ERR_INVALID_VALUE, "lse_temperature_scale must be positive and finite");
+  if (!aligned(lse_t, 4)) return fail(MSA_ERR_INVALID_VALUE, "misaligned lse_temperature pointer");
+  return MSA_OK;
+}
+
 // Entries per kv-centric work item: kKvChunkRows (query, head) rows.
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
 struct KvLayout {
   size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, o_part, lse_part,
-      total;
+      lse_t_part, total;
   long long max_items;
 };
 
@@ -112,6 +121,7 @@ KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
   L.items = off; off += align256(L.max_items * 16);
   L.o_part = off; off += align256(static_cast<size_t>(cap) * Hq * kD * 2);
   L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 8);
+  L.lse_t_part = off; off += align256(static_cast<size_t>(cap) * Hq * 4);
   L.total = off;
   return L;
 }
@@ -155,10 +165,12 @@ PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int num_splits, int path)
   return pl;
 }
 
+// fp32 partials [splits][rows][D], then the split LSEs and temperature-scaled LSEs
+// [splits][rows], rows = B * Sq * Hq
 size_t paged_workspace(int B, int Sq, int Hq, int splits) {
   if (splits <= 1) return 0;
   const size_t rows = static_cast<size_t>(B) * Sq * Hq;
-  return align256(splits * rows * kD * 4) + align256(splits * rows * 4);
+  return align256(splits * rows * kD * 4) + 2 * align256(splits * rows * 4);
 }
 
 // The kv-centric pipeline: k2q CSR (unless given), chunk schedule, item table,
@@ -167,7 +179,8 @@ size_t paged_workspace(int B, int Sq, int Hq, int splits) {
 // its tables already built on the stream.
 int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
                   const int32_t* csr_q_idx, const int32_t* csr_slot, const KvLayout& L, char* ws,
-                  const VarlenTables* vt, uint16_t* o, float* lse, hipStream_t st) {
+                  const VarlenTables* vt, uint16_t* o, float* lse, float* lse_t,
+                  hipStream_t st) {
   const int nrows = p.nrows;
   const long long nq = vt ? p.total_q : static_cast<long long>(p.B) * p.Sq;
   const int32_t* row_ptr = csr_row_ptr;
@@ -197,6 +210,7 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   p.chunk_entries = chunk;
   p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
   p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
+  p.lse_t_part = lse_t ? reinterpret_cast<float*>(ws + L.lse_t_part) : nullptr;
   if (vt) {
     p.rowbase = vt->rowbase;
     p.row_seq = vt->row_seq;
@@ -213,10 +227,10 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   if (vt) {
     const CombineVarlen cv{vt->q_rows};
     e = launch_combine_slots(p.o_part, p.lse_part, q2k, 1, static_cast<int>(nq), p.Hq, p.Hkv,
-                             p.topk, 0, o, lse, st, &cv);
+                             p.topk, 0, o, lse, st, &cv, p.lse_t_part, lse_t);
   } else {
     e = launch_combine_slots(p.o_part, p.lse_part, q2k, p.B, p.Sq, p.Hq, p.Hkv, p.topk, p.nblk, o,
-                             lse, st);
+                             lse, st, nullptr, p.lse_t_part, lse_t);
   }
   return e == hipSuccess ? MSA_OK : hip_fail(e, "combine");
 }
@@ -268,11 +282,15 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
                    const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
                    int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                   float softmax_scale, int path, void* o, float* lse, void* workspace,
+                   float softmax_scale, int path, void* o, float* lse,
+                   float lse_temperature_scale, float* lse_temperature, void* workspace,
                    size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_common(B, Sq, Hq, Hkv, D, topk, blk_kv);
   if (rc) return rc;
+  rc = check_temperature(lse_temperature_scale, lse_temperature);
+  if (rc) return rc;
+  const float inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
   if (Skv <= 0 || Skv % kBlk)
     return fail(MSA_ERR_INVALID_VALUE, "Skv (%d) must be a positive multiple of 128", Skv);
   if (!q || !k || !v || !q2k || !o || !lse)
@@ -307,6 +325,8 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     p.scale_log2 = scale * kLog2e;
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
+    p.inv_temp = inv_temp;
+    p.lse_t = lse_temperature;
     prof_mark(g_prof_before, st);
     hipError_t e = launch_tile(p, st);
     prof_mark(g_prof_after, st);
@@ -325,6 +345,8 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     p.splits = 1;
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
+    p.inv_temp = inv_temp;
+    p.lse_t = lse_temperature;
     prof_mark(g_prof_before, st);
     hipError_t e = launch_qcentric(p, false, st);
     prof_mark(g_prof_after, st);
@@ -350,8 +372,10 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   p.cap = static_cast<long long>(B) * Sq * topk;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
+  p.inv_temp = inv_temp;
   return run_kvcentric(p, q2k, have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
-                       static_cast<char*>(workspace), nullptr, static_cast<uint16_t*>(o), lse, st);
+                       static_cast<char*>(workspace), nullptr, static_cast<uint16_t*>(o), lse,
+                       lse_temperature, st);
 }
 
 size_t msa_build_k2q_csr_workspace_size(int B, int Hkv, int Sq, int topk, int num_kv_blocks) {
@@ -412,13 +436,17 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
                           const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
                           const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
                           int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                          float softmax_scale, int path, void* o, float* lse, void* workspace,
+                          float softmax_scale, int path, void* o, float* lse,
+                          float lse_temperature_scale, float* lse_temperature, void* workspace,
                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (B <= 0 || total_q < 0 || total_k < 0)
     return fail(MSA_ERR_INVALID_VALUE, "B must be positive, total_q and total_k non-negative");
   int rc = check_common(B, 1, Hq, Hkv, D, topk, blk_kv);
   if (rc) return rc;
+  rc = check_temperature(lse_temperature_scale, lse_temperature);
+  if (rc) return rc;
+  const float inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
   if (static_cast<long long>(total_q) * topk > 0x7FFFFFFFLL)
     return fail(MSA_ERR_INVALID_VALUE, "total_q*topk exceeds the int32 index range");
   if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_KVCENTRIC)
@@ -464,6 +492,8 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
     p.splits = 1;
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
+    p.inv_temp = inv_temp;
+    p.lse_t = lse_temperature;
     prof_mark(g_prof_before, st);
     hipError_t e = launch_qcentric(p, false, st);
     prof_mark(g_prof_after, st);
@@ -499,8 +529,9 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.total_k = total_k;
+  p.inv_temp = inv_temp;
   return run_kvcentric(p, q2k, have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
-                       ws + tbytes, &vt, static_cast<uint16_t*>(o), lse, st);
+                       ws + tbytes, &vt, static_cast<uint16_t*>(o), lse, lse_temperature, st);
 }
 
 size_t msa_build_k2q_csr_varlen_workspace_size(int B, int Hkv, int total_q, int topk,
@@ -567,10 +598,13 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, int path, void* o, float* lse, void* workspace,
+                         int num_splits, int path, void* o, float* lse,
+                         float lse_temperature_scale, float* lse_temperature, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_common(B, Sq, Hq, Hkv, D, topk, page_size);
+  if (rc) return rc;
+  rc = check_temperature(lse_temperature_scale, lse_temperature);
   if (rc) return rc;
   if (num_pages <= 0 || max_pages <= 0)
     return fail(MSA_ERR_INVALID_VALUE, "num_pages and max_pages must be positive");
@@ -605,6 +639,8 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
   p.splits = splits;
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
+  p.inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
+  p.lse_t = lse_temperature;
   if (splits > 1) {
     const size_t need = paged_workspace(B, Sq, Hq, splits);
     if (!workspace || workspace_bytes < need)
@@ -612,7 +648,11 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
     if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
     const size_t rows = static_cast<size_t>(B) * Sq * Hq;
     p.o_part = static_cast<float*>(workspace);
-    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(splits * rows * kD * 4));
+    char* wsc = static_cast<char*>(workspace);
+    p.lse_part = reinterpret_cast<float*>(wsc + align256(splits * rows * kD * 4));
+    if (lse_temperature)
+      p.lse_t_part = reinterpret_cast<float*>(wsc + align256(splits * rows * kD * 4) +
+                                              align256(splits * rows * 4));
   }
   prof_mark(g_prof_before, st);
   hipError_t e = plan.path == MSA_PATH_DECODE ? launch_paged_decode(p, st)
@@ -620,7 +660,8 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
   prof_mark(g_prof_after, st);
   if (e != hipSuccess) return hip_fail(e, "paged forward");
   if (splits > 1) {
-    e = launch_combine_splits(p.o_part, p.lse_part, B, Sq, Hq, splits, static_cast<uint16_t*>(o), lse, st);
+    e = launch_combine_splits(p.o_part, p.lse_part, B, Sq, Hq, splits, static_cast<uint16_t*>(o),
+                              lse, st, p.lse_t_part, lse_temperature);
     if (e != hipSuccess) return hip_fail(e, "split combine");
   }
   return MSA_OK;

@@ -29,9 +29,11 @@ namespace {
 __global__ __launch_bounds__(256) void combine_slots_kernel(
     const uint16_t* __restrict__ o_part, const float2* __restrict__ lse_part,
     const int32_t* __restrict__ q2k, int B, int Sq, int Hq, int Hkv, int topk, int nblk,
-    const int2* __restrict__ q_rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const int2* __restrict__ q_rows, uint16_t* __restrict__ o, float* __restrict__ lse,
+    const float* __restrict__ lse_t_part, float* __restrict__ lse_t) {
   __shared__ float wts[16][kMaxTopk];
   __shared__ float row_lse[16];
+  __shared__ float row_lse_t[16];
   const long long rows = static_cast<long long>(B) * Sq * Hq;  // varlen: B = 1, Sq = total_q
   const long long rh0 = static_cast<long long>(blockIdx.x) * 16;
   const int tid = threadIdx.x;
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
     const int rl = tid >> 4, t0 = tid & 15;
     const long long rh = rh0 + rl;
     float l[2] = {-INFINITY, -INFINITY}, mr[2] = {0.f, 0.f};
+    float lt[2] = {-INFINITY, -INFINITY};  // temperature-scaled block LSEs
     if (rh < rows) {
       const long long gq = rh / Hq;
       const int head = static_cast<int>(rh % Hq);
@@ -56,6 +59,7 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
             const float2 lm = lse_part[(gq * topk + t) * Hq + head];
             l[k] = lm.x;
             mr[k] = lm.y;
+            if (lse_t_part) lt[k] = lse_t_part[(gq * topk + t) * Hq + head];
           }
         }
       }
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
     }
 #pragma unroll
     for (int d = 8; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 16);
-    const float L = m == -INFINITY ? -INFINITY : m + fast_log2(sum) * kLn2;
+    const float L = m == -INFINITY ? -INFINITY : fmaf(fast_log2(sum), kLn2, m);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int t = t0 + 16 * k;
@@ -79,6 +83,20 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
         wts[rl][t] = (l[k] == -INFINITY || L == -INFINITY) ? 0.f : fast_exp2((mr[k] - L) * kLog2e);
     }
     if (t0 == 0) row_lse[rl] = L;
+    if (lse_t_part) {  // the same log-sum-exp over the temperature-scaled block LSEs
+      float mt = fmaxf(lt[0], lt[1]);
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) mt = fmaxf(mt, __shfl_xor(mt, d, 16));
+      float st = 0.f;
+      if (mt != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (lt[k] != -INFINITY) st += fast_exp2((lt[k] - mt) * kLog2e);
+      }
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) st += __shfl_xor(st, d, 16);
+      if (t0 == 0) row_lse_t[rl] = mt == -INFINITY ? -INFINITY : fmaf(fast_log2(st), kLn2, mt);
+    }
   }
   __syncthreads();
   const int rl = tid & 15, dc = tid >> 4;
@@ -113,19 +131,21 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   *reinterpret_cast<u32x4*>(o + rh * kD + 8 * dc) = out;
   if (dc == 0) {
-    if (q_rows) {
-      lse[rh] = row_lse[rl];  // [total_q][Hq]
-    } else {
+    long long li = rh;  // varlen: [total_q][Hq]
+    if (!q_rows) {
       const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-      lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = row_lse[rl];
+      li = (static_cast<long long>(b) * Hq + head) * Sq + qpos;
     }
+    lse[li] = row_lse[rl];
+    if (lse_t_part) lse_t[li] = row_lse_t[rl];
   }
 }
 
 // split partials [splits][B*Sq][Hq][D] (fp32) and [splits][B*Sq][Hq]
 __global__ __launch_bounds__(256) void combine_splits_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int B, int Sq, int Hq,
-    int splits, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    int splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    const float* __restrict__ lse_t_part, float* __restrict__ lse_t) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   const long long rows = static_cast<long long>(B) * Sq * Hq;
   if (idx >= rows * 16) return;
@@ -160,7 +180,16 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(
   *reinterpret_cast<u32x4*>(o + rh * kD + 8 * dc) = out;
   if (dc == 0) {
     const int b = static_cast<int>(gq / Sq), qpos = static_cast<int>(gq % Sq);
-    lse[(static_cast<long long>(b) * Hq + head) * Sq + qpos] = L;
+    const long long li = (static_cast<long long>(b) * Hq + head) * Sq + qpos;
+    lse[li] = L;
+    if (lse_t_part) {  // log-sum-exp of the splits' temperature-scaled LSEs
+      float mt = -INFINITY;
+      for (int sp = 0; sp < splits; ++sp) mt = fmaxf(mt, lse_t_part[sp * rows + rh]);
+      float st = 0.f;
+      if (mt != -INFINITY)
+        for (int sp = 0; sp < splits; ++sp) st += expf(lse_t_part[sp * rows + rh] - mt);
+      lse_t[li] = mt == -INFINITY ? -INFINITY : mt + logf(st);
+    }
   }
 }
 
@@ -168,24 +197,26 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(
 
 hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
-                                float* lse, hipStream_t stream, const CombineVarlen* v) {
+                                float* lse, hipStream_t stream, const CombineVarlen* v,
+                                const float* lse_t_part, float* lse_t) {
   const long long total = static_cast<long long>(B) * Sq * Hq * 16;
   const long long blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (v && B != 1) return hipErrorInvalidValue;  // a varlen batch passes B = 1, Sq = total_q
   hipLaunchKernelGGL(combine_slots_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, o_part, lse_part, q2k, B, Sq, Hq, Hkv, topk, nblk,
-                     v ? v->q_rows : nullptr, o, lse);
+                     v ? v->q_rows : nullptr, o, lse, lse_t_part, lse_t);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_splits(const float* o_part, const float* lse_part, int B, int Sq, int Hq,
-                                 int splits, uint16_t* o, float* lse, hipStream_t stream) {
+                                 int splits, uint16_t* o, float* lse, hipStream_t stream,
+                                 const float* lse_t_part, float* lse_t) {
   const long long total = static_cast<long long>(B) * Sq * Hq * 16;
   const long long blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(combine_splits_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, o_part, lse_part, B, Sq, Hq, splits, o, lse);
+                     stream, o_part, lse_part, B, Sq, Hq, splits, o, lse, lse_t_part, lse_t);
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@
 // fragment reads are free of bank conflicts. Every wave owns up to
 // kMaxQPerWave queries and runs, for each of its queries whose bit is set,
 // S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (N = the qpk
-// heads) with an online softmax per lane column.
+// heads) with an online softmax per lane column (and, when a temperature-scaled
+// LSE is requested, a second running sum of 2^((x - m) / T) beside it).
 #include "msa_internal.hpp"
 
 #include <math.h>
@@ -56,7 +57,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       (__attribute__((address_space(3))) const void*)(p)));
 }
 
-template <int QPW>
+template <int QPW, bool TEMP>
 __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcParams p) {
   // ring of kStages sub-tile buffers; separate arrays keep the stage buffers
   // distinct objects for the compiler's tracking of the direct-to-LDS loads
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
   const bool head_ok = n < p.qpk;
   bf16x8 qf[QPW][4];
   float m_run[QPW], l_run[QPW];
+  float lt_run[QPW];  // TEMP: sum of 2^((x - m_run) / T), x the scores in log2 units
   f32x4 oacc[QPW][8];
   long long qend[QPW];
 #pragma unroll
@@ -114,6 +116,7 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     }
     m_run[k] = -INFINITY;
     l_run[k] = 0.f;
+    lt_run[k] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[k][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -245,17 +248,23 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[k], mx);  // finite: key jb is visible to q
       const float alpha = fast_exp2(m_run[k] - m_new);
-      float ps = 0.f;
+      float ps = 0.f, pst = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          if (TEMP) pst += fast_exp2((x[mt][i] - m_new) * p.inv_temp);
           x[mt][i] = fast_exp2(x[mt][i] - m_new);
           ps += x[mt][i];
         }
       ps += __shfl_xor(ps, 16);
       ps += __shfl_xor(ps, 32);
       l_run[k] = l_run[k] * alpha + ps;
+      if (TEMP) {
+        pst += __shfl_xor(pst, 16);
+        pst += __shfl_xor(pst, 32);
+        lt_run[k] = lt_run[k] * fast_exp2((m_run[k] - m_new) * p.inv_temp) + pst;
+      }
       m_run[k] = m_new;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) oacc[k][dt] *= alpha;
@@ -328,6 +337,8 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     const bool any = l_run[k] > 0.f;
     const float inv = any ? 1.f / l_run[k] : 0.f;
     const float lse_v = any ? (m_run[k] + fast_log2(l_run[k])) * kLn2 : -INFINITY;
+    const float lset_v =
+        any ? (m_run[k] * p.inv_temp + fast_log2(lt_run[k])) * kLn2 : -INFINITY;
     const long long grow = static_cast<long long>(b) * p.Sq + q;
     if (p.splits == 1) {
       uint16_t* orow = p.o + (grow * p.Hq + head) * kD + 4 * g;
@@ -337,7 +348,11 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
                          pack_bf16x2(oacc[k][dt][2] * inv, oacc[k][dt][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
       }
-      if (g == 0) p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + q] = lse_v;
+      if (g == 0) {
+        const long long li = (static_cast<long long>(b) * p.Hq + head) * p.Sq + q;
+        p.lse[li] = lse_v;
+        if (TEMP) p.lse_t[li] = lset_v;
+      }
     } else {
       // a split that saw no key of this query leaves its O partial unwritten:
       // the split combine reads O only where the partial LSE is finite
@@ -348,9 +363,20 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
         for (int dt = 0; dt < 8; ++dt)
           *reinterpret_cast<f32x4*>(orow + 16 * dt) = oacc[k][dt] * inv;
       }
-      if (g == 0) p.lse_part[prow] = lse_v;
+      if (g == 0) {
+        p.lse_part[prow] = lse_v;
+        if (TEMP) p.lse_t_part[prow] = lset_v;
+      }
     }
   }
+}
+
+template <int QPW>
+void decode_launch(const QcParams& p, dim3 grid, hipStream_t stream) {
+  if (p.lse_t)
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, false>), grid, dim3(256), 0, stream, p);
 }
 
 }  // namespace
@@ -366,10 +392,10 @@ hipError_t launch_paged_decode(const QcParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(items));
   const int qpw = (p.Sq + 3) / 4;
   switch (qpw) {
-    case 1: hipLaunchKernelGGL(paged_decode_kernel<1>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(paged_decode_kernel<2>, grid, dim3(256), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(paged_decode_kernel<3>, grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(paged_decode_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    case 1: decode_launch<1>(p, grid, stream); break;
+    case 2: decode_launch<2>(p, grid, stream); break;
+    case 3: decode_launch<3>(p, grid, stream); break;
+    case 4: decode_launch<4>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

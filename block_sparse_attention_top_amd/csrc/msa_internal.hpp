@@ -161,6 +161,11 @@ struct QcParams {
   float* lse;                // [B,Hq,Sq]
   float* o_part;             // [splits][B*Sq][Hq][D]
   float* lse_part;           // [splits][B*Sq][Hq]
+  // temperature-scaled LSE (log-sum-exp of the scores divided by T), written when
+  // lse_t != nullptr, in the layout of lse; partials [splits][B*Sq][Hq] when split
+  float inv_temp;            // 1 / T
+  float* lse_t;
+  float* lse_t_part;
   // variable-length batch (contiguous K/V only): cu_q != nullptr. Then q is
   // [total_q,Hq,D], k/v [total_k,Hkv,D], q2k [Hkv,total_q,topk], o [total_q,Hq,D],
   // lse [total_q,Hq]; B is the sequence count and Sq, Skv, nblk are unused.
@@ -185,6 +190,8 @@ struct TileParams {
   float scale_log2;
   uint16_t* o;
   float* lse;
+  float inv_temp;  // temperature-scaled LSE into lse_t (layout of lse) when lse_t != nullptr
+  float* lse_t;
   int ntiles;     // set by the launcher
   int xcd_pairs;  // set by the launcher: (b, hkv) pairs mapped onto XCD groups
 };
@@ -208,6 +215,8 @@ struct KvParams {
   uint16_t* o_part;          // bf16 [B*Sq][topk][Hkv][16 dim chunks][qpk][8], unnormalised:
                              // sum_j e^(s_j - M) V_j
   float2* lse_part;          // [B*Sq][topk][Hq]: (LSE of the block, reference max M), natural log
+  float inv_temp;            // 1 / T of the temperature-scaled LSE
+  float* lse_t_part;         // [B*Sq][topk][Hq] temperature-scaled LSE of the block, or nullptr
   // variable-length batch: cu_q != nullptr, rows r of sequence row_seq[r] hold its
   // block r - rowbase[b]; B*Sq above reads total_q (cap = total_q * topk)
   const int32_t* cu_q;
@@ -228,12 +237,15 @@ int device_cu_count();
 struct CombineVarlen {
   const int2* q_rows;  // VarlenTables::q_rows
 };
+// lse_t_part / lse_t (both or neither): merge of the temperature-scaled block LSEs
 hipError_t launch_combine_slots(const uint16_t* o_part, const float2* lse_part, const int32_t* q2k,
                                 int B, int Sq, int Hq, int Hkv, int topk, int nblk, uint16_t* o,
-                                float* lse, hipStream_t stream, const CombineVarlen* v = nullptr);
+                                float* lse, hipStream_t stream, const CombineVarlen* v = nullptr,
+                                const float* lse_t_part = nullptr, float* lse_t = nullptr);
 // combine of split partials (split-KV q-centric / paged decode)
 hipError_t launch_combine_splits(const float* o_part, const float* lse_part, int B, int Sq, int Hq,
-                                 int splits, uint16_t* o, float* lse, hipStream_t stream);
+                                 int splits, uint16_t* o, float* lse, hipStream_t stream,
+                                 const float* lse_t_part = nullptr, float* lse_t = nullptr);
 
 // exclusive scan of n int32 values: out[0..n] (out[n] = total); tmp >= scan_tmp_ints(n) ints
 size_t scan_tmp_ints(long long n);

@@ -12,6 +12,11 @@
 // unnormalised: U = sum_j e^(s_j - M) V_j with the block's reference max M,
 // stored beside (LSE of the block, M); the combine applies e^(M - LSE_total).
 //
+// With a temperature-scaled LSE requested (TEMP), each block also gets the
+// log-sum-exp of its scores divided by T, from a second sum of
+// 2^((s - M) c / T) kept beside the softmax sum; the combine merges those by
+// log-sum-exp like the ordinary LSE.
+//
 // A variable-length batch (packed Q/K/V with cu_seqlens) differs only in where
 // a row's keys and queries live: row r is block r - rowbase[b] of sequence b
 // (from the per-row sequence table), the block's keys start at cu_seqlens_k[b]
@@ -36,7 +41,7 @@ namespace msa {
 
 namespace {
 
-template <int QPK>
+template <int QPK, bool TEMP>
 __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   constexpr int kEnt = kKvChunkRows / QPK < kKvMaxEntries ? kKvChunkRows / QPK : kKvMaxEntries;
   __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
@@ -108,6 +113,10 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   const long long kend = min(kvlen - blk0, static_cast<long long>(kBlk));  // keys of the block
   const int nsteps = (ne + EPW - 1) / EPW;
   const float c2 = p.scale_log2;
+  const float c2t = c2 * p.inv_temp;
+  // the reference max moves when exceeded by 8 / max(1, 1/T) in log2 units, so that
+  // neither the softmax sum's nor the temperature sum's terms exceed 2^8
+  const float c2m = TEMP ? c2 * fmaxf(1.f, p.inv_temp) : c2;
   // lane offsets inside the tiles: K fragment row n, chunk h; V transposed reads
   const int kbase0 = n * kKStride + h * 16;
   const int vbase0 = (4 * h + rr) * kVStride + 32 * (j16 & 1) + 8 * cq;
@@ -149,6 +158,7 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
     // row sum is accumulated in fp32 (summing the bf16-rounded values instead
     // moves the LSE by up to ~1.4e-3 when a few keys dominate a row).
     float m_ref = -INFINITY, ps = 0.f;
+    float pst = 0.f;  // TEMP: sum of 2^((s - m_ref) * c2 / T)
     f32x16 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
@@ -183,10 +193,11 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (hf == 0) {
         m_ref = mx;
-      } else if (__any((mx - m_ref) * c2 > 8.f)) {
+      } else if (__any((mx - m_ref) * c2m > 8.f)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
         ps *= alpha;
+        if (TEMP) pst *= m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2t);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
         m_ref = m_new;
@@ -201,6 +212,9 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
           const float p1 = fast_exp2(fmaf(sacc[mt][2 * i + 1], c2, nmc));
           pk[mt][i] = pack_bf16x2(p0, p1);
           ps += p0 + p1;
+          if (TEMP)
+            pst += fast_exp2(fmaf(sacc[mt][2 * i], c2t, nmc * p.inv_temp)) +
+                   fast_exp2(fmaf(sacc[mt][2 * i + 1], c2t, nmc * p.inv_temp));
         }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -218,6 +232,7 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
       }
     }
     ps += __shfl_xor(ps, 32);
+    if (TEMP) pst += __shfl_xor(pst, 32);
     // lane (n, h) holds dims 32*dt + 8*q4 + 4*h .. +3 of row n (unnormalised) as
     // bf16 pairs. Swapping the odd-q4 half of lane h=0 with the even-q4 half of
     // lane h=1 (v_permlane32_swap) leaves each lane 16 contiguous bytes:
@@ -257,9 +272,15 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
         }
       if (h == 0) {
         const long long prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;
-        const float mnat = (m_ref == -INFINITY ? 0.f : m_ref) * c2 * kLn2;
-        const float lse_b = ps > 0.f ? mnat + fast_log2(ps) * kLn2 : -INFINITY;
+        // both LSEs as one explicit fma of the same shape, so that T = 1 gives equal bits
+        const float mr = m_ref == -INFINITY ? 0.f : m_ref;
+        const float mnat = mr * c2 * kLn2;
+        const float lse_b = ps > 0.f ? fmaf(fast_log2(ps), kLn2, mnat) : -INFINITY;
         p.lse_part[prow] = make_float2(lse_b, mnat);
+        if (TEMP) {
+          const float mnat_t = mr * c2t * kLn2;
+          p.lse_t_part[prow] = ps > 0.f ? fmaf(fast_log2(pst), kLn2, mnat_t) : -INFINITY;
+        }
       }
     }
     rc = rn;
@@ -280,6 +301,14 @@ __global__ void kv_items_kernel(const int32_t* __restrict__ row_ptr,
     items[c] = make_int4(hkv, r, e, min(chunk_entries, end - e));
 }
 
+template <int QPK>
+void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
+  if (p.lse_t_part)
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, false>), grid, dim3(256), 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
@@ -294,12 +323,13 @@ hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (p.chunk_entries * p.qpk > kKvChunkRows || p.chunk_entries > kKvMaxEntries)
     return hipErrorInvalidValue;
+  const dim3 g(grid);
   switch (p.qpk) {
-    case 1: hipLaunchKernelGGL(kvcentric_kernel<1>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(kvcentric_kernel<2>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(kvcentric_kernel<4>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(kvcentric_kernel<8>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(kvcentric_kernel<16>, dim3(grid), dim3(256), 0, stream, p); break;
+    case 1: kv_launch<1>(p, g, stream); break;
+    case 2: kv_launch<2>(p, g, stream); break;
+    case 4: kv_launch<4>(p, g, stream); break;
+    case 8: kv_launch<8>(p, g, stream); break;
+    case 16: kv_launch<16>(p, g, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -20,6 +20,10 @@
 // normalised fp32 partial (O, LSE) that the split combine merges (the
 // split-KV decode of `sparse_decode_atten_func` on the page "MSA interface.py").
 //
+// The temperature-scaled LSE (TEMP) keeps a second running sum of
+// 2^((x - m) / T) next to the softmax sum; the running max needs no second copy
+// because max(x / T) = max(x) / T for T > 0.
+//
 // Variable-length batches (packed Q/K/V with cu_seqlens, contiguous K/V): a
 // wave finds the sequence of its query row by binary search over
 // cu_seqlens_q; block ids count from the sequence's first key and the causal
@@ -34,7 +38,7 @@ namespace {
 
 constexpr int kSub = 32;  // tokens per sub-tile
 
-template <bool PAGED>
+template <bool PAGED, bool TEMP>
 __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[kSub * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vs[kSub * kVStride];
@@ -146,6 +150,7 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   };
 
   float m_run = -INFINITY, l_run = 0.f;
+  float lt_run = 0.f;  // TEMP: sum of 2^((x - m_run) / T), x the scores in log2 units
   f32x4 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -179,17 +184,23 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);  // finite: key jb is visible
     const float alpha = fast_exp2(m_run - m_new);
-    float ps = 0.f;
+    float ps = 0.f, pst = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (TEMP) pst += fast_exp2((x[mt][i] - m_new) * p.inv_temp);
         x[mt][i] = fast_exp2(x[mt][i] - m_new);
         ps += x[mt][i];
       }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
+    if (TEMP) {
+      pst += __shfl_xor(pst, 16);
+      pst += __shfl_xor(pst, 32);
+      lt_run = lt_run * fast_exp2((m_run - m_new) * p.inv_temp) + pst;
+    }
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   const bool any = l_run > 0.f;
   const float inv = any ? 1.f / l_run : 0.f;
   const float lse_v = any ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
+  const float lset_v = any ? (m_run * p.inv_temp + fast_log2(lt_run)) * kLn2 : -INFINITY;
   if (!head_ok) return;
   if (p.splits == 1) {
     uint16_t* orow = p.o + (grow * p.Hq + head) * kD + 4 * g;
@@ -238,17 +250,20 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
       *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
     }
     if (g == 0) {
-      if (!PAGED && p.cu_q)
-        p.lse[grow * p.Hq + head] = lse_v;
-      else
-        p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos] = lse_v;
+      const long long li = (!PAGED && p.cu_q) ? grow * p.Hq + head
+                                              : (static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos;
+      p.lse[li] = lse_v;
+      if (TEMP) p.lse_t[li] = lset_v;
     }
   } else {
     const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;  // paged
     float* orow = p.o_part + prow * kD + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = oacc[dt] * inv;
-    if (g == 0) p.lse_part[prow] = lse_v;
+    if (g == 0) {
+      p.lse_part[prow] = lse_v;
+      if (TEMP) p.lse_t_part[prow] = lset_v;
+    }
   }
 }
 
@@ -261,10 +276,15 @@ hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
-  if (paged)
-    hipLaunchKernelGGL(qcentric_kernel<true>, grid, dim3(64), 0, stream, p);
+  const bool temp = p.lse_t != nullptr;
+  if (paged && temp)
+    hipLaunchKernelGGL((qcentric_kernel<true, true>), grid, dim3(64), 0, stream, p);
+  else if (paged)
+    hipLaunchKernelGGL((qcentric_kernel<true, false>), grid, dim3(64), 0, stream, p);
+  else if (temp)
+    hipLaunchKernelGGL((qcentric_kernel<false, true>), grid, dim3(64), 0, stream, p);
   else
-    hipLaunchKernelGGL(qcentric_kernel<false>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((qcentric_kernel<false, false>), grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

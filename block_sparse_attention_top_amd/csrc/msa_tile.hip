@@ -61,7 +61,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       (__attribute__((address_space(3))) const void*)(p)));
 }
 
-template <int QPK>
+template <int QPK, bool TEMP>
 __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
   constexpr int EPW = 32 / QPK;     // queries per wave
   constexpr int T = kWaves * EPW;   // queries per tile
@@ -193,6 +193,11 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
   };
 
   float m_ref = -INFINITY, ls = 0.f;  // reference max (raw score units), row sum
+  float lt = 0.f;  // TEMP: row sum of 2^((s - m_ref) * c2 / T)
+  // the reference max moves when exceeded by 8 / max(1, 1/T) in log2 units, so that
+  // neither sum's terms exceed 2^8
+  const float c2t = c2 * p.inv_temp;
+  const float c2m = TEMP ? c2 * fmaxf(1.f, p.inv_temp) : c2;
   f32x16 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
@@ -242,10 +247,11 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[mt][i], sacc[mt][i + 1]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // the reference max moves only when exceeded by 2^8 (a row's first keys always)
-      if (__any((mx - m_ref) * c2 > 8.f)) {
+      if (__any((mx - m_ref) * c2m > 8.f)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
         ls *= alpha;
+        if (TEMP) lt *= m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2t);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
         m_ref = m_new;
@@ -260,6 +266,9 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
           const float p1 = fast_exp2(fmaf(sacc[mt][2 * i + 1], c2, nmc));
           pk[mt][i] = pack_bf16x2(p0, p1);
           ls += p0 + p1;
+          if (TEMP)
+            lt += fast_exp2(fmaf(sacc[mt][2 * i], c2t, nmc * p.inv_temp)) +
+                  fast_exp2(fmaf(sacc[mt][2 * i + 1], c2t, nmc * p.inv_temp));
         }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
 
   // 5. epilogue: O = O^T / sum, LSE = reference max + log(sum)
   ls += __shfl_xor(ls, 32);
+  if (TEMP) lt += __shfl_xor(lt, 32);
   const bool any = ls > 0.f;
   const float inv = any ? 1.f / ls : 0.f;
   // lane (n, h) holds dims 32*dt + 8*q4 + 4*h .. +3 of row n; swapping the odd-q4
@@ -328,9 +338,12 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {
                           ow[dt][2 * pp + 1][1]};
         *reinterpret_cast<u32x4*>(orow + 32 * dt + 16 * pp + 8 * h) = v4;
       }
-    if (h == 0)
-      p.lse[(static_cast<long long>(b) * p.Hq + head) * p.Sq + q] =
-          any ? ((m_ref == -INFINITY ? 0.f : m_ref) * c2 + fast_log2(ls)) * kLn2 : -INFINITY;
+    if (h == 0) {
+      const long long li = (static_cast<long long>(b) * p.Hq + head) * p.Sq + q;
+      const float mr = m_ref == -INFINITY ? 0.f : m_ref;
+      p.lse[li] = any ? fmaf(mr, c2, fast_log2(ls)) * kLn2 : -INFINITY;
+      if (TEMP) p.lse_t[li] = any ? fmaf(mr, c2t, fast_log2(lt)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -356,10 +369,16 @@ hipError_t launch_tile(TileParams p, hipStream_t stream) {
     grid = pairs * p.ntiles;
   }
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  if (p.qpk == 16)
-    hipLaunchKernelGGL(tile_kernel<16>, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, p);
+  const dim3 g(static_cast<unsigned>(grid)), blk(512);
+  const bool temp = p.lse_t != nullptr;
+  if (p.qpk == 16 && temp)
+    hipLaunchKernelGGL((tile_kernel<16, true>), g, blk, 0, stream, p);
+  else if (p.qpk == 16)
+    hipLaunchKernelGGL((tile_kernel<16, false>), g, blk, 0, stream, p);
+  else if (temp)
+    hipLaunchKernelGGL((tile_kernel<8, true>), g, blk, 0, stream, p);
   else
-    hipLaunchKernelGGL(tile_kernel<8>, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((tile_kernel<8, false>), g, blk, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -14,6 +14,9 @@
  *   O[b][q][h]   = sum_j softmax_j(scale * <Q, K_j>) V_j        (bf16 out)
  *   LSE[b][h][q] = log sum_j exp(scale * <Q, K_j>)               (natural log, fp32)
  *   J empty  ->  O = 0, LSE = -inf.
+ *   Optionally the temperature-scaled LSE (lse_temperature_scale of
+ *   sparse_atten_func): LSE_T[b][h][q] = log sum_j exp(scale * <Q, K_j> / T),
+ *   -inf when J is empty.
  *
  * Conventions shared by every entry point
  *   - Device pointers unless stated. bf16 tensors are raw 16-bit patterns.
@@ -32,6 +35,12 @@
  *     [0, num_pages) are treated as unused slots (no device-side error).
  *     The slots of one index row must name distinct blocks; repeated ids
  *     give unspecified results.
+ *   - Every forward entry point takes (lse_temperature_scale, lse_temperature):
+ *     lse_temperature NULL skips the temperature-scaled LSE; otherwise it is an
+ *     fp32 output in the layout of lse and lse_temperature_scale = T must be
+ *     positive and finite. T = 1 gives exactly the bits of lse. (The page's
+ *     binding returns lse itself for T = 1; the Python binding here does the
+ *     same unless asked to compute it.)
  *   - Return value: MSA_OK, or an error code with a message available from
  *     msa_last_error(). Argument errors are detected on the host before any
  *     launch, and then nothing is written.
@@ -80,6 +89,7 @@ enum msa_path {
  *   path     enum msa_path
  *   o        bf16 [B, Sq, Hq, D]   (out)
  *   lse      fp32 [B, Hq, Sq]      (out)
+ *   lse_temperature_scale, lse_temperature   fp32 [B, Hq, Sq] or NULL (out)
  *   workspace / workspace_bytes   at least msa_sparse_fwd_workspace_size(...)
  */
 size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk,
@@ -90,7 +100,8 @@ int msa_sparse_fwd_path(int B, int Sq, int Skv, int Hq, int Hkv, int topk, int p
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
                    const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
                    int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                   float softmax_scale, int path, void* o, float* lse, void* workspace,
+                   float softmax_scale, int path, void* o, float* lse,
+                   float lse_temperature_scale, float* lse_temperature, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /*
@@ -137,6 +148,7 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
  *                 (MSA_ERR_NOT_SUPPORTED for the tile and decode paths)
  *   o             bf16 [total_q, Hq, D]   (out)
  *   lse           fp32 [total_q, Hq]      (out; the packed layout of the page)
+ *   lse_temperature_scale, lse_temperature   fp32 [total_q, Hq] or NULL (out)
  *   workspace     at least msa_sparse_fwd_varlen_workspace_size(...)
  * total_q == 0 returns MSA_OK without touching anything.
  */
@@ -149,7 +161,8 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
                           const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
                           const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
                           int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                          float softmax_scale, int path, void* o, float* lse, void* workspace,
+                          float softmax_scale, int path, void* o, float* lse,
+                          float lse_temperature_scale, float* lse_temperature, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /*
@@ -196,7 +209,7 @@ int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
  *               MSA_PATH_DECODE (reads each distinct block of a (b, hkv) once: for
  *               index rows that share blocks; MSA_ERR_NOT_SUPPORTED when
  *               Sq > 16 or Sq * topk > 512)
- *   o, lse      as msa_sparse_fwd
+ *   o, lse, lse_temperature_scale, lse_temperature   as msa_sparse_fwd
  *   workspace   at least msa_paged_sparse_fwd_workspace_size(...) with the same
  *               num_splits and path (zero when one split results)
  * Duplicate ids within one index row: the decode path counts each block once;
@@ -213,7 +226,8 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, int path, void* o, float* lse, void* workspace,
+                         int num_splits, int path, void* o, float* lse,
+                         float lse_temperature_scale, float* lse_temperature, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /*

@@ -85,11 +85,11 @@ def main() -> int:
     w = (wl.VARLEN_WORKLOADS[args.workload] if args.workload in wl.VARLEN_WORKLOADS
          else wl.WORKLOADS[args.workload])
     if w.paged:
-        dom = {"paged-qcentric": "qcentric_kernel<true>",
-               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}>"}[args.path]
+        dom = {"paged-qcentric": "qcentric_kernel<true, false>",
+               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false>"}[args.path]
     else:
-        dom = {"q-centric": "qcentric_kernel<false>",
-               "kv-centric": f"kvcentric_kernel<{w.qpk}>",
+        dom = {"q-centric": "qcentric_kernel<false, false>",
+               "kv-centric": f"kvcentric_kernel<{w.qpk}, false>",
                "query-tile": "tile_kernel"}[args.path]
     lines = [f"# Kernel profile: {w.name}, {args.path} path", ""]
     if args.commands:

@@ -38,12 +38,12 @@ def fwd(**kw):
     lib = msa.load_library()
     a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, rp=None, qi=None, sl=None, B=1, Sq=256, Skv=256,
              Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1, scale=0.0, path=0, o=FAKE, lse=FAKE,
-             ws=None, wsb=0)
+             temp=1.0, lset=None, ws=None, wsb=0)
     a.update(kw)
     return lib.msa_sparse_fwd(a["q"], a["k"], a["v"], a["q2k"], a["rp"], a["qi"], a["sl"], a["B"],
                               a["Sq"], a["Skv"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
-                              a["causal"], a["scale"], a["path"], a["o"], a["lse"], a["ws"],
-                              a["wsb"], None)
+                              a["causal"], a["scale"], a["path"], a["o"], a["lse"], a["temp"],
+                              a["lset"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -51,6 +51,10 @@ def fwd(**kw):
     (dict(Hq=6, Hkv=4), 1), (dict(topk=33), 2), (dict(topk=0), 1), (dict(B=0), 1),
     (dict(Sq=0), 1), (dict(Skv=200), 1), (dict(q=None), 1), (dict(o=FAKE + 8), 1),
     (dict(lse=FAKE + 2), 1), (dict(path=7), 1), (dict(rp=FAKE), 1),
+    # temperature-scaled LSE: T must be positive and finite, the buffer aligned
+    (dict(lset=FAKE, temp=0.0), 1), (dict(lset=FAKE, temp=-2.0), 1),
+    (dict(lset=FAKE, temp=float("inf")), 1), (dict(lset=FAKE, temp=float("nan")), 1),
+    (dict(lset=FAKE + 2, temp=2.0), 1),
     # kv-centric without (enough) workspace
     (dict(path=2), 1), (dict(path=2, ws=FAKE, wsb=16), 1),
     # kv-centric with too many CSR rows for the LDS-resident passes
@@ -92,8 +96,8 @@ def test_csr_and_paged_reject():
                                  None) == 1
     # paged: page_size != 128, missing seqused_k, forced splits without workspace,
     # negative splits, unknown or kv-centric path, decode path with Sq > 16
-    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, 0, FAKE, FAKE, None,
-                         0, None]
+    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, 0, FAKE, FAKE, 1.0,
+                         None, None, 0, None]
     a = list(args); a[12] = 64
     assert lib.msa_paged_sparse_fwd(*a) == 2
     a = list(args); a[4] = None
@@ -107,6 +111,8 @@ def test_csr_and_paged_reject():
     assert lib.msa_paged_sparse_fwd(*a) == 1
     a = list(args); a[18] = 3; a[7] = 17
     assert lib.msa_paged_sparse_fwd(*a) == 2
+    a = list(args); a[21] = 0.0; a[22] = FAKE  # temperature buffer with T = 0
+    assert lib.msa_paged_sparse_fwd(*a) == 1
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):
@@ -143,13 +149,13 @@ def fwd_varlen(**kw):
     lib = msa.load_library()
     a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, cuq=FAKE, cuk=FAKE, rp=None, qi=None, sl=None,
              rows=0, B=3, tq=300, tk=900, Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1,
-             scale=0.0, path=0, o=FAKE, lse=FAKE, ws=None, wsb=0)
+             scale=0.0, path=0, o=FAKE, lse=FAKE, temp=1.0, lset=None, ws=None, wsb=0)
     a.update(kw)
     return lib.msa_sparse_fwd_varlen(a["q"], a["k"], a["v"], a["q2k"], a["cuq"], a["cuk"],
                                      a["rp"], a["qi"], a["sl"], a["rows"], a["B"], a["tq"],
                                      a["tk"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
                                      a["causal"], a["scale"], a["path"], a["o"], a["lse"],
-                                     a["ws"], a["wsb"], None)
+                                     a["temp"], a["lset"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -164,6 +170,7 @@ def fwd_varlen(**kw):
     (dict(path=2), 1), (dict(path=2, tk=128 * 20000), 2),
     # keys may be absent only when total_k == 0
     (dict(k=None), 1),
+    (dict(lset=FAKE, temp=0.0), 1),
 ])
 def test_sparse_fwd_varlen_rejects(kw, code):
     assert fwd_varlen(**kw) == code
