@@ -39,19 +39,21 @@ def _load():
         build()
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_sparse_attention.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, D, P,
-                                                I64, P, P, D, P, I]
+        lib.oracle_sparse_attention.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, D,
+                                                P, I64, P, P, D, P, I]
         lib.oracle_sparse_attention.restype = I
-        lib.oracle_paged_sparse_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I,
-                                                      I, I, D, P, I64, P, P, D, P, I]
+        lib.oracle_paged_sparse_attention.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, I, I,
+                                                      I, I, I, D, P, I64, P, P, D, P, I]
         lib.oracle_paged_sparse_attention.restype = I
         lib.oracle_k2q_csr.argtypes = [P, I, I, I, I, I, P, P, P]
         lib.oracle_k2q_csr.restype = I
-        lib.oracle_sparse_attention_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, D,
-                                                       P, I64, P, P, D, P, I]
+        lib.oracle_sparse_attention_varlen.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, I, I,
+                                                       D, P, I64, P, P, D, P, I]
         lib.oracle_sparse_attention_varlen.restype = I
         lib.oracle_k2q_csr_varlen.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
         lib.oracle_k2q_csr_varlen.restype = I
+        lib.oracle_fp8_e4m3_decode.argtypes = [P, I64, P]
+        lib.oracle_fp8_e4m3_decode.restype = I
         _lib = lib
     return _lib
 
@@ -62,6 +64,24 @@ def _ptr(a: Optional[np.ndarray]):
 
 def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _kv(k, v):
+    """K/V as given: uint16 (bf16 bits) or uint8 (fp8 e4m3fn bytes); returns (k, v, fp8)."""
+    fp8 = np.asarray(k).dtype == np.uint8
+    if fp8 != (np.asarray(v).dtype == np.uint8):
+        raise ValueError("k and v must both be bf16 bits (uint16) or both fp8 bytes (uint8)")
+    dt = np.uint8 if fp8 else np.uint16
+    return _c(k, dt), _c(v, dt), int(fp8)
+
+
+def fp8_e4m3_decode(x) -> np.ndarray:
+    """The oracle's fp8 e4m3fn decoding of a uint8 array (float64, same shape)."""
+    a = _c(x, np.uint8)
+    out = np.empty(a.shape, dtype=np.float64)
+    if _load().oracle_fp8_e4m3_decode(_ptr(a), a.size, _ptr(out)) != 0:
+        raise ValueError("oracle_fp8_e4m3_decode: invalid arguments")
+    return out
 
 
 def _shape_out(o, lse, rows, B, Sq, Hq, D, lse_t=None):
@@ -87,12 +107,14 @@ def sparse_attention(q, k, v, q2k, *, causal: bool, blk: int = 128,
                      temperature: Optional[float] = None, nthreads: int = 0):
     """Oracle forward, contiguous K/V.
 
-    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] as uint16 bf16 bits; q2k [B,Hkv,Sq,topk].
+    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] as uint16 bf16 bits (or uint8 fp8 e4m3fn bytes:
+    the fp8 KV cache); q2k [B,Hkv,Sq,topk].
     rows=None: returns O [B,Sq,Hq,D] and LSE [B,Hq,Sq] (float64).
     rows = array of b*Sq+q ids: returns O [n,Hq,D] and LSE [n,Hq].
     temperature: also return the temperature-scaled LSE (same layout as LSE).
     """
-    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    q = _c(q, np.uint16)
+    k, v, fp8 = _kv(k, v)
     q2k = _c(q2k, np.int32)
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
@@ -105,7 +127,8 @@ def sparse_attention(q, k, v, q2k, *, causal: bool, blk: int = 128,
     o = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
     temp, lse_t = _temperature_out(n, Hq, temperature)
-    rc = _load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(seq), B, Sq,
+    rc = _load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), fp8, _ptr(q2k), _ptr(seq), B,
+                                         Sq,
                                          Skv, Hq, Hkv, D, topk, blk, int(causal), scale,
                                          _ptr(rws), n, _ptr(o), _ptr(lse), temp, _ptr(lse_t),
                                          nthreads)
@@ -118,7 +141,8 @@ def paged_sparse_attention(q, k_pool, v_pool, page_table, seqused_k, q2k, *, cau
                            softmax_scale: Optional[float] = None, rows=None,
                            temperature: Optional[float] = None, nthreads: int = 0):
     """Oracle forward, paged K/V pool [num_pages,Hkv,page_size,D], page_table [B,max_pages]."""
-    q, k_pool, v_pool = _c(q, np.uint16), _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    q = _c(q, np.uint16)
+    k_pool, v_pool, fp8 = _kv(k_pool, v_pool)
     page_table, seqused_k, q2k = (_c(page_table, np.int32), _c(seqused_k, np.int32),
                                   _c(q2k, np.int32))
     B, Sq, Hq, D = q.shape
@@ -133,7 +157,8 @@ def paged_sparse_attention(q, k_pool, v_pool, page_table, seqused_k, q2k, *, cau
     lse = np.empty((n, Hq), dtype=np.float64)
     temp, lse_t = _temperature_out(n, Hq, temperature)
     rc = _load().oracle_paged_sparse_attention(
-        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seqused_k), _ptr(q2k), B, Sq,
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), fp8, _ptr(page_table), _ptr(seqused_k), _ptr(q2k),
+        B, Sq,
         Hq, Hkv, D, topk, page_size, num_pages, max_pages, int(causal), scale, _ptr(rws), n,
         _ptr(o), _ptr(lse), temp, _ptr(lse_t), nthreads)
     if rc != 0:
@@ -169,7 +194,8 @@ def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal:
     layout of the interface page) for the given global rows, n = total_q when rows=None;
     with a temperature, also the temperature-scaled LSE [n,Hq].
     """
-    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    q = _c(q, np.uint16)
+    k, v, fp8 = _kv(k, v)
     q2k, cq, ck = _c(q2k, np.int32), _c(cu_seqlens_q, np.int32), _c(cu_seqlens_k, np.int32)
     total_q, Hq, D = q.shape
     _, Hkv, _ = k.shape
@@ -182,7 +208,8 @@ def sparse_attention_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, *, causal:
     o = np.empty((n, Hq, D), dtype=np.float64)
     lse = np.empty((n, Hq), dtype=np.float64)
     temp, lse_t = _temperature_out(n, Hq, temperature)
-    rc = _load().oracle_sparse_attention_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cq),
+    rc = _load().oracle_sparse_attention_varlen(_ptr(q), _ptr(k), _ptr(v), fp8, _ptr(q2k),
+                                                _ptr(cq),
                                                 _ptr(ck), B, Hq, Hkv, D, topk, blk, int(causal),
                                                 scale, _ptr(rws), n, _ptr(o), _ptr(lse), temp,
                                                 _ptr(lse_t), nthreads)

@@ -22,14 +22,37 @@ static double bf16_value(uint16_t bits) {
   return (double)f;
 }
 
+/* fp8 e4m3fn (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * exponent and mantissa all ones = NaN): (-1)^s (1 + m/8) 2^(e-7), or m 2^-9 for e = 0 */
+static double fp8_value(uint8_t bits) {
+  const int s = bits >> 7, e = (bits >> 3) & 15, m = bits & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+int oracle_fp8_e4m3_decode(const uint8_t* in, int64_t n, double* out) {
+  if (!in || !out || n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = fp8_value(in[i]);
+  return 0;
+}
+
 /* Where the keys and values of one sequence live. */
 typedef struct {
-  const uint16_t* k;
-  const uint16_t* v;
+  const void* k;  /* bf16 bits, or fp8 e4m3fn bytes when fp8 */
+  const void* v;
   const int32_t* page_table; /* NULL: contiguous [B, Skv, Hkv, D] */
   int Skv;                   /* contiguous only */
   int Hkv, D, page_size, num_pages, max_pages;
+  int fp8;                   /* K/V stored as fp8 e4m3fn */
 } kv_source;
+
+static double k_value(const kv_source* s, int64_t i) {
+  return s->fp8 ? fp8_value(((const uint8_t*)s->k)[i]) : bf16_value(((const uint16_t*)s->k)[i]);
+}
+static double v_value(const kv_source* s, int64_t i) {
+  return s->fp8 ? fp8_value(((const uint8_t*)s->v)[i]) : bf16_value(((const uint16_t*)s->v)[i]);
+}
 
 /* Row offset (in elements) of key/value token j of sequence b, head hkv,
  * or -1 when the token has no storage (page id out of range). */
@@ -81,7 +104,7 @@ static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t
           const int64_t off = kv_offset(src, b, hkv, j);
           if (off < 0) continue;
           double dot = 0.0;
-          for (int d = 0; d < D; ++d) dot += bf16_value(qh[d]) * bf16_value(src->k[off + d]);
+          for (int d = 0; d < D; ++d) dot += bf16_value(qh[d]) * k_value(src, off + d);
           score[n++] = scale * dot;
           if (scale * dot > m) m = scale * dot;
         }
@@ -111,7 +134,7 @@ static void attend_row(const kv_source* src, const uint16_t* qrow, const int32_t
           if (off < 0) continue;
           const double p = exp(score[i++] - m);
           l += p;
-          for (int d = 0; d < D; ++d) acc[d] += p * bf16_value(src->v[off + d]);
+          for (int d = 0; d < D; ++d) acc[d] += p * v_value(src, off + d);
         }
       }
       for (int d = 0; d < D; ++d) oh[d] = acc[d] / l;
@@ -162,7 +185,7 @@ static int run_rows(const kv_source* src, const uint16_t* q, const int32_t* q2k,
   return failed ? -1 : 0;
 }
 
-int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+int oracle_sparse_attention(const uint16_t* q, const void* k, const void* v, int kv_fp8,
                             const int32_t* q2k, const int32_t* seqused_k, int B, int Sq, int Skv,
                             int Hq, int Hkv, int D, int topk, int blk, int causal, double scale,
                             const int64_t* rows, int64_t nrows, double* o, double* lse,
@@ -171,13 +194,13 @@ int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t
       Hq <= 0 || Hq % Hkv || D <= 0 || topk <= 0 || blk <= 0 || Skv % blk ||
       (lse_t && !(temp > 0.0)))
     return -1;
-  kv_source src = {k, v, NULL, Skv, Hkv, D, blk, 0, 0};
+  kv_source src = {k, v, NULL, Skv, Hkv, D, blk, 0, 0, kv_fp8 ? 1 : 0};
   return run_rows(&src, q, q2k, seqused_k, B, Sq, Hq, Hkv, D, topk, blk, Skv / blk, Skv, causal,
                   scale, rows, nrows, o, lse, temp, lse_t, nthreads);
 }
 
-int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
-                                  const uint16_t* v_pool, const int32_t* page_table,
+int oracle_paged_sparse_attention(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                  int kv_fp8, const int32_t* page_table,
                                   const int32_t* seqused_k, const int32_t* q2k, int B, int Sq,
                                   int Hq, int Hkv, int D, int topk, int page_size, int num_pages,
                                   int max_pages, int causal, double scale, const int64_t* rows,
@@ -187,7 +210,8 @@ int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
       Sq <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || D <= 0 || topk <= 0 || page_size <= 0 ||
       num_pages <= 0 || max_pages <= 0 || (lse_t && !(temp > 0.0)))
     return -1;
-  kv_source src = {k_pool, v_pool, page_table, 0, Hkv, D, page_size, num_pages, max_pages};
+  kv_source src = {k_pool, v_pool, page_table, 0, Hkv, D, page_size, num_pages, max_pages,
+                   kv_fp8 ? 1 : 0};
   return run_rows(&src, q, q2k, seqused_k, B, Sq, Hq, Hkv, D, topk, page_size, max_pages,
                   (int64_t)max_pages * page_size, causal, scale, rows, nrows, o, lse, temp,
                   lse_t, nthreads);
@@ -247,7 +271,7 @@ static int varlen_args_ok(const int32_t* cu_q, const int32_t* cu_k, int B) {
   return 1;
 }
 
-int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+int oracle_sparse_attention_varlen(const uint16_t* q, const void* k, const void* v, int kv_fp8,
                                    const int32_t* q2k, const int32_t* cu_seqlens_q,
                                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                    int topk, int blk, int causal, double scale,
@@ -289,9 +313,9 @@ int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const u
         const int Sq_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
         const int Skv_b = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
         const int nblk_b = (Skv_b + blk - 1) / blk;
-        const kv_source src = {k + (int64_t)cu_seqlens_k[b] * Hkv * D,
-                               v + (int64_t)cu_seqlens_k[b] * Hkv * D, NULL, Skv_b, Hkv, D,
-                               blk, 0, 0};
+        const int64_t koff = (int64_t)cu_seqlens_k[b] * Hkv * D * (kv_fp8 ? 1 : 2);
+        const kv_source src = {(const char*)k + koff, (const char*)v + koff, NULL, Skv_b, Hkv,
+                               D, blk, 0, 0, kv_fp8 ? 1 : 0};
         attend_row(&src, q + g * Hq * D, q2k + g * topk, total_q * topk, 0,
                    (int)(g - cu_seqlens_q[b]), Sq_b, Hq, Hkv, D, topk, blk, nblk_b, Skv_b,
                    causal, scale, mark, score, acc, o + i * Hq * D, lse + i * Hq, temp,

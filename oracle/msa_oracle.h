@@ -28,7 +28,9 @@ extern "C" {
 /*
  * Sparse attention, contiguous K/V.
  *   q        [B, Sq, Hq, D]   bf16 bits
- *   k, v     [B, Skv, Hkv, D] bf16 bits
+ *   k, v     [B, Skv, Hkv, D] bf16 bits, or fp8 e4m3fn bytes when kv_fp8 (the
+ *            fp8 KV cache of `sparse_atten_func`: each K/V element is the
+ *            e4m3fn value, used as is -- no scale)
  *   q2k      [B, Hkv, Sq, topk] int32 block ids, -1 (or any id outside
  *            [0, Skv/blk)) = unused slot; duplicates count once
  *   seqused_k NULL or [B]: keys j >= seqused_k[b] are masked and the causal
@@ -41,7 +43,7 @@ extern "C" {
  *            page and of `sparse_atten_func` on the interface page)
  * Returns 0, or -1 on invalid arguments.
  */
-int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+int oracle_sparse_attention(const uint16_t* q, const void* k, const void* v, int kv_fp8,
                             const int32_t* q2k, const int32_t* seqused_k, int B, int Sq, int Skv,
                             int Hq, int Hkv, int D, int topk, int blk, int causal, double scale,
                             const int64_t* rows, int64_t nrows, double* o, double* lse,
@@ -54,8 +56,8 @@ int oracle_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t
  * are masked and the causal limit is q + seqused_k[b] - Sq. Valid block ids
  * are [0, max_pages). Other arguments as above.
  */
-int oracle_paged_sparse_attention(const uint16_t* q, const uint16_t* k_pool,
-                                  const uint16_t* v_pool, const int32_t* page_table,
+int oracle_paged_sparse_attention(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                  int kv_fp8, const int32_t* page_table,
                                   const int32_t* seqused_k, const int32_t* q2k, int B, int Sq,
                                   int Hq, int Hkv, int D, int topk, int page_size, int num_pages,
                                   int max_pages, int causal, double scale, const int64_t* rows,
@@ -87,7 +89,7 @@ int oracle_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nbl
  *   rows  NULL (all total_q rows) or nrows global row ids
  *   o     [nrows, Hq, D] double; lse [nrows, Hq] double
  */
-int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+int oracle_sparse_attention_varlen(const uint16_t* q, const void* k, const void* v, int kv_fp8,
                                    const int32_t* q2k, const int32_t* cu_seqlens_q,
                                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                    int topk, int blk, int causal, double scale,
@@ -104,6 +106,12 @@ int oracle_sparse_attention_varlen(const uint16_t* q, const uint16_t* k, const u
 int oracle_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
                           const int32_t* cu_seqlens_k, int B, int Hkv, int topk, int blk,
                           int total_rows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot);
+
+/*
+ * The fp8 e4m3fn decoding the K/V reads use: n bytes -> n values (NaN for the
+ * two NaN patterns). Returns 0, or -1 on invalid arguments.
+ */
+int oracle_fp8_e4m3_decode(const uint8_t* in, int64_t n, double* out);
 
 #ifdef __cplusplus
 }

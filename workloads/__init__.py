@@ -280,3 +280,31 @@ VARLEN_WORKLOADS = {
 def make_varlen_workload_inputs(w: VarlenWorkload) -> dict:
     return make_varlen_inputs(w.seed, w.q_lens, w.k_lens, w.Hkv, w.qpk, w.topk, w.mode, w.D,
                               w.blk)
+
+
+# ---------------------------------------------------------------------------
+# fp8 e4m3fn K/V cache inputs (the fp8 KV cache of `sparse_atten_func`: K/V
+# elements stored as OCP float8_e4m3fn, no scale). Conversions use torch's CPU
+# float8_e4m3fn dtype: round to nearest even on the way in, exact on the way out.
+# ---------------------------------------------------------------------------
+def bf16_bits_to_fp8(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp8 e4m3fn bytes (uint8), round to nearest even."""
+    import torch
+    f = torch.from_numpy(bf16_to_f32(np.ascontiguousarray(x)))
+    return f.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp8 e4m3fn bytes -> the bf16 bit patterns of the same values (exact)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def with_fp8_kv(inp: dict) -> dict:
+    """A copy of uniform, paged or varlen inputs with K/V (or the pools) as fp8 bytes."""
+    out = dict(inp)
+    for name in ("k", "v", "k_pool", "v_pool"):
+        if name in out:
+            out[name] = bf16_bits_to_fp8(out[name])
+    return out
