@@ -96,8 +96,9 @@ def log(msg: str) -> None:
 
 
 def decode_algorithmic_bytes(w, inp) -> int:
-    """Distinct valid selected blocks per (b, hkv) x 128 tokens x D x 2 B x 2 (K and V),
-    plus Q, O, LSE, q2k, page table and seqused."""
+    """Distinct valid selected blocks per (b, hkv) x 128 tokens x D x element size x 2
+    (K and V; 2 B for bf16, 1 B for the fp8 cache), plus Q, O, LSE, q2k, page table and
+    seqused."""
     q2k = inp["q2k"]
     blocks = 0
     for b in range(w.B):
@@ -105,7 +106,7 @@ def decode_algorithmic_bytes(w, inp) -> int:
             ids = q2k[b, h].reshape(-1)
             ids = ids[(ids >= 0) & (ids < w.max_pages)]
             blocks += np.unique(ids).size
-    kv = blocks * 128 * w.D * 2 * 2
+    kv = blocks * 128 * w.D * inp["k_pool"].itemsize * 2
     q = w.B * w.Sq * w.Hq * w.D * 2
     return int(kv + 2 * q + w.B * w.Sq * w.Hq * 4 + q2k.nbytes + inp["page_table"].nbytes +
                inp["seqused_k"].nbytes)
@@ -114,7 +115,8 @@ def decode_algorithmic_bytes(w, inp) -> int:
 class Case:
     """One workload uploaded to the GPU with a callable that runs one step."""
 
-    def __init__(self, key: str, path: str, splits: int = 0, temperature=None):
+    def __init__(self, key: str, path: str, splits: int = 0, temperature=None,
+                 kv_dtype: str = "bf16"):
         import torch
         import block_sparse_attention_top_amd as msa
         import workloads as wl
@@ -129,6 +131,9 @@ class Case:
         w = self.w
         t0 = time.time()
         self.inp = wl.make_varlen_workload_inputs(w) if self.varlen else wl.make_inputs(w)
+        self.kv_dtype = kv_dtype
+        if kv_dtype == "fp8":  # the fp8 e4m3fn K/V cache (bytes, read as fp8 by the library)
+            self.inp = wl.with_fp8_kv(self.inp)
         log(f"[bench] {key}: inputs generated in {time.time() - t0:.1f}s")
         dev = lambda x: (torch.from_numpy(x).view(torch.bfloat16) if x.dtype == np.uint16
                          else torch.from_numpy(x)).to("cuda")
@@ -263,25 +268,30 @@ class Case:
                 "kernel_TFLOP_per_s": self.flops / (kernel_ms * 1e-3) / 1e12,
                 "effective_flop": self.flops, "path": self.path_name}
 
-    def dominant_kernel(self) -> str:
+    def dominant_kernel(self, temp: bool = False, fp8: bool = False) -> str:
+        """Name of the dominant kernel instance (template arguments as the profiler
+        prints them)."""
+        t, f = ("true" if temp else "false"), ("true" if fp8 else "false")
         if self.w.paged:
-            return {"paged-qcentric": "qcentric_kernel<true, false>",
-                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}, false>"}[self.path_name]
-        return {"q-centric": "qcentric_kernel<false, false>",
-                "kv-centric": f"kvcentric_kernel<{self.w.qpk}, false>",
-                "query-tile": "tile_kernel"}[self.path_name]
+            return {"paged-qcentric": f"qcentric_kernel<true, {t}, {f}>",
+                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}, {t}>"
+                    }[self.path_name]
+        return {"q-centric": f"qcentric_kernel<false, {t}, {f}>",
+                "kv-centric": f"kvcentric_kernel<{self.w.qpk}, {t}, {f}>",
+                "query-tile": f"tile_kernel<{self.w.qpk}, {t}>"}[self.path_name]
 
 
 def measured_traffic(case: "Case"):
     """HBM bytes per launch of the dominant kernel from the committed counter summary
     profiles/traffic_<workload>_<path>.json (FETCH_SIZE and WRITE_SIZE, scaled by a
     plain copy of known size), if it was taken on the current kernel sources."""
-    f = os.path.join(PROFILES, f"traffic_{case.key}_{case.path_name}.json")
+    fp8 = case.kv_dtype == "fp8"
+    f = os.path.join(PROFILES, f"traffic_{case.key}_{case.path_name}{'-fp8' if fp8 else ''}.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
         d = json.load(fh)
-    if d.get("source_digest") != source_digest(case.dominant_kernel()):
+    if d.get("source_digest") != source_digest(case.dominant_kernel(False, fp8)):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -354,6 +364,8 @@ def main() -> int:
                     help="KV splits of the paged workload (0 = the library's choice)")
     ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="K/V element type (fp8 = the e4m3fn cache)")
     ap.add_argument("--lse-temperature", type=float, default=None, metavar="T",
                     help="also compute the temperature-scaled LSE with this T")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,7 +380,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
-    case = Case(args.workload, args.path, args.splits, args.lse_temperature)
+    case = Case(args.workload, args.path, args.splits, args.lse_temperature, args.kv_dtype)
     log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
         f"({case.path_name})")
     ms, kernel_ms = case.time_steps(args.steps, args.warmup)
@@ -388,8 +400,9 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     roof["kernel"] = case.dominant_kernel()
-    if args.lse_temperature is not None:  # the kernels' temperature variants
-        roof["kernel"] = roof["kernel"].replace(", false>", ", true>")
+    if args.lse_temperature is not None or args.kv_dtype == "fp8":  # the kernels' variants
+        roof["kernel"] = case.dominant_kernel(args.lse_temperature is not None,
+                                              args.kv_dtype == "fp8")
     roof["kernel_ms"] = kernel_ms
     brk = case.breakdown(args.steps, args.warmup)
     if brk is not None:
@@ -413,13 +426,14 @@ def main() -> int:
         "config": ({"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
                     "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": case.splits,
-                    "lse_temperature": args.lse_temperature,
+                    "lse_temperature": args.lse_temperature, "kv_dtype": args.kv_dtype,
                     "parallelism": "none"} if not case.varlen else
                    {"workload": w.name, "B": w.B, "varlen": True, "total_q": w.total_q,
                     "total_k": w.total_k, "q_lens": list(w.q_lens), "k_lens": list(w.k_lens),
                     "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": 1,
-                    "lse_temperature": args.lse_temperature, "parallelism": "none"}),
+                    "lse_temperature": args.lse_temperature, "kv_dtype": args.kv_dtype,
+                    "parallelism": "none"}),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -8,8 +8,8 @@ fallback: if libmsa.so is missing or the GPU is absent the calls raise.
 """
 from __future__ import annotations
 
-from ._ffi import (MSA_PATH_AUTO, MSA_PATH_DECODE, MSA_PATH_KVCENTRIC, MSA_PATH_QCENTRIC,
-                   MSA_PATH_TILE,
+from ._ffi import (MSA_DTYPE_BF16, MSA_DTYPE_FP8_E4M3, MSA_PATH_AUTO, MSA_PATH_DECODE,
+                   MSA_PATH_KVCENTRIC, MSA_PATH_QCENTRIC, MSA_PATH_TILE,
                    MsaError, MsaNotSupportedError, MsaValueError, lib_path, load_library,
                    msa_build_k2q_csr, msa_build_k2q_csr_workspace_size, msa_last_error,
                    msa_paged_sparse_fwd, msa_paged_sparse_fwd_path, msa_paged_sparse_fwd_splits,
@@ -20,7 +20,7 @@ from ._ffi import (MSA_PATH_AUTO, MSA_PATH_DECODE, MSA_PATH_KVCENTRIC, MSA_PATH_
 
 __all__ = [
     "MSA_PATH_AUTO", "MSA_PATH_QCENTRIC", "MSA_PATH_KVCENTRIC", "MSA_PATH_DECODE",
-    "MSA_PATH_TILE", "MsaError",
+    "MSA_PATH_TILE", "MSA_DTYPE_BF16", "MSA_DTYPE_FP8_E4M3", "MsaError",
     "MsaValueError", "MsaNotSupportedError", "lib_path", "load_library", "msa_sparse_fwd",
     "msa_sparse_fwd_path", "msa_sparse_fwd_workspace_size", "msa_build_k2q_csr",
     "msa_build_k2q_csr_workspace_size", "msa_paged_sparse_fwd", "msa_paged_sparse_fwd_path",

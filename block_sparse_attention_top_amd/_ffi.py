@@ -12,6 +12,7 @@ _LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_VALUE, MSA_ERR_NOT_SUPPORTED, MSA_ERR_HIP = 0, 1, 2, 3
 MSA_PATH_AUTO, MSA_PATH_QCENTRIC, MSA_PATH_KVCENTRIC, MSA_PATH_DECODE, MSA_PATH_TILE = 0, 1, 2, 3, 4
+MSA_DTYPE_BF16, MSA_DTYPE_FP8_E4M3 = 0, 1
 
 _lib = None
 
@@ -50,8 +51,8 @@ def load_library():
     lib.msa_sparse_fwd_workspace_size.restype = S
     lib.msa_sparse_fwd_path.argtypes = [I] * 7
     lib.msa_sparse_fwd_path.restype = I
-    lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, P, F,
-                                   P, P, S, P]
+    lib.msa_sparse_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, P,
+                                   F, P, P, S, P]
     lib.msa_sparse_fwd.restype = I
     lib.msa_build_k2q_csr_workspace_size.argtypes = [I] * 5
     lib.msa_build_k2q_csr_workspace_size.restype = S
@@ -62,7 +63,7 @@ def load_library():
     lib.msa_sparse_fwd_varlen_path.argtypes = [I] * 7
     lib.msa_sparse_fwd_varlen_path.restype = I
     lib.msa_sparse_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
-                                          I, F, I, P, P, F, P, P, S, P]
+                                          I, F, I, I, P, P, F, P, P, S, P]
     lib.msa_sparse_fwd_varlen.restype = I
     lib.msa_build_k2q_csr_varlen_workspace_size.argtypes = [I] * 5
     lib.msa_build_k2q_csr_varlen_workspace_size.restype = S
@@ -75,7 +76,7 @@ def load_library():
     lib.msa_paged_sparse_fwd_splits.argtypes = [I] * 6
     lib.msa_paged_sparse_fwd_splits.restype = I
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
-                                         P, P, F, P, P, S, P]
+                                         I, P, P, F, P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
     lib.msa_set_profiling_events.argtypes = [P, P]
     lib.msa_set_profiling_events.restype = I
@@ -125,6 +126,22 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _kv_dtype(k: torch.Tensor, v: torch.Tensor, names=("k", "v")) -> int:
+    """bf16 K/V, or the fp8 e4m3fn cache (torch.float8_e4m3fn, or uint8 holding its bytes)."""
+    fp8 = {getattr(torch, "float8_e4m3fn", None), torch.uint8}
+    for t, nm in zip((k, v), names):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{nm} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
+        return MSA_DTYPE_BF16
+    if k.dtype in fp8 and v.dtype in fp8:
+        return MSA_DTYPE_FP8_E4M3
+    raise TypeError(f"{names[0]}/{names[1]} must both be bf16 or both fp8 e4m3fn, "
+                    f"got {k.dtype} / {v.dtype}")
 
 
 def _stream(stream) -> int:
@@ -177,10 +194,12 @@ def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None
                    blk_kv: int = 128, o=None, lse=None, return_temperature_lse: bool = False,
                    lse_temperature_scale: Optional[float] = None, lse_temperature=None,
                    temperature_fast_path: bool = True, workspace=None, stream=None):
-    """Sparse forward with contiguous K/V. Returns (O bf16 [B,Sq,Hq,D], LSE fp32 [B,Hq,Sq]),
-    plus the temperature-scaled LSE (same layout) when return_temperature_lse."""
+    """Sparse forward with contiguous K/V (bf16, or the fp8 e4m3fn cache). Returns
+    (O bf16 [B,Sq,Hq,D], LSE fp32 [B,Hq,Sq]), plus the temperature-scaled LSE (same
+    layout) when return_temperature_lse."""
     lib = load_library()
-    _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    kv_dtype = _kv_dtype(k, v)
     _dev(q2k, "q2k", torch.int32)
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
@@ -199,8 +218,8 @@ def msa_sparse_fwd(q, k, v, q2k, csr_row_ptr=None, csr_q_idx=None, csr_slot=None
     ws, wsn = _workspace(nbytes, q.device, workspace)
     rc = lib.msa_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(csr_row_ptr),
                             _ptr(csr_q_idx), _ptr(csr_slot), B, Sq, Skv, Hq, Hkv, D, topk, blk_kv,
-                            int(bool(causal)), float(softmax_scale), int(path), _ptr(o), _ptr(lse),
-                            temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
+                            int(bool(causal)), float(softmax_scale), int(path), kv_dtype, _ptr(o),
+                            _ptr(lse), temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
     if return_temperature_lse:
         return o, lse, (lse if alias else lse_t)
@@ -250,9 +269,10 @@ def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=
                           temperature_fast_path: bool = True, workspace=None, stream=None):
     """Sparse forward of a variable-length batch (packed q [total_q,Hq,D], k/v
     [total_k,Hkv,D], q2k [Hkv,total_q,topk], cu_seqlens [B+1] on the device).
-    Returns (O bf16 [total_q,Hq,D], LSE fp32 [total_q,Hq])."""
+    Returns (O bf16 [total_q,Hq,D], LSE fp32 [total_q,Hq]). K/V bf16 or fp8 e4m3fn."""
     lib = load_library()
-    _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    kv_dtype = _kv_dtype(k, v)
     _dev(q2k, "q2k", torch.int32)
     _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
     total_q, Hq, D = q.shape
@@ -280,7 +300,7 @@ def msa_sparse_fwd_varlen(q, k, v, q2k, cu_seqlens_q, cu_seqlens_k, csr_row_ptr=
         _ptr(q), _ptr(k), _ptr(v), _ptr(q2k), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         _ptr(csr_row_ptr), _ptr(csr_q_idx), _ptr(csr_slot), int(csr_total_rows), B, total_q,
         total_k, Hq, Hkv, D, topk, blk_kv, int(bool(causal)), float(softmax_scale), int(path),
-        _ptr(o), _ptr(lse), temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
+        kv_dtype, _ptr(o), _ptr(lse), temp, _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
     if return_temperature_lse:
         return o, lse, (lse if alias else lse_t)
@@ -343,8 +363,9 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
                          temperature_fast_path: bool = True, workspace=None, stream=None):
     """Sparse forward through a page table. Returns (O, LSE[, LSE_T]) as msa_sparse_fwd."""
     lib = load_library()
-    _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16), _dev(page_table, "page_table", torch.int32)
+    _dev(q, "q", torch.bfloat16)
+    kv_dtype = _kv_dtype(k_pool, v_pool, ("k_pool", "v_pool"))
+    _dev(page_table, "page_table", torch.int32)
     _dev(seqused_k, "seqused_k", torch.int32), _dev(q2k, "q2k", torch.int32)
     B, Sq, Hq, D = q.shape
     num_pages, Hkv, page_size, _ = k_pool.shape
@@ -363,7 +384,7 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
     rc = lib.msa_paged_sparse_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                                   _ptr(seqused_k), _ptr(q2k), B, Sq, Hq, Hkv, D, topk, page_size,
                                   num_pages, max_pages, int(bool(causal)), float(softmax_scale),
-                                  int(num_splits), int(path), _ptr(o), _ptr(lse), temp,
+                                  int(num_splits), int(path), kv_dtype, _ptr(o), _ptr(lse), temp,
                                   _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
     if return_temperature_lse:

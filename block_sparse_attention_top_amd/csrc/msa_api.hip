@@ -84,6 +84,17 @@ int resolve_varlen_path(int path, int B, long long total_q, long long total_k, i
   return MSA_PATH_KVCENTRIC;
 }
 
+// K/V element type: bf16 or the fp8 e4m3fn cache; the direct-to-LDS kernels (paged
+// decode, query tile) read bf16 only.
+int check_kv_dtype(int kv_dtype, int path_taken) {
+  if (kv_dtype != MSA_DTYPE_BF16 && kv_dtype != MSA_DTYPE_FP8_E4M3)
+    return fail(MSA_ERR_INVALID_VALUE, "unknown kv_dtype %d", kv_dtype);
+  if (kv_dtype == MSA_DTYPE_FP8_E4M3 && (path_taken == MSA_PATH_DECODE || path_taken == MSA_PATH_TILE))
+    return fail(MSA_ERR_NOT_SUPPORTED, "the %s path reads bf16 K/V only",
+                path_taken == MSA_PATH_DECODE ? "decode" : "query-tile");
+  return MSA_OK;
+}
+
 // Temperature-scaled LSE request: no buffer = off; else T must be positive and finite.
 int check_temperature(float scale, const float* lse_t) {
   if (!lse_t) return MSA_OK;
@@ -282,7 +293,7 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
                    const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
                    int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                   float softmax_scale, int path, void* o, float* lse,
+                   float softmax_scale, int path, int kv_dtype, void* o, float* lse,
                    float lse_temperature_scale, float* lse_temperature, void* workspace,
                    size_t workspace_bytes, void* stream) {
   g_last_error.clear();
@@ -309,6 +320,9 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
+  rc = check_kv_dtype(kv_dtype, which);
+  if (rc) return rc;
+  const int kv_fp8 = kv_dtype == MSA_DTYPE_FP8_E4M3;
 
   if (which == MSA_PATH_TILE) {
     if (!tile_supported(qpk, topk))
@@ -336,8 +350,9 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   if (which == MSA_PATH_QCENTRIC) {
     QcParams p{};
     p.q = static_cast<const uint16_t*>(q);
-    p.k = static_cast<const uint16_t*>(k);
-    p.v = static_cast<const uint16_t*>(v);
+    p.k = k;
+    p.v = v;
+    p.kv_fp8 = kv_fp8;
     p.q2k = q2k;
     p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
     p.nblk = nblk; p.causal = causal ? 1 : 0;
@@ -365,8 +380,9 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
   if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
   KvParams p{};
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
+  p.k = k;
+  p.v = v;
+  p.kv_fp8 = kv_fp8;
   p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
   p.nblk = nblk; p.nrows = static_cast<int>(nrows);
   p.cap = static_cast<long long>(B) * Sq * topk;
@@ -436,7 +452,7 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
                           const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
                           const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
                           int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                          float softmax_scale, int path, void* o, float* lse,
+                          float softmax_scale, int path, int kv_dtype, void* o, float* lse,
                           float lse_temperature_scale, float* lse_temperature, void* workspace,
                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
@@ -475,12 +491,16 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int which = resolve_varlen_path(path, B, total_q, total_k, Hq, topk);
   if (total_k == 0) which = MSA_PATH_QCENTRIC;  // no keys: every row is empty
+  rc = check_kv_dtype(kv_dtype, which);
+  if (rc) return rc;
+  const int kv_fp8 = kv_dtype == MSA_DTYPE_FP8_E4M3;
 
   if (which == MSA_PATH_QCENTRIC) {
     QcParams p{};
     p.q = static_cast<const uint16_t*>(q);
-    p.k = static_cast<const uint16_t*>(k);
-    p.v = static_cast<const uint16_t*>(v);
+    p.k = k;
+    p.v = v;
+    p.kv_fp8 = kv_fp8;
     p.q2k = q2k;
     p.cu_q = cu_seqlens_q;
     p.cu_k = cu_seqlens_k;
@@ -518,8 +538,9 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
   if (e != hipSuccess) return hip_fail(e, "varlen tables");
   KvParams p{};
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
+  p.k = k;
+  p.v = v;
+  p.kv_fp8 = kv_fp8;
   p.B = 1; p.Sq = total_q; p.Skv = 0; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
   p.nblk = 0; p.nrows = static_cast<int>(nrows);
   p.cap = static_cast<long long>(total_q) * topk;
@@ -598,7 +619,7 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, int path, void* o, float* lse,
+                         int num_splits, int path, int kv_dtype, void* o, float* lse,
                          float lse_temperature_scale, float* lse_temperature, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
@@ -622,13 +643,16 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                 4 * kMaxQPerWave, kDecMaxEntries, Sq, topk);
   const PagedPlan plan = paged_plan(B, Sq, Hkv, topk, num_splits, path);
   const int splits = plan.splits;
+  rc = check_kv_dtype(kv_dtype, plan.path);
+  if (rc) return rc;
   const int qpk = Hq / Hkv;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   QcParams p{};
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k_pool);
-  p.v = static_cast<const uint16_t*>(v_pool);
+  p.k = k_pool;
+  p.v = v_pool;
+  p.kv_fp8 = kv_dtype == MSA_DTYPE_FP8_E4M3;
   p.q2k = q2k;
   p.page_table = page_table;
   p.seqused = seqused_k;

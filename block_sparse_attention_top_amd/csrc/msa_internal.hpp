@@ -89,6 +89,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// fp8 e4m3fn K/V cache: 16 fp8 bytes -> 16 bf16 values (exact; e4m3fn is a subset
+// of bf16), with the gfx950 conversion v_cvt_scalef32_pk_bf16_fp8 at scale 1
+// (two bytes per instruction, OCP e4m3fn, NaN codes to NaN). out[0] holds
+// elements 0..7, out[1] elements 8..15.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 out[2]) {
+  out[0] = u32x4{fp8x2_to_bf16x2<false>(in[0]), fp8x2_to_bf16x2<true>(in[0]),
+                 fp8x2_to_bf16x2<false>(in[1]), fp8x2_to_bf16x2<true>(in[1])};
+  out[1] = u32x4{fp8x2_to_bf16x2<false>(in[2]), fp8x2_to_bf16x2<true>(in[2]),
+                 fp8x2_to_bf16x2<false>(in[3]), fp8x2_to_bf16x2<true>(in[3])};
+}
+
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407359f;
 
@@ -146,8 +161,9 @@ hipError_t launch_varlen_tables(const int32_t* cu_q, const int32_t* cu_k, int B,
 // ---------------------------------------------------------------------------
 struct QcParams {
   const uint16_t* q;
-  const uint16_t* k;         // contiguous [B,Skv,Hkv,D] or pool [num_pages,Hkv,128,D]
-  const uint16_t* v;
+  const void* k;             // contiguous [B,Skv,Hkv,D] or pool [num_pages,Hkv,128,D]
+  const void* v;             // (bf16, or fp8 e4m3fn bytes when kv_fp8)
+  int kv_fp8;
   const int32_t* q2k;        // [B,Hkv,Sq,topk]
   const int32_t* page_table; // paged only: [B,max_pages]
   const int32_t* seqused;    // paged only: [B]
@@ -200,8 +216,9 @@ hipError_t launch_tile(TileParams p, hipStream_t stream);
 
 struct KvParams {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const void* k;             // bf16, or fp8 e4m3fn bytes when kv_fp8
+  const void* v;
+  int kv_fp8;
   const int32_t* row_ptr;    // [Hkv, nrows+1]
   const int32_t* q_idx;      // [Hkv, cap]
   const int32_t* slot;       // [Hkv, cap]

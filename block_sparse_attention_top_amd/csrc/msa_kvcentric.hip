@@ -12,6 +12,9 @@
 // unnormalised: U = sum_j e^(s_j - M) V_j with the block's reference max M,
 // stored beside (LSE of the block, M); the combine applies e^(M - LSE_total).
 //
+// An fp8 e4m3fn K/V cache (FP8) is widened exactly to bf16 while the block's
+// tiles are staged into LDS; everything after runs on the same bf16 tiles.
+//
 // With a temperature-scaled LSE requested (TEMP), each block also gets the
 // log-sum-exp of its scores divided by T, from a second sum of
 // 2^((s - M) c / T) kept beside the softmax sum; the combine merges those by
@@ -41,7 +44,7 @@ namespace msa {
 
 namespace {
 
-template <int QPK, bool TEMP>
+template <int QPK, bool TEMP, bool FP8>
 __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   constexpr int kEnt = kKvChunkRows / QPK < kKvMaxEntries ? kKvChunkRows / QPK : kKvMaxEntries;
   __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
@@ -81,21 +84,39 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
     ent_t[i] = p.slot[hkv * p.cap + e0 + i];
   }
   {
-    // rows past the sequence's last key re-read that key; they are masked out of S
-    u32x4 rk[8], rv[8];
+    // rows past the sequence's last key re-read that key; they are masked out of S.
+    // 16-byte loads of 8 bf16, or of 16 fp8 widened to two bf16 chunks (exact).
+    constexpr int kEpc = FP8 ? 16 : 8;      // elements per load
+    constexpr int kCpr = kD / kEpc;         // loads per row
+    constexpr int kLpt = kBlk * kCpr / 256; // loads per thread
+    constexpr int kEsz = FP8 ? 1 : 2;
+    const char* kb = static_cast<const char*>(p.k);
+    const char* vb = static_cast<const char*>(p.v);
+    u32x4 rk[kLpt], rv[kLpt];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLpt; ++i) {
       const int ci = i * 256 + tid;
-      const int row = ci >> 4, c = ci & 15;
+      const int row = ci / kCpr, c = ci % kCpr;
       const long long tok = kbeg + min(blk0 + row, kvlen - 1);
-      const long long off = (tok * p.Hkv + hkv) * kD + c * 8;
-      rk[i] = *reinterpret_cast<const u32x4*>(p.k + off);
-      rv[i] = *reinterpret_cast<const u32x4*>(p.v + off);
+      const long long off = ((tok * p.Hkv + hkv) * kD + c * kEpc) * kEsz;
+      rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      rv[i] = *reinterpret_cast<const u32x4*>(vb + off);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLpt; ++i) {
       const int ci = i * 256 + tid;
-      const int row = ci >> 4, c = ci & 15;
+      const int row = ci / kCpr, c = ci % kCpr;
+      if (FP8) {
+        u32x4 kw[2], vw[2];
+        fp8x16_to_bf16x16(rk[i], kw);
+        fp8x16_to_bf16x16(rv[i], vw);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          *reinterpret_cast<u32x4*>(ks + k_off(row, 2 * c + h2)) = kw[h2];
+          *reinterpret_cast<u32x4*>(vs + v_off(row, 2 * c + h2)) = vw[h2];
+        }
+        continue;
+      }
       *reinterpret_cast<u32x4*>(ks + k_off(row, c)) = rk[i];
       *reinterpret_cast<u32x4*>(vs + v_off(row, c)) = rv[i];
     }
@@ -303,10 +324,15 @@ __global__ void kv_items_kernel(const int32_t* __restrict__ row_ptr,
 
 template <int QPK>
 void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
-  if (p.lse_t_part)
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, true>), grid, dim3(256), 0, stream, p);
+  const dim3 blk(256);
+  if (p.lse_t_part && p.kv_fp8)
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, true>), grid, blk, 0, stream, p);
+  else if (p.lse_t_part)
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, false>), grid, blk, 0, stream, p);
+  else if (p.kv_fp8)
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, true>), grid, blk, 0, stream, p);
   else
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, false>), grid, blk, 0, stream, p);
 }
 
 }  // namespace

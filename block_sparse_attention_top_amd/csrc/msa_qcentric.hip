@@ -20,6 +20,10 @@
 // normalised fp32 partial (O, LSE) that the split combine merges (the
 // split-KV decode of `sparse_decode_atten_func` on the page "MSA interface.py").
 //
+// With an fp8 e4m3fn K/V cache (FP8) each 16-byte load brings 16 elements, which
+// are widened exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8) while being stored to
+// LDS, so the products run on the same bf16 tiles.
+//
 // The temperature-scaled LSE (TEMP) keeps a second running sum of
 // 2^((x - m) / T) next to the softmax sum; the running max needs no second copy
 // because max(x / T) = max(x) / T for T > 0.
@@ -38,7 +42,7 @@ namespace {
 
 constexpr int kSub = 32;  // tokens per sub-tile
 
-template <bool PAGED, bool TEMP>
+template <bool PAGED, bool TEMP, bool FP8>
 __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[kSub * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vs[kSub * kVStride];
@@ -120,32 +124,51 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     }
   };
 
-  u32x4 kr[8], vr[8];
+  // A sub-tile is 32 rows of 128 elements: 16-byte loads of 8 bf16 (8 per lane) or of
+  // 16 fp8 (4 per lane, each widened to two bf16 chunks on the way to LDS).
+  constexpr int kEpc = FP8 ? 16 : 8;          // elements per 16-byte load
+  constexpr int kCpr = kD / kEpc;             // loads per row
+  constexpr int kLpl = kSub * kCpr / 64;      // loads per lane
+  constexpr int kEsz = FP8 ? 1 : 2;           // bytes per K/V element
+  const char* kb = static_cast<const char*>(p.k);
+  const char* vb = static_cast<const char*>(p.v);
+  u32x4 kr[kLpl], vr[kLpl];
   auto load = [&](int s, int pg, int u) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLpl; ++i) {
       const int ci = i * 64 + lane;
-      const int row = ci >> 4, c = ci & 15;
-      long long off;
+      const int row = ci / kCpr, c = ci % kCpr;
+      long long off;  // in elements
       if (PAGED)
-        off = ((static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * u + row) * kD + c * 8;
+        off = ((static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * u + row) * kD + c * kEpc;
       else  // rows past the sequence's last key re-read that key (stored as zeros)
         off = ((kbeg + min(static_cast<long long>(s) * kBlk + kSub * u + row, kvlen - 1)) * p.Hkv +
-               hkv) * kD + c * 8;
-      kr[i] = *reinterpret_cast<const u32x4*>(p.k + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(p.v + off);
+               hkv) * kD + c * kEpc;
+      kr[i] = *reinterpret_cast<const u32x4*>(kb + off * kEsz);
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + off * kEsz);
     }
   };
   // keys past `end` are stored as zeros so that no value there can leak into P*V
   auto store = [&](int s, int u) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLpl; ++i) {
       const int ci = i * 64 + lane;
-      const int row = ci >> 4, c = ci & 15;
+      const int row = ci / kCpr, c = ci % kCpr;
       const bool ok = static_cast<long long>(s) * kBlk + kSub * u + row < end;
       const u32x4 z = {0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(ks + k_off(row, c)) = ok ? kr[i] : z;
-      *reinterpret_cast<u32x4*>(vs + v_off(row, c)) = ok ? vr[i] : z;
+      if (FP8) {
+        u32x4 kw[2], vw[2];
+        fp8x16_to_bf16x16(kr[i], kw);
+        fp8x16_to_bf16x16(vr[i], vw);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          *reinterpret_cast<u32x4*>(ks + k_off(row, 2 * c + h2)) = ok ? kw[h2] : z;
+          *reinterpret_cast<u32x4*>(vs + v_off(row, 2 * c + h2)) = ok ? vw[h2] : z;
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(ks + k_off(row, c)) = ok ? kr[i] : z;
+        *reinterpret_cast<u32x4*>(vs + v_off(row, c)) = ok ? vr[i] : z;
+      }
     }
   };
 
@@ -276,15 +299,17 @@ hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
-  const bool temp = p.lse_t != nullptr;
-  if (paged && temp)
-    hipLaunchKernelGGL((qcentric_kernel<true, true>), grid, dim3(64), 0, stream, p);
-  else if (paged)
-    hipLaunchKernelGGL((qcentric_kernel<true, false>), grid, dim3(64), 0, stream, p);
-  else if (temp)
-    hipLaunchKernelGGL((qcentric_kernel<false, true>), grid, dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((qcentric_kernel<false, false>), grid, dim3(64), 0, stream, p);
+  const int variant = (paged ? 4 : 0) + (p.lse_t ? 2 : 0) + (p.kv_fp8 ? 1 : 0);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((qcentric_kernel<false, false, false>), grid, dim3(64), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((qcentric_kernel<false, false, true>), grid, dim3(64), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((qcentric_kernel<false, true, false>), grid, dim3(64), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((qcentric_kernel<false, true, true>), grid, dim3(64), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((qcentric_kernel<true, false, false>), grid, dim3(64), 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((qcentric_kernel<true, false, true>), grid, dim3(64), 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((qcentric_kernel<true, true, false>), grid, dim3(64), 0, stream, p); break;
+    default: hipLaunchKernelGGL((qcentric_kernel<true, true, true>), grid, dim3(64), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 

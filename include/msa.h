@@ -75,6 +75,17 @@ enum msa_path {
                              share blocks) */
 };
 
+/* K/V element type (kv_dtype of every forward entry point). */
+enum msa_dtype {
+  MSA_DTYPE_BF16 = 0,     /* bf16 K/V */
+  MSA_DTYPE_FP8_E4M3 = 1  /* the fp8 KV cache of sparse_atten_func: OCP float8_e4m3fn bytes,
+                             no scale, widened exactly to bf16 for both products, so the
+                             result equals the bf16 path on the dequantized K/V bit for
+                             bit; K/V tensors keep their shapes with 1-byte elements.
+                             The q-centric and kv-centric kernels read it; the decode and
+                             query-tile paths return MSA_ERR_NOT_SUPPORTED */
+};
+
 /*
  * Sparse forward, contiguous K/V (sparse_atten_func, dense KV layout).
  *   q        bf16 [B, Sq, Hq, D]
@@ -87,6 +98,7 @@ enum msa_path {
  *   causal   0 none, 1 bottom-right (limit q + Skv - Sq)
  *   softmax_scale  <= 0 selects D^-0.5
  *   path     enum msa_path
+ *   kv_dtype enum msa_dtype
  *   o        bf16 [B, Sq, Hq, D]   (out)
  *   lse      fp32 [B, Hq, Sq]      (out)
  *   lse_temperature_scale, lse_temperature   fp32 [B, Hq, Sq] or NULL (out)
@@ -100,7 +112,7 @@ int msa_sparse_fwd_path(int B, int Sq, int Skv, int Hq, int Hkv, int topk, int p
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
                    const int32_t* csr_row_ptr, const int32_t* csr_q_idx, const int32_t* csr_slot,
                    int B, int Sq, int Skv, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                   float softmax_scale, int path, void* o, float* lse,
+                   float softmax_scale, int path, int kv_dtype, void* o, float* lse,
                    float lse_temperature_scale, float* lse_temperature, void* workspace,
                    size_t workspace_bytes, void* stream);
 
@@ -146,6 +158,7 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
  *                 kv-centric path only
  *   path          MSA_PATH_AUTO, MSA_PATH_QCENTRIC or MSA_PATH_KVCENTRIC
  *                 (MSA_ERR_NOT_SUPPORTED for the tile and decode paths)
+ *   kv_dtype      enum msa_dtype
  *   o             bf16 [total_q, Hq, D]   (out)
  *   lse           fp32 [total_q, Hq]      (out; the packed layout of the page)
  *   lse_temperature_scale, lse_temperature   fp32 [total_q, Hq] or NULL (out)
@@ -161,7 +174,7 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
                           const int32_t* csr_row_ptr, const int32_t* csr_q_idx,
                           const int32_t* csr_slot, int csr_total_rows, int B, int total_q,
                           int total_k, int Hq, int Hkv, int D, int topk, int blk_kv, int causal,
-                          float softmax_scale, int path, void* o, float* lse,
+                          float softmax_scale, int path, int kv_dtype, void* o, float* lse,
                           float lse_temperature_scale, float* lse_temperature, void* workspace,
                           size_t workspace_bytes, void* stream);
 
@@ -209,6 +222,7 @@ int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
  *               MSA_PATH_DECODE (reads each distinct block of a (b, hkv) once: for
  *               index rows that share blocks; MSA_ERR_NOT_SUPPORTED when
  *               Sq > 16 or Sq * topk > 512)
+ *   kv_dtype    enum msa_dtype (fp8 with the q-centric path only)
  *   o, lse, lse_temperature_scale, lse_temperature   as msa_sparse_fwd
  *   workspace   at least msa_paged_sparse_fwd_workspace_size(...) with the same
  *               num_splits and path (zero when one split results)
@@ -226,7 +240,7 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
                          int num_pages, int max_pages, int causal, float softmax_scale,
-                         int num_splits, int path, void* o, float* lse,
+                         int num_splits, int path, int kv_dtype, void* o, float* lse,
                          float lse_temperature_scale, float* lse_temperature, void* workspace,
                          size_t workspace_bytes, void* stream);
 

@@ -76,6 +76,7 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--commands", help="text file with the commands that produced the dirs")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"])
     args = ap.parse_args()
 
     import bench
@@ -84,14 +85,17 @@ def main() -> int:
     durs = kernel_durations(args.trace)
     w = (wl.VARLEN_WORKLOADS[args.workload] if args.workload in wl.VARLEN_WORKLOADS
          else wl.WORKLOADS[args.workload])
+    f8 = "true" if args.kv_dtype == "fp8" else "false"
     if w.paged:
-        dom = {"paged-qcentric": "qcentric_kernel<true, false>",
+        dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8}>",
                "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false>"}[args.path]
     else:
-        dom = {"q-centric": "qcentric_kernel<false, false>",
-               "kv-centric": f"kvcentric_kernel<{w.qpk}, false>",
-               "query-tile": "tile_kernel"}[args.path]
-    lines = [f"# Kernel profile: {w.name}, {args.path} path", ""]
+        dom = {"q-centric": f"qcentric_kernel<false, false, {f8}>",
+               "kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}>",
+               "query-tile": f"tile_kernel<{w.qpk}, false>"}[args.path]
+    tag = "" if args.kv_dtype == "bf16" else "-fp8"
+    lines = [f"# Kernel profile: {w.name}, {args.path} path"
+             + ("" if not tag else ", fp8 e4m3fn K/V cache"), ""]
     if args.commands:
         lines += ["Commands (run from the repository root on one MI355X):", "", "```"]
         lines += open(args.commands).read().strip().splitlines()
@@ -132,12 +136,12 @@ def main() -> int:
                       f"{write_b / 1e9:.3f} GB written",
                       f"- total {traffic / 1e9:.3f} GB per launch"]
     os.makedirs(args.out, exist_ok=True)
-    md = os.path.join(args.out, f"kernels_{args.workload}_{args.path}.md")
+    md = os.path.join(args.out, f"kernels_{args.workload}_{args.path}{tag}.md")
     with open(md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("wrote", md)
     if traffic is not None:
-        js = os.path.join(args.out, f"traffic_{args.workload}_{args.path}.json")
+        js = os.path.join(args.out, f"traffic_{args.workload}_{args.path}{tag}.json")
         with open(js, "w") as fh:
             json.dump({"workload": w.name, "path": args.path, "kernel": dom,
                        "hbm_bytes_per_launch": traffic, "kernel_avg_us": dom_avg,

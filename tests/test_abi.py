@@ -37,13 +37,13 @@ FAKE = 0x10000  # never dereferenced: every call below fails host validation fir
 def fwd(**kw):
     lib = msa.load_library()
     a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, rp=None, qi=None, sl=None, B=1, Sq=256, Skv=256,
-             Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1, scale=0.0, path=0, o=FAKE, lse=FAKE,
-             temp=1.0, lset=None, ws=None, wsb=0)
+             Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1, scale=0.0, path=0, kvd=0, o=FAKE,
+             lse=FAKE, temp=1.0, lset=None, ws=None, wsb=0)
     a.update(kw)
     return lib.msa_sparse_fwd(a["q"], a["k"], a["v"], a["q2k"], a["rp"], a["qi"], a["sl"], a["B"],
                               a["Sq"], a["Skv"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
-                              a["causal"], a["scale"], a["path"], a["o"], a["lse"], a["temp"],
-                              a["lset"], a["ws"], a["wsb"], None)
+                              a["causal"], a["scale"], a["path"], a["kvd"], a["o"], a["lse"],
+                              a["temp"], a["lset"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -55,6 +55,8 @@ def fwd(**kw):
     (dict(lset=FAKE, temp=0.0), 1), (dict(lset=FAKE, temp=-2.0), 1),
     (dict(lset=FAKE, temp=float("inf")), 1), (dict(lset=FAKE, temp=float("nan")), 1),
     (dict(lset=FAKE + 2, temp=2.0), 1),
+    # K/V dtype: unknown code; fp8 on the query-tile path
+    (dict(kvd=2), 1), (dict(kvd=-1), 1), (dict(kvd=1, path=4), 2),
     # kv-centric without (enough) workspace
     (dict(path=2), 1), (dict(path=2, ws=FAKE, wsb=16), 1),
     # kv-centric with too many CSR rows for the LDS-resident passes
@@ -96,8 +98,8 @@ def test_csr_and_paged_reject():
                                  None) == 1
     # paged: page_size != 128, missing seqused_k, forced splits without workspace,
     # negative splits, unknown or kv-centric path, decode path with Sq > 16
-    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, 0, FAKE, FAKE, 1.0,
-                         None, None, 0, None]
+    args = [FAKE] * 6 + [32, 8, 64, 4, 128, 16, 128, 16384, 512, 1, 0.0, 0, 0, 0, FAKE, FAKE,
+                         1.0, None, None, 0, None]
     a = list(args); a[12] = 64
     assert lib.msa_paged_sparse_fwd(*a) == 2
     a = list(args); a[4] = None
@@ -111,7 +113,11 @@ def test_csr_and_paged_reject():
     assert lib.msa_paged_sparse_fwd(*a) == 1
     a = list(args); a[18] = 3; a[7] = 17
     assert lib.msa_paged_sparse_fwd(*a) == 2
-    a = list(args); a[21] = 0.0; a[22] = FAKE  # temperature buffer with T = 0
+    a = list(args); a[22] = 0.0; a[23] = FAKE  # temperature buffer with T = 0
+    assert lib.msa_paged_sparse_fwd(*a) == 1
+    a = list(args); a[18] = 3; a[19] = 1  # fp8 K/V on the decode path
+    assert lib.msa_paged_sparse_fwd(*a) == 2
+    a = list(args); a[19] = 5  # unknown K/V dtype
     assert lib.msa_paged_sparse_fwd(*a) == 1
 
 
@@ -149,13 +155,13 @@ def fwd_varlen(**kw):
     lib = msa.load_library()
     a = dict(q=FAKE, k=FAKE, v=FAKE, q2k=FAKE, cuq=FAKE, cuk=FAKE, rp=None, qi=None, sl=None,
              rows=0, B=3, tq=300, tk=900, Hq=16, Hkv=1, D=128, topk=4, blk=128, causal=1,
-             scale=0.0, path=0, o=FAKE, lse=FAKE, temp=1.0, lset=None, ws=None, wsb=0)
+             scale=0.0, path=0, kvd=0, o=FAKE, lse=FAKE, temp=1.0, lset=None, ws=None, wsb=0)
     a.update(kw)
     return lib.msa_sparse_fwd_varlen(a["q"], a["k"], a["v"], a["q2k"], a["cuq"], a["cuk"],
                                      a["rp"], a["qi"], a["sl"], a["rows"], a["B"], a["tq"],
                                      a["tk"], a["Hq"], a["Hkv"], a["D"], a["topk"], a["blk"],
-                                     a["causal"], a["scale"], a["path"], a["o"], a["lse"],
-                                     a["temp"], a["lset"], a["ws"], a["wsb"], None)
+                                     a["causal"], a["scale"], a["path"], a["kvd"], a["o"],
+                                     a["lse"], a["temp"], a["lset"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -170,7 +176,7 @@ def fwd_varlen(**kw):
     (dict(path=2), 1), (dict(path=2, tk=128 * 20000), 2),
     # keys may be absent only when total_k == 0
     (dict(k=None), 1),
-    (dict(lset=FAKE, temp=0.0), 1),
+    (dict(lset=FAKE, temp=0.0), 1), (dict(kvd=3), 1),
 ])
 def test_sparse_fwd_varlen_rejects(kw, code):
     assert fwd_varlen(**kw) == code

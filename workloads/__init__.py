@@ -287,18 +287,30 @@ def make_varlen_workload_inputs(w: VarlenWorkload) -> dict:
 # elements stored as OCP float8_e4m3fn, no scale). Conversions use torch's CPU
 # float8_e4m3fn dtype: round to nearest even on the way in, exact on the way out.
 # ---------------------------------------------------------------------------
+_FP8_LUT = None
+
+
 def bf16_bits_to_fp8(x: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns -> fp8 e4m3fn bytes (uint8), round to nearest even."""
-    import torch
-    f = torch.from_numpy(bf16_to_f32(np.ascontiguousarray(x)))
-    return f.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    """bf16 bit patterns -> fp8 e4m3fn bytes (uint8), round to nearest even: a 65536-entry
+    table made once by torch's conversion of every bf16 pattern, then a gather."""
+    global _FP8_LUT
+    if _FP8_LUT is None:
+        import torch
+        allbits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+        f = allbits.view(torch.bfloat16).to(torch.float32)
+        lut = f.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        _FP8_LUT = np.empty(65536, dtype=np.uint8)
+        _FP8_LUT[allbits.numpy().view(np.uint16)] = lut
+    return _FP8_LUT[np.ascontiguousarray(x, dtype=np.uint16)]
 
 
 def fp8_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp8 e4m3fn bytes -> the bf16 bit patterns of the same values (exact)."""
+    """fp8 e4m3fn bytes -> the bf16 bit patterns of the same values (exact), through a
+    256-entry table made by torch's conversion."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).view(torch.float8_e4m3fn)
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    lut = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    lut = lut.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return lut[np.ascontiguousarray(x, dtype=np.uint8)]
 
 
 def with_fp8_kv(inp: dict) -> dict:
