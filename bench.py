@@ -270,15 +270,22 @@ class Case:
 
     def dominant_kernel(self, temp: bool = False, fp8: bool = False) -> str:
         """Name of the dominant kernel instance (template arguments as the profiler
-        prints them)."""
+        prints them; the q-centric kernel runs two waves per row when the rows are
+        fewer than 8 per compute unit)."""
+        import torch
         t, f = ("true" if temp else "false"), ("true" if fp8 else "false")
-        if self.w.paged:
-            return {"paged-qcentric": f"qcentric_kernel<true, {t}, {f}>",
-                    "paged-decode": f"paged_decode_kernel<{(self.w.Sq + 3) // 4}, {t}>"
-                    }[self.path_name]
-        return {"q-centric": f"qcentric_kernel<false, {t}, {f}>",
-                "kv-centric": f"kvcentric_kernel<{self.w.qpk}, {t}, {f}>",
-                "query-tile": f"tile_kernel<{self.w.qpk}, {t}>"}[self.path_name]
+        w = self.w
+        if self.path_name in ("paged-qcentric", "q-centric"):
+            rows = w.total_q if self.varlen else w.B * w.Sq
+            items = rows * w.Hkv * self.splits
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            waves = 2 if items < 8 * cus else 1
+            paged = "true" if w.paged else "false"
+            return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
+        if w.paged:
+            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}>"
+        return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
+                "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
 
 
 def measured_traffic(case: "Case"):

@@ -7,7 +7,11 @@
 // seqused_k (paged) and the bottom-right causal limit q + kvlen - Sq, with a
 // natural-log LSE and (O = 0, LSE = -inf) for an empty key set.
 //
-// Layout on gfx950: the qpk heads of one row are the N = 16 columns of
+// Layout on gfx950: a workgroup of one or two waves takes one index row (or one
+// split of it); with two, wave w streams slots w, w + 2, ... with its own online
+// softmax and LDS tiles, and the two states are merged by log-sum-exp at the end
+// (twice the waves in flight without a separate combine pass). Within a wave, the qpk
+// heads of the row are the N = 16 columns of
 // v_mfma_f32_16x16x32_bf16 (zero-padded when qpk < 16). Each selected block
 // is streamed as four 32-token sub-tiles: K and V are fetched with 16-byte
 // loads into registers one sub-tile ahead, stored to LDS (padded rows), and
@@ -42,12 +46,24 @@ namespace {
 
 constexpr int kSub = 32;  // tokens per sub-tile
 
-template <bool PAGED, bool TEMP, bool FP8>
-__global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[kSub * kKStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[kSub * kVStride];
+// Orders one wave's LDS accesses for the compiler (the hardware keeps a wave's LDS
+// operations in order); each wave stages and reads only its own tiles.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  const int lane = threadIdx.x;
+// kWaves waves per index row (or split), each taking every kWaves-th slot
+template <bool PAGED, bool TEMP, bool FP8, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks_all[kWaves][kSub * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vs_all[kWaves][kSub * kVStride];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* ks = ks_all[wave];
+  uint8_t* vs = vs_all[wave];
   const int n = lane & 15;  // head column
   const int g = lane >> 4;  // 16-lane group
 
@@ -119,7 +135,7 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
         }
         if (ok) return;
       }
-      ++t;
+      t += kWaves;
       u = 0;
     }
   };
@@ -241,21 +257,61 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
     }
   };
 
-  int t = t0, u = 0, s = 0, pg = 0;
+  int t = t0 + wave, u = 0, s = 0, pg = 0;  // this wave's slots: t0 + wave, + kWaves, ...
   seek(t, u, s, pg);
   if (t < t1) load(s, pg, u);
   while (t < t1) {
     int tn = t, un = u + 1, sn = s, pgn = pg;
     seek(tn, un, sn, pgn);
-    __syncthreads();
+    wave_lds_sync();
     store(s, u);
     if (tn < t1) load(sn, pgn, un);
-    __syncthreads();
+    wave_lds_sync();
     compute(s, u);
     t = tn;
     u = un;
     s = sn;
     pg = pgn;
+  }
+
+  // merge the waves' states into wave 0: wave w > 0 publishes (O, m, l[, lt]) in its V
+  // tile, lane-major so that both sides access consecutive words
+  if (kWaves > 1) {
+    constexpr int kPub = 35;  // 32 accumulator words + m, l, lt per lane
+    static_assert(kPub * 64 * 4 <= kSub * kVStride, "merge buffer exceeds the V tile");
+    float* pub = reinterpret_cast<float*>(vs);
+    wave_lds_sync();
+    if (wave > 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pub[(4 * dt + i) * 64 + lane] = oacc[dt][i];
+      pub[32 * 64 + lane] = m_run;
+      pub[33 * 64 + lane] = l_run;
+      pub[34 * 64 + lane] = lt_run;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float* other = reinterpret_cast<const float*>(vs_all[w]);
+      const float m1 = other[32 * 64 + lane], l1 = other[33 * 64 + lane];
+      const float mm = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+      l_run = l_run * a0 + l1 * a1;
+      if (TEMP) {
+        const float b0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - mm) * p.inv_temp);
+        const float b1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - mm) * p.inv_temp);
+        lt_run = lt_run * b0 + other[34 * 64 + lane] * b1;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[dt][i] = oacc[dt][i] * a0 + other[(4 * dt + i) * 64 + lane] * a1;
+      m_run = mm;
+    }
   }
 
   // epilogue: lane (n, g) holds dims 16*dt + 4*g + i of head n
@@ -290,6 +346,21 @@ __global__ __launch_bounds__(64) void qcentric_kernel(QcParams p) {
   }
 }
 
+template <int W>
+void qc_launch(int variant, const QcParams& p, dim3 grid, hipStream_t stream) {
+  const dim3 blk(64 * W);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((qcentric_kernel<false, false, false, W>), grid, blk, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((qcentric_kernel<false, false, true, W>), grid, blk, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((qcentric_kernel<false, true, false, W>), grid, blk, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((qcentric_kernel<false, true, true, W>), grid, blk, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((qcentric_kernel<true, false, false, W>), grid, blk, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((qcentric_kernel<true, false, true, W>), grid, blk, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((qcentric_kernel<true, true, false, W>), grid, blk, 0, stream, p); break;
+    default: hipLaunchKernelGGL((qcentric_kernel<true, true, true, W>), grid, blk, 0, stream, p); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
@@ -299,17 +370,15 @@ hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
+  // Two waves per row when the rows alone leave the compute units short of waves
+  // (decode: the 32 x 8-query paged workload has 1024 (row, KV head) items);
+  // otherwise one (large prefill, where the second wave only adds Q loads and a merge).
+  const bool two = items < 8LL * device_cu_count();
   const int variant = (paged ? 4 : 0) + (p.lse_t ? 2 : 0) + (p.kv_fp8 ? 1 : 0);
-  switch (variant) {
-    case 0: hipLaunchKernelGGL((qcentric_kernel<false, false, false>), grid, dim3(64), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((qcentric_kernel<false, false, true>), grid, dim3(64), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((qcentric_kernel<false, true, false>), grid, dim3(64), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((qcentric_kernel<false, true, true>), grid, dim3(64), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((qcentric_kernel<true, false, false>), grid, dim3(64), 0, stream, p); break;
-    case 5: hipLaunchKernelGGL((qcentric_kernel<true, false, true>), grid, dim3(64), 0, stream, p); break;
-    case 6: hipLaunchKernelGGL((qcentric_kernel<true, true, false>), grid, dim3(64), 0, stream, p); break;
-    default: hipLaunchKernelGGL((qcentric_kernel<true, true, true>), grid, dim3(64), 0, stream, p); break;
-  }
+  if (two)
+    qc_launch<2>(variant, p, grid, stream);
+  else
+    qc_launch<1>(variant, p, grid, stream);
   return hipGetLastError();
 }
 

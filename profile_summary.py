@@ -86,11 +86,12 @@ def main() -> int:
     w = (wl.VARLEN_WORKLOADS[args.workload] if args.workload in wl.VARLEN_WORKLOADS
          else wl.WORKLOADS[args.workload])
     f8 = "true" if args.kv_dtype == "fp8" else "false"
+    # q-centric names end with the wave count the launcher picked: matched as a prefix
     if w.paged:
-        dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8}>",
+        dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8},",
                "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false>"}[args.path]
     else:
-        dom = {"q-centric": f"qcentric_kernel<false, false, {f8}>",
+        dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",
                "kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}>",
                "query-tile": f"tile_kernel<{w.qpk}, false>"}[args.path]
     tag = "" if args.kv_dtype == "bf16" else "-fp8"
@@ -110,7 +111,12 @@ def main() -> int:
                      f"{max(v):.1f} | {sum(v) / 1e3:.3f} |")
     dom_durs = [x for n, v in durs.items() if dom in n for x in v]
     dom_avg = statistics.mean(dom_durs) if dom_durs else None
-    lines += ["", f"Dominant kernel: `{dom}`, average {dom_avg:.1f} us per launch." if dom_avg
+    full = [short(n) for n in durs if dom in n]
+    if full:  # the instance as the trace names it
+        dom_name = full[0]
+    else:
+        dom_name = dom
+    lines += ["", f"Dominant kernel: `{dom_name}`, average {dom_avg:.1f} us per launch." if dom_avg
               else f"Dominant kernel `{dom}` not found in the trace."]
 
     traffic = None
@@ -143,7 +149,7 @@ def main() -> int:
     if traffic is not None:
         js = os.path.join(args.out, f"traffic_{args.workload}_{args.path}{tag}.json")
         with open(js, "w") as fh:
-            json.dump({"workload": w.name, "path": args.path, "kernel": dom,
+            json.dump({"workload": w.name, "path": args.path, "kernel": dom_name,
                        "hbm_bytes_per_launch": traffic, "kernel_avg_us": dom_avg,
                        "source_digest": bench.source_digest(dom)}, fh, indent=1)
             fh.write("\n")
