@@ -16,7 +16,8 @@ from ._ffi import (MSA_DTYPE_BF16, MSA_DTYPE_FP8_E4M3, MSA_PATH_AUTO, MSA_PATH_D
                    msa_paged_sparse_fwd_workspace_size, msa_set_profiling_events, msa_sparse_fwd,
                    msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_sparse_fwd_varlen,
                    msa_sparse_fwd_varlen_path, msa_sparse_fwd_varlen_workspace_size,
-                   msa_build_k2q_csr_varlen, msa_build_k2q_csr_varlen_workspace_size, msa_version)
+                   msa_build_k2q_csr_varlen, msa_build_k2q_csr_varlen_workspace_size, msa_version,
+                   DecodePlan, MsaDecodePlan, msa_paged_decode_plan, msa_paged_decode_run)
 
 __all__ = [
     "MSA_PATH_AUTO", "MSA_PATH_QCENTRIC", "MSA_PATH_KVCENTRIC", "MSA_PATH_DECODE",
@@ -28,4 +29,5 @@ __all__ = [
     "msa_set_profiling_events", "msa_version", "msa_sparse_fwd_varlen",
     "msa_sparse_fwd_varlen_path", "msa_sparse_fwd_varlen_workspace_size",
     "msa_build_k2q_csr_varlen", "msa_build_k2q_csr_varlen_workspace_size",
+    "DecodePlan", "MsaDecodePlan", "msa_paged_decode_plan", "msa_paged_decode_run",
 ]

@@ -33,6 +33,18 @@ class MsaNotSupportedError(MsaError, NotImplementedError):
     """MSA_ERR_NOT_SUPPORTED: a shape or option outside the supported set."""
 
 
+class MsaDecodePlan(ctypes.Structure):
+    """msa_decode_plan of include/msa.h (host part of a dense-decode plan)."""
+    _fields_ = [("batch", ctypes.c_int), ("seqlen_q", ctypes.c_int),
+                ("num_qo_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
+                ("max_pages", ctypes.c_int), ("kv_chunk_size_pages", ctypes.c_int),
+                ("split_kv", ctypes.c_int), ("padded_work_count", ctypes.c_int),
+                ("partial_rows", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in ("kv_pages", "split_counts", "o_indptr", "merge_indptr",
+                                      "work_offsets", "work_items", "work_count", "o_partial",
+                                      "lse_partial", "lse_t_partial", "bytes")]
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -78,6 +90,13 @@ def load_library():
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
                                          I, P, P, F, P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
+    PL = ctypes.POINTER(MsaDecodePlan)
+    lib.msa_paged_decode_plan_init.argtypes = [I, I, I, I, I, I, I, I, I, I, PL]
+    lib.msa_paged_decode_plan_init.restype = I
+    lib.msa_paged_decode_plan.argtypes = [P, PL, P, S, P]
+    lib.msa_paged_decode_plan.restype = I
+    lib.msa_paged_decode_run.argtypes = [P, P, P, P, P, PL, P, S, I, I, F, P, P, F, P, P]
+    lib.msa_paged_decode_run.restype = I
     lib.msa_set_profiling_events.argtypes = [P, P]
     lib.msa_set_profiling_events.restype = I
     lib.msa_last_error.argtypes = []
@@ -386,6 +405,99 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
                                   num_pages, max_pages, int(bool(causal)), float(softmax_scale),
                                   int(num_splits), int(path), kv_dtype, _ptr(o), _ptr(lse), temp,
                                   _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
+    return o, lse
+
+
+class DecodePlan:
+    """A dense paged-decode plan: the host struct and the device plan buffer (schedule
+    arrays and partial workspace). The schedule arrays are exposed as int32 views."""
+
+    def __init__(self, info: MsaDecodePlan, buffer: torch.Tensor):
+        self.info = info
+        self.buffer = buffer
+
+    def _i32(self, off: int, n: int) -> torch.Tensor:
+        return self.buffer[off:off + 4 * n].view(torch.int32)
+
+    @property
+    def kv_pages(self):
+        return self._i32(self.info.kv_pages, self.info.batch)
+
+    @property
+    def split_counts(self):
+        return self._i32(self.info.split_counts, self.info.batch)
+
+    @property
+    def o_indptr(self):
+        return self._i32(self.info.o_indptr, self.info.batch + 1)
+
+    @property
+    def merge_indptr(self):
+        return self._i32(self.info.merge_indptr, self.info.batch * self.info.seqlen_q + 1)
+
+    @property
+    def work_count(self):
+        return self._i32(self.info.work_count, 1)
+
+    @property
+    def work_items(self):
+        n = self.info.padded_work_count
+        return self._i32(self.info.work_items, 4 * n).view(n, 4)
+
+
+def msa_paged_decode_plan(page_table, seqused_k, *, seqlen_q: int, max_seqlen_k: int,
+                          num_qo_heads: int, num_kv_heads: int, head_dim: int = 128,
+                          page_size: int = 128, max_grid_size: int = 0, fixed_split_size: int = 0,
+                          disable_split_kv: bool = False, stream=None) -> DecodePlan:
+    """Plan of the dense paged decode (q2k = None): sizes on the host, the split-KV
+    schedule built on the device from seqused_k."""
+    lib = load_library()
+    _dev(page_table, "page_table", torch.int32), _dev(seqused_k, "seqused_k", torch.int32)
+    B = page_table.shape[0]
+    info = MsaDecodePlan()
+    _check(lib.msa_paged_decode_plan_init(B, int(seqlen_q), int(num_qo_heads), int(num_kv_heads),
+                                          int(head_dim), int(page_size), int(max_seqlen_k),
+                                          int(max_grid_size), int(fixed_split_size),
+                                          int(bool(disable_split_kv)), ctypes.byref(info)))
+    if page_table.shape[1] != info.max_pages:
+        raise ValueError(f"page_table must have {info.max_pages} columns (ceil(max_seqlen_k / "
+                         f"{page_size}))")
+    buf = torch.empty(int(info.bytes), dtype=torch.uint8, device=page_table.device)
+    _check(lib.msa_paged_decode_plan(_ptr(seqused_k), ctypes.byref(info), _ptr(buf), buf.numel(),
+                                     _stream(stream)))
+    return DecodePlan(info, buf)
+
+
+def msa_paged_decode_run(plan: DecodePlan, q, k_pool, v_pool, page_table, seqused_k, *,
+                         causal: bool = True, softmax_scale: float = 0.0, o=None, lse=None,
+                         return_temperature_lse: bool = False,
+                         lse_temperature_scale: Optional[float] = None, lse_temperature=None,
+                         temperature_fast_path: bool = True, stream=None):
+    """Run the dense paged decode on a plan. Returns (O bf16 [B,Sq,Hq,D], LSE [B,Hq,Sq]),
+    plus the temperature-scaled LSE when asked."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16), _dev(page_table, "page_table", torch.int32)
+    _dev(seqused_k, "seqused_k", torch.int32)
+    info = plan.info
+    B, Sq, Hq, D = q.shape
+    if (B, Sq, Hq) != (info.batch, info.seqlen_q, info.num_qo_heads):
+        raise ValueError("q does not match the plan")
+    if o is None:
+        o = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
+    rc = lib.msa_paged_decode_run(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                  _ptr(seqused_k), ctypes.byref(info), _ptr(plan.buffer),
+                                  plan.buffer.numel(), k_pool.shape[0], int(bool(causal)),
+                                  float(softmax_scale), _ptr(o), _ptr(lse), temp, _ptr(lse_t),
+                                  _stream(stream))
     _check(rc)
     if return_temperature_lse:
         return o, lse, (lse if alias else lse_t)

@@ -595,6 +595,164 @@ int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
   return e == hipSuccess ? MSA_OK : hip_fail(e, "k2q CSR build (varlen)");
 }
 
+// ---------------------------------------------------------------------------
+// Dense paged decode: plan / run
+// ---------------------------------------------------------------------------
+int msa_paged_decode_plan_init(int B, int Sq, int Hq, int Hkv, int D, int page_size,
+                               int max_seqlen_k, int max_grid_size, int fixed_split_pages,
+                               int disable_split_kv, msa_decode_plan* plan) {
+  g_last_error.clear();
+  if (!plan) return fail(MSA_ERR_INVALID_VALUE, "null plan");
+  int rc = check_common(B, Sq, Hq, Hkv, D, 1, page_size);
+  if (rc) return rc;
+  if (Sq > 4 * kMaxQPerWave)
+    return fail(MSA_ERR_NOT_SUPPORTED, "dense decode needs Sq <= %d (got %d)", 4 * kMaxQPerWave, Sq);
+  if (max_seqlen_k <= 0) return fail(MSA_ERR_INVALID_VALUE, "max_seqlen_k must be positive");
+  if (max_grid_size < 0 || fixed_split_pages < 0)
+    return fail(MSA_ERR_INVALID_VALUE, "max_grid_size and fixed_split_pages must be >= 0");
+  const int max_pages = (max_seqlen_k + kBlk - 1) / kBlk;
+  int chunk;
+  if (fixed_split_pages > 0) {
+    if (fixed_split_pages > kDecMaxEntries)
+      return fail(MSA_ERR_NOT_SUPPORTED, "fixed_split_pages %d exceeds %d", fixed_split_pages,
+                  kDecMaxEntries);
+    chunk = fixed_split_pages;
+  } else if (disable_split_kv) {
+    if (max_pages > kDecMaxEntries)
+      return fail(MSA_ERR_NOT_SUPPORTED,
+                  "disable_split_kv needs max_seqlen_k <= %d tokens (one chunk per sequence)",
+                  kDecMaxEntries * kBlk);
+    chunk = max_pages;
+  } else {
+    // aim at max_grid (sequence, chunk, KV head) items: split only when the
+    // sequences alone leave the grid short
+    const long long target = max_grid_size > 0 ? max_grid_size : 2LL * device_cu_count();
+    const long long units = static_cast<long long>(B) * Hkv;
+    const long long want = units >= target ? 1 : (target + units - 1) / units;
+    chunk = static_cast<int>((max_pages + want - 1) / want);
+    chunk = std::max(1, std::min(chunk, kDecMaxEntries));
+  }
+  const int max_chunks = (max_pages + chunk - 1) / chunk;
+  msa_decode_plan P{};
+  P.batch = B; P.seqlen_q = Sq; P.num_qo_heads = Hq; P.num_kv_heads = Hkv; P.max_pages = max_pages;
+  P.kv_chunk_size_pages = chunk;
+  P.split_kv = max_chunks > 1 ? 1 : 0;
+  const long long padded = static_cast<long long>(B) * max_chunks;
+  if (padded * Hkv > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
+  P.padded_work_count = static_cast<int>(padded);
+  P.partial_rows = static_cast<int64_t>(padded) * Sq;
+  size_t off = 0;
+  P.kv_pages = off; off += align256(static_cast<size_t>(B) * 4);
+  P.split_counts = off; off += align256(static_cast<size_t>(B) * 4);
+  P.o_indptr = off; off += align256((static_cast<size_t>(B) + 1) * 4);
+  P.merge_indptr = off; off += align256((static_cast<size_t>(B) * Sq + 1) * 4);
+  P.work_offsets = off; off += align256(static_cast<size_t>(B) * 4);
+  P.work_items = off; off += align256(static_cast<size_t>(padded) * 16);
+  P.work_count = off; off += 256;
+  const size_t prow = P.split_kv ? static_cast<size_t>(P.partial_rows) * Hq : 0;
+  P.o_partial = off; off += align256(prow * kD * 4);
+  P.lse_partial = off; off += align256(prow * 4);
+  P.lse_t_partial = off; off += align256(prow * 4);
+  P.bytes = off;
+  *plan = P;
+  return MSA_OK;
+}
+
+static int check_plan_buffer(const msa_decode_plan* plan, const void* buffer, size_t bytes) {
+  if (!plan || !buffer) return fail(MSA_ERR_INVALID_VALUE, "null plan or plan buffer");
+  if (plan->batch <= 0 || plan->seqlen_q <= 0 || plan->kv_chunk_size_pages <= 0 ||
+      plan->kv_chunk_size_pages > kDecMaxEntries || plan->padded_work_count <= 0)
+    return fail(MSA_ERR_INVALID_VALUE, "plan not initialised by msa_paged_decode_plan_init");
+  if (bytes < plan->bytes)
+    return fail(MSA_ERR_INVALID_VALUE, "plan buffer too small: need %zu bytes", plan->bytes);
+  if (!aligned(buffer, 256)) return fail(MSA_ERR_INVALID_VALUE, "plan buffer must be 256-byte aligned");
+  return MSA_OK;
+}
+
+static DecodeSchedule schedule_at(const msa_decode_plan* plan, void* buffer) {
+  char* b = static_cast<char*>(buffer);
+  DecodeSchedule s;
+  s.kv_pages = reinterpret_cast<int32_t*>(b + plan->kv_pages);
+  s.counts = reinterpret_cast<int32_t*>(b + plan->split_counts);
+  s.o_indptr = reinterpret_cast<int32_t*>(b + plan->o_indptr);
+  s.merge_indptr = reinterpret_cast<int32_t*>(b + plan->merge_indptr);
+  s.work_off = reinterpret_cast<int32_t*>(b + plan->work_offsets);
+  s.items = reinterpret_cast<int4*>(b + plan->work_items);
+  s.work_count = reinterpret_cast<int32_t*>(b + plan->work_count);
+  return s;
+}
+
+int msa_paged_decode_plan(const int32_t* seqused_k, const msa_decode_plan* plan, void* buffer,
+                          size_t buffer_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_plan_buffer(plan, buffer, buffer_bytes);
+  if (rc) return rc;
+  if (!seqused_k || !aligned(seqused_k, 4)) return fail(MSA_ERR_INVALID_VALUE, "bad seqused_k pointer");
+  const hipError_t e =
+      launch_decode_schedule(seqused_k, plan->batch, plan->seqlen_q, plan->max_pages,
+                             plan->kv_chunk_size_pages, plan->split_kv != 0,
+                             schedule_at(plan, buffer), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "decode schedule");
+}
+
+int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seqused_k,
+                         const msa_decode_plan* plan, void* buffer, size_t buffer_bytes,
+                         int num_pages, int causal, float softmax_scale, void* o, float* lse,
+                         float lse_temperature_scale, float* lse_temperature, void* stream) {
+  g_last_error.clear();
+  int rc = check_plan_buffer(plan, buffer, buffer_bytes);
+  if (rc) return rc;
+  rc = check_temperature(lse_temperature_scale, lse_temperature);
+  if (rc) return rc;
+  if (num_pages <= 0) return fail(MSA_ERR_INVALID_VALUE, "num_pages must be positive");
+  if (!q || !k_pool || !v_pool || !page_table || !seqused_k || !o || !lse)
+    return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seqused_k, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
+  const msa_decode_plan& P = *plan;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(kD));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const DecodeSchedule S = schedule_at(plan, buffer);
+  char* b = static_cast<char*>(buffer);
+  QcParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = k_pool;
+  p.v = v_pool;
+  p.page_table = page_table;
+  p.seqused = seqused_k;
+  p.B = P.batch; p.Sq = P.seqlen_q; p.Hq = P.num_qo_heads; p.Hkv = P.num_kv_heads;
+  p.qpk = P.num_qo_heads / P.num_kv_heads;
+  p.max_pages = P.max_pages; p.num_pages = num_pages; p.nblk = P.max_pages;
+  p.Skv = P.max_pages * kBlk;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.splits = 1;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
+  p.lse_t = lse_temperature;
+  p.o_part = reinterpret_cast<float*>(b + P.o_partial);
+  p.lse_part = reinterpret_cast<float*>(b + P.lse_partial);
+  p.lse_t_part = lse_temperature ? reinterpret_cast<float*>(b + P.lse_t_partial) : nullptr;
+  p.dec_items = S.items;
+  p.dec_counts = S.counts;
+  p.dec_o_indptr = S.o_indptr;
+  p.dec_work_count = S.work_count;
+  prof_mark(g_prof_before, st);
+  hipError_t e = launch_dense_decode(p, P.padded_work_count, st);
+  prof_mark(g_prof_after, st);
+  if (e != hipSuccess) return hip_fail(e, "dense decode");
+  if (P.split_kv) {
+    e = launch_merge_decode(p.o_part, p.lse_part, p.lse_t_part, S.counts, S.o_indptr, P.batch,
+                            P.seqlen_q, P.num_qo_heads, static_cast<uint16_t*>(o), lse,
+                            lse_temperature, st);
+    if (e != hipSuccess) return hip_fail(e, "decode merge");
+  }
+  return MSA_OK;
+}
+
 int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path) {
   if (path != MSA_PATH_AUTO) return path;
   return paged_plan(B, Sq, Hkv, topk, 0, path).path;

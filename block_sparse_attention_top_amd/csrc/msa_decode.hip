@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       (__attribute__((address_space(3))) const void*)(p)));
 }
 
-template <int QPW, bool TEMP>
+template <int QPW, bool TEMP, bool DENSE>
 __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcParams p) {
   // ring of kStages sub-tile buffers; separate arrays keep the stage buffers
   // distinct objects for the compiler's tracking of the direct-to-LDS loads
@@ -73,13 +73,26 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   long long item = blockIdx.x;
-  const int sp = static_cast<int>(item % p.splits);
-  item /= p.splits;
-  const int hkv = static_cast<int>(item % p.Hkv);
-  const int b = static_cast<int>(item / p.Hkv);
-  const long long kvlen = p.seqused[b];
-  const int nent = p.Sq * p.topk;
-  const int32_t* sel = p.q2k + (static_cast<long long>(b) * p.Hkv + hkv) * p.Sq * p.topk;
+  int sp, hkv, b;
+  int4 work = {0, 0, 0, 0};  // DENSE: (b, chunk, first page, pages)
+  if (DENSE) {
+    hkv = static_cast<int>(item % p.Hkv);
+    const long long w = item / p.Hkv;
+    if (w >= *p.dec_work_count) return;  // padding past the schedule's items
+    work = p.dec_items[w];
+    b = work.x;
+    sp = work.y;
+  } else {
+    sp = static_cast<int>(item % p.splits);
+    item /= p.splits;
+    hkv = static_cast<int>(item % p.Hkv);
+    b = static_cast<int>(item / p.Hkv);
+  }
+  long long kvlen = p.seqused[b];
+  if (DENSE) kvlen = kvlen < 0 ? 0 : min(kvlen, static_cast<long long>(p.max_pages) * kBlk);
+  const int nent = DENSE ? 0 : p.Sq * p.topk;
+  const int32_t* sel =
+      DENSE ? nullptr : p.q2k + (static_cast<long long>(b) * p.Hkv + hkv) * p.Sq * p.topk;
 
   // visible key range [0, end_q) of query q
   auto end_of = [&](int q) -> long long {
@@ -121,6 +134,22 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     for (int dt = 0; dt < 8; ++dt) oacc[k][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  int U = 0;
+  if (DENSE) {
+    // the chunk's pages in order, selected by every query; a page id outside the
+    // pool is read as page 0 (in bounds) and selected by no query
+    U = work.w;
+    const unsigned all = p.Sq >= 32 ? 0xFFFFFFFFu : ((1u << p.Sq) - 1u);
+    for (int u = tid; u < U; u += 256) {
+      const int s = work.z + u;
+      const int pg = p.page_table[static_cast<long long>(b) * p.max_pages + s];
+      const bool ok = pg >= 0 && pg < p.num_pages;
+      ublk[u] = s;
+      upage[u] = ok ? pg : 0;
+      umask[u] = ok ? all : 0u;
+    }
+    __syncthreads();
+  } else {
   // 1. valid entries: id in range, page in range, block starts before the row's end
   for (int i = tid; i < nent; i += 256) {
     const int q = i / p.topk;
@@ -163,7 +192,6 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     if (lane == 0) fmask[ps * 4 + wave] = bal;
   }
   __syncthreads();
-  int U = 0;
 #pragma unroll
   for (int c = 0; c < 4 * kDecPasses; ++c) U += __popcll(fmask[c]);
 #pragma unroll
@@ -178,8 +206,9 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     umask[pos] = qmask[ps];
   }
   __syncthreads();
-  const int u0 = static_cast<int>(static_cast<long long>(U) * sp / p.splits);
-  const int u1 = static_cast<int>(static_cast<long long>(U) * (sp + 1) / p.splits);
+  }  // sparse union
+  const int u0 = DENSE ? 0 : static_cast<int>(static_cast<long long>(U) * sp / p.splits);
+  const int u1 = DENSE ? U : static_cast<int>(static_cast<long long>(U) * (sp + 1) / p.splits);
 
   // Sub-tile stream: (u, sub) for u in [u0, u1) and sub < 4 while some query
   // sees it. A stage past the end re-reads the last issued sub-tile (in bounds,
@@ -340,7 +369,8 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     const float lset_v =
         any ? (m_run[k] * p.inv_temp + fast_log2(lt_run[k])) * kLn2 : -INFINITY;
     const long long grow = static_cast<long long>(b) * p.Sq + q;
-    if (p.splits == 1) {
+    const int count = DENSE ? p.dec_counts[b] : p.splits;
+    if (count == 1) {
       uint16_t* orow = p.o + (grow * p.Hq + head) * kD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -356,7 +386,10 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     } else {
       // a split that saw no key of this query leaves its O partial unwritten:
       // the split combine reads O only where the partial LSE is finite
-      const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;
+      const long long prow =
+          DENSE ? (static_cast<long long>(p.dec_o_indptr[b]) + static_cast<long long>(q) * count + sp) *
+                          p.Hq + head
+                : (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;
       if (any) {
         float* orow = p.o_part + prow * kD + 4 * g;
 #pragma unroll
@@ -371,12 +404,24 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
   }
 }
 
-template <int QPW>
+template <int QPW, bool DENSE>
 void decode_launch(const QcParams& p, dim3 grid, hipStream_t stream) {
   if (p.lse_t)
-    hipLaunchKernelGGL((paged_decode_kernel<QPW, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, true, DENSE>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((paged_decode_kernel<QPW, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, false, DENSE>), grid, dim3(256), 0, stream, p);
+}
+
+template <bool DENSE>
+hipError_t decode_dispatch(const QcParams& p, dim3 grid, hipStream_t stream) {
+  switch ((p.Sq + 3) / 4) {
+    case 1: decode_launch<1, DENSE>(p, grid, stream); break;
+    case 2: decode_launch<2, DENSE>(p, grid, stream); break;
+    case 3: decode_launch<3, DENSE>(p, grid, stream); break;
+    case 4: decode_launch<4, DENSE>(p, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -389,16 +434,14 @@ hipError_t launch_paged_decode(const QcParams& p, hipStream_t stream) {
   const long long items = static_cast<long long>(p.B) * p.Hkv * p.splits;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL || !paged_decode_supported(p.Sq, p.topk)) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(items));
-  const int qpw = (p.Sq + 3) / 4;
-  switch (qpw) {
-    case 1: decode_launch<1>(p, grid, stream); break;
-    case 2: decode_launch<2>(p, grid, stream); break;
-    case 3: decode_launch<3>(p, grid, stream); break;
-    case 4: decode_launch<4>(p, grid, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return decode_dispatch<false>(p, dim3(static_cast<unsigned>(items)), stream);
+}
+
+hipError_t launch_dense_decode(const QcParams& p, int padded_work, hipStream_t stream) {
+  const long long items = static_cast<long long>(padded_work) * p.Hkv;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7FFFFFFFLL || p.Sq < 1 || p.Sq > 4 * kMaxQPerWave) return hipErrorInvalidValue;
+  return decode_dispatch<true>(p, dim3(static_cast<unsigned>(items)), stream);
 }
 
 }  // namespace msa

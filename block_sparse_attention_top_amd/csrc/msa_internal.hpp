@@ -188,12 +188,42 @@ struct QcParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   long long total_q, total_k;
+  // dense paged decode (every key of the sequence, split-KV by a device schedule):
+  // work item w = (b, chunk, first page, pages) for w < *dec_work_count; chunk c of
+  // sequence b (of dec_counts[b] chunks) writes partial rows o_indptr[b] + q * count + c
+  // when count > 1, else the final O / LSE
+  const int4* dec_items;
+  const int32_t* dec_counts;
+  const int32_t* dec_o_indptr;
+  const int32_t* dec_work_count;
 };
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream);
 // paged decode over the union of the blocks of each (b, hkv): splits partition that
 // union; needs Sq <= 4 * kMaxQPerWave and Sq * topk <= kDecMaxEntries
 bool paged_decode_supported(int Sq, int topk);
 hipError_t launch_paged_decode(const QcParams& p, hipStream_t stream);
+// dense decode over a schedule: grid = padded_work * Hkv (items past the count exit)
+hipError_t launch_dense_decode(const QcParams& p, int padded_work, hipStream_t stream);
+// the schedule: per sequence the pages ceil(seqused / 128) (clamped to max_pages), the
+// chunk count max(1, ceil(pages / chunk_pages)) (1 when !split), o_indptr (exclusive
+// prefix of count * Sq), merge_indptr[b * Sq + q] = o_indptr[b] + q * count, the work
+// items and their count
+struct DecodeSchedule {
+  int32_t* kv_pages;      // [B]
+  int32_t* counts;        // [B]
+  int32_t* o_indptr;      // [B+1]
+  int32_t* merge_indptr;  // [B*Sq+1]
+  int32_t* work_off;      // [B] first work item of each sequence
+  int4* items;            // [padded work]
+  int32_t* work_count;    // [1]
+};
+hipError_t launch_decode_schedule(const int32_t* seqused, int B, int Sq, int max_pages,
+                                  int chunk_pages, bool split, const DecodeSchedule& s,
+                                  hipStream_t stream);
+// merge of the dense decode's partial rows (sequences with more than one chunk)
+hipError_t launch_merge_decode(const float* o_part, const float* lse_part, const float* lse_t_part,
+                               const int32_t* counts, const int32_t* o_indptr, int B, int Sq,
+                               int Hq, uint16_t* o, float* lse, float* lse_t, hipStream_t stream);
 
 // query-tile kernel (contiguous K/V): a workgroup per 256 / qpk consecutive
 // queries of one (b, hkv), streaming the union of their selected blocks once

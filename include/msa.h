@@ -245,6 +245,59 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * Dense paged decode with a plan/run split-KV schedule: the q2k = None path of
+ * sparse_decode_atten_func and SparseDecodePagedAttentionWrapper.plan / .run on
+ * the page "MSA interface.py". Every query row attends to all keys of its
+ * sequence (j < seqused_k[b], causal limit q + seqused_k[b] - Sq): the definition
+ * at the top of this file with every block selected. Q bf16 [B, Sq, Hq, D]
+ * (Sq <= 16), K/V bf16 pools [num_pages, Hkv, 128, D], O [B, Sq, Hq, D],
+ * LSE [B, Hq, Sq]. A workgroup takes one (sequence, chunk of pages, KV head) and
+ * reads each page once for all Sq query rows; a sequence cut into several chunks
+ * gets fp32 partial rows, merged by log-sum-exp afterwards.
+ *
+ * msa_paged_decode_plan_init (host only) fixes the chunk size and the layout of a
+ * plan buffer (device memory the caller allocates, `bytes` long, 256-byte
+ * aligned): the schedule arrays and the partial-row workspace.
+ *   max_seqlen_k       upper bound of seqused_k (sizes the plan)
+ *   max_grid_size      0 = two workgroups per compute unit: the target number of
+ *                      (sequence, chunk, KV head) items when splitting
+ *   fixed_split_pages  0 = automatic; else the chunk size in pages (1..512)
+ *   disable_split_kv   one chunk per sequence (needs max_seqlen_k <= 512 pages)
+ * msa_paged_decode_plan builds the schedule on the device from seqused_k on
+ * `stream`, into the plan buffer; it stays valid while seqused_k does not change,
+ * and any number of runs may use it. msa_paged_decode_run runs the decode.
+ * The schedule arrays (int32, at the byte offsets in the plan): kv_pages[B]
+ * (ceil(seqused / 128)), split_counts[B] (chunks of each sequence), o_indptr[B+1]
+ * (first partial row of each sequence; it advances by Sq * chunks),
+ * merge_indptr[B*Sq+1] (the partial rows of query row (b, q) are
+ * merge_indptr[b*Sq+q] + 0 .. split_counts[b]-1), work_items (int4: sequence,
+ * chunk, first page, pages) and work_count[1].
+ */
+typedef struct msa_decode_plan {
+  int batch, seqlen_q, num_qo_heads, num_kv_heads, max_pages;
+  int kv_chunk_size_pages; /* pages per chunk */
+  int split_kv;            /* 0: every sequence in one chunk */
+  int padded_work_count;   /* batch * ceil(max_pages / chunk): bound on the work items */
+  int64_t partial_rows;    /* capacity of the partial rows: batch * Sq * max chunks */
+  size_t kv_pages, split_counts, o_indptr, merge_indptr, work_offsets, work_items,
+      work_count, o_partial, lse_partial, lse_t_partial; /* byte offsets in the buffer */
+  size_t bytes;            /* plan buffer size */
+} msa_decode_plan;
+
+int msa_paged_decode_plan_init(int B, int Sq, int Hq, int Hkv, int D, int page_size,
+                               int max_seqlen_k, int max_grid_size, int fixed_split_pages,
+                               int disable_split_kv, msa_decode_plan* plan);
+int msa_paged_decode_plan(const int32_t* seqused_k, const msa_decode_plan* plan, void* buffer,
+                          size_t buffer_bytes, void* stream);
+/* num_pages: pool size (page ids outside [0, num_pages) read as unused blocks);
+ * the page table is [B, plan->max_pages]. Other arguments as msa_paged_sparse_fwd. */
+int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seqused_k,
+                         const msa_decode_plan* plan, void* buffer, size_t buffer_bytes,
+                         int num_pages, int causal, float softmax_scale, void* o, float* lse,
+                         float lse_temperature_scale, float* lse_temperature, void* stream);
+
+/*
  * Profiling hook (for benchmarks): when both are non-NULL, every later
  * forward call on this thread records `before` and `after` (hipEvent_t handles
  * created by the caller) on its stream immediately around the launch of its

@@ -215,3 +215,57 @@ def test_csr_varlen_rejects():
     assert lib.msa_build_k2q_csr_varlen(*a) == 1
     a = list(base); a[12] = None; a[13] = 0
     assert lib.msa_build_k2q_csr_varlen(*a) == 1
+
+
+def test_decode_plan_init():
+    import ctypes
+    lib = msa.load_library()
+    P = msa.MsaDecodePlan()
+    # 32 sequences x 4 KV heads of 64K tokens: split so that ~2 items per compute unit
+    assert lib.msa_paged_decode_plan_init(32, 8, 64, 4, 128, 128, 65536, 512, 0, 0,
+                                          ctypes.byref(P)) == 0
+    assert P.max_pages == 512 and P.kv_chunk_size_pages == 128 and P.split_kv == 1
+    assert P.padded_work_count == 32 * 4 and P.partial_rows == 32 * 4 * 8
+    assert P.bytes >= P.partial_rows * 64 * 128 * 4
+    # enough sequences: no split; forced single-page chunks; chunks capped at 512 pages
+    assert lib.msa_paged_decode_plan_init(512, 8, 64, 4, 128, 128, 4096, 512, 0, 0,
+                                          ctypes.byref(P)) == 0
+    assert P.split_kv == 0 and P.kv_chunk_size_pages == 32 and P.partial_rows == 512 * 8
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 384, 0, 1, 0,
+                                          ctypes.byref(P)) == 0
+    assert P.kv_chunk_size_pages == 1 and P.padded_work_count == 12
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 1 << 20, 16, 0, 0,
+                                          ctypes.byref(P)) == 0
+    assert P.kv_chunk_size_pages == 512
+    # rejected: Sq > 16, chunk > 512 pages, one chunk for a 1M-token sequence, bad sizes
+    assert lib.msa_paged_decode_plan_init(4, 17, 64, 4, 128, 128, 4096, 0, 0, 0,
+                                          ctypes.byref(P)) == 2
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 4096, 0, 513, 0,
+                                          ctypes.byref(P)) == 2
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 1 << 20, 0, 0, 1,
+                                          ctypes.byref(P)) == 2
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 0, 0, 0, 0,
+                                          ctypes.byref(P)) == 1
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 64, 128, 4096, 0, 0, 0,
+                                          ctypes.byref(P)) == 2
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 4096, 0, 0, 0, None) == 1
+
+
+def test_decode_plan_and_run_reject_bad_buffers():
+    import ctypes
+    lib = msa.load_library()
+    P = msa.MsaDecodePlan()
+    assert lib.msa_paged_decode_plan_init(4, 8, 64, 4, 128, 128, 4096, 0, 0, 0,
+                                          ctypes.byref(P)) == 0
+    assert lib.msa_paged_decode_plan(FAKE, ctypes.byref(P), FAKE, P.bytes - 1, None) == 1
+    assert lib.msa_paged_decode_plan(FAKE, ctypes.byref(P), FAKE + 16, P.bytes, None) == 1
+    assert lib.msa_paged_decode_plan(None, ctypes.byref(P), FAKE, P.bytes, None) == 1
+    Z = msa.MsaDecodePlan()  # never initialised
+    assert lib.msa_paged_decode_plan(FAKE, ctypes.byref(Z), FAKE, 1 << 30, None) == 1
+    run = [FAKE] * 5 + [ctypes.byref(P), FAKE, P.bytes, 16, 1, 0.0, FAKE, FAKE, 1.0, None, None]
+    a = list(run); a[8] = 0  # num_pages
+    assert lib.msa_paged_decode_run(*a) == 1
+    a = list(run); a[0] = None
+    assert lib.msa_paged_decode_run(*a) == 1
+    a = list(run); a[13] = 0.0; a[14] = FAKE  # temperature buffer with T = 0
+    assert lib.msa_paged_decode_run(*a) == 1
