@@ -95,6 +95,16 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def dense_decode_algorithmic_bytes(w, inp) -> int:
+    """Every page of each sequence's keys (ceil(seqused / 128)) x KV heads x 128 tokens x D x
+    element size x 2 (K and V), plus Q, O, LSE, page table and seqused."""
+    pages = int(((inp["seqused_k"].astype(np.int64) + 127) // 128).sum())
+    kv = pages * w.Hkv * 128 * w.D * inp["k_pool"].itemsize * 2
+    q = w.B * w.Sq * w.Hq * w.D * 2
+    return int(kv + 2 * q + w.B * w.Sq * w.Hq * 4 + inp["page_table"].nbytes +
+               inp["seqused_k"].nbytes)
+
+
 def decode_algorithmic_bytes(w, inp) -> int:
     """Distinct valid selected blocks per (b, hkv) x 128 tokens x D x element size x 2
     (K and V; 2 B for bf16, 1 B for the fp8 cache), plus Q, O, LSE, q2k, page table and
@@ -159,7 +169,19 @@ class Case:
             return
         self.o = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
-        if w.paged:
+        if w.paged and w.dense:
+            # plan once (schedule on the device), then each step is one run
+            plan = msa.msa_paged_decode_plan(t["page_table"], t["seqused_k"], seqlen_q=w.Sq,
+                                             max_seqlen_k=w.Skv, num_qo_heads=w.Hq,
+                                             num_kv_heads=w.Hkv)
+            self.plan = plan
+            self.path_name = "paged-dense-decode"
+            self.splits = plan.info.kv_chunk_size_pages  # pages per chunk
+            self.step = lambda: msa.msa_paged_decode_run(
+                plan, t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"],
+                causal=w.causal, o=self.o, lse=self.lse, **tk)
+            self.bytes = dense_decode_algorithmic_bytes(w, self.inp)
+        elif w.paged:
             p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, PATHS[path])
             if p not in (1, 3):
                 raise SystemExit(f"path {path} does not apply to the paged workload {key}")
@@ -282,8 +304,10 @@ class Case:
             waves = 2 if items < 8 * cus else 1
             paged = "true" if w.paged else "false"
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
+        if w.paged and w.dense:
+            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}, true>"
         if w.paged:
-            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}>"
+            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}, false>"
         return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
                 "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
 
@@ -331,6 +355,12 @@ def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
             oracle.sparse_attention_varlen(inp["q"], inp["k"], inp["v"], inp["q2k"],
                                            inp["cu_seqlens_q"], inp["cu_seqlens_k"],
                                            causal=w.causal, rows=rows, nthreads=threads)
+        elif w.paged and w.dense:  # every block selected
+            full = np.ascontiguousarray(np.broadcast_to(
+                np.arange(w.max_pages, dtype=np.int32), (w.B, w.Hkv, w.Sq, w.max_pages)))
+            oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                          inp["page_table"], inp["seqused_k"], full,
+                                          causal=w.causal, rows=rows, nthreads=threads)
         elif w.paged:
             oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
                                           inp["page_table"], inp["seqused_k"], inp["q2k"],
@@ -396,7 +426,8 @@ def main() -> int:
     w = case.w
     traffic = measured_traffic(case) if args.lse_temperature is None else None
     if w.paged:
-        value, unit, metric = m["GB_per_s"], "GB/s", "paged sparse decode GB/s"
+        value, unit = m["GB_per_s"], "GB/s"
+        metric = "paged dense decode GB/s" if w.dense else "paged sparse decode GB/s"
         ach = m["kernel_GB_per_s"]
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "traffic": traffic}

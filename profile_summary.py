@@ -89,7 +89,9 @@ def main() -> int:
     # q-centric names end with the wave count the launcher picked: matched as a prefix
     if w.paged:
         dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8},",
-               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false>"}[args.path]
+               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false, false>",
+               "paged-dense-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false, true>",
+               }[args.path]
     else:
         dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",
                "kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}>",

@@ -112,6 +112,7 @@ class Workload:
     paged: bool = False
     seqused_trim: int = 0          # paged: seqused_k = Skv - trim
     shuffle_pages: bool = True
+    dense: bool = False            # paged: every key of the sequence (no index table)
     seed: int = DEFAULT_SEED
     note: str = ""
 
@@ -153,6 +154,10 @@ WORKLOADS = {
     "c5": Workload("c5_paged_decode_b32_sq8_hq64_hkv4_kv64k_top16", B=32, Sq=8, Skv=65536,
                    Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL, paged=True,
                    seqused_trim=17),
+    # the same decode batch attending to every key (the dense decode path)
+    "c5d": Workload("c5d_paged_dense_decode_b32_sq8_hq64_hkv4_kv64k", B=32, Sq=8, Skv=65536,
+                    Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL, paged=True,
+                    seqused_trim=17, dense=True),
 }
 
 
