@@ -304,12 +304,19 @@ class Case:
             waves = 2 if items < 8 * cus else 1
             paged = "true" if w.paged else "false"
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
-        if w.paged and w.dense:
-            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}, true>"
         if w.paged:
-            return f"paged_decode_kernel<{(w.Sq + 3) // 4}, {t}, false>"
+            return f"paged_decode_kernel<{decode_instance(w)}>".replace("TEMP", t)
         return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
                 "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
+
+
+def decode_instance(w) -> str:
+    """Template arguments of the paged decode kernel the launcher picks: the dense
+    decode with at most 128 (query, head) columns per KV head runs the 32x32 core
+    with one column group per wave; otherwise queries are grouped four to a wave."""
+    if w.dense and w.Sq * w.qpk <= 128:
+        return "1, TEMP, true, true"
+    return f"{(w.Sq + 3) // 4}, TEMP, {'true' if w.dense else 'false'}, false"
 
 
 def measured_traffic(case: "Case"):

@@ -89,8 +89,10 @@ def main() -> int:
     # q-centric names end with the wave count the launcher picked: matched as a prefix
     if w.paged:
         dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8},",
-               "paged-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false, false>",
-               "paged-dense-decode": f"paged_decode_kernel<{(w.Sq + 3) // 4}, false, true>",
+               "paged-decode": "paged_decode_kernel<"
+                               + bench.decode_instance(w).replace("TEMP", "false") + ">",
+               "paged-dense-decode": "paged_decode_kernel<"
+                                     + bench.decode_instance(w).replace("TEMP", "false") + ">",
                }[args.path]
     else:
         dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",
