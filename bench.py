@@ -36,12 +36,13 @@ HBM_PEAK_GBS = 8000.0
 PATHS = {"auto": 0, "q": 1, "kv": 2, "decode": 3, "tile": 4}
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc")
-# the source file of each dominant kernel (with the shared header)
+# the source files of each dominant kernel (besides the shared header)
 KERNEL_SOURCES = {
-    "qcentric_kernel": "msa_qcentric.hip",
-    "kvcentric_kernel": "msa_kvcentric.hip",
-    "paged_decode_kernel": "msa_decode.hip",
-    "tile_kernel": "msa_tile.hip",
+    "qcentric_kernel": ("msa_qcentric.hip",),
+    "kvcentric_kernel": ("msa_kvcentric.hip",),
+    "paged_decode_kernel": ("msa_decode.hip", "msa_lds.hpp"),
+    "dense_decode_kernel": ("msa_decode_dense.hip", "msa_lds.hpp"),
+    "tile_kernel": ("msa_tile.hip", "msa_lds.hpp"),
 }
 
 
@@ -49,9 +50,9 @@ def source_digest(kernel: str) -> str:
     """Hash of a kernel's source and the shared header: a counter summary is reused
     only while the kernel it measured is unchanged."""
     import hashlib
-    src = next(f for k, f in KERNEL_SOURCES.items() if kernel.startswith(k))
+    srcs = next(f for k, f in KERNEL_SOURCES.items() if kernel.startswith(k))
     h = hashlib.sha256()
-    for f in (src, "msa_internal.hpp"):
+    for f in srcs + ("msa_internal.hpp",):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -305,18 +306,20 @@ class Case:
             paged = "true" if w.paged else "false"
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
         if w.paged:
-            return f"paged_decode_kernel<{decode_instance(w)}>".replace("TEMP", t)
+            return decode_instance(w).replace("TEMP", t)
         return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
                 "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
 
 
 def decode_instance(w) -> str:
-    """Template arguments of the paged decode kernel the launcher picks: the dense
-    decode with at most 128 (query, head) columns per KV head runs the 32x32 core
-    with one column group per wave; otherwise queries are grouped four to a wave."""
+    """The paged decode kernel instance the launcher picks (TEMP stands for the
+    temperature template argument): the dense decode with at most 128 (query, head)
+    columns per KV head runs the 32-column kernel; otherwise the union kernel groups
+    queries four to a wave."""
     if w.dense and w.Sq * w.qpk <= 128:
-        return "1, TEMP, true, true"
-    return f"{(w.Sq + 3) // 4}, TEMP, {'true' if w.dense else 'false'}, false"
+        return "dense_decode_kernel<TEMP>"
+    return (f"paged_decode_kernel<{(w.Sq + 3) // 4}, TEMP, "
+            f"{'true' if w.dense else 'false'}>")
 
 
 def measured_traffic(case: "Case"):

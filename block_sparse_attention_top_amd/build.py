@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["msa_api.hip", "msa_qcentric.hip", "msa_kvcentric.hip", "msa_combine.hip",
-           "msa_csr.hip", "msa_decode.hip",
+           "msa_csr.hip", "msa_decode.hip", "msa_decode_dense.hip",
            "msa_tile.hip", "msa_varlen.hip", "msa_decode_plan.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms are kept out of the generated code on purpose

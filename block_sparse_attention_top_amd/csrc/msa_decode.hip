@@ -23,6 +23,7 @@
 // heads) with an online softmax per lane column (and, when a temperature-scaled
 // LSE is requested, a second running sum of 2^((x - m) / T) beside it).
 #include "msa_internal.hpp"
+#include "msa_lds.hpp"
 
 #include <math.h>
 
@@ -39,33 +40,8 @@ constexpr int kRow = 256;  // bytes per K/V row in the decode tiles (no padding)
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 // V: transposed reads take 8 rows x one 32-byte chunk pair per half wave.
 __device__ __forceinline__ int swz_v(int r) { return 2 * (r & 7); }
-// Dense 32x32x16 core (K and V tiles alike): 4(r & 3) ^ ((r >> 2) & 3) keeps both the
-// 32-row K fragment reads and the transposed V reads of 32 columns free of bank
-// conflicts (checked with an LDS bank model that reproduces the conflict cycles
-// measured for padded strides).
-__device__ __forceinline__ int swz_d(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
 
-// s_waitcnt immediates (gfx9 encoding): vmcnt <= n (n < 16) with lgkmcnt(0)
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4); }
-
-// One 16-byte direct global->LDS load per lane: lane l's 16 bytes from `src` land
-// at LDS byte lds_base + 16 * l (lds_base wave-uniform, in M0). Written as inline
-// assembly so that the compiler does not track it: its waits for these loads
-// would otherwise cover every stage of the ring before any LDS read. Completion
-// is tracked by hand with vmcnt (loads retire in issue order), and the asm
-// clobbers memory so no LDS access moves across it.
-__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)(p)));
-}
-
-// M32 (dense only, Sq * qpk <= 128): every wave owns 32 (query, head) columns and runs
-// S^T = K Q^T and O^T += V^T P^T as v_mfma_f32_32x32x16_bf16 over them, reading each
-// K/V fragment once for two queries' heads instead of once per query
-template <int QPW, bool TEMP, bool DENSE, bool M32>
+template <int QPW, bool TEMP, bool DENSE>
 __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcParams p) {
   // ring of kStages sub-tile buffers; separate arrays keep the stage buffers
   // distinct objects for the compiler's tracking of the direct-to-LDS loads
@@ -124,7 +100,6 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
   long long qend[QPW];
 #pragma unroll
   for (int k = 0; k < QPW; ++k) {
-    if (M32) break;
     const int q = wave + 4 * k;
     const int qq = q < p.Sq ? q : 0;
     qend[k] = q < p.Sq ? end_of(q) : 0;
@@ -141,30 +116,6 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     lt_run[k] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[k][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // M32 column state: lane (n32, h32) = column n32 (row 32 * wave + n32 of the Sq x qpk
-  // query-major rows), k-half h32
-  const int n32 = lane & 31, h32 = lane >> 5;
-  const int r32 = 32 * wave + n32;
-  const int q32 = r32 / p.qpk;
-  const bool col_ok = M32 && q32 < p.Sq;
-  const int head32 = hkv * p.qpk + r32 % p.qpk;
-  const long long qend32 = col_ok ? end_of(q32) : 0;
-  bf16x8 qm[M32 ? 8 : 1];
-  f32x16 om[M32 ? 4 : 1];
-  float mm_run = -INFINITY, lm_run = 0.f, ltm_run = 0.f;  // per lane: half a column's sums
-  if (M32) {
-    const uint16_t* qrow =
-        p.q + ((static_cast<long long>(b) * p.Sq + (col_ok ? q32 : 0)) * p.Hq + head32) * kD + 8 * h32;
-#pragma unroll
-    for (int kq = 0; kq < 8; ++kq) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * kq);
-      if (!col_ok) v = u32x4{0, 0, 0, 0};
-      qm[kq] = as_bf16x8(v);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) om[dt] = f32x16{};
   }
 
   int U = 0;
@@ -271,80 +222,15 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     for (int j = 0; j < 2; ++j) {
       const int r = 4 * (2 * wave + j) + lrow;
       const long long rs = r < last ? r : last;
-      const int sk = M32 ? swz_d(r) : swz_k(r), sv = M32 ? swz_d(r) : swz_v(r);
-      const uint16_t* ksrc = static_cast<const uint16_t*>(p.k) + (base + rs) * kD + 8 * (lpos ^ sk);
-      const uint16_t* vsrc = static_cast<const uint16_t*>(p.v) + (base + rs) * kD + 8 * (lpos ^ sv);
+      const uint16_t* ksrc = static_cast<const uint16_t*>(p.k) + (base + rs) * kD + 8 * (lpos ^ swz_k(r));
+      const uint16_t* vsrc = static_cast<const uint16_t*>(p.v) + (base + rs) * kD + 8 * (lpos ^ swz_v(r));
       lds_load16(ksrc, lds_addr(kd) + 4 * (2 * wave_u + j) * kRow);
       lds_load16(vsrc, lds_addr(vd) + 4 * (2 * wave_u + j) * kRow);
     }
   };
 
   const int rr = (lane & 15) >> 2, cq = lane & 3;
-  // M32 lane offsets (bytes) in the swizzled tiles: K fragment = row n32, logical chunk
-  // 2 kq + h32, i.e. physical chunk 2 kq ^ (h32 ^ swz(n32)); transposed V reads of rows
-  // 16 kk + 4 h32 + rr (+ 8), logical byte 64 dt + 32 (j16 & 1) + 8 cq, whose chunk's
-  // low two bits XOR with (h32 [+ 2]) and high two bits with rr
-  const int j16 = lane >> 4;
-  const int k32 = n32 * kRow + 16 * (h32 ^ swz_d(n32));
-  const int vlo32 = (4 * h32 + rr) * kRow + 16 * ((2 * (j16 & 1) + (cq >> 1)) ^ h32) + 8 * (cq & 1);
-  const int vhi32 = (4 * h32 + rr + 8) * kRow + 16 * ((2 * (j16 & 1) + (cq >> 1)) ^ (h32 + 2)) + 8 * (cq & 1);
-  auto compute32 = [&](int u, int sub, const uint8_t* ks, const uint8_t* vs) {
-    const unsigned msk = umask[u];
-    const long long jb = static_cast<long long>(ublk[u]) * kBlk + kSub * sub;
-    const bool sees = col_ok && ((msk >> q32) & 1u);
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kq = 0; kq < 8; ++kq) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (k32 ^ (32 * kq))));
-      sacc = mfma32(a, qm[kq], sacc);
-    }
-    // lane (n32, h32) holds tokens 8 (i / 4) + 4 h32 + i % 4 of column n32
-    float x[16];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const long long j = jb + 8 * (i >> 2) + 4 * h32 + (i & 3);
-      x[i] = (sees && j < qend32) ? sacc[i] * p.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(mm_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key yet: every term 0
-    const float alpha = fast_exp2(mm_run - m_use);
-    float ps = 0.f, pst = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (TEMP)
-        pst += fast_exp2((x[2 * i] - m_use) * p.inv_temp) +
-               fast_exp2((x[2 * i + 1] - m_use) * p.inv_temp);
-      const float p0 = fast_exp2(x[2 * i] - m_use), p1 = fast_exp2(x[2 * i + 1] - m_use);
-      pk[i] = pack_bf16x2(p0, p1);
-      ps += p0 + p1;
-    }
-    lm_run = lm_run * alpha + ps;
-    if (TEMP) ltm_run = ltm_run * fast_exp2((mm_run - m_use) * p.inv_temp) + pst;
-    mm_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) om[dt] *= alpha;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 pw = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
-      const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dx = 64 * (dt ^ rr);
-        const i16x4 lo4 = lds_read_tr16(vs + 16 * kk * kRow + vlo32 + dx);
-        const i16x4 hi4 = lds_read_tr16(vs + 16 * kk * kRow + vhi32 + dx);
-        om[dt] = mfma32(cat_tr(lo4, hi4), pb, om[dt]);
-      }
-    }
-  };
   auto compute = [&](int u, int sub, const uint8_t* ks, const uint8_t* vs) {
-    if (M32) {
-      compute32(u, sub, ks, vs);
-      return;
-    }
     const unsigned msk = umask[u];
     const long long jb = static_cast<long long>(ublk[u]) * kBlk + kSub * sub;
 #pragma unroll
@@ -455,56 +341,7 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
   }
 
-  // 4. epilogue
-  if (M32) {
-    // lane (n32, h32) holds dims 32 dt + 8 (i / 4) + 4 h32 + i % 4 of column n32
-    const float ps = lm_run + __shfl_xor(lm_run, 32);
-    const float pst = ltm_run + __shfl_xor(ltm_run, 32);
-    if (!col_ok) return;
-    const bool any = ps > 0.f;
-    const float inv = any ? 1.f / ps : 0.f;
-    const float lse_v = any ? (mm_run + fast_log2(ps)) * kLn2 : -INFINITY;
-    const float lset_v = any ? (mm_run * p.inv_temp + fast_log2(pst)) * kLn2 : -INFINITY;
-    const int count = p.dec_counts[b];
-    const long long grow = static_cast<long long>(b) * p.Sq + q32;
-    if (count == 1) {
-      uint16_t* orow = p.o + (grow * p.Hq + head32) * kD + 4 * h32;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2 w = {pack_bf16x2(om[dt][4 * j] * inv, om[dt][4 * j + 1] * inv),
-                           pack_bf16x2(om[dt][4 * j + 2] * inv, om[dt][4 * j + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * j) = w;
-        }
-      if (h32 == 0) {
-        const long long li = (static_cast<long long>(b) * p.Hq + head32) * p.Sq + q32;
-        p.lse[li] = lse_v;
-        if (TEMP) p.lse_t[li] = lset_v;
-      }
-    } else {
-      const long long prow =
-          (static_cast<long long>(p.dec_o_indptr[b]) + static_cast<long long>(q32) * count + sp) *
-              p.Hq + head32;
-      if (any) {
-        float* orow = p.o_part + prow * kD + 4 * h32;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 v = {om[dt][4 * j] * inv, om[dt][4 * j + 1] * inv,
-                             om[dt][4 * j + 2] * inv, om[dt][4 * j + 3] * inv};
-            *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * j) = v;
-          }
-      }
-      if (h32 == 0) {
-        p.lse_part[prow] = lse_v;
-        if (TEMP) p.lse_t_part[prow] = lset_v;
-      }
-    }
-    return;
-  }
-  // lane (n, g) holds dims 16*dt + 4*g + i of head n
+  // 4. epilogue: lane (n, g) holds dims 16*dt + 4*g + i of head n
   if (!head_ok) return;
 #pragma unroll
   for (int k = 0; k < QPW; ++k) {
@@ -551,20 +388,16 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
   }
 }
 
-template <int QPW, bool DENSE, bool M32 = false>
+template <int QPW, bool DENSE>
 void decode_launch(const QcParams& p, dim3 grid, hipStream_t stream) {
   if (p.lse_t)
-    hipLaunchKernelGGL((paged_decode_kernel<QPW, true, DENSE, M32>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, true, DENSE>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((paged_decode_kernel<QPW, false, DENSE, M32>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_kernel<QPW, false, DENSE>), grid, dim3(256), 0, stream, p);
 }
 
 template <bool DENSE>
 hipError_t decode_dispatch(const QcParams& p, dim3 grid, hipStream_t stream) {
-  if (DENSE && p.Sq * p.qpk <= 128) {  // 32x32x16 core over 32 (query, head) columns per wave
-    decode_launch<1, true, true>(p, grid, stream);
-    return hipGetLastError();
-  }
   switch ((p.Sq + 3) / 4) {
     case 1: decode_launch<1, DENSE>(p, grid, stream); break;
     case 2: decode_launch<2, DENSE>(p, grid, stream); break;
@@ -588,7 +421,7 @@ hipError_t launch_paged_decode(const QcParams& p, hipStream_t stream) {
   return decode_dispatch<false>(p, dim3(static_cast<unsigned>(items)), stream);
 }
 
-hipError_t launch_dense_decode(const QcParams& p, int padded_work, hipStream_t stream) {
+hipError_t launch_dense_decode_grouped(const QcParams& p, int padded_work, hipStream_t stream) {
   const long long items = static_cast<long long>(padded_work) * p.Hkv;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL || p.Sq < 1 || p.Sq > 4 * kMaxQPerWave) return hipErrorInvalidValue;

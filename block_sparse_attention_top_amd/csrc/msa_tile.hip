@@ -24,6 +24,7 @@
 // written. Tiles are placed so that the XCDs serving one KV head share its K/V
 // in their L2, largest (latest causal) tiles first.
 #include "msa_internal.hpp"
+#include "msa_lds.hpp"
 
 #include <math.h>
 
@@ -49,17 +50,6 @@ constexpr int kVLoads = kVTileB / 1024;           // 40
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) lgkmcnt(0)
 constexpr int kWaitAll = 0 | (7 << 4);
 
-// One 16-byte direct global->LDS load per lane (lane l lands at lds_base + 16 l;
-// lds_base wave-uniform, in M0). Inline assembly keeps the compiler from tracking
-// it (its own waits would cover both buffers before every LDS read); completion is
-// waited for by hand, and the memory clobber keeps LDS accesses from moving across.
-__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)(p)));
-}
 
 template <int QPK, bool TEMP>
 __global__ __launch_bounds__(512, 1) void tile_kernel(TileParams p) {

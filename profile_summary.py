@@ -89,10 +89,8 @@ def main() -> int:
     # q-centric names end with the wave count the launcher picked: matched as a prefix
     if w.paged:
         dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8},",
-               "paged-decode": "paged_decode_kernel<"
-                               + bench.decode_instance(w).replace("TEMP", "false") + ">",
-               "paged-dense-decode": "paged_decode_kernel<"
-                                     + bench.decode_instance(w).replace("TEMP", "false") + ">",
+               "paged-decode": bench.decode_instance(w).replace("TEMP", "false"),
+               "paged-dense-decode": bench.decode_instance(w).replace("TEMP", "false"),
                }[args.path]
     else:
         dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",
