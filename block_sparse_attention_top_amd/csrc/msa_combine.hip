@@ -107,11 +107,14 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
   const int hkv = head / qpk, head_i = head % qpk;
   const uint16_t* base = o_part + (dc * qpk + head_i) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t0 = 0; t0 < topk; t0 += 16) {
-    u32x4 raw[16];
-    float wgt[16];
+  // eight slots' loads in flight per thread keeps the kernel at ~64 VGPRs, so more
+  // blocks per CU overlap their weight phase with other blocks' loads
+  constexpr int kBatch = 8;
+  for (int t0 = 0; t0 < topk; t0 += kBatch) {
+    u32x4 raw[kBatch];
+    float wgt[kBatch];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const int t = t0 + k;
       wgt[k] = t < topk ? wts[rl][t] : 0.f;
       const long long blk = (gq * topk + t) * Hkv + hkv;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void combine_slots_kernel(
                             : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < kBatch; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += wgt[k] * __uint_as_float(raw[k][i] << 16);
