@@ -54,6 +54,11 @@ def _load():
         lib.oracle_k2q_csr_varlen.restype = I
         lib.oracle_fp8_e4m3_decode.argtypes = [P, I64, P]
         lib.oracle_fp8_e4m3_decode.restype = I
+        lib.oracle_fp8_e4m3_round.argtypes = [P, I64, P]
+        lib.oracle_fp8_e4m3_round.restype = I
+        lib.oracle_paged_decode_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, D, P,
+                                                I64, P, P, D, P, I]
+        lib.oracle_paged_decode_fp8.restype = I
         _lib = lib
     return _lib
 
@@ -82,6 +87,44 @@ def fp8_e4m3_decode(x) -> np.ndarray:
     if _load().oracle_fp8_e4m3_decode(_ptr(a), a.size, _ptr(out)) != 0:
         raise ValueError("oracle_fp8_e4m3_decode: invalid arguments")
     return out
+
+
+def fp8_e4m3_round(x) -> np.ndarray:
+    """The oracle's rounding to the nearest fp8 e4m3fn value (ties to even), float64."""
+    a = _c(x, np.float64)
+    out = np.empty(a.shape, dtype=np.float64)
+    if _load().oracle_fp8_e4m3_round(_ptr(a), a.size, _ptr(out)) != 0:
+        raise ValueError("oracle_fp8_e4m3_round: invalid arguments")
+    return out
+
+
+def paged_decode_fp8(q, k_pool, v_pool, page_table, seqused_k, *, causal: bool,
+                     softmax_scale: Optional[float] = None, rows=None,
+                     temperature: Optional[float] = None, nthreads: int = 0):
+    """Oracle fp8 dense paged decode (the test page's `_decode_paged_dense_reference`):
+    q [B, Sq, Hq, D], k_pool / v_pool [num_pages, Hkv, page_size, D], all fp8 e4m3fn
+    bytes (uint8); every key of the sequence, probabilities rounded to e4m3 before the
+    P V product, the row sum unrounded. Returns (O, LSE[, LSE_T]) shaped like
+    paged_sparse_attention's."""
+    q, k_pool, v_pool = _c(q, np.uint8), _c(k_pool, np.uint8), _c(v_pool, np.uint8)
+    page_table, seqused_k = _c(page_table, np.int32), _c(seqused_k, np.int32)
+    B, Sq, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    assert page_table.shape[0] == B and seqused_k.shape == (B,) and v_pool.shape == k_pool.shape
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    rws = _c(rows, np.int64)
+    n = B * Sq if rws is None else rws.size
+    o = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    temp, lse_t = _temperature_out(n, Hq, temperature)
+    rc = _load().oracle_paged_decode_fp8(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(seqused_k), B, Sq, Hq, Hkv,
+        D, page_size, num_pages, max_pages, int(causal), scale, _ptr(rws), n, _ptr(o), _ptr(lse),
+        temp, _ptr(lse_t), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_paged_decode_fp8: invalid arguments")
+    return _shape_out(o, lse, rws, B, Sq, Hq, D, lse_t)
 
 
 def _shape_out(o, lse, rows, B, Sq, Hq, D, lse_t=None):

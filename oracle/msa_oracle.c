@@ -384,3 +384,112 @@ int oracle_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
   free(rowbase);
   return 0;
 }
+
+/* Nearest fp8 e4m3fn value of x, ties to the even code: 4 significant bits for
+ * |x| >= 2^-6 (quantum 2^(e-4) with |x| = f 2^e, f in [0.5, 1)), a fixed
+ * quantum of 2^-9 below; rint rounds half to even in the default mode. */
+static double fp8_round(double x) {
+  if (isnan(x)) return NAN;
+  const double a = fabs(x);
+  if (a >= 464.0) return NAN;  /* past the midpoint above 448: no finite code */
+  double r;
+  if (a < ldexp(1.0, -6)) {
+    r = ldexp(rint(ldexp(a, 9)), -9);
+  } else {
+    int e;
+    frexp(a, &e);
+    r = ldexp(rint(ldexp(a, 4 - e)), e - 4);
+    if (r > 448.0) r = 448.0;  /* (448, 464) rounds down to the largest code */
+  }
+  return x < 0 ? -r : r;
+}
+
+int oracle_fp8_e4m3_round(const double* in, int64_t n, double* out) {
+  if (!in || !out || n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = fp8_round(in[i]);
+  return 0;
+}
+
+int oracle_paged_decode_fp8(const uint8_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, const int32_t* seqused_k, int B, int Sq,
+                            int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
+                            int causal, double scale, const int64_t* rows, int64_t nrows,
+                            double* o, double* lse, double temp, double* lse_t, int nthreads) {
+  if (!q || !k_pool || !v_pool || !page_table || !seqused_k || !o || !lse || B <= 0 || Sq <= 0 ||
+      Hkv <= 0 || Hq <= 0 || Hq % Hkv || D <= 0 || page_size <= 0 || num_pages <= 0 ||
+      max_pages <= 0 || (lse_t && !(temp > 0.0)))
+    return -1;
+  if (!rows) nrows = (int64_t)B * Sq;
+  const int qpk = Hq / Hkv;
+  const int64_t full_len = (int64_t)max_pages * page_size;
+  kv_source src = {k_pool, v_pool, page_table, 0, Hkv, D, page_size, num_pages, max_pages, 1};
+  int failed = 0;
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+  {
+    double* score = (double*)malloc(sizeof(double) * (size_t)(full_len > 0 ? full_len : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!score || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t g = rows ? rows[i] : i;
+        if (g < 0 || g >= (int64_t)B * Sq) {
+#pragma omp atomic write
+          failed = 1;
+          continue;
+        }
+        const int b = (int)(g / Sq), qpos = (int)(g % Sq);
+        int64_t kvlen = seqused_k[b] < full_len ? seqused_k[b] : full_len;
+        if (kvlen < 0) kvlen = 0;
+        const int64_t limit = causal ? (int64_t)qpos + kvlen - Sq : INT64_MAX;
+        for (int h = 0; h < Hq; ++h) {
+          const int hkv = h / qpk;
+          const uint8_t* qh = q + (g * Hq + h) * D;
+          double* oh = o + (i * Hq + h) * D;
+          /* pass 1: scores of the visible keys (ascending key order) and their max */
+          int64_t n = 0;
+          double m = -INFINITY;
+          for (int64_t j = 0; j < kvlen && j <= limit; ++j) {
+            const int64_t off = kv_offset(&src, b, hkv, j);
+            if (off < 0) continue;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += fp8_value(qh[d]) * k_value(&src, off + d);
+            score[n++] = scale * dot;
+            if (scale * dot > m) m = scale * dot;
+          }
+          if (n == 0) {
+            for (int d = 0; d < D; ++d) oh[d] = 0.0;
+            lse[i * Hq + h] = -INFINITY;
+            if (lse_t) lse_t[i * Hq + h] = -INFINITY;
+            continue;
+          }
+          if (lse_t) {
+            double lt = 0.0;
+            for (int64_t k2 = 0; k2 < n; ++k2) lt += exp((score[k2] - m) / temp);
+            lse_t[i * Hq + h] = m / temp + log(lt);
+          }
+          /* pass 2: unrounded row sum; values weighted by the e4m3-rounded probabilities */
+          for (int d = 0; d < D; ++d) acc[d] = 0.0;
+          double l = 0.0;
+          int64_t k1 = 0;
+          for (int64_t j = 0; j < kvlen && j <= limit; ++j) {
+            const int64_t off = kv_offset(&src, b, hkv, j);
+            if (off < 0) continue;
+            const double p = exp(score[k1++] - m);
+            l += p;
+            const double pq = fp8_round(p);
+            for (int d = 0; d < D; ++d) acc[d] += pq * v_value(&src, off + d);
+          }
+          for (int d = 0; d < D; ++d) oh[d] = acc[d] / l;
+          lse[i * Hq + h] = m + log(l);
+        }
+      }
+    }
+    free(score);
+    free(acc);
+  }
+  return failed ? -1 : 0;
+}

@@ -113,6 +113,40 @@ int oracle_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
  */
 int oracle_fp8_e4m3_decode(const uint8_t* in, int64_t n, double* out);
 
+/*
+ * Rounding to the nearest fp8 e4m3fn value, ties to the even code (the
+ * `.to(torch.float8_e4m3fn)` cast the test page applies to the unnormalised
+ * probabilities of the fp8 decode): n values -> n values. Finite magnitudes up
+ * to 448 round into the format (subnormal step 2^-9, 3 mantissa bits above
+ * 2^-6); magnitudes >= 464 and NaN give NaN (the format has no infinity).
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_fp8_e4m3_round(const double* in, int64_t n, double* out);
+
+/*
+ * The fp8 dense paged decode of the test page (`_decode_paged_dense_reference`,
+ * checked against `sparse_decode_atten_func` with q2k = None): Q, K and V are
+ * fp8 e4m3fn bytes; every key of the sequence is visible up to seqused_k[b]
+ * (and the bottom-right causal limit q + seqused_k[b] - Sq when causal). Per
+ * (row, head), with scores s_j = scale * q . k_j and m = max_j s_j:
+ *   row_sum = sum_j exp(s_j - m)                      (unrounded)
+ *   O       = sum_j e4m3(exp(s_j - m)) v_j / row_sum  (probabilities rounded
+ *                                                      to e4m3 before P V)
+ *   LSE     = m + log(row_sum)
+ * Empty rows give O = 0, LSE = -inf. A page id outside [0, num_pages) makes its
+ * keys contribute nothing.
+ *   q        [B * Sq, Hq, D] fp8 bytes
+ *   k_pool, v_pool  [num_pages, Hkv, page_size, D] fp8 bytes
+ *   page_table [B, max_pages]; seqused_k [B]
+ *   rows, o, lse, temp, lse_t  as for oracle_paged_sparse_attention (lse_t is the
+ *            log-sum-exp of the unrounded scores divided by temp)
+ */
+int oracle_paged_decode_fp8(const uint8_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                            const int32_t* page_table, const int32_t* seqused_k, int B, int Sq,
+                            int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
+                            int causal, double scale, const int64_t* rows, int64_t nrows,
+                            double* o, double* lse, double temp, double* lse_t, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
