@@ -101,9 +101,9 @@ def dense_decode_algorithmic_bytes(w, inp) -> int:
     element size x 2 (K and V), plus Q, O, LSE, page table and seqused."""
     pages = int(((inp["seqused_k"].astype(np.int64) + 127) // 128).sum())
     kv = pages * w.Hkv * 128 * w.D * inp["k_pool"].itemsize * 2
-    q = w.B * w.Sq * w.Hq * w.D * 2
-    return int(kv + 2 * q + w.B * w.Sq * w.Hq * 4 + inp["page_table"].nbytes +
-               inp["seqused_k"].nbytes)
+    q = w.B * w.Sq * w.Hq * w.D  # elements of Q read (bf16 or fp8) and of O written (bf16)
+    return int(kv + q * inp["q"].itemsize + q * 2 + w.B * w.Sq * w.Hq * 4 +
+               inp["page_table"].nbytes + inp["seqused_k"].nbytes)
 
 
 def decode_algorithmic_bytes(w, inp) -> int:
@@ -145,6 +145,8 @@ class Case:
         self.kv_dtype = kv_dtype
         if kv_dtype == "fp8":  # the fp8 e4m3fn K/V cache (bytes, read as fp8 by the library)
             self.inp = wl.with_fp8_kv(self.inp)
+            if w.paged and w.dense:  # the pages' fp8 decode: Q fp8 as well
+                self.inp["q"] = wl.bf16_bits_to_fp8(self.inp["q"])
         log(f"[bench] {key}: inputs generated in {time.time() - t0:.1f}s")
         dev = lambda x: (torch.from_numpy(x).view(torch.bfloat16) if x.dtype == np.uint16
                          else torch.from_numpy(x)).to("cuda")
@@ -306,18 +308,18 @@ class Case:
             paged = "true" if w.paged else "false"
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
         if w.paged:
-            return decode_instance(w).replace("TEMP", t)
+            return decode_instance(w, fp8).replace("TEMP", t)
         return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
                 "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
 
 
-def decode_instance(w) -> str:
+def decode_instance(w, fp8: bool = False) -> str:
     """The paged decode kernel instance the launcher picks (TEMP stands for the
     temperature template argument): the dense decode with at most 128 (query, head)
-    columns per KV head runs the 32-column kernel; otherwise the union kernel groups
-    queries four to a wave."""
+    columns per KV head runs the 32-column kernel (bf16 or the fp8 decode); otherwise
+    the union kernel groups queries four to a wave."""
     if w.dense and w.Sq * w.qpk <= 128:
-        return "dense_decode_kernel<TEMP>"
+        return f"dense_decode_kernel<TEMP, {'true' if fp8 else 'false'}>"
     return (f"paged_decode_kernel<{(w.Sq + 3) // 4}, TEMP, "
             f"{'true' if w.dense else 'false'}>")
 
@@ -365,6 +367,10 @@ def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
             oracle.sparse_attention_varlen(inp["q"], inp["k"], inp["v"], inp["q2k"],
                                            inp["cu_seqlens_q"], inp["cu_seqlens_k"],
                                            causal=w.causal, rows=rows, nthreads=threads)
+        elif w.paged and w.dense and case.kv_dtype == "fp8":  # the pages' fp8 decode
+            oracle.paged_decode_fp8(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                    inp["seqused_k"], causal=w.causal, rows=rows,
+                                    nthreads=threads)
         elif w.paged and w.dense:  # every block selected
             full = np.ascontiguousarray(np.broadcast_to(
                 np.arange(w.max_pages, dtype=np.int32), (w.B, w.Hkv, w.Sq, w.max_pages)))
@@ -475,6 +481,8 @@ def main() -> int:
                     "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": case.splits,
                     "lse_temperature": args.lse_temperature, "kv_dtype": args.kv_dtype,
+                    "q_dtype": str(case.inp["q"].dtype).replace("uint8", "fp8").replace(
+                        "uint16", "bf16"),
                     "parallelism": "none"} if not case.varlen else
                    {"workload": w.name, "B": w.B, "varlen": True, "total_q": w.total_q,
                     "total_k": w.total_k, "q_lens": list(w.q_lens), "k_lens": list(w.k_lens),

@@ -95,7 +95,7 @@ def load_library():
     lib.msa_paged_decode_plan_init.restype = I
     lib.msa_paged_decode_plan.argtypes = [P, PL, P, S, P]
     lib.msa_paged_decode_plan.restype = I
-    lib.msa_paged_decode_run.argtypes = [P, P, P, P, P, PL, P, S, I, I, F, P, P, F, P, P]
+    lib.msa_paged_decode_run.argtypes = [P, P, P, P, P, PL, P, S, I, I, I, F, P, P, F, P, P]
     lib.msa_paged_decode_run.restype = I
     lib.msa_set_profiling_events.argtypes = [P, P]
     lib.msa_set_profiling_events.restype = I
@@ -477,10 +477,18 @@ def msa_paged_decode_run(plan: DecodePlan, q, k_pool, v_pool, page_table, sequse
                          lse_temperature_scale: Optional[float] = None, lse_temperature=None,
                          temperature_fast_path: bool = True, stream=None):
     """Run the dense paged decode on a plan. Returns (O bf16 [B,Sq,Hq,D], LSE [B,Hq,Sq]),
-    plus the temperature-scaled LSE when asked."""
+    plus the temperature-scaled LSE when asked. Q, K and V all bf16, or all fp8
+    e4m3fn (torch.float8_e4m3fn, or uint8 holding its bytes): the pages' fp8 decode,
+    probabilities rounded to e4m3 before the P V product."""
     lib = load_library()
-    _dev(q, "q", torch.bfloat16), _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16), _dev(page_table, "page_table", torch.int32)
+    dtype = _kv_dtype(k_pool, v_pool, ("k_pool", "v_pool"))
+    if dtype == MSA_DTYPE_BF16:
+        _dev(q, "q", torch.bfloat16)
+    elif not (isinstance(q, torch.Tensor) and q.is_cuda and q.is_contiguous()
+              and q.dtype in (getattr(torch, "float8_e4m3fn", None), torch.uint8)):
+        raise TypeError("the fp8 decode takes q as contiguous fp8 e4m3fn on the GPU, like "
+                        "k_pool / v_pool")
+    _dev(page_table, "page_table", torch.int32)
     _dev(seqused_k, "seqused_k", torch.int32)
     info = plan.info
     B, Sq, Hq, D = q.shape
@@ -495,7 +503,7 @@ def msa_paged_decode_run(plan: DecodePlan, q, k_pool, v_pool, page_table, sequse
                                       lse_temperature, temperature_fast_path)
     rc = lib.msa_paged_decode_run(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                                   _ptr(seqused_k), ctypes.byref(info), _ptr(plan.buffer),
-                                  plan.buffer.numel(), k_pool.shape[0], int(bool(causal)),
+                                  plan.buffer.numel(), k_pool.shape[0], dtype, int(bool(causal)),
                                   float(softmax_scale), _ptr(o), _ptr(lse), temp, _ptr(lse_t),
                                   _stream(stream))
     _check(rc)

@@ -698,13 +698,21 @@ int msa_paged_decode_plan(const int32_t* seqused_k, const msa_decode_plan* plan,
 int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k,
                          const msa_decode_plan* plan, void* buffer, size_t buffer_bytes,
-                         int num_pages, int causal, float softmax_scale, void* o, float* lse,
-                         float lse_temperature_scale, float* lse_temperature, void* stream) {
+                         int num_pages, int dtype, int causal, float softmax_scale, void* o,
+                         float* lse, float lse_temperature_scale, float* lse_temperature,
+                         void* stream) {
   g_last_error.clear();
   int rc = check_plan_buffer(plan, buffer, buffer_bytes);
   if (rc) return rc;
   rc = check_temperature(lse_temperature_scale, lse_temperature);
   if (rc) return rc;
+  rc = check_kv_dtype(dtype, MSA_PATH_AUTO);
+  if (rc) return rc;
+  if (dtype == MSA_DTYPE_FP8_E4M3 &&
+      plan->seqlen_q * (plan->num_qo_heads / plan->num_kv_heads) > 128)
+    return fail(MSA_ERR_NOT_SUPPORTED,
+                "the fp8 dense decode needs Sq * Hq / Hkv <= 128 (got %d * %d)", plan->seqlen_q,
+                plan->num_qo_heads / plan->num_kv_heads);
   if (num_pages <= 0) return fail(MSA_ERR_INVALID_VALUE, "num_pages must be positive");
   if (!q || !k_pool || !v_pool || !page_table || !seqused_k || !o || !lse)
     return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
@@ -720,6 +728,7 @@ int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
   p.q = static_cast<const uint16_t*>(q);
   p.k = k_pool;
   p.v = v_pool;
+  p.kv_fp8 = dtype == MSA_DTYPE_FP8_E4M3 ? 1 : 0;  // Q too: the pages' fp8 decode
   p.page_table = page_table;
   p.seqused = seqused_k;
   p.B = P.batch; p.Sq = P.seqlen_q; p.Hq = P.num_qo_heads; p.Hkv = P.num_kv_heads;

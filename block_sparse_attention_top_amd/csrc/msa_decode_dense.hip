@@ -24,6 +24,15 @@
 // The load addresses are a scalar base per (page, sub-tile) plus loop-invariant
 // 32-bit lane offsets, and masking runs only on sub-tiles that cross some
 // column's causal limit, so the per-sub-tile vector work is the softmax itself.
+//
+// FP8 is the fp8 decode of those pages (Q, K and V fp8 e4m3fn; the unnormalised
+// probabilities rounded to e4m3 before the P V product, the row sum kept
+// unrounded, as the test page's dense decode reference states). Every fp8 value
+// is exact in bf16 and every product of two of them exact in fp32, so the kernel
+// keeps the bf16 matrix path: Q is widened once, the K/V sub-tiles (8 KiB of fp8)
+// stream through a five-stage direct-to-LDS ring and one cooperative pass per
+// sub-tile widens the next sub-tile into one of two swizzled bf16 buffers while
+// the current one is consumed, and P is rounded to e4m3 and widened back.
 #include "msa_internal.hpp"
 #include "msa_lds.hpp"
 
@@ -37,16 +46,28 @@ constexpr int kSub = 32;              // tokens per sub-tile
 constexpr int kRow = 256;             // bytes per K/V row in LDS (no padding)
 constexpr int kTile = kSub * kRow;    // one sub-tile of K (or V): 8 KiB
 constexpr int kCols = 128;            // (query, head) columns per workgroup
+constexpr int kTile8 = kSub * kD;     // one fp8 sub-tile of K (or V): 4 KiB
+constexpr int kStages8 = 5;           // fp8 ring depth
 
 // 16-byte chunk c of LDS row r sits at chunk position c ^ swz(r) of that row
 __device__ __forceinline__ int swz(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
 
-template <bool TEMP>
+// 8 fp8 values -> 8 bf16 (exact)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  const u32x4 r = {fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                   fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+  return as_bf16x8(r);
+}
+
+// (p0, p1) rounded to e4m3 (nearest, ties to even), widened back: a bf16 pair
+__device__ __forceinline__ uint32_t e4m3_round_bf16x2(float p0, float p1) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 f8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, p0, p1, 1.0f, false);
+  return fp8x2_to_bf16x2<false>(__builtin_bit_cast(uint32_t, f8));
+}
+
+template <bool TEMP, bool FP8>
 __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
-  // ring of four stages (K sub-tile at offset 0, V sub-tile at kTile); separate
-  // arrays keep the stage buffers distinct objects
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTile], st1[2 * kTile];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * kTile], st3[2 * kTile];
   __shared__ int upage[kDecMaxEntries];  // the chunk's page ids (an id outside the pool: -1)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -88,13 +109,20 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
 
   bf16x8 qm[8];
   {
-    const uint16_t* qrow =
-        p.q + ((static_cast<long long>(b) * p.Sq + (col_ok ? q32 : 0)) * p.Hq + head) * kD + 8 * h32;
+    const long long qoff =
+        ((static_cast<long long>(b) * p.Sq + (col_ok ? q32 : 0)) * p.Hq + head) * kD + 8 * h32;
 #pragma unroll
     for (int kq = 0; kq < 8; ++kq) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * kq);
-      if (!col_ok) v = u32x4{0, 0, 0, 0};
-      qm[kq] = as_bf16x8(v);
+      if (FP8) {
+        u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(p.q) + qoff +
+                                                  16 * kq);
+        if (!col_ok) w = u32x2{0, 0};
+        qm[kq] = fp8x8_to_bf16x8(w);
+      } else {
+        u32x4 v = *reinterpret_cast<const u32x4*>(p.q + qoff + 16 * kq);
+        if (!col_ok) v = u32x4{0, 0, 0, 0};
+        qm[kq] = as_bf16x8(v);
+      }
     }
   }
   f32x16 om[4];
@@ -121,11 +149,15 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
   const int tail = ntok - kSub * (T - 1);  // keys in the last sub-tile (1..32)
   __syncthreads();                         // page list complete
 
-  auto issue = [&](int t, uint8_t* buf) {
-    const int u = t >> 2, sub = t & 3;
-    int pg = __builtin_amdgcn_readfirstlane(upage[u]);
+  // scalar base of sub-tile t (page row 32 (t % 4) of the chunk's page t / 4)
+  auto row_base = [&](int t) -> long long {
+    int pg = __builtin_amdgcn_readfirstlane(upage[t >> 2]);
     pg = pg < 0 ? 0 : pg;  // an id outside the pool reads page 0 (in bounds), masked below
-    const long long row0 = (static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * sub;
+    return (static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * (t & 3);
+  };
+
+  auto issue = [&](int t, uint8_t* buf) {
+    const long long row0 = row_base(t);
     const uint8_t* kb = static_cast<const uint8_t*>(p.k) + row0 * kRow;
     const uint8_t* vb = static_cast<const uint8_t*>(p.v) + row0 * kRow;
     uint32_t o0 = loff[0], o1 = loff[1];
@@ -193,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
     for (int i = 0; i < 8; ++i) {
       const float p0 = fast_exp2(fmaf(sacc[2 * i], c2, nmc));
       const float p1 = fast_exp2(fmaf(sacc[2 * i + 1], c2, nmc));
-      pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
+      pw[i >> 2][i & 3] = FP8 ? e4m3_round_bf16x2(p0, p1) : pack_bf16x2(p0, p1);
       ps += p0 + p1;
       if (TEMP)
         pst += fast_exp2(fmaf(sacc[2 * i], c2t, nmc * p.inv_temp)) +
@@ -214,33 +246,99 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
     }
   };
 
-  // Ring of four stages: while stage t is consumed, stages t+1 and t+2 are in
-  // flight and stage t+3 goes into the buffer that t-1 used (free once every wave
-  // has passed this phase's barrier). Each wave issues 4 loads per stage, so "own
-  // loads of stage t landed" is vmcnt <= 8; the barrier then makes every wave's
-  // share visible. Stages past the end re-read the last sub-tile (in bounds) so
-  // that every phase issues the same number of loads.
-  if (T > 0) {
-    issue(0, st0);
-    issue(min(1, T - 1), st1);
-    issue(min(2, T - 1), st2);
-    int t = 0;
-#define MSA_DENSE_PHASE(cur, nxt)                              \
-    {                                                          \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));         \
-      __builtin_amdgcn_s_barrier();                            \
-      issue(min(t + 3, T - 1), nxt);                           \
-      compute(t, cur);                                         \
-      if (++t >= T) break;                                     \
+  if constexpr (!FP8) {
+    // ring of four stages (K sub-tile at offset 0, V sub-tile at kTile); separate
+    // arrays keep the stage buffers distinct objects
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTile], st1[2 * kTile];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * kTile], st3[2 * kTile];
+    // Ring of four stages: while stage t is consumed, stages t+1 and t+2 are in
+    // flight and stage t+3 goes into the buffer that t-1 used (free once every wave
+    // has passed this phase's barrier). Each wave issues 4 loads per stage, so "own
+    // loads of stage t landed" is vmcnt <= 8; the barrier then makes every wave's
+    // share visible. Stages past the end re-read the last sub-tile (in bounds) so
+    // that every phase issues the same number of loads.
+    if (T > 0) {
+      issue(0, st0);
+      issue(min(1, T - 1), st1);
+      issue(min(2, T - 1), st2);
+      int t = 0;
+  #define MSA_DENSE_PHASE(cur, nxt)                              \
+      {                                                          \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));         \
+        __builtin_amdgcn_s_barrier();                            \
+        issue(min(t + 3, T - 1), nxt);                           \
+        compute(t, cur);                                         \
+        if (++t >= T) break;                                     \
+      }
+      while (true) {
+        MSA_DENSE_PHASE(st0, st3)
+        MSA_DENSE_PHASE(st1, st0)
+        MSA_DENSE_PHASE(st2, st1)
+        MSA_DENSE_PHASE(st3, st2)
+      }
+  #undef MSA_DENSE_PHASE
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
     }
-    while (true) {
-      MSA_DENSE_PHASE(st0, st3)
-      MSA_DENSE_PHASE(st1, st0)
-      MSA_DENSE_PHASE(st2, st1)
-      MSA_DENSE_PHASE(st3, st2)
+  } else {
+    // fp8 ring of five stages (K sub-tile at 0, V sub-tile at kTile8) and two bf16
+    // buffers in the layout the compute reads
+    __shared__ __attribute__((aligned(1024))) uint8_t ring8[kStages8 * 2 * kTile8];
+    __shared__ __attribute__((aligned(1024))) uint8_t wide[2 * 2 * kTile];
+    // direct loads of an fp8 sub-tile: wave w writes rows 8w .. 8w+7 of K and of V,
+    // lane l row 8w + l / 8, 16-byte chunk l % 8, row-major without padding
+    const int r8 = 8 * wave + (lane >> 3), c8 = lane & 7;
+    const uint32_t loff8 = r8 * kD + 16 * c8;
+    auto issue8 = [&](int t, int slot) {
+      const long long row0 = row_base(t);
+      const uint8_t* kb = static_cast<const uint8_t*>(p.k) + row0 * kD;
+      const uint8_t* vb = static_cast<const uint8_t*>(p.v) + row0 * kD;
+      uint32_t o = loff8;
+      if (t == T - 1 && tail < kSub) o = min(r8, tail - 1) * kD + 16 * c8;  // wave-uniform branch
+      const uint32_t kd = lds_addr(ring8) + slot * (2 * kTile8) + 8 * wave_u * kD;
+      lds_load16_s(kb, o, kd);
+      lds_load16_s(vb, o, kd + kTile8);
+    };
+    // widen ring slot `slot` into bf16 buffer `wb`: thread = (row tid / 8, 16 fp8 of
+    // chunk tid % 8), written as logical bf16 chunks 2c and 2c + 1 of that row
+    const int rw = tid >> 3, cw = tid & 7;
+    const int wlo = rw * kRow + 16 * ((2 * cw) ^ swz(rw));
+    const int whi = rw * kRow + 16 * ((2 * cw + 1) ^ swz(rw));
+    auto widen = [&](int slot, int wb) {
+      const uint8_t* src = ring8 + slot * (2 * kTile8) + rw * kD + 16 * cw;
+      uint8_t* dst = wide + wb * (2 * kTile);
+      u32x4 o2[2];
+      fp8x16_to_bf16x16(*reinterpret_cast<const u32x4*>(src), o2);
+      *reinterpret_cast<u32x4*>(dst + wlo) = o2[0];
+      *reinterpret_cast<u32x4*>(dst + whi) = o2[1];
+      fp8x16_to_bf16x16(*reinterpret_cast<const u32x4*>(src + kTile8), o2);
+      *reinterpret_cast<u32x4*>(dst + kTile + wlo) = o2[0];
+      *reinterpret_cast<u32x4*>(dst + kTile + whi) = o2[1];
+    };
+    // While sub-tile t is consumed from bf16 buffer t % 2, sub-tile t+1 is widened
+    // into the other buffer and sub-tiles t+2 .. t+5 are in flight; sub-tile t+5 goes
+    // into ring slot t % 5, whose sub-tile t was widened in the previous phase. Each
+    // wave issues 2 loads per sub-tile, so "own loads of t+1 landed" is vmcnt <= 6;
+    // the barrier then makes every wave's share visible and retires the previous
+    // phase's widening and compute. Sub-tiles past the end re-read the last one.
+    if (T > 0) {
+#pragma unroll
+      for (int s = 0; s < kStages8; ++s) issue8(min(s, T - 1), s);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));
+      __builtin_amdgcn_s_barrier();
+      widen(0, 0);
+      int t = 0, slot_in = 0, slot_next = 1;  // slot_in = t % 5, slot_next = (t + 1) % 5
+      while (true) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
+        __builtin_amdgcn_s_barrier();
+        issue8(min(t + kStages8, T - 1), slot_in);
+        if (t + 1 < T) widen(slot_next, (t + 1) & 1);
+        compute(t, wide + (t & 1) * (2 * kTile));
+        if (++t >= T) break;
+        slot_in = slot_next;
+        slot_next = slot_next == kStages8 - 1 ? 0 : slot_next + 1;
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
     }
-#undef MSA_DENSE_PHASE
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
   }
 
   // epilogue: lane (n32, h32) holds dims 32 dt + 8 (i / 4) + 4 h32 + i % 4 of its column
@@ -300,15 +398,22 @@ hipError_t launch_dense_decode_grouped(const QcParams& p, int padded_work, hipSt
 
 // Sq * qpk <= 128 runs the 32-column kernel above
 hipError_t launch_dense_decode(const QcParams& p, int padded_work, hipStream_t stream) {
-  if (p.Sq * p.qpk > kCols) return launch_dense_decode_grouped(p, padded_work, stream);
+  if (p.Sq * p.qpk > kCols) {
+    if (p.kv_fp8) return hipErrorInvalidValue;  // the grouped kernel reads bf16 only
+    return launch_dense_decode_grouped(p, padded_work, stream);
+  }
   const long long items = static_cast<long long>(padded_work) * p.Hkv;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL || p.Sq < 1) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
-  if (p.lse_t)
-    hipLaunchKernelGGL(dense_decode_kernel<true>, grid, dim3(256), 0, stream, p);
+  if (p.kv_fp8 && p.lse_t)
+    hipLaunchKernelGGL((dense_decode_kernel<true, true>), grid, dim3(256), 0, stream, p);
+  else if (p.kv_fp8)
+    hipLaunchKernelGGL((dense_decode_kernel<false, true>), grid, dim3(256), 0, stream, p);
+  else if (p.lse_t)
+    hipLaunchKernelGGL((dense_decode_kernel<true, false>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(dense_decode_kernel<false>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((dense_decode_kernel<false, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

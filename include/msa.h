@@ -83,7 +83,9 @@ enum msa_dtype {
                              result equals the bf16 path on the dequantized K/V bit for
                              bit; K/V tensors keep their shapes with 1-byte elements.
                              The q-centric and kv-centric kernels read it; the decode and
-                             query-tile paths return MSA_ERR_NOT_SUPPORTED */
+                             query-tile paths return MSA_ERR_NOT_SUPPORTED. For the dense
+                             decode (msa_paged_decode_run) it is the pages' fp8 decode:
+                             Q, K and V fp8, see there */
 };
 
 /*
@@ -250,7 +252,7 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
  * the page "MSA interface.py". Every query row attends to all keys of its
  * sequence (j < seqused_k[b], causal limit q + seqused_k[b] - Sq): the definition
  * at the top of this file with every block selected. Q bf16 [B, Sq, Hq, D]
- * (Sq <= 16), K/V bf16 pools [num_pages, Hkv, 128, D], O [B, Sq, Hq, D],
+ * (Sq <= 16; fp8 below), K/V bf16 pools [num_pages, Hkv, 128, D], O [B, Sq, Hq, D],
  * LSE [B, Hq, Sq]. A workgroup takes one (sequence, chunk of pages, KV head) and
  * reads each page once for all Sq query rows; a sequence cut into several chunks
  * gets fp32 partial rows, merged by log-sum-exp afterwards.
@@ -290,12 +292,23 @@ int msa_paged_decode_plan_init(int B, int Sq, int Hq, int Hkv, int D, int page_s
 int msa_paged_decode_plan(const int32_t* seqused_k, const msa_decode_plan* plan, void* buffer,
                           size_t buffer_bytes, void* stream);
 /* num_pages: pool size (page ids outside [0, num_pages) read as unused blocks);
- * the page table is [B, plan->max_pages]. Other arguments as msa_paged_sparse_fwd. */
+ * the page table is [B, plan->max_pages].
+ * dtype: MSA_DTYPE_BF16 (Q, K, V bf16) or MSA_DTYPE_FP8_E4M3, the fp8 decode of
+ *   sparse_decode_atten_func as the test page "test_sparse_atten.py" checks it
+ *   (`_decode_paged_dense_reference`): Q [B, Sq, Hq, D] and the K/V pools are OCP
+ *   float8_e4m3fn bytes (no scale), the unnormalised probabilities are rounded to
+ *   e4m3 (nearest, ties to even) before the P V product while the row sum and the
+ *   LSE use the unrounded ones; O stays bf16. Only for Sq * Hq / Hkv <= 128
+ *   (else MSA_ERR_NOT_SUPPORTED). The rounding point is the kernel's running
+ *   reference maximum rather than the row's final maximum, which changes results
+ *   within the e4m3 rounding (the page allows 0.125 on O and 2e-3 on the LSE).
+ * Other arguments as msa_paged_sparse_fwd. */
 int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k,
                          const msa_decode_plan* plan, void* buffer, size_t buffer_bytes,
-                         int num_pages, int causal, float softmax_scale, void* o, float* lse,
-                         float lse_temperature_scale, float* lse_temperature, void* stream);
+                         int num_pages, int dtype, int causal, float softmax_scale, void* o,
+                         float* lse, float lse_temperature_scale, float* lse_temperature,
+                         void* stream);
 
 /*
  * Profiling hook (for benchmarks): when both are non-NULL, every later

@@ -90,7 +90,8 @@ def main() -> int:
     if w.paged:
         dom = {"paged-qcentric": f"qcentric_kernel<true, false, {f8},",
                "paged-decode": bench.decode_instance(w).replace("TEMP", "false"),
-               "paged-dense-decode": bench.decode_instance(w).replace("TEMP", "false"),
+               "paged-dense-decode": bench.decode_instance(w, f8 == "true").replace("TEMP",
+                                                                                    "false"),
                }[args.path]
     else:
         dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",

@@ -262,10 +262,19 @@ def test_decode_plan_and_run_reject_bad_buffers():
     assert lib.msa_paged_decode_plan(None, ctypes.byref(P), FAKE, P.bytes, None) == 1
     Z = msa.MsaDecodePlan()  # never initialised
     assert lib.msa_paged_decode_plan(FAKE, ctypes.byref(Z), FAKE, 1 << 30, None) == 1
-    run = [FAKE] * 5 + [ctypes.byref(P), FAKE, P.bytes, 16, 1, 0.0, FAKE, FAKE, 1.0, None, None]
+    run = [FAKE] * 5 + [ctypes.byref(P), FAKE, P.bytes, 16, 0, 1, 0.0, FAKE, FAKE, 1.0, None,
+                        None]
     a = list(run); a[8] = 0  # num_pages
     assert lib.msa_paged_decode_run(*a) == 1
     a = list(run); a[0] = None
     assert lib.msa_paged_decode_run(*a) == 1
-    a = list(run); a[13] = 0.0; a[14] = FAKE  # temperature buffer with T = 0
+    a = list(run); a[14] = 0.0; a[15] = FAKE  # temperature buffer with T = 0
     assert lib.msa_paged_decode_run(*a) == 1
+    a = list(run); a[9] = 7  # unknown dtype
+    assert lib.msa_paged_decode_run(*a) == 1
+    # the fp8 decode covers Sq * qpk <= 128 columns: 16 queries x 16 heads is refused
+    P16 = msa.MsaDecodePlan()
+    assert lib.msa_paged_decode_plan_init(4, 16, 64, 4, 128, 128, 4096, 0, 0, 0,
+                                          ctypes.byref(P16)) == 0
+    a = list(run); a[5] = ctypes.byref(P16); a[7] = P16.bytes; a[9] = 1
+    assert lib.msa_paged_decode_run(*a) == 2
