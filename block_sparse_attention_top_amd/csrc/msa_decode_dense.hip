@@ -27,12 +27,14 @@
 //
 // FP8 is the fp8 decode of those pages (Q, K and V fp8 e4m3fn; the unnormalised
 // probabilities rounded to e4m3 before the P V product, the row sum kept
-// unrounded, as the test page's dense decode reference states). Every fp8 value
-// is exact in bf16 and every product of two of them exact in fp32, so the kernel
-// keeps the bf16 matrix path: Q is widened once, the K/V sub-tiles (8 KiB of fp8)
-// stream through a five-stage direct-to-LDS ring and one cooperative pass per
-// sub-tile widens the next sub-tile into one of two swizzled bf16 buffers while
-// the current one is consumed, and P is rounded to e4m3 and widened back.
+// unrounded, as the test page's dense decode reference states). It runs on the
+// fp8 matrix cores: sub-tiles of 64 tokens (16 KiB of fp8 K and V, the same ring
+// and stage size), S^T = K Q^T and O^T += V^T P^T as v_mfma_f32_32x32x64_f8f6f4
+// (K fragments by ds_read_b128, V^T fragments by the transposing
+// ds_read_b64_tr_b8), and P packed to e4m3 with the hardware's round-to-nearest-
+// even conversion -- which is exactly the rounding the definition asks for.
+// Rows of the fp8 tiles (128 B) hold 16-byte chunk c at position c ^ ((r >> 1) & 7),
+// conflict-free for both fragment reads.
 #include "msa_internal.hpp"
 #include "msa_lds.hpp"
 
@@ -46,24 +48,33 @@ constexpr int kSub = 32;              // tokens per sub-tile
 constexpr int kRow = 256;             // bytes per K/V row in LDS (no padding)
 constexpr int kTile = kSub * kRow;    // one sub-tile of K (or V): 8 KiB
 constexpr int kCols = 128;            // (query, head) columns per workgroup
-constexpr int kTile8 = kSub * kD;     // one fp8 sub-tile of K (or V): 4 KiB
-constexpr int kStages8 = 5;           // fp8 ring depth
+constexpr int kSub8 = 64;             // tokens per fp8 sub-tile
+constexpr int kTile8 = kSub8 * kD;    // one fp8 sub-tile of K (or V): 8 KiB
+
+// fp8 tiles: 16-byte chunk c of row r (128 B) at chunk position c ^ swz8(r)
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 x e4m3 (format code 0 for both), no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  const i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  return r;
+}
 
 // 16-byte chunk c of LDS row r sits at chunk position c ^ swz(r) of that row
 __device__ __forceinline__ int swz(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
 
-// 8 fp8 values -> 8 bf16 (exact)
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
-  const u32x4 r = {fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
-                   fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
-  return as_bf16x8(r);
-}
-
-// (p0, p1) rounded to e4m3 (nearest, ties to even), widened back: a bf16 pair
-__device__ __forceinline__ uint32_t e4m3_round_bf16x2(float p0, float p1) {
+// four probabilities rounded to e4m3 (nearest, ties to even) and packed, first in
+// the lowest byte
+__device__ __forceinline__ uint32_t e4m3x4(float p0, float p1, float p2, float p3) {
   typedef short s16x2 __attribute__((ext_vector_type(2)));
-  const s16x2 f8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, p0, p1, 1.0f, false);
-  return fp8x2_to_bf16x2<false>(__builtin_bit_cast(uint32_t, f8));
+  s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, p0, p1, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p2, p3, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 template <bool TEMP, bool FP8>
@@ -82,7 +93,9 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
   const long long t0 = static_cast<long long>(work.z) * kBlk;
   const long long tend = min(kvlen, t0 + static_cast<long long>(npg) * kBlk);
   const int ntok = tend > t0 ? static_cast<int>(tend - t0) : 0;
-  const int T = (ntok + kSub - 1) / kSub;  // sub-tiles
+  constexpr int kSubT = FP8 ? kSub8 : kSub;  // tokens per sub-tile
+  constexpr int kPerPage = kBlk / kSubT;     // sub-tiles per page
+  const int T = (ntok + kSubT - 1) / kSubT;  // sub-tiles
 
   for (int u = tid; u < npg; u += 256) {
     const int pg = p.page_table[static_cast<long long>(b) * p.max_pages + work.z + u];
@@ -107,19 +120,26 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
   for (int d = 1; d < 64; d <<= 1) wmin = min(wmin, __shfl_xor(wmin, d));
   wmin = __builtin_amdgcn_readfirstlane(wmin);
 
-  bf16x8 qm[8];
+  // Q as MFMA B fragments: bf16, lane (n32, h32) dims 16 kq + 8 h32 .. +7; fp8, dims
+  // 64 kq + 32 h32 .. +31 (the byte order the K fragments use too)
+  bf16x8 qm[FP8 ? 1 : 8];
+  i32x8 qf[FP8 ? 2 : 1];
   {
-    const long long qoff =
-        ((static_cast<long long>(b) * p.Sq + (col_ok ? q32 : 0)) * p.Hq + head) * kD + 8 * h32;
+    const long long qrow = (static_cast<long long>(b) * p.Sq + (col_ok ? q32 : 0)) * p.Hq + head;
+    if constexpr (FP8) {
+      const uint8_t* q8 = reinterpret_cast<const uint8_t*>(p.q) + qrow * kD + 32 * h32;
 #pragma unroll
-    for (int kq = 0; kq < 8; ++kq) {
-      if (FP8) {
-        u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(p.q) + qoff +
-                                                  16 * kq);
-        if (!col_ok) w = u32x2{0, 0};
-        qm[kq] = fp8x8_to_bf16x8(w);
-      } else {
-        u32x4 v = *reinterpret_cast<const u32x4*>(p.q + qoff + 16 * kq);
+      for (int kq = 0; kq < 2; ++kq) {
+        u32x4 lo = *reinterpret_cast<const u32x4*>(q8 + 64 * kq);
+        u32x4 hi = *reinterpret_cast<const u32x4*>(q8 + 64 * kq + 16);
+        if (!col_ok) lo = hi = u32x4{0, 0, 0, 0};
+        qf[kq] = cat8(lo, hi);
+      }
+    } else {
+      const uint16_t* qb = p.q + qrow * kD + 8 * h32;
+#pragma unroll
+      for (int kq = 0; kq < 8; ++kq) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qb + 16 * kq);
         if (!col_ok) v = u32x4{0, 0, 0, 0};
         qm[kq] = as_bf16x8(v);
       }
@@ -146,14 +166,15 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
     const int r = 4 * (2 * wave + j) + lrow;
     loff[j] = r * kRow + 16 * (lpos ^ swz(r));
   }
-  const int tail = ntok - kSub * (T - 1);  // keys in the last sub-tile (1..32)
+  const int tail = ntok - kSubT * (T - 1);  // keys in the last sub-tile (1..kSubT)
   __syncthreads();                         // page list complete
 
-  // scalar base of sub-tile t (page row 32 (t % 4) of the chunk's page t / 4)
+  // scalar base of sub-tile t (page row kSubT (t % kPerPage) of the chunk's page
+  // t / kPerPage)
   auto row_base = [&](int t) -> long long {
-    int pg = __builtin_amdgcn_readfirstlane(upage[t >> 2]);
+    int pg = __builtin_amdgcn_readfirstlane(upage[t / kPerPage]);
     pg = pg < 0 ? 0 : pg;  // an id outside the pool reads page 0 (in bounds), masked below
-    return (static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSub * (t & 3);
+    return (static_cast<long long>(pg) * p.Hkv + hkv) * kBlk + kSubT * (t % kPerPage);
   };
 
   auto issue = [&](int t, uint8_t* buf) {
@@ -225,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
     for (int i = 0; i < 8; ++i) {
       const float p0 = fast_exp2(fmaf(sacc[2 * i], c2, nmc));
       const float p1 = fast_exp2(fmaf(sacc[2 * i + 1], c2, nmc));
-      pw[i >> 2][i & 3] = FP8 ? e4m3_round_bf16x2(p0, p1) : pack_bf16x2(p0, p1);
+      pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
       ps += p0 + p1;
       if (TEMP)
         pst += fast_exp2(fmaf(sacc[2 * i], c2t, nmc * p.inv_temp)) +
@@ -246,99 +267,160 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
     }
   };
 
-  if constexpr (!FP8) {
-    // ring of four stages (K sub-tile at offset 0, V sub-tile at kTile); separate
-    // arrays keep the stage buffers distinct objects
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTile], st1[2 * kTile];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * kTile], st3[2 * kTile];
-    // Ring of four stages: while stage t is consumed, stages t+1 and t+2 are in
-    // flight and stage t+3 goes into the buffer that t-1 used (free once every wave
-    // has passed this phase's barrier). Each wave issues 4 loads per stage, so "own
-    // loads of stage t landed" is vmcnt <= 8; the barrier then makes every wave's
-    // share visible. Stages past the end re-read the last sub-tile (in bounds) so
-    // that every phase issues the same number of loads.
-    if (T > 0) {
-      issue(0, st0);
-      issue(min(1, T - 1), st1);
-      issue(min(2, T - 1), st2);
-      int t = 0;
-  #define MSA_DENSE_PHASE(cur, nxt)                              \
-      {                                                          \
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));         \
-        __builtin_amdgcn_s_barrier();                            \
-        issue(min(t + 3, T - 1), nxt);                           \
-        compute(t, cur);                                         \
-        if (++t >= T) break;                                     \
-      }
-      while (true) {
-        MSA_DENSE_PHASE(st0, st3)
-        MSA_DENSE_PHASE(st1, st0)
-        MSA_DENSE_PHASE(st2, st1)
-        MSA_DENSE_PHASE(st3, st2)
-      }
-  #undef MSA_DENSE_PHASE
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
-    }
-  } else {
-    // fp8 ring of five stages (K sub-tile at 0, V sub-tile at kTile8) and two bf16
-    // buffers in the layout the compute reads
-    __shared__ __attribute__((aligned(1024))) uint8_t ring8[kStages8 * 2 * kTile8];
-    __shared__ __attribute__((aligned(1024))) uint8_t wide[2 * 2 * kTile];
-    // direct loads of an fp8 sub-tile: wave w writes rows 8w .. 8w+7 of K and of V,
-    // lane l row 8w + l / 8, 16-byte chunk l % 8, row-major without padding
-    const int r8 = 8 * wave + (lane >> 3), c8 = lane & 7;
-    const uint32_t loff8 = r8 * kD + 16 * c8;
-    auto issue8 = [&](int t, int slot) {
-      const long long row0 = row_base(t);
-      const uint8_t* kb = static_cast<const uint8_t*>(p.k) + row0 * kD;
-      const uint8_t* vb = static_cast<const uint8_t*>(p.v) + row0 * kD;
-      uint32_t o = loff8;
-      if (t == T - 1 && tail < kSub) o = min(r8, tail - 1) * kD + 16 * c8;  // wave-uniform branch
-      const uint32_t kd = lds_addr(ring8) + slot * (2 * kTile8) + 8 * wave_u * kD;
-      lds_load16_s(kb, o, kd);
-      lds_load16_s(vb, o, kd + kTile8);
-    };
-    // widen ring slot `slot` into bf16 buffer `wb`: thread = (row tid / 8, 16 fp8 of
-    // chunk tid % 8), written as logical bf16 chunks 2c and 2c + 1 of that row
-    const int rw = tid >> 3, cw = tid & 7;
-    const int wlo = rw * kRow + 16 * ((2 * cw) ^ swz(rw));
-    const int whi = rw * kRow + 16 * ((2 * cw + 1) ^ swz(rw));
-    auto widen = [&](int slot, int wb) {
-      const uint8_t* src = ring8 + slot * (2 * kTile8) + rw * kD + 16 * cw;
-      uint8_t* dst = wide + wb * (2 * kTile);
-      u32x4 o2[2];
-      fp8x16_to_bf16x16(*reinterpret_cast<const u32x4*>(src), o2);
-      *reinterpret_cast<u32x4*>(dst + wlo) = o2[0];
-      *reinterpret_cast<u32x4*>(dst + whi) = o2[1];
-      fp8x16_to_bf16x16(*reinterpret_cast<const u32x4*>(src + kTile8), o2);
-      *reinterpret_cast<u32x4*>(dst + kTile + wlo) = o2[0];
-      *reinterpret_cast<u32x4*>(dst + kTile + whi) = o2[1];
-    };
-    // While sub-tile t is consumed from bf16 buffer t % 2, sub-tile t+1 is widened
-    // into the other buffer and sub-tiles t+2 .. t+5 are in flight; sub-tile t+5 goes
-    // into ring slot t % 5, whose sub-tile t was widened in the previous phase. Each
-    // wave issues 2 loads per sub-tile, so "own loads of t+1 landed" is vmcnt <= 6;
-    // the barrier then makes every wave's share visible and retires the previous
-    // phase's widening and compute. Sub-tiles past the end re-read the last one.
-    if (T > 0) {
+  // fp8 sub-tiles (64 rows of 128 B for K and for V): wave w writes rows 16w .. 16w+15
+  // of each, lane l row 16w + 8j + l / 8 at chunk position l % 8 with logical chunk
+  // (l % 8) ^ swz8(row); past the chunk's last key the last key's row is read
+  const int rw8 = 16 * wave + (lane >> 3), pw8 = lane & 7;
+  uint32_t loff8[2];
 #pragma unroll
-      for (int s = 0; s < kStages8; ++s) issue8(min(s, T - 1), s);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));
-      __builtin_amdgcn_s_barrier();
-      widen(0, 0);
-      int t = 0, slot_in = 0, slot_next = 1;  // slot_in = t % 5, slot_next = (t + 1) % 5
-      while (true) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
-        __builtin_amdgcn_s_barrier();
-        issue8(min(t + kStages8, T - 1), slot_in);
-        if (t + 1 < T) widen(slot_next, (t + 1) & 1);
-        compute(t, wide + (t & 1) * (2 * kTile));
-        if (++t >= T) break;
-        slot_in = slot_next;
-        slot_next = slot_next == kStages8 - 1 ? 0 : slot_next + 1;
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
+  for (int j = 0; j < 2; ++j) loff8[j] = (rw8 + 8 * j) * kD + 16 * (pw8 ^ swz8(rw8 + 8 * j));
+  auto issue8 = [&](int t, uint8_t* buf) {
+    const long long row0 = row_base(t);
+    const uint8_t* kb = static_cast<const uint8_t*>(p.k) + row0 * kD;
+    const uint8_t* vb = static_cast<const uint8_t*>(p.v) + row0 * kD;
+    uint32_t o0 = loff8[0], o1 = loff8[1];
+    if (t == T - 1 && tail < kSub8) {  // wave-uniform
+      o0 = min(rw8, tail - 1) * kD + 16 * (pw8 ^ swz8(rw8));
+      o1 = min(rw8 + 8, tail - 1) * kD + 16 * (pw8 ^ swz8(rw8 + 8));
     }
+    const uint32_t kd = lds_addr(buf) + 16 * wave_u * kD, vd = kd + kTile8;
+    lds_load16_s(kb, o0, kd);
+    lds_load16_s(vb, o0, vd);
+    lds_load16_s(kb, o1, kd + 8 * kD);
+    lds_load16_s(vb, o1, vd + 8 * kD);
+  };
+  // fp8 fragment offsets. K (A of S^T = K Q^T, 32x32x64): lane (n32, h32) reads row
+  // 32 tt + n32, dims 64 kq + 32 h32 .. +31 = logical chunks 4 kq + 2 h32 (+1). V^T (A of
+  // O^T = V^T P^T) by ds_read_b64_tr_b8: in each 16-lane group g, lane pairs (2b, 2b+1)
+  // address token row T0 + b at dims D0 and D0 + 8, so lane j receives dim D0 + j of the
+  // 8 tokens T0 .. T0+7; read i covers tokens 16 i + 8 h .. +7 (the byte order P takes
+  // below), D0 = 32 dt + 16 (g & 1).
+  const int gq = lane >> 4, lq = lane & 15;
+  auto compute8 = [&](int t, const uint8_t* buf) {
+    if (upage[t / kPerPage] < 0) return;  // wave-uniform: a page outside the pool adds nothing
+    const uint8_t* ks = buf;
+    const uint8_t* vs = buf + kTile8;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int r = 32 * tt + n32;
+      const uint8_t* krow = ks + r * kD;
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int c = 4 * kq + 2 * h32;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + 16 * (c ^ swz8(r)));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + 16 * ((c + 1) ^ swz8(r)));
+        sacc[tt] = mfma_f8(cat8(lo, hi), qf[kq], kq == 0 ? f32x16{} : sacc[tt]);
+      }
+    }
+    // lane (n32, h32) holds tokens 32 tt + 8 (i / 4) + 4 h32 + i % 4 of column n32
+    if (kSub8 * t + kSub8 > wmin) {  // wave-uniform: some column's limit falls in here
+      const int vis = lim - kSub8 * t;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * tt + 8 * (i >> 2) + 4 * h32 + (i & 3) >= vis) sacc[tt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[tt][i], sacc[tt][i + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any((mx - m_ref) * c2m > 8.f)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
+      l_run *= alpha;
+      if (TEMP) lt_run *= m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2t);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) om[dt] *= alpha;
+      m_ref = m_new;
+    }
+    const float nmc = -(m_ref == -INFINITY ? 0.f : m_ref) * c2;
+    // P as e4m3: word q = 4 tt + i / 4 holds tokens 8 q + 4 h32 .. +3
+    uint32_t pq[8];
+    float ps = 0.f, pst = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = fast_exp2(fmaf(sacc[tt][4 * q4 + e], c2, nmc));
+          ps += pv[e];
+          if (TEMP) pst += fast_exp2(fmaf(sacc[tt][4 * q4 + e], c2t, nmc * p.inv_temp));
+        }
+        pq[4 * tt + q4] = e4m3x4(pv[0], pv[1], pv[2], pv[3]);
+      }
+    l_run += ps;
+    if (TEMP) lt_run += pst;
+    // swap word 2i + 1 of the low half-wave with word 2i of the high one: lane h then
+    // holds tokens 16 i + 8 h .. +7 in words 2i, 2i+1 (the B fragment's byte order)
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(pq[2 * i2], pq[2 * i2 + 1], false, false);
+      pq[2 * i2] = sw[0];
+      pq[2 * i2 + 1] = sw[1];
+    }
+    const i32x8 pb = {(int)pq[0], (int)pq[1], (int)pq[2], (int)pq[3],
+                      (int)pq[4], (int)pq[5], (int)pq[6], (int)pq[7]};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int chunk = 2 * dt + (gq & 1);
+      i32x8 a;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int row = 16 * i2 + 8 * (gq >> 1) + (lq >> 1);
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vs + row * kD +
+                                                       16 * (chunk ^ swz8(row)) + 8 * (lq & 1)));
+        a[2 * i2] = v[0];
+        a[2 * i2 + 1] = v[1];
+      }
+      om[dt] = mfma_f8(a, pb, om[dt]);
+    }
+  };
+
+  // ring of four stages (K sub-tile at offset 0, V sub-tile at kTile (bf16) or kTile8
+  // (fp8); 16 KiB either way); separate arrays keep the stage buffers distinct objects
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTile], st1[2 * kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * kTile], st3[2 * kTile];
+  auto issue_t = [&](int t, uint8_t* buf) {
+    if constexpr (FP8) issue8(t, buf); else issue(t, buf);
+  };
+  auto compute_t = [&](int t, const uint8_t* buf) {
+    if constexpr (FP8) compute8(t, buf); else compute(t, buf);
+  };
+  // Ring of four stages: while stage t is consumed, stages t+1 and t+2 are in
+  // flight and stage t+3 goes into the buffer that t-1 used (free once every wave
+  // has passed this phase's barrier). Each wave issues 4 loads per stage, so "own
+  // loads of stage t landed" is vmcnt <= 8; the barrier then makes every wave's
+  // share visible. Stages past the end re-read the last sub-tile (in bounds) so
+  // that every phase issues the same number of loads.
+  if (T > 0) {
+    issue_t(0, st0);
+    issue_t(min(1, T - 1), st1);
+    issue_t(min(2, T - 1), st2);
+    int t = 0;
+#define MSA_DENSE_PHASE(cur, nxt)                              \
+    {                                                          \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));         \
+      __builtin_amdgcn_s_barrier();                            \
+      issue_t(min(t + 3, T - 1), nxt);                         \
+      compute_t(t, cur);                                       \
+      if (++t >= T) break;                                     \
+    }
+    while (true) {
+      MSA_DENSE_PHASE(st0, st3)
+      MSA_DENSE_PHASE(st1, st0)
+      MSA_DENSE_PHASE(st2, st1)
+      MSA_DENSE_PHASE(st3, st2)
+    }
+#undef MSA_DENSE_PHASE
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // no load outlives the loop
   }
 
   // epilogue: lane (n32, h32) holds dims 32 dt + 8 (i / 4) + 4 h32 + i % 4 of its column
