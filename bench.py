@@ -147,6 +147,9 @@ class Case:
             self.inp = wl.with_fp8_kv(self.inp)
             if w.paged and w.dense:  # the pages' fp8 decode: Q fp8 as well
                 self.inp["q"] = wl.bf16_bits_to_fp8(self.inp["q"])
+        # the fp8 dense decode multiplies on the fp8 matrix cores; every other fp8 path
+        # widens the cache to bf16 first
+        self.compute_fp8 = kv_dtype == "fp8" and w.paged and w.dense
         log(f"[bench] {key}: inputs generated in {time.time() - t0:.1f}s")
         dev = lambda x: (torch.from_numpy(x).view(torch.bfloat16) if x.dtype == np.uint16
                          else torch.from_numpy(x)).to("cuda")
@@ -476,7 +479,7 @@ def main() -> int:
     line = {
         "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8" if case.compute_fp8 else "bf16", "data": "synthetic",
         "config": ({"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq,
                     "Hkv": w.Hkv, "D": w.D, "topk": w.topk, "blk_kv": w.blk,
                     "causal": w.causal, "path": case.path_name, "splits": case.splits,
