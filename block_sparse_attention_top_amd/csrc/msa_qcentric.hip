@@ -68,6 +68,18 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   const int g = lane >> 4;  // 16-lane group
 
   long long item = blockIdx.x;
+  if (PAGED) {
+    // Workgroups are dealt round-robin over the 8 XCDs; this permutation puts the
+    // Sq x splits items of one (b, hkv) on one XCD, so the blocks its query rows
+    // share (the diagonal one at least) are fetched into a single L2. Groups past the
+    // last multiple of 8 keep the identity order.
+    const long long S = static_cast<long long>(p.Sq) * p.splits;
+    const long long full = (static_cast<long long>(p.B) * p.Hkv / 8) * 8 * S;
+    if (item < full) {
+      const long long k = item / 8;
+      item = ((item % 8) + 8 * (k / S)) * S + k % S;
+    }
+  }
   const int sp = static_cast<int>(item % p.splits);
   item /= p.splits;
   // the row's sequence b: its query position and count, its first key and key count
