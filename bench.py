@@ -429,7 +429,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sparse forward has no multi-GPU path in this build)", file=sys.stderr)
+              "(the sparse forward runs on one GPU; sharding is described, not built)", file=sys.stderr)
         return 2
 
     import torch
