@@ -186,3 +186,27 @@ def test_dense_equals_sparse_with_every_block():
     torch.cuda.synchronize()
     compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), bf16_dev_to_f64(o2),
             lse2.cpu().numpy().astype(np.float64), "dense-vs-sparse")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_decode_bad_pages_and_nan_tails(causal):
+    """Page ids outside the pool drop their keys (as in the oracle); keys at or past
+    seqused_k never matter, even when they hold NaN."""
+    lens = [1000, 700, 257]
+    w, inp = dense_inputs(99, 3, 1024, lens)
+    pt = inp["page_table"].copy()
+    pt[0, 2] = -1
+    num_pages = inp["k_pool"].shape[0]
+    pt[1, 1] = num_pages + 5
+    inp["page_table"] = pt
+    for b, n in enumerate(lens):
+        pg = pt[b, (n - 1) // 128]
+        if 0 <= pg < num_pages and n % 128:
+            inp["k_pool"][pg, :, n % 128:] = 0x7FC0  # bf16 NaN
+            inp["v_pool"][pg, :, n % 128:] = 0x7FC0
+    say(f"[dense] bad pages, NaN tails, causal={causal}")
+    p, (o, lse) = run_dense(inp, w, 1024, causal=causal)
+    o_ref, lse_ref = oracle_dense(inp, w, causal=causal)
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
+            lse_ref.transpose(0, 2, 1), "dense-bad-pages")
+    assert torch.isfinite(o.float()).all()

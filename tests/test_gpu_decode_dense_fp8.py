@@ -170,3 +170,24 @@ def test_fp8_decode_refusals():
     qb = torch.zeros(inp["q"].shape, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(TypeError):  # fp8 pools need an fp8 query
         msa.msa_paged_decode_run(p, qb, fp8_dev(inp["k_pool"]), fp8_dev(inp["v_pool"]), pt, seq)
+
+
+def test_fp8_decode_bad_pages_and_nan_tails():
+    """Page ids outside the pool drop their keys (as in the oracle); keys at or past
+    seqused_k never matter, even when their bytes are the e4m3fn NaN code."""
+    lens = [1000, 700, 257]
+    w, inp = fp8_inputs(120, 3, 1024, lens)
+    pt = inp["page_table"].copy()
+    pt[0, 2] = -1
+    num_pages = inp["k_pool"].shape[0]
+    pt[1, 1] = num_pages + 5
+    inp["page_table"] = pt
+    for b, n in enumerate(lens):  # NaN in every unused row of the last page
+        pg = pt[b, (n - 1) // 128]
+        if 0 <= pg < num_pages and n % 128:
+            inp["k_pool"][pg, :, n % 128:] = 0x7F
+            inp["v_pool"][pg, :, n % 128:] = 0x7F
+    say("[fp8 dense] bad pages, NaN tails")
+    o, lse = run_fp8(inp, w, 1024)
+    check(*as_rows(o, lse), *oracle_rows(inp), "fp8-bad-pages")
+    assert torch.isfinite(o.float()).all()
