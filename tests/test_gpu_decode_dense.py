@@ -210,3 +210,16 @@ def test_dense_decode_bad_pages_and_nan_tails(causal):
     compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
             lse_ref.transpose(0, 2, 1), "dense-bad-pages")
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("sq", [16, 12])
+def test_dense_decode_wide_columns(sq):
+    """More than 128 (query, head) columns per KV head (16 heads x 12 or 16 queries) run
+    through the union kernel's dense mode (up to 4 queries per wave)."""
+    lens = [2000, 300, 1024]
+    w, inp = dense_inputs(100 + sq, 3, 2048, lens, sq=sq)
+    say(f"[dense] wide columns Sq={sq}")
+    p, (o, lse) = run_dense(inp, w, 2048, max_grid_size=48)
+    o_ref, lse_ref = oracle_dense(inp, w)
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
+            lse_ref.transpose(0, 2, 1), f"dense-wide-{sq}")
