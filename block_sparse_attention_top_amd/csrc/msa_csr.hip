@@ -230,6 +230,88 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
   }
 }
 
+// The same stable scatter with four waves per (tile, KV head): wave w takes the
+// w-th quarter of the tile's queries. The waves first histogram their quarters
+// into their own LDS counters; an exclusive prefix over the waves then gives each
+// wave, per row, the position after the entries of the lower quarters; each wave
+// finally runs the ballot-ranked scatter above on its quarter. Same output bits,
+// four times the waves. LDS: 4 * nrows ints.
+template <bool VARLEN>
+__global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q, int ntiles,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ q_idx,
+                                                           int32_t* __restrict__ slot) {
+  extern __shared__ int lds[];
+  constexpr int kPer = 16;  // entries per lane per round
+  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrows = a.nrows;
+  const long long cap = a.nq * a.topk;
+  const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
+  const long long g0 = static_cast<long long>(tile) * tile_q;
+  const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
+  const long long sub = (g1 - g0 + 3) / 4;
+  const long long w0 = std::min(g1, g0 + wave * sub), w1 = std::min(g1, w0 + sub);
+  int* cursor = lds + wave * nrows;
+  for (int r = tid; r < 4 * nrows; r += 256) lds[r] = 0;
+  __syncthreads();
+  for (long long e = w0 * a.topk + lane; e < w1 * a.topk; e += 64) {
+    const int row = entry_row<VARLEN>(a, hkv, e);
+    if (row >= 0) atomicAdd(&cursor[row], 1);
+  }
+  __syncthreads();
+  const int base_h = offsets[seg];
+  for (int r = tid; r < nrows; r += 256) {
+    int run = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = lds[w * nrows + r];
+      lds[w * nrows + r] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const long long e_end = w1 * a.topk;
+  int32_t* qi = q_idx + hkv * cap;
+  int32_t* sl = slot ? slot + hkv * cap : nullptr;
+  for (long long rb = w0 * a.topk; rb < e_end; rb += 64 * kPer) {
+    int rows[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long e = rb + 64 * k + lane;
+      rows[k] = e < e_end ? entry_row<VARLEN>(a, hkv, e) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const long long e = rb + 64 * k + lane;
+      const int row = rows[k];
+      unsigned long long pending = __ballot(row >= 0);
+      int rank = 0, cnt = 0;
+      while (pending) {
+        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+        const int lrow = __shfl(row, leader);
+        const unsigned long long peers = __ballot(row == lrow);
+        if (row == lrow) {
+          rank = __popcll(peers & __lanemask_lt());
+          cnt = __popcll(peers);
+        }
+        pending &= ~peers;
+      }
+      // this wave's cursors only: its lanes read before the last-ranked lane of a row
+      // writes (one wave, LDS accesses in program order)
+      int pos = 0;
+      if (row >= 0) pos = cursor[row] + rank;
+      __builtin_amdgcn_wave_barrier();
+      if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
+      if (row >= 0) {
+        qi[pos] = static_cast<int32_t>(e / a.topk);
+        if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
 template <bool VARLEN>
@@ -341,7 +423,10 @@ hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t*
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
-  if (ordered)
+  if (ordered && 4 * lds <= 64 * 1024)  // within the default dynamic LDS limit
+    hipLaunchKernelGGL(csr_scatter4_kernel<VARLEN>, grid, dim3(256), 4 * lds, stream, a,
+                       plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  else if (ordered)
     hipLaunchKernelGGL(csr_scatter_kernel<VARLEN>, grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
   else

@@ -171,6 +171,24 @@ def test_csr_bit_exact_patterns_with_holes(mode):
     assert_csr_equal(q2k, 64, f"mode{mode}-holes")
 
 
+@pytest.mark.parametrize("key", ["c2", "c4b"])
+def test_csr_bit_exact_full_size(key):
+    """The public (ordered) CSR at the full workload sizes: c4b has 3072 rows and 6.3M
+    entries, c2 4 KV heads x 64 rows."""
+    w = wl.WORKLOADS[key]
+    q2k = wl.q2k_table(w.seed, w.mode, w.B, w.Hkv, w.Sq, w.Skv, w.blk, w.topk)
+    assert_csr_equal(q2k, w.Skv // w.blk, f"{key} full size")
+
+
+def test_csr_bit_exact_with_duplicate_ids():
+    """A repeated id in a row gives two entries of that row, in slot order (the
+    definition's (query, slot) order); the scatter ranks equal rows by lane."""
+    q2k = wl.q2k_table(23, wl.MODE_PERM, 1, 2, 2000, 4096, 128, 16)
+    q2k[..., 5] = q2k[..., 2]
+    q2k[..., 11] = q2k[..., 2]
+    assert_csr_equal(q2k, 32, "duplicates")
+
+
 def test_csr_deterministic_and_prebuilt_csr_used():
     w, inp = contiguous_case(1, 700, 2048, 2, 8, 8, True, wl.MODE_CAUSAL, seed=4)
     import block_sparse_attention_top_amd as msa
