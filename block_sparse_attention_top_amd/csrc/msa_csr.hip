@@ -149,6 +149,24 @@ __device__ __forceinline__ int entry_row(const CsrSrc& a, int hkv, long long e) 
   }
 }
 
+// Stable rank of each lane among the lower lanes holding the same row, and the
+// number of lanes holding it (row < 0: not counted). One pass per distinct row:
+// the lowest pending lane's row is read with v_readlane (no LDS round trip) and its
+// peers found by one ballot.
+__device__ __forceinline__ void rank_in_batch(int row, int& rank, int& cnt) {
+  unsigned long long pending = __ballot(row >= 0);
+  const unsigned long long below = __lanemask_lt();
+  while (pending) {
+    const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+    const int lrow = __builtin_amdgcn_readlane(row, leader);
+    const unsigned long long peers = __ballot(row == lrow);
+    const bool mine = row == lrow;
+    rank = mine ? __popcll(peers & below) : rank;
+    cnt = mine ? __popcll(peers) : cnt;
+    pending &= ~peers;
+  }
+}
+
 template <bool VARLEN>
 __global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
                                                         int32_t* __restrict__ counts) {
@@ -205,18 +223,8 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
       const int row = rows[k];
-      unsigned long long pending = __ballot(row >= 0);
       int rank = 0, cnt = 0;
-      while (pending) {
-        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-        const int lrow = __shfl(row, leader);
-        const unsigned long long peers = __ballot(row == lrow);
-        if (row == lrow) {
-          rank = __popcll(peers & __lanemask_lt());
-          cnt = __popcll(peers);
-        }
-        pending &= ~peers;
-      }
+      rank_in_batch(row, rank, cnt);
       int pos = 0;
       if (row >= 0) pos = cursor[row] + rank;
       __syncthreads();
@@ -285,18 +293,8 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
       const int row = rows[k];
-      unsigned long long pending = __ballot(row >= 0);
       int rank = 0, cnt = 0;
-      while (pending) {
-        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-        const int lrow = __shfl(row, leader);
-        const unsigned long long peers = __ballot(row == lrow);
-        if (row == lrow) {
-          rank = __popcll(peers & __lanemask_lt());
-          cnt = __popcll(peers);
-        }
-        pending &= ~peers;
-      }
+      rank_in_batch(row, rank, cnt);
       // this wave's cursors only: its lanes read before the last-ranked lane of a row
       // writes (one wave, LDS accesses in program order)
       int pos = 0;
