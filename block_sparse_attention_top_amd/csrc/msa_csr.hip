@@ -131,10 +131,21 @@ struct CsrSrc {
   long long nq;        // B * Sq, or total_q
 };
 
+// n / d for an entry or query index. With I32 (every entry index of the build below
+// 2^31) it is the 32-bit unsigned division, a short instruction sequence; the 64-bit
+// one is a long software routine and dominated the count and scatter kernels.
+template <bool I32>
+__device__ __forceinline__ long long idx_div(long long n, int d) {
+  if constexpr (I32)
+    return static_cast<long long>(static_cast<uint32_t>(n) / static_cast<uint32_t>(d));
+  else
+    return n / d;
+}
+
 // CSR row of entry e = (query, slot) of KV head hkv, or -1 when its slot is unused
-template <bool VARLEN>
+template <bool VARLEN, bool I32>
 __device__ __forceinline__ int entry_row(const CsrSrc& a, int hkv, long long e) {
-  const long long gq = e / a.topk;
+  const long long gq = idx_div<I32>(e, a.topk);
   if (VARLEN) {
     const int s = a.q2k[static_cast<long long>(hkv) * a.nq * a.topk + e];
     const int2 qr = a.q_rows[gq];
@@ -143,7 +154,8 @@ __device__ __forceinline__ int entry_row(const CsrSrc& a, int hkv, long long e) 
     return r < a.nrows ? static_cast<int>(r) : -1;
   } else {
     const int t = static_cast<int>(e - gq * a.topk);
-    const int b = static_cast<int>(gq / a.Sq), qpos = static_cast<int>(gq - static_cast<long long>(b) * a.Sq);
+    const int b = static_cast<int>(idx_div<I32>(gq, a.Sq));
+    const int qpos = static_cast<int>(gq - static_cast<long long>(b) * a.Sq);
     const int s = a.q2k[((static_cast<long long>(b) * a.Hkv + hkv) * a.Sq + qpos) * a.topk + t];
     return (s >= 0 && s < a.nblk) ? b * a.nblk + s : -1;
   }
@@ -167,19 +179,50 @@ __device__ __forceinline__ void rank_in_batch(int row, int& rank, int& cnt) {
   }
 }
 
-template <bool VARLEN>
+constexpr int kCsrBatch = 8;  // entries per thread whose index loads are in flight together
+
+// Query tile of workgroup x. Workgroups are dealt round-robin over the 8 XCDs, and
+// consecutive tiles write adjacent counts and adjacent runs of a row's entries, so
+// the tiles are permuted to run in groups of ntiles / 8 consecutive tiles per XCD:
+// a cache line that several tiles fill is then merged in one XCD's L2 instead of
+// being written back in pieces from several. The last ntiles % 8 keep their place.
+__device__ __forceinline__ int csr_tile_of(int x, int ntiles) {
+  const int per = ntiles >> 3;
+  return x < 8 * per ? (x & 7) * per + (x >> 3) : x;
+}
+
+// rows[k] = CSR row of entry e0 + stride k, or -1 from e_end on (e0 < e_end). The
+// index is clamped into range so that every load is unconditional and all N are in
+// flight together: a load under a branch is waited for where the branch joins.
+template <bool VARLEN, bool I32, int N>
+__device__ __forceinline__ void load_rows(const CsrSrc& a, int hkv, long long e0, int stride,
+                                          long long e_end, int (&rows)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const long long e = e0 + static_cast<long long>(stride) * k;
+    const int r = entry_row<VARLEN, I32>(a, hkv, e < e_end ? e : e_end - 1);
+    rows[k] = e < e_end ? r : -1;
+  }
+}
+
+template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
                                                         int32_t* __restrict__ counts) {
   extern __shared__ int cnt[];
-  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int nrows = a.nrows;
   for (int r = threadIdx.x; r < nrows; r += blockDim.x) cnt[r] = 0;
   __syncthreads();
   const long long g0 = static_cast<long long>(tile) * tile_q;
   const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
-  for (long long e = g0 * a.topk + threadIdx.x; e < g1 * a.topk; e += blockDim.x) {
-    const int row = entry_row<VARLEN>(a, hkv, e);
-    if (row >= 0) atomicAdd(&cnt[row], 1);
+  const long long e1 = g1 * a.topk;
+  // kCsrBatch entries per thread per round, their index loads issued together
+  for (long long rb = g0 * a.topk; rb < e1; rb += 256 * kCsrBatch) {
+    int rows[kCsrBatch];
+    load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, 256, e1, rows);
+#pragma unroll
+    for (int k = 0; k < kCsrBatch; ++k)
+      if (rows[k] >= 0) atomicAdd(&cnt[rows[k]], 1);
   }
   __syncthreads();
   for (int r = threadIdx.x; r < nrows; r += blockDim.x)
@@ -191,14 +234,14 @@ __global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, in
 // batches of 64 consecutive entries; a lane's rank among the lower lanes holding
 // the same row comes from ballots (one pass per distinct row in the batch), so
 // entries of a row keep ascending (query, slot) order.
-template <bool VARLEN>
+template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, int ntiles,
                                                          const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ q_idx,
                                                          int32_t* __restrict__ slot) {
   extern __shared__ int cursor[];
   constexpr int kPer = 16;  // entries per lane per round
-  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int lane = threadIdx.x;
   const int nrows = a.nrows;
   const long long cap = a.nq * a.topk;
@@ -214,11 +257,7 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
   for (long long rb = g0 * a.topk; rb < e_end; rb += 64 * kPer) {
     int rows[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const long long e = rb + 64 * k + lane;
-      rows[k] = e < e_end ? entry_row<VARLEN>(a, hkv, e) : -1;
-    }
+    load_rows<VARLEN, I32>(a, hkv, rb + lane, 64, e_end, rows);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
@@ -230,8 +269,9 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
       __syncthreads();
       if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
       if (row >= 0) {
-        qi[pos] = static_cast<int32_t>(e / a.topk);
-        if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
+        const long long q = idx_div<I32>(e, a.topk);
+        qi[pos] = static_cast<int32_t>(q);
+        if (sl) sl[pos] = static_cast<int32_t>(e - q * a.topk);
       }
       __syncthreads();
     }
@@ -244,14 +284,14 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
 // wave, per row, the position after the entries of the lower quarters; each wave
 // finally runs the ballot-ranked scatter above on its quarter. Same output bits,
 // four times the waves. LDS: 4 * nrows ints.
-template <bool VARLEN>
+template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q, int ntiles,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ q_idx,
                                                            int32_t* __restrict__ slot) {
   extern __shared__ int lds[];
   constexpr int kPer = 16;  // entries per lane per round
-  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nrows = a.nrows;
   const long long cap = a.nq * a.topk;
@@ -263,9 +303,12 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
   int* cursor = lds + wave * nrows;
   for (int r = tid; r < 4 * nrows; r += 256) lds[r] = 0;
   __syncthreads();
-  for (long long e = w0 * a.topk + lane; e < w1 * a.topk; e += 64) {
-    const int row = entry_row<VARLEN>(a, hkv, e);
-    if (row >= 0) atomicAdd(&cursor[row], 1);
+  for (long long rb = w0 * a.topk; rb < w1 * a.topk; rb += 64 * kCsrBatch) {
+    int rows[kCsrBatch];
+    load_rows<VARLEN, I32>(a, hkv, rb + lane, 64, w1 * a.topk, rows);
+#pragma unroll
+    for (int k = 0; k < kCsrBatch; ++k)
+      if (rows[k] >= 0) atomicAdd(&cursor[rows[k]], 1);
   }
   __syncthreads();
   const int base_h = offsets[seg];
@@ -284,11 +327,7 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
   for (long long rb = w0 * a.topk; rb < e_end; rb += 64 * kPer) {
     int rows[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const long long e = rb + 64 * k + lane;
-      rows[k] = e < e_end ? entry_row<VARLEN>(a, hkv, e) : -1;
-    }
+    load_rows<VARLEN, I32>(a, hkv, rb + lane, 64, e_end, rows);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
@@ -302,8 +341,9 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
       __builtin_amdgcn_wave_barrier();
       if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
       if (row >= 0) {
-        qi[pos] = static_cast<int32_t>(e / a.topk);
-        if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
+        const long long q = idx_div<I32>(e, a.topk);
+        qi[pos] = static_cast<int32_t>(q);
+        if (sl) sl[pos] = static_cast<int32_t>(e - q * a.topk);
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -312,12 +352,13 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
 
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
-template <bool VARLEN>
+// LDS: nrows + 1 cursors (the last one absorbs the unused slots).
+template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ q_idx, int32_t* __restrict__ slot) {
   extern __shared__ int cursor[];
-  const int tile = blockIdx.x, hkv = blockIdx.y;
+  const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int nrows = a.nrows;
   const long long cap = a.nq * a.topk;
   const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
@@ -329,12 +370,22 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
   const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
   int32_t* qi = q_idx + hkv * cap;
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
-  for (long long e = g0 * a.topk + threadIdx.x; e < g1 * a.topk; e += blockDim.x) {
-    const int row = entry_row<VARLEN>(a, hkv, e);
-    if (row < 0) continue;
-    const int pos = atomicAdd(&cursor[row], 1);
-    qi[pos] = static_cast<int32_t>(e / a.topk);
-    if (sl) sl[pos] = static_cast<int32_t>(e % a.topk);
+  const long long e1 = g1 * a.topk;
+  for (long long rb = g0 * a.topk; rb < e1; rb += 256 * kCsrBatch) {
+    int rows[kCsrBatch], pos[kCsrBatch];
+    load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, 256, e1, rows);
+    // every atomic is issued before any result is used; an unused slot counts on
+    // the spare cursor past the last row
+#pragma unroll
+    for (int k = 0; k < kCsrBatch; ++k) pos[k] = atomicAdd(&cursor[rows[k] >= 0 ? rows[k] : nrows], 1);
+#pragma unroll
+    for (int k = 0; k < kCsrBatch; ++k) {
+      if (rows[k] < 0) continue;
+      const long long e = rb + 256 * k + threadIdx.x;
+      const long long q = idx_div<I32>(e, a.topk);
+      qi[pos[k]] = static_cast<int32_t>(q);
+      if (sl) sl[pos[k]] = static_cast<int32_t>(e - q * a.topk);
+    }
   }
 }
 
@@ -401,12 +452,30 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows) {
 
 namespace {
 
-template <bool VARLEN>
-hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                     hipStream_t stream, bool ordered) {
+// Tiles of the order-free build: long enough that a (row, tile) segment averages
+// at least 8 entries, a 32-byte run of q_idx and of slot, so that the scatter's
+// 4-byte stores fill whole sectors instead of each landing in a line of its own
+// (with 3072 rows and ~64-query tiles a segment holds one or two entries). Never
+// more tiles, hence never more counts, than the ordered plan, whose workspace size
+// is the one published.
+CsrPlan csr_plan_unordered(int Hkv, long long nq, int topk, int nrows) {
+  CsrPlan plan = csr_plan(1, Hkv, static_cast<int>(nq), topk, nrows);
+  const long long want = std::min<long long>(nq, (8LL * nrows + topk - 1) / topk);
+  if (want > plan.tile_q) {
+    plan.tile_q = static_cast<int>(want);
+    plan.ntiles = static_cast<int>((nq + want - 1) / want);
+    plan.counts = static_cast<long long>(Hkv) * nrows * plan.ntiles;
+  }
+  return plan;
+}
+
+template <bool VARLEN, bool I32>
+hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
+                          void* ws, hipStream_t stream, bool ordered) {
   const int nrows = a.nrows;
   // the plan depends on the query count and the rows only: B * Sq == nq
-  const CsrPlan plan = csr_plan(1, a.Hkv, static_cast<int>(a.nq), a.topk, nrows);
+  const CsrPlan plan = ordered ? csr_plan(1, a.Hkv, static_cast<int>(a.nq), a.topk, nrows)
+                               : csr_plan_unordered(a.Hkv, a.nq, a.topk, nrows);
   char* base = static_cast<char*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(base);
   base += align256(plan.counts * 4);
@@ -415,25 +484,34 @@ hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t*
   int32_t* tmp = reinterpret_cast<int32_t*>(base);
   const size_t lds = static_cast<size_t>(nrows) * sizeof(int);
   const dim3 grid(plan.ntiles, a.Hkv);
-  hipLaunchKernelGGL(csr_count_kernel<VARLEN>, grid, dim3(256), lds, stream, a, plan.tile_q,
+  hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32>), grid, dim3(256), lds, stream, a, plan.tile_q,
                      plan.ntiles, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
   if (ordered && 4 * lds <= 64 * 1024)  // within the default dynamic LDS limit
-    hipLaunchKernelGGL(csr_scatter4_kernel<VARLEN>, grid, dim3(256), 4 * lds, stream, a,
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32>), grid, dim3(256), 4 * lds, stream, a,
                        plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   else if (ordered)
-    hipLaunchKernelGGL(csr_scatter_kernel<VARLEN>, grid, dim3(64), lds, stream, a, plan.tile_q,
+    hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
   else
-    hipLaunchKernelGGL(csr_scatter_unordered_kernel<VARLEN>, grid, dim3(256), lds, stream, a,
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32>), grid, dim3(256),
+                       lds + sizeof(int), stream, a,
                        plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
   hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
                      offsets, a.Hkv, nrows, plan.ntiles, row_ptr);
   return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
+                     hipStream_t stream, bool ordered) {
+  if (a.nq * a.topk < (1LL << 31))
+    return build_csr_impl<VARLEN, true>(a, row_ptr, q_idx, slot, ws, stream, ordered);
+  return build_csr_impl<VARLEN, false>(a, row_ptr, q_idx, slot, ws, stream, ordered);
 }
 
 }  // namespace
