@@ -37,6 +37,7 @@
 // per lane column (two 64-token halves, online), O^T = V^T P^T (V fragments by
 // the transposing ds_read_b64_tr_b16).
 #include "msa_internal.hpp"
+#include "msa_lds.hpp"
 
 #include <math.h>
 
@@ -159,10 +160,39 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
       R.q[kq] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * kq));
   };
 
+  // A step's partial is stored at the start of the wave's next step, ahead of that
+  // step's Q loads. Vector memory loads and stores share one in-order counter on
+  // gfx950 (vmcnt), so waiting for the Q rows never waits for stores issued after them.
+  struct Pending {
+    u32x4 v[8];          // 16-byte runs of the unnormalised partial, in store order
+    uint16_t* ob;        // this lane's first 16-byte run
+    long long prow;      // (query, slot, head) row of the block LSEs
+    float lse_b, mnat, lse_t;
+    bool ok;
+  };
+  Pending pend;
+  pend.ok = false;
+  auto flush = [&](const Pending& pd) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      // written once, read once by the combine: non-temporal
+      __builtin_nontemporal_store(pd.v[k], reinterpret_cast<u32x4*>(pd.ob + (2 * k + h) * (QPK * 8)));
+    if (h == 0) {
+      p.lse_part[pd.prow] = make_float2(pd.lse_b, pd.mnat);
+      if (TEMP) p.lse_t_part[pd.prow] = pd.lse_t;
+    }
+  };
+
   Rows rc, rn;
   int step = wave;
   if (step < nsteps) fetch(step, rc);
   for (; step < nsteps; step += 4) {
+    // Every load and store still in flight here was issued a whole step ago. Waiting
+    // for all of them explicitly (vmcnt(0), lgkmcnt(0)) leaves the compiler's wait-count
+    // pass with nothing outstanding, so the conditional stores and Q loads below cannot
+    // make it wait for the loads just issued before the first product.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    if (pend.ok) flush(pend);
     if (step + 4 < nsteps) fetch(step + 4, rn);
     // The tile offsets are made opaque per step so that the K fragments are
     // re-read from LDS each step instead of being held in registers.
@@ -277,35 +307,31 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
           ow[dt][2 * pp][w2] = sw[0];
           ow[dt][2 * pp + 1][w2] = sw[1];
         }
-    if (rc.ok) {
-      // Partial block of (query, slot, KV head): [dim chunk c][head][8 dims] with
-      // c = dims / 8, so one store instruction writes QPK * 32 contiguous bytes per query.
+    // Partial block of (query, slot, KV head): [dim chunk c][head][8 dims] with
+    // c = dims / 8, so one store instruction writes QPK * 32 contiguous bytes per query.
+    pend.ok = rc.ok;
+    {
       const long long pblk = ((static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hkv + hkv);
-      uint16_t* ob = p.o_part + pblk * (QPK * kD) + head_i * 8;
+      pend.ob = p.o_part + pblk * (QPK * kD) + head_i * 8;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const u32x4 v4 = {ow[dt][2 * pp][0], ow[dt][2 * pp][1], ow[dt][2 * pp + 1][0],
-                            ow[dt][2 * pp + 1][1]};
-          // written once, read once by the combine: non-temporal
-          __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(ob + (4 * dt + 2 * pp + h) * (QPK * 8)));
-        }
-      if (h == 0) {
-        const long long prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;
-        // both LSEs as one explicit fma of the same shape, so that T = 1 gives equal bits
-        const float mr = m_ref == -INFINITY ? 0.f : m_ref;
-        const float mnat = mr * c2 * kLn2;
-        const float lse_b = ps > 0.f ? fmaf(fast_log2(ps), kLn2, mnat) : -INFINITY;
-        p.lse_part[prow] = make_float2(lse_b, mnat);
-        if (TEMP) {
-          const float mnat_t = mr * c2t * kLn2;
-          p.lse_t_part[prow] = ps > 0.f ? fmaf(fast_log2(pst), kLn2, mnat_t) : -INFINITY;
-        }
+        for (int pp = 0; pp < 2; ++pp)
+          pend.v[2 * dt + pp] = u32x4{ow[dt][2 * pp][0], ow[dt][2 * pp][1], ow[dt][2 * pp + 1][0],
+                                      ow[dt][2 * pp + 1][1]};
+      pend.prow = (static_cast<long long>(rc.gq) * p.topk + rc.t) * p.Hq + head;
+      // both LSEs as one explicit fma of the same shape, so that T = 1 gives equal bits
+      const float mr = m_ref == -INFINITY ? 0.f : m_ref;
+      pend.mnat = mr * c2 * kLn2;
+      pend.lse_b = ps > 0.f ? fmaf(fast_log2(ps), kLn2, pend.mnat) : -INFINITY;
+      if (TEMP) {
+        const float mnat_t = mr * c2t * kLn2;
+        pend.lse_t = ps > 0.f ? fmaf(fast_log2(pst), kLn2, mnat_t) : -INFINITY;
       }
     }
     rc = rn;
   }
+  if (pend.ok) flush(pend);
 }
 
 // items[c] = (hkv, row, first entry, entry count) for every chunk c of every row
