@@ -108,8 +108,8 @@ int check_temperature(float scale, const float* lse_t) {
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
 struct KvLayout {
-  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, o_part, lse_part,
-      lse_t_part, total;
+  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, items_by_q,
+      sort_counts, o_part, lse_part, lse_t_part, total;
   long long max_items;
 };
 
@@ -130,6 +130,8 @@ KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
   // sum over rows of ceil(len / chunk) <= nnz / chunk + rows
   L.max_items = static_cast<long long>(Hkv) * (cap / chunk_entries_for(Hq / Hkv) + nrows + 1);
   L.items = off; off += align256(L.max_items * 16);
+  L.items_by_q = off; off += align256(L.max_items * 16);
+  L.sort_counts = off; off += align256(256 * 4);
   L.o_part = off; off += align256(static_cast<size_t>(cap) * Hq * kD * 2);
   L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 8);
   L.lse_t_part = off; off += align256(static_cast<size_t>(cap) * Hq * 4);
@@ -197,6 +199,10 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* row_ptr = csr_row_ptr;
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
+  // When Q is larger than the 256 MB last-level cache (MALL), the 16 or so gathers of
+  // each Q row would come from HBM: the CSR is then built in query order and the
+  // items run in order of their first query, so that the Q rows in use stay cached.
+  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 256.0 * (1 << 20);
   hipError_t e;
   if (!row_ptr) {
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
@@ -204,10 +210,10 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
     int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
     if (vt)
       e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi, sl,
-                                  ws + L.csr_ws, st, /*ordered=*/false);
+                                  ws + L.csr_ws, st, /*ordered=*/by_query);
     else
       e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, sl, ws + L.csr_ws, st,
-                           /*ordered=*/false);
+                           /*ordered=*/by_query);
     if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
     row_ptr = rp; q_idx = qi; slot = sl;
   }
@@ -230,6 +236,14 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   p.items = items;
   e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
+  if (by_query) {
+    int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
+    e = launch_kv_items_by_query(items, chunk_ptr, p.Hkv * nrows, q_idx, nq * p.topk, nq,
+                                 L.max_items, reinterpret_cast<int32_t*>(ws + L.sort_counts), sorted,
+                                 st);
+    if (e != hipSuccess) return hip_fail(e, "kv-centric item order");
+    p.items = sorted;
+  }
   if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
   prof_mark(g_prof_before, st);
   e = launch_kvcentric(p, static_cast<int>(L.max_items), st);

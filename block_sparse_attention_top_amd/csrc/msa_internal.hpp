@@ -276,6 +276,13 @@ struct KvParams {
 hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
                            int chunk_entries, int4* items, hipStream_t stream);
+// items reordered by the first query of each (q_idx [Hkv][cap]; nq query rows); the
+// item count is chunk_ptr[nchunk_rows], read on the device, at most max_items;
+// counts: 256 ints of scratch
+hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr, int nchunk_rows,
+                                    const int32_t* q_idx, long long cap, long long nq,
+                                    long long max_items, int32_t* counts, int4* out,
+                                    hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 

@@ -348,6 +348,71 @@ __global__ void kv_items_kernel(const int32_t* __restrict__ row_ptr,
     items[c] = make_int4(hkv, r, e, min(chunk_entries, end - e));
 }
 
+// The item table reordered by the first query of each item: a counting sort over
+// kQueryBuckets query ranges. With the CSR rows ascending in query, an item covers
+// a narrow query range, and items that run together then gather Q rows from a small
+// part of Q. Order inside a bucket is arbitrary: each item writes its own partials,
+// so the results do not depend on it.
+constexpr int kQueryBuckets = 256;  // = the block size of the passes below
+
+__device__ __forceinline__ int item_bucket(const int4& it, const int32_t* q_idx, long long cap,
+                                           long long nq) {
+  const long long q = q_idx[it.x * cap + it.z];
+  return static_cast<int>(min(q * kQueryBuckets / nq, static_cast<long long>(kQueryBuckets - 1)));
+}
+
+__global__ __launch_bounds__(kQueryBuckets) void kv_sort_zero(int32_t* __restrict__ counts) {
+  counts[threadIdx.x] = 0;
+}
+
+// COUNT: counts[b] += items of this block in bucket b. Else (scatter): each block
+// reserves a range of every bucket with one atomic on the running cursors and
+// places its items there.
+template <bool COUNT>
+__global__ __launch_bounds__(kQueryBuckets) void kv_sort_pass(
+    const int4* __restrict__ items, const int32_t* __restrict__ chunk_ptr, int nchunk_rows,
+    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ counts,
+    int4* __restrict__ out) {
+  __shared__ int h[kQueryBuckets];
+  __shared__ int base[kQueryBuckets];
+  const int total = chunk_ptr[nchunk_rows];
+  const int c = blockIdx.x * kQueryBuckets + threadIdx.x;
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  int4 it = make_int4(0, 0, 0, 0);
+  int b = -1, rank = 0;
+  if (c < total) {
+    it = items[c];
+    b = item_bucket(it, q_idx, cap, nq);
+    rank = atomicAdd(&h[b], 1);
+  }
+  __syncthreads();
+  const int n = h[threadIdx.x];
+  if (COUNT) {
+    if (n) atomicAdd(&counts[threadIdx.x], n);
+    return;
+  }
+  base[threadIdx.x] = n ? atomicAdd(&counts[threadIdx.x], n) : 0;
+  __syncthreads();
+  if (b >= 0) out[base[b] + rank] = it;
+}
+
+// exclusive scan of the bucket counts, in place (one block)
+__global__ __launch_bounds__(kQueryBuckets) void kv_sort_scan(int32_t* __restrict__ counts) {
+  __shared__ int v[kQueryBuckets];
+  const int t = threadIdx.x;
+  const int own = counts[t];
+  v[t] = own;
+  __syncthreads();
+  for (int d = 1; d < kQueryBuckets; d <<= 1) {
+    const int add = t >= d ? v[t - d] : 0;
+    __syncthreads();
+    v[t] += add;
+    __syncthreads();
+  }
+  counts[t] = v[t] - own;
+}
+
 template <int QPK>
 void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
   const dim3 blk(256);
@@ -368,6 +433,22 @@ hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int
   const long long n = static_cast<long long>(Hkv) * nrows;
   hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr, int nchunk_rows,
+                                    const int32_t* q_idx, long long cap, long long nq,
+                                    long long max_items, int32_t* counts, int4* out,
+                                    hipStream_t stream) {
+  if (nq <= 0 || max_items <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((max_items + kQueryBuckets - 1) / kQueryBuckets));
+  const dim3 blk(kQueryBuckets);
+  hipLaunchKernelGGL(kv_sort_zero, dim3(1), blk, 0, stream, counts);
+  hipLaunchKernelGGL(kv_sort_pass<true>, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
+                     cap, nq, counts, out);
+  hipLaunchKernelGGL(kv_sort_scan, dim3(1), blk, 0, stream, counts);
+  hipLaunchKernelGGL(kv_sort_pass<false>, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
+                     cap, nq, counts, out);
   return hipGetLastError();
 }
 
