@@ -199,10 +199,12 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* row_ptr = csr_row_ptr;
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
-  // When Q is larger than the 256 MB last-level cache (MALL), the 16 or so gathers of
-  // each Q row would come from HBM: the CSR is then built in query order and the
-  // items run in order of their first query, so that the Q rows in use stay cached.
-  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 256.0 * (1 << 20);
+  // When Q does not fit beside the partials' stream in the 256 MB last-level cache
+  // (MALL), the 16 or so gathers of each Q row come mostly from HBM. The items then
+  // run in order of their first query, so that the Q rows in use stay cached. The
+  // order-free CSR lists each row's entries tile by tile, in ascending query tiles,
+  // so an item's first query marks where its query range starts.
+  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 160.0 * (1 << 20);
   hipError_t e;
   if (!row_ptr) {
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
@@ -210,10 +212,10 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
     int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
     if (vt)
       e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi, sl,
-                                  ws + L.csr_ws, st, /*ordered=*/by_query);
+                                  ws + L.csr_ws, st, /*ordered=*/false);
     else
       e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, sl, ws + L.csr_ws, st,
-                           /*ordered=*/by_query);
+                           /*ordered=*/false);
     if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
     row_ptr = rp; q_idx = qi; slot = sl;
   }
