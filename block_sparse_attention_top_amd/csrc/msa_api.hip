@@ -204,7 +204,7 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   // run in order of their first query, so that the Q rows in use stay cached. The
   // order-free CSR lists each row's entries tile by tile, in ascending query tiles,
   // so an item's first query marks where its query range starts.
-  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 160.0 * (1 << 20);
+  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 100.0 * (1 << 20);
   hipError_t e;
   if (!row_ptr) {
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
