@@ -223,9 +223,10 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   }
   const int chunk = chunk_entries_for(p.qpk);
   int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
+  int32_t* sort_counts = by_query ? reinterpret_cast<int32_t*>(ws + L.sort_counts) : nullptr;
   e = launch_chunk_schedule(row_ptr, p.Hkv, nrows, chunk,
                             reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
-                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st);
+                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st, sort_counts, 256);
   if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
   p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot; p.chunk_ptr = chunk_ptr;
   p.chunk_entries = chunk;
@@ -238,13 +239,13 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   }
   int4* items = reinterpret_cast<int4*>(ws + L.items);
   p.items = items;
-  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, st);
+  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, st, q_idx, nq * p.topk, nq,
+                      sort_counts);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
   if (by_query) {
     int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
     e = launch_kv_items_by_query(items, chunk_ptr, p.Hkv * nrows, q_idx, nq * p.topk, nq,
-                                 L.max_items, reinterpret_cast<int32_t*>(ws + L.sort_counts), sorted,
-                                 st);
+                                 L.max_items, sort_counts, sorted, st);
     if (e != hipSuccess) return hip_fail(e, "kv-centric item order");
     p.items = sorted;
   }

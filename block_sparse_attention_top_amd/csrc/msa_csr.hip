@@ -410,6 +410,57 @@ __global__ void chunk_count_kernel(const int32_t* __restrict__ row_ptr, int Hkv,
 
 inline unsigned blocks_for(long long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
 
+// The whole chunk schedule in one workgroup when there are at most
+// kSmallSchedThreads * kSmallSchedPer (KV head, row) pairs: each thread counts the
+// chunks of kSmallSchedPer consecutive rows, one block-wide scan turns the counts
+// into chunk_ptr (exclusive, with the total at [n]). It also clears `zero_ints`
+// (a caller's counters), saving the launches of the separate count, scan and clear.
+constexpr int kSmallSchedThreads = 1024;
+constexpr int kSmallSchedPer = 16;
+__global__ __launch_bounds__(kSmallSchedThreads) void chunk_schedule_small_kernel(
+    const int32_t* __restrict__ row_ptr, int Hkv, int nrows, int chunk_entries,
+    int32_t* __restrict__ chunk_ptr, int32_t* __restrict__ zero_ints, int nzero) {
+  __shared__ int sum[kSmallSchedThreads];
+  const int t = threadIdx.x;
+  const int n = Hkv * nrows;
+  int cnt[kSmallSchedPer];
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < kSmallSchedPer; ++k) {
+    const int idx = t * kSmallSchedPer + k;
+    int c = 0;
+    if (idx < n) {
+      const int hkv = idx / nrows, r = idx % nrows;
+      const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
+      c = (rp[r + 1] - rp[r] + chunk_entries - 1) / chunk_entries;
+    }
+    cnt[k] = c;
+    local += c;
+  }
+  sum[t] = local;
+  __syncthreads();
+  for (int d = 1; d < kSmallSchedThreads; d <<= 1) {
+    const int add = t >= d ? sum[t - d] : 0;
+    __syncthreads();
+    sum[t] += add;
+    __syncthreads();
+  }
+  int run = sum[t] - local;
+#pragma unroll
+  for (int k = 0; k < kSmallSchedPer; ++k) {
+    const int idx = t * kSmallSchedPer + k;
+    if (idx < n) chunk_ptr[idx] = run;
+    run += cnt[k];
+  }
+  if (t == kSmallSchedThreads - 1) chunk_ptr[n] = sum[t];
+  for (int i = t; i < nzero; i += kSmallSchedThreads) zero_ints[i] = 0;
+}
+
+__global__ void zero_ints_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 size_t scan_tmp_ints(long long n) { return static_cast<size_t>((n + kScanTile - 1) / kScanTile) + 1; }
@@ -542,8 +593,17 @@ hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, in
 
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
                                  int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int32_t* zero_ints, int nzero) {
   const long long n = static_cast<long long>(Hkv) * nrows;
+  if (n <= static_cast<long long>(kSmallSchedThreads) * kSmallSchedPer) {
+    hipLaunchKernelGGL(chunk_schedule_small_kernel, dim3(1), dim3(kSmallSchedThreads), 0, stream,
+                       row_ptr, Hkv, nrows, chunk_entries, chunk_ptr, zero_ints,
+                       zero_ints ? nzero : 0);
+    return hipGetLastError();
+  }
+  if (zero_ints && nzero > 0)
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(blocks_for(nzero, 256)), dim3(256), 0, stream,
+                       zero_ints, nzero);
   hipLaunchKernelGGL(chunk_count_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, stream, row_ptr,
                      Hkv, nrows, chunk_entries, chunk_counts);
   hipError_t err = hipGetLastError();

@@ -274,11 +274,15 @@ struct KvParams {
 };
 // grid = an upper bound on the item count (workgroups past the count exit)
 hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
+// With bucket_counts given (256 ints, zero on entry), also counts the items per query
+// bucket of their first query (q_idx [Hkv][cap], nq query rows) for the item order below.
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, hipStream_t stream);
+                           int chunk_entries, int4* items, hipStream_t stream,
+                           const int32_t* q_idx = nullptr, long long cap = 0, long long nq = 0,
+                           int32_t* bucket_counts = nullptr);
 // items reordered by the first query of each (q_idx [Hkv][cap]; nq query rows); the
 // item count is chunk_ptr[nchunk_rows], read on the device, at most max_items;
-// counts: 256 ints of scratch
+// counts: the 256 bucket counts launch_kv_items produced (overwritten)
 hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr, int nchunk_rows,
                                     const int32_t* q_idx, long long cap, long long nq,
                                     long long max_items, int32_t* counts, int4* out,
@@ -326,9 +330,10 @@ hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, in
                                    int total_q, int topk,
                                    int nrows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
                                    void* ws, hipStream_t stream, bool ordered = true);
-// per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix
+// per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix;
+// also sets zero_ints[0, nzero) to 0 when zero_ints is given
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
                                  int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int32_t* zero_ints = nullptr, int nzero = 0);
 
 }  // namespace msa

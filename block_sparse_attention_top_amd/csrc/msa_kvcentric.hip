@@ -334,25 +334,6 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   if (pend.ok) flush(pend);
 }
 
-// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row
-__global__ void kv_items_kernel(const int32_t* __restrict__ row_ptr,
-                                const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
-                                int chunk_entries, int4* __restrict__ items) {
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long long>(Hkv) * nrows) return;
-  const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
-  const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
-  const int beg = rp[r], end = rp[r + 1];
-  int c = chunk_ptr[idx];
-  for (int e = beg; e < end; e += chunk_entries, ++c)
-    items[c] = make_int4(hkv, r, e, min(chunk_entries, end - e));
-}
-
-// The item table reordered by the first query of each item: a counting sort over
-// kQueryBuckets query ranges. With the CSR rows ascending in query, an item covers
-// a narrow query range, and items that run together then gather Q rows from a small
-// part of Q. Order inside a bucket is arbitrary: each item writes its own partials,
-// so the results do not depend on it.
 constexpr int kQueryBuckets = 256;  // = the block size of the passes below
 
 __device__ __forceinline__ int item_bucket(const int4& it, const int32_t* q_idx, long long cap,
@@ -361,17 +342,65 @@ __device__ __forceinline__ int item_bucket(const int4& it, const int32_t* q_idx,
   return static_cast<int>(min(q * kQueryBuckets / nq, static_cast<long long>(kQueryBuckets - 1)));
 }
 
-__global__ __launch_bounds__(kQueryBuckets) void kv_sort_zero(int32_t* __restrict__ counts) {
-  counts[threadIdx.x] = 0;
+// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row; with
+// bucket_counts, each item is also counted in the query bucket of its first query (the
+// first queries of 8 chunks loaded together, counts gathered per block in LDS).
+__global__ __launch_bounds__(256) void kv_items_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
+    int chunk_entries, int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap,
+    long long nq, int32_t* __restrict__ bucket_counts) {
+  __shared__ int hist[kQueryBuckets];
+  if (bucket_counts) {
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+  }
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < static_cast<long long>(Hkv) * nrows) {
+    const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
+    const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
+    const int beg = rp[r], end = rp[r + 1];
+    int c = chunk_ptr[idx];
+    constexpr int kB = 8;
+    for (int e0 = beg; e0 < end; e0 += kB * chunk_entries) {
+      int q[kB];
+      if (bucket_counts) {
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+          const int e = e0 + k * chunk_entries;
+          q[k] = q_idx[hkv * cap + (e < end ? e : end - 1)];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int e = e0 + k * chunk_entries;
+        if (e >= end) break;
+        items[c++] = make_int4(hkv, r, e, min(chunk_entries, end - e));
+        if (bucket_counts)
+          atomicAdd(&hist[static_cast<int>(min(q[k] * kQueryBuckets / nq,
+                                               static_cast<long long>(kQueryBuckets - 1)))], 1);
+      }
+    }
+  }
+  if (bucket_counts) {
+    __syncthreads();
+    const int n = hist[threadIdx.x];
+    if (n) atomicAdd(&bucket_counts[threadIdx.x], n);
+  }
 }
 
-// COUNT: counts[b] += items of this block in bucket b. Else (scatter): each block
-// reserves a range of every bucket with one atomic on the running cursors and
-// places its items there.
-template <bool COUNT>
-__global__ __launch_bounds__(kQueryBuckets) void kv_sort_pass(
+// The item table reordered by the first query of each item: a counting sort over
+// kQueryBuckets query ranges. With the CSR rows ascending in query, an item covers
+// a narrow query range, and items that run together then gather Q rows from a small
+// part of Q. Order inside a bucket is arbitrary: each item writes its own partials,
+// so the results do not depend on it. The counts come from the item-table kernel
+// (on counters the chunk schedule cleared); a scan and a scatter follow.
+//
+// Scatter of the items into bucket order: each block reserves a range of every bucket
+// with one atomic on the running cursors (the scanned counts) and places its items
+// there.
+__global__ __launch_bounds__(kQueryBuckets) void kv_sort_scatter(
     const int4* __restrict__ items, const int32_t* __restrict__ chunk_ptr, int nchunk_rows,
-    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ cursor,
     int4* __restrict__ out) {
   __shared__ int h[kQueryBuckets];
   __shared__ int base[kQueryBuckets];
@@ -388,11 +417,7 @@ __global__ __launch_bounds__(kQueryBuckets) void kv_sort_pass(
   }
   __syncthreads();
   const int n = h[threadIdx.x];
-  if (COUNT) {
-    if (n) atomicAdd(&counts[threadIdx.x], n);
-    return;
-  }
-  base[threadIdx.x] = n ? atomicAdd(&counts[threadIdx.x], n) : 0;
+  base[threadIdx.x] = n ? atomicAdd(&cursor[threadIdx.x], n) : 0;
   __syncthreads();
   if (b >= 0) out[base[b] + rank] = it;
 }
@@ -429,10 +454,14 @@ void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, hipStream_t stream) {
+                           int chunk_entries, int4* items, hipStream_t stream,
+                           const int32_t* q_idx, long long cap, long long nq,
+                           int32_t* bucket_counts) {
   const long long n = static_cast<long long>(Hkv) * nrows;
+  if (bucket_counts && nq <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items);
+                     stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items, q_idx, cap, nq,
+                     bucket_counts);
   return hipGetLastError();
 }
 
@@ -443,11 +472,8 @@ hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr,
   if (nq <= 0 || max_items <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((max_items + kQueryBuckets - 1) / kQueryBuckets));
   const dim3 blk(kQueryBuckets);
-  hipLaunchKernelGGL(kv_sort_zero, dim3(1), blk, 0, stream, counts);
-  hipLaunchKernelGGL(kv_sort_pass<true>, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
-                     cap, nq, counts, out);
   hipLaunchKernelGGL(kv_sort_scan, dim3(1), blk, 0, stream, counts);
-  hipLaunchKernelGGL(kv_sort_pass<false>, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
+  hipLaunchKernelGGL(kv_sort_scatter, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
                      cap, nq, counts, out);
   return hipGetLastError();
 }
