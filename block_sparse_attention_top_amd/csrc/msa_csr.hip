@@ -356,15 +356,21 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
 template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ q_idx, int32_t* __restrict__ slot) {
+    int32_t* __restrict__ q_idx, int32_t* __restrict__ slot, int32_t* __restrict__ row_ptr) {
   extern __shared__ int cursor[];
   const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int nrows = a.nrows;
   const long long cap = a.nq * a.topk;
   const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
   const int base_h = offsets[seg];
-  for (int r = threadIdx.x; r < nrows; r += blockDim.x)
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
     cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
+    // tile 0 holds each row's first position: the row pointers of this KV head
+    if (row_ptr && tile == 0) row_ptr[static_cast<long long>(hkv) * (nrows + 1) + r] = cursor[r];
+  }
+  if (row_ptr && tile == 0 && threadIdx.x == 0)
+    row_ptr[static_cast<long long>(hkv) * (nrows + 1) + nrows] =
+        offsets[seg + static_cast<long long>(nrows) * ntiles] - base_h;
   __syncthreads();
   const long long g0 = static_cast<long long>(tile) * tile_q;
   const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
@@ -425,15 +431,18 @@ __global__ __launch_bounds__(kSmallSchedThreads) void chunk_schedule_small_kerne
   const int n = Hkv * nrows;
   int cnt[kSmallSchedPer];
   int local = 0;
+  // indices clamped into range so that all loads are unconditional and in flight together
+  int len[kSmallSchedPer];
 #pragma unroll
   for (int k = 0; k < kSmallSchedPer; ++k) {
-    const int idx = t * kSmallSchedPer + k;
-    int c = 0;
-    if (idx < n) {
-      const int hkv = idx / nrows, r = idx % nrows;
-      const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
-      c = (rp[r + 1] - rp[r] + chunk_entries - 1) / chunk_entries;
-    }
+    const int idx = min(t * kSmallSchedPer + k, n - 1);
+    const int hkv = idx / nrows, r = idx % nrows;
+    const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
+    len[k] = rp[r + 1] - rp[r];
+  }
+#pragma unroll
+  for (int k = 0; k < kSmallSchedPer; ++k) {
+    const int c = t * kSmallSchedPer + k < n ? (len[k] + chunk_entries - 1) / chunk_entries : 0;
     cnt[k] = c;
     local += c;
   }
@@ -547,13 +556,15 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   else if (ordered)
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
-  else
+  else  // the order-free scatter also writes the row pointers (from its tile-0 blocks)
     hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32>), grid, dim3(256),
                        lds + sizeof(int), stream, a,
-                       plan.tile_q, plan.ntiles, offsets, q_idx, slot);
-  const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
-  hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
-                     offsets, a.Hkv, nrows, plan.ntiles, row_ptr);
+                       plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
+  if (ordered) {
+    const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
+    hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
+                       offsets, a.Hkv, nrows, plan.ntiles, row_ptr);
+  }
   return hipGetLastError();
 }
 
