@@ -205,8 +205,8 @@ __device__ __forceinline__ void load_rows(const CsrSrc& a, int hkv, long long e0
   }
 }
 
-template <bool VARLEN, bool I32>
-__global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
+template <bool VARLEN, bool I32, int NT>
+__global__ __launch_bounds__(NT) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
                                                         int32_t* __restrict__ counts) {
   extern __shared__ int cnt[];
   const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
@@ -217,9 +217,9 @@ __global__ __launch_bounds__(256) void csr_count_kernel(CsrSrc a, int tile_q, in
   const long long g1 = std::min<long long>(a.nq, g0 + tile_q);
   const long long e1 = g1 * a.topk;
   // kCsrBatch entries per thread per round, their index loads issued together
-  for (long long rb = g0 * a.topk; rb < e1; rb += 256 * kCsrBatch) {
+  for (long long rb = g0 * a.topk; rb < e1; rb += NT * kCsrBatch) {
     int rows[kCsrBatch];
-    load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, 256, e1, rows);
+    load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, NT, e1, rows);
 #pragma unroll
     for (int k = 0; k < kCsrBatch; ++k)
       if (rows[k] >= 0) atomicAdd(&cnt[rows[k]], 1);
@@ -544,8 +544,15 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   int32_t* tmp = reinterpret_cast<int32_t*>(base);
   const size_t lds = static_cast<size_t>(nrows) * sizeof(int);
   const dim3 grid(plan.ntiles, a.Hkv);
-  hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32>), grid, dim3(256), lds, stream, a, plan.tile_q,
-                     plan.ntiles, counts);
+  // With at most one tile per compute unit (long order-free tiles on the largest
+  // problems), the count runs 1024 threads per tile so that 16 waves per compute unit
+  // keep index loads in flight; otherwise 256.
+  if (static_cast<long long>(plan.ntiles) * a.Hkv <= device_cu_count())
+    hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32, 1024>), grid, dim3(1024), lds, stream, a,
+                       plan.tile_q, plan.ntiles, counts);
+  else
+    hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32, 256>), grid, dim3(256), lds, stream, a,
+                       plan.tile_q, plan.ntiles, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
