@@ -13,7 +13,7 @@ Metrics (the pages' benchmark harness, "test_sparse_atten.py"):
   decode:  GB/s of algorithmic bytes = distinct selected K/V blocks of each
            (sequence, KV head) * 64 KiB + Q + O + LSE + q2k + page table
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c2|vmix|...]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3u|c2|vmix|...]
                        [--path auto|q|kv|decode] [--splits N] [--extra c5,c3u]
                        [--lse-temperature T] [--no-cpu-baseline]
 (--extra workloads run with the automatic path)
@@ -216,27 +216,32 @@ class Case:
 
     def time_steps(self, steps: int, warmup: int) -> tuple:
         """(mean ms per step, mean ms of the dominant kernel) over `steps` back-to-back
-        calls; step time from events on torch's current stream (the launch stream),
-        kernel time from events the library records around its dominant kernel."""
+        calls each. The step time comes from a plain loop bracketed by events on torch's
+        current stream (the launch stream), with nothing else recorded inside it. The
+        kernel time comes from a second loop of the same length in which the library
+        records a pair of events around its dominant kernel, on the launch stream."""
         import torch
         import block_sparse_attention_top_amd as msa
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        ev = HipEvents(steps)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
-        for i in range(steps):
-            msa.msa_set_profiling_events(*ev.pairs[i])
+        for _ in range(steps):
             self.step()
         end.record()
         end.synchronize()
+        step_ms = start.elapsed_time(end) / steps
+        ev = HipEvents(steps)
+        for i in range(steps):
+            msa.msa_set_profiling_events(*ev.pairs[i])
+            self.step()
         msa.msa_set_profiling_events(None, None)
         torch.cuda.synchronize()
         kernel_ms = ev.mean_ms()
         ev.close()
-        return start.elapsed_time(end) / steps, kernel_ms
+        return step_ms, kernel_ms
 
     def breakdown(self, steps: int, warmup: int):
         """kv-centric only: mean ms of the k2q CSR build alone, of the forward given a
@@ -327,6 +332,48 @@ def decode_instance(w, fp8: bool = False) -> str:
             f"{'true' if w.dense else 'false'}>")
 
 
+def skew_diagnostics(w, q2k: np.ndarray, varlen_rows=None) -> dict:
+    """How the index table spreads over the KV blocks, in the manner of the test page's
+    benchmark printout (its q2k fan-out and k2q CSR row summaries): per KV head and
+    block, the number of (query, slot) entries that select it (the CSR row lengths),
+    the share of block 0 (the sink), and the spread (max / mean, p50) of those counts;
+    per query row, the number of valid slots."""
+    if varlen_rows is not None:  # packed [Hkv, total_q, topk] with per-query block counts
+        hkv_n, nq, topk = q2k.shape
+        nb = np.repeat(varlen_rows["nblk"], varlen_rows["q_lens"])[None, :, None]
+        base = np.repeat(varlen_rows["rowbase"], varlen_rows["q_lens"])[None, :, None]
+        ok = (q2k >= 0) & (q2k < nb)
+        rows = (q2k + base)[ok] + np.nonzero(ok)[0] * varlen_rows["nrows"]
+        nrows = varlen_rows["nrows"]
+        per_row = ok.sum(axis=2).reshape(-1)
+        block0 = int(((q2k == 0) & ok).sum())
+    else:
+        nblk = w.max_pages if w.paged else w.Skv // w.blk
+        nrows = w.B * nblk
+        ok = (q2k >= 0) & (q2k < nblk)
+        b = np.arange(w.B).reshape(-1, 1, 1, 1)
+        h = np.arange(w.Hkv).reshape(1, -1, 1, 1)
+        rows = (h * nrows + b * nblk + q2k)[ok]
+        per_row = ok.sum(axis=3).reshape(-1)
+        block0 = int(((q2k == 0) & ok).sum())
+    hkv_n = w.Hkv
+    counts = np.bincount(rows.reshape(-1), minlength=hkv_n * nrows).astype(np.float64)
+    valid = int(counts.sum())
+    mean = counts.mean() if counts.size else 0.0
+    return {
+        "valid_entries": valid,
+        "csr_rows": int(counts.size),
+        "row_len_max": int(counts.max()) if counts.size else 0,
+        "row_len_mean": round(float(mean), 1),
+        "row_len_p50": float(np.median(counts)) if counts.size else 0.0,
+        "row_len_max_over_mean": round(float(counts.max() / mean), 2) if mean else None,
+        "block0_share": round(block0 / valid, 4) if valid else None,
+        "empty_rows": int((counts == 0).sum()),
+        "fanout_min": int(per_row.min()), "fanout_mean": round(float(per_row.mean()), 2),
+        "queries_with_no_slot": int((per_row == 0).sum()),
+    }
+
+
 def measured_traffic(case: "Case"):
     """HBM bytes per launch of the dominant kernel from the committed counter summary
     profiles/traffic_<workload>_<path>.json (FETCH_SIZE and WRITE_SIZE, scaled by a
@@ -414,11 +461,15 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c3u",
+                    help="the workload timed for the headline value (default: B1, Sq=Skv=32768, "
+                         "Hq 64 / Hkv 4, topk 16, uniform selections)")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS))
     ap.add_argument("--splits", type=int, default=0,
                     help="KV splits of the paged workload (0 = the library's choice)")
-    ap.add_argument("--extra", default="", help="comma-separated workloads reported beside")
+    ap.add_argument("--extra", default="c5",
+                    help="comma-separated workloads reported beside (default: the paged decode "
+                         "batch c5; '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="K/V element type (fp8 = the e4m3fn cache)")
@@ -437,6 +488,16 @@ def main() -> int:
         copy_calibration(args.copy_calibration)
         return 0
     case = Case(args.workload, args.path, args.splits, args.lse_temperature, args.kv_dtype)
+    skew = None
+    w_ = case.w
+    if "q2k" in case.inp and not getattr(w_, "dense", False):
+        vr = None
+        if case.varlen:
+            nblk = (np.asarray(w_.k_lens) + w_.blk - 1) // w_.blk
+            vr = {"nblk": nblk, "q_lens": np.asarray(w_.q_lens),
+                  "rowbase": np.concatenate([[0], np.cumsum(nblk)[:-1]]), "nrows": int(nblk.sum())}
+        skew = skew_diagnostics(w_, case.inp["q2k"], vr)
+        log(f"[bench] {args.workload}: index skew {skew}")
     log(f"[bench] {args.workload}: timing {args.steps} steps after {args.warmup} warmup "
         f"({case.path_name})")
     ms, kernel_ms = case.time_steps(args.steps, args.warmup)
@@ -456,6 +517,9 @@ def main() -> int:
         ach = m["kernel_TFLOP_per_s"]
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+    # the whole step (every launch of the call) against the same peak, beside the
+    # dominant kernel's own fraction
+    roof["step_frac"] = (m["hbm_frac"] if w.paged else m["mfma_frac"])
     roof["kernel"] = case.dominant_kernel()
     if args.lse_temperature is not None or args.kv_dtype == "fp8":  # the kernels' variants
         roof["kernel"] = case.dominant_kernel(args.lse_temperature is not None,
@@ -468,6 +532,8 @@ def main() -> int:
     for key in [k for k in args.extra.split(",") if k]:
         c = Case(key, "auto")
         extra[key] = c.metric(*c.time_steps(args.steps, args.warmup))
+        extra[key]["workload"] = c.w.name
+        extra[key]["kernel"] = c.dominant_kernel()
         log(f"[bench] {key}: {extra[key]}")
         del c
         torch.cuda.empty_cache()
@@ -498,6 +564,8 @@ def main() -> int:
     }
     if brk is not None:
         line["breakdown"] = brk
+    if skew is not None:
+        line["index_skew"] = skew
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)

@@ -104,6 +104,12 @@ int check_temperature(float scale, const float* lse_t) {
   return MSA_OK;
 }
 
+// Streams of the kv-centric item order: one per KV head, up to one per XCD. With a
+// single KV head one stream keeps every running item in one query range, so that the
+// Q rows they gather share the last-level cache (measured faster than 8 query-range
+// streams at 393 216 queries x 2 heads: 2.14 against 2.23 ms per step).
+int kv_streams(int Hkv) { return Hkv >= 8 ? 8 : (Hkv >= 4 ? 4 : (Hkv >= 2 ? 2 : 1)); }
+
 // Entries per kv-centric work item: kKvChunkRows (query, head) rows.
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
@@ -131,7 +137,7 @@ KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
   L.max_items = static_cast<long long>(Hkv) * (cap / chunk_entries_for(Hq / Hkv) + nrows + 1);
   L.items = off; off += align256(L.max_items * 16);
   L.items_by_q = off; off += align256(L.max_items * 16);
-  L.sort_counts = off; off += align256(256 * 4);
+  L.sort_counts = off; off += align256(kKvSortInts * 4);
   L.o_part = off; off += align256(static_cast<size_t>(cap) * Hq * kD * 2);
   L.lse_part = off; off += align256(static_cast<size_t>(cap) * Hq * 8);
   L.lse_t_part = off; off += align256(static_cast<size_t>(cap) * Hq * 4);
@@ -199,14 +205,6 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* row_ptr = csr_row_ptr;
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
-  // Each Q row is gathered once per selected block (16 or so times). Once Q is large
-  // next to the 256 MB last-level cache (MALL), which the partials also stream
-  // through, those gathers come partly from HBM. From 100 MB of Q the items then run
-  // in order of their first query, so that the Q rows in use stay cached: measured
-  // -6% per step at 537 MB of Q, -2.5% at 201 MB with 2 heads per KV head, -0.5% at
-  // 134 MB. The order-free CSR lists each row's entries tile by tile, in ascending
-  // query tiles, so an item's first query marks where its query range starts.
-  const bool by_query = static_cast<double>(nq) * p.Hq * kD * 2 > 100.0 * (1 << 20);
   hipError_t e;
   if (!row_ptr) {
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
@@ -223,12 +221,13 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   }
   const int chunk = chunk_entries_for(p.qpk);
   int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
-  int32_t* sort_counts = by_query ? reinterpret_cast<int32_t*>(ws + L.sort_counts) : nullptr;
+  const KvSortBuffers sb = kv_sort_buffers(reinterpret_cast<int32_t*>(ws + L.sort_counts));
   e = launch_chunk_schedule(row_ptr, p.Hkv, nrows, chunk,
                             reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
-                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st, sort_counts, 256);
+                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st, sb.counts,
+                            kKvSortZeroInts);
   if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
-  p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot; p.chunk_ptr = chunk_ptr;
+  p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot;
   p.chunk_entries = chunk;
   p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
   p.lse_part = reinterpret_cast<float2*>(ws + L.lse_part);
@@ -237,21 +236,25 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
     p.rowbase = vt->rowbase;
     p.row_seq = vt->row_seq;
   }
+  // The item table, then the same items ordered by (KV head, first query) and cut into
+  // one stream per XCD: the items running together on an XCD then gather Q rows from
+  // one narrow query range of one KV head, which stays in that XCD's L2. The order-free
+  // CSR lists each row's entries in ascending query tiles, so an item's first query
+  // marks where its query range starts.
   int4* items = reinterpret_cast<int4*>(ws + L.items);
-  p.items = items;
-  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, st, q_idx, nq * p.topk, nq,
-                      sort_counts);
+  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, q_idx, nq * p.topk, nq,
+                      sb.counts, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
-  if (by_query) {
-    int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
-    e = launch_kv_items_by_query(items, chunk_ptr, p.Hkv * nrows, q_idx, nq * p.topk, nq,
-                                 L.max_items, sort_counts, sorted, st);
-    if (e != hipSuccess) return hip_fail(e, "kv-centric item order");
-    p.items = sorted;
-  }
+  int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
+  e = launch_kv_items_by_key(items, p.Hkv, q_idx, nq * p.topk, nq, L.max_items, sb, sorted, st);
+  if (e != hipSuccess) return hip_fail(e, "kv-centric item order");
+  p.items = sorted;
+  p.key_start = sb.key_start;
+  p.stream_next = sb.next;
+  p.streams = kv_streams(p.Hkv);
   if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
   prof_mark(g_prof_before, st);
-  e = launch_kvcentric(p, static_cast<int>(L.max_items), st);
+  e = launch_kvcentric(p, L.max_items, st);
   prof_mark(g_prof_after, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric forward");
   if (vt) {

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
 
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
-// LDS: nrows + 1 cursors (the last one absorbs the unused slots).
+// LDS: nrows cursors (at most kMaxCsrRows ints = 64 KiB, the dynamic LDS limit).
 template <bool VARLEN, bool I32>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
@@ -380,10 +380,11 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
   for (long long rb = g0 * a.topk; rb < e1; rb += 256 * kCsrBatch) {
     int rows[kCsrBatch], pos[kCsrBatch];
     load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, 256, e1, rows);
-    // every atomic is issued before any result is used; an unused slot counts on
-    // the spare cursor past the last row
+    // every atomic is issued before any result is used; an unused slot adds 0 to
+    // row 0's cursor, which leaves it unchanged
 #pragma unroll
-    for (int k = 0; k < kCsrBatch; ++k) pos[k] = atomicAdd(&cursor[rows[k] >= 0 ? rows[k] : nrows], 1);
+    for (int k = 0; k < kCsrBatch; ++k)
+      pos[k] = atomicAdd(&cursor[rows[k] >= 0 ? rows[k] : 0], rows[k] >= 0 ? 1 : 0);
 #pragma unroll
     for (int k = 0; k < kCsrBatch; ++k) {
       if (rows[k] < 0) continue;
@@ -564,8 +565,7 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
   else  // the order-free scatter also writes the row pointers (from its tile-0 blocks)
-    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32>), grid, dim3(256),
-                       lds + sizeof(int), stream, a,
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32>), grid, dim3(256), lds, stream, a,
                        plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
   if (ordered) {
     const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);

@@ -13,6 +13,10 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxCsrRows = 16384;  // B * num_kv_blocks: the CSR passes keep one int per row in LDS
 constexpr int kKvChunkRows = 2048;  // (query, head) rows per kv-centric work item
 constexpr int kKvMaxEntries = 512;  // CSR entries per kv-centric work item (LDS bound)
+// kv-centric item order: kKvStreams streams (one per XCD) of kKvBucketsPerStream keys
+constexpr int kKvStreams = 8;
+constexpr int kKvBucketsPerStream = 256;
+constexpr int kKvKeys = kKvStreams * kKvBucketsPerStream;
 constexpr int kDecMaxEntries = 512; // Sq * topk index entries per paged decode workgroup
 constexpr int kDecPasses = kDecMaxEntries / 256;
 constexpr int kMaxQPerWave = 4;     // query rows per wave in the paged decode kernel (Sq <= 16)
@@ -106,6 +110,15 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 in, u32x4 out[2]) {
 
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407359f;
+
+// Query range of global query q among `buckets` equal ranges of nq queries:
+// floor(q * buckets / nq), clamped to [0, buckets - 1], with the product in 64 bits
+// (q * 256 leaves the int32 range once q reaches 2^23). Every kernel that buckets
+// an item by its first query calls this one function, so that all of them agree.
+__host__ __device__ __forceinline__ int query_bucket(long long q, long long nq, int buckets) {
+  const long long b = q * buckets / nq;
+  return static_cast<int>(b < 0 ? 0 : (b >= buckets ? buckets - 1 : b));
+}
 
 // floor(a / b) for b > 0
 __host__ __device__ __forceinline__ long long floor_div(long long a, long long b) {
@@ -252,8 +265,10 @@ struct KvParams {
   const int32_t* row_ptr;    // [Hkv, nrows+1]
   const int32_t* q_idx;      // [Hkv, cap]
   const int32_t* slot;       // [Hkv, cap]
-  const int32_t* chunk_ptr;  // [Hkv*nrows + 1] exclusive prefix of per-row chunk counts
-  const int4* items;         // [total chunks] (hkv, row, first entry, entry count)
+  const int4* items;         // (hkv, row, first entry, entry count), in key order
+  const int32_t* key_start;  // [kKvKeys + 1] first item of each key (the streams' bounds)
+  int32_t* stream_next;      // [kKvStreams] items taken from each stream (zero on entry)
+  int streams;               // streams the key range is cut into: 1, 2, 4 or 8
   int B, Sq, Skv, Hq, Hkv, qpk, topk, nblk, nrows;
   long long cap;             // B*Sq*topk
   int chunk_entries;         // CSR entries per work item
@@ -272,21 +287,32 @@ struct KvParams {
   const int32_t* row_seq;
   long long total_q, total_k;
 };
-// grid = an upper bound on the item count (workgroups past the count exit)
-hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream);
-// With bucket_counts given (256 ints, zero on entry), also counts the items per query
-// bucket of their first query (q_idx [Hkv][cap], nq query rows) for the item order below.
+// persistent grid (two workgroups per compute unit, at most max_items) over the
+// streams of the key-ordered item table
+hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t stream);
+// The item order's counters: counts[kKvKeys] and next[kKvStreams] must be zero on entry
+// (the chunk schedule clears kKvSortZeroInts ints from `counts`, which `next` follows).
+struct KvSortBuffers {
+  int32_t* counts;     // [kKvKeys] items per key
+  int32_t* next;       // [kKvStreams] items taken from each stream (KvParams::stream_next)
+  int32_t* cursor;     // [kKvKeys] scatter cursors
+  int32_t* key_start;  // [kKvKeys + 1] first item of each key
+};
+constexpr int kKvSortZeroInts = kKvKeys + 16;
+constexpr int kKvSortInts = kKvSortZeroInts + kKvKeys + kKvKeys + 1;
+inline KvSortBuffers kv_sort_buffers(int32_t* base) {
+  return KvSortBuffers{base, base + kKvKeys, base + kKvSortZeroInts,
+                       base + kKvSortZeroInts + kKvKeys};
+}
+// items[c] for every chunk of every row, and the per-key item counts (q_idx [Hkv][cap],
+// nq query rows; key_counts zero on entry)
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, hipStream_t stream,
-                           const int32_t* q_idx = nullptr, long long cap = 0, long long nq = 0,
-                           int32_t* bucket_counts = nullptr);
-// items reordered by the first query of each (q_idx [Hkv][cap]; nq query rows); the
-// item count is chunk_ptr[nchunk_rows], read on the device, at most max_items;
-// counts: the 256 bucket counts launch_kv_items produced (overwritten)
-hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr, int nchunk_rows,
-                                    const int32_t* q_idx, long long cap, long long nq,
-                                    long long max_items, int32_t* counts, int4* out,
-                                    hipStream_t stream);
+                           int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
+                           long long nq, int32_t* key_counts, hipStream_t stream);
+// the item table in key order (at most max_items items; the count is read on the device)
+hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_idx, long long cap,
+                                  long long nq, long long max_items, const KvSortBuffers& sb,
+                                  int4* out, hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 

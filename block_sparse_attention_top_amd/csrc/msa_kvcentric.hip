@@ -41,23 +41,23 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace msa {
 
 namespace {
 
-template <int QPK, bool TEMP, bool FP8>
-__global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
-  constexpr int kEnt = kKvChunkRows / QPK < kKvMaxEntries ? kKvChunkRows / QPK : kKvMaxEntries;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[kBlk * kVStride];
-  __shared__ int ent_q[kEnt];
-  __shared__ int ent_t[kEnt];
+template <int QPK>
+constexpr int kv_item_entries() {
+  return kKvChunkRows / QPK < kKvMaxEntries ? kKvChunkRows / QPK : kKvMaxEntries;
+}
 
-  const int total = p.chunk_ptr[p.Hkv * p.nrows];
-  const int w = blockIdx.x;
-  if (w >= total) return;
+// One work item: stage the block's K/V tiles and the chunk's entries in LDS, then
+// each wave computes the partials of 32 gathered (query, head) rows per step.
+template <int QPK, bool TEMP, bool FP8>
+__device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint8_t* ks,
+                                        uint8_t* vs, int* ent_q, int* ent_t) {
   const int tid = threadIdx.x;
-  const int4 item = p.items[w];
   const int hkv = item.x, r = item.y, e0 = item.z, ne = item.w;
   // the row's sequence b and block s; the sequence's first query and query
   // count, first key and key count
@@ -334,26 +334,72 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   if (pend.ok) flush(pend);
 }
 
-constexpr int kQueryBuckets = 256;  // = the block size of the passes below
-
-__device__ __forceinline__ int item_bucket(const int4& it, const int32_t* q_idx, long long cap,
-                                           long long nq) {
-  const long long q = q_idx[it.x * cap + it.z];
-  return static_cast<int>(min(q * kQueryBuckets / nq, static_cast<long long>(kQueryBuckets - 1)));
+// Persistent kv-centric kernel. The item table is ordered by key (KV head, first
+// query) and cut into p.streams streams of equal key ranges, so that a stream is the
+// items of one KV head (or of one query range of it) in query order. Workgroups are
+// dealt round-robin over the 8 XCDs, so team blockIdx % p.streams runs on the same
+// XCDs throughout; it takes the items of its own stream first, in order, through
+// the stream's counter, so that the items running together on an XCD gather Q rows
+// from one narrow query range of one KV head, which its L2 keeps. A workgroup whose
+// stream is exhausted moves on to the next stream. Every item is taken exactly once
+// (one atomic per take), no workgroup waits for another, and each workgroup stops
+// after finding all streams exhausted.
+template <int QPK, bool TEMP, bool FP8>
+__global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
+  constexpr int kEnt = kv_item_entries<QPK>();
+  __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[kBlk * kVStride];
+  __shared__ int ent_q[kEnt];
+  __shared__ int ent_t[kEnt];
+  __shared__ int s_item;
+  const int nst = p.streams;  // 1, 2, 4 or 8: divides kKvStreams
+  const int keys_per_stream = kKvKeys / nst;
+  const int team = blockIdx.x % nst;
+  int tried = 0;  // streams found exhausted (thread 0)
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int got = -1;
+      while (tried < nst) {
+        const int st = (team + tried) % nst;
+        const int beg = p.key_start[st * keys_per_stream];
+        const int end = p.key_start[(st + 1) * keys_per_stream];
+        if (beg < end) {
+          const int i = atomicAdd(&p.stream_next[st], 1);
+          if (i < end - beg) {
+            got = beg + i;
+            break;
+          }
+        }
+        ++tried;
+      }
+      s_item = got;
+    }
+    __syncthreads();
+    const int w = s_item;
+    if (w < 0) break;
+    kv_item<QPK, TEMP, FP8>(p, p.items[w], ks, vs, ent_q, ent_t);
+    __syncthreads();  // LDS tiles and s_item are reused by the next item
+  }
 }
 
-// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row; with
-// bucket_counts, each item is also counted in the query bucket of its first query (the
-// first queries of 8 chunks loaded together, counts gathered per block in LDS).
+// Key of a work item: its KV head and first query as one coordinate
+// c = hkv * nq + first query, bucketed into kKvKeys equal ranges. Stream s holds
+// keys [s * kKvBucketsPerStream, (s + 1) * kKvBucketsPerStream).
+__device__ __forceinline__ int item_key(int hkv, long long first_q, long long nq, int Hkv) {
+  return query_bucket(static_cast<long long>(hkv) * nq + first_q, static_cast<long long>(Hkv) * nq,
+                      kKvKeys);
+}
+
+// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row; each
+// item is also counted under its key (the first queries of 8 chunks loaded together,
+// counts gathered per block in LDS) into key_counts[kKvKeys] (zero on entry).
 __global__ __launch_bounds__(256) void kv_items_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
     int chunk_entries, int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap,
-    long long nq, int32_t* __restrict__ bucket_counts) {
-  __shared__ int hist[kQueryBuckets];
-  if (bucket_counts) {
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-  }
+    long long nq, int32_t* __restrict__ key_counts) {
+  __shared__ int hist[kKvKeys];
+  for (int i = threadIdx.x; i < kKvKeys; i += 256) hist[i] = 0;
+  __syncthreads();
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx < static_cast<long long>(Hkv) * nrows) {
     const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
@@ -363,79 +409,87 @@ __global__ __launch_bounds__(256) void kv_items_kernel(
     constexpr int kB = 8;
     for (int e0 = beg; e0 < end; e0 += kB * chunk_entries) {
       int q[kB];
-      if (bucket_counts) {
 #pragma unroll
-        for (int k = 0; k < kB; ++k) {
-          const int e = e0 + k * chunk_entries;
-          q[k] = q_idx[hkv * cap + (e < end ? e : end - 1)];
-        }
+      for (int k = 0; k < kB; ++k) {
+        const int e = e0 + k * chunk_entries;
+        q[k] = q_idx[hkv * cap + (e < end ? e : end - 1)];
       }
 #pragma unroll
       for (int k = 0; k < kB; ++k) {
         const int e = e0 + k * chunk_entries;
         if (e >= end) break;
         items[c++] = make_int4(hkv, r, e, min(chunk_entries, end - e));
-        if (bucket_counts)
-          atomicAdd(&hist[static_cast<int>(min(q[k] * kQueryBuckets / nq,
-                                               static_cast<long long>(kQueryBuckets - 1)))], 1);
+        atomicAdd(&hist[item_key(hkv, q[k], nq, Hkv)], 1);
       }
     }
   }
-  if (bucket_counts) {
-    __syncthreads();
-    const int n = hist[threadIdx.x];
-    if (n) atomicAdd(&bucket_counts[threadIdx.x], n);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kKvKeys; i += 256) {
+    const int n = hist[i];
+    if (n) atomicAdd(&key_counts[i], n);
   }
 }
 
-// The item table reordered by the first query of each item: a counting sort over
-// kQueryBuckets query ranges. With the CSR rows ascending in query, an item covers
-// a narrow query range, and items that run together then gather Q rows from a small
-// part of Q. Order inside a bucket is arbitrary: each item writes its own partials,
-// so the results do not depend on it. The counts come from the item-table kernel
-// (on counters the chunk schedule cleared); a scan and a scatter follow.
-//
-// Scatter of the items into bucket order: each block reserves a range of every bucket
-// with one atomic on the running cursors (the scanned counts) and places its items
-// there.
-__global__ __launch_bounds__(kQueryBuckets) void kv_sort_scatter(
-    const int4* __restrict__ items, const int32_t* __restrict__ chunk_ptr, int nchunk_rows,
-    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ cursor,
-    int4* __restrict__ out) {
-  __shared__ int h[kQueryBuckets];
-  __shared__ int base[kQueryBuckets];
-  const int total = chunk_ptr[nchunk_rows];
-  const int c = blockIdx.x * kQueryBuckets + threadIdx.x;
-  h[threadIdx.x] = 0;
-  __syncthreads();
-  int4 it = make_int4(0, 0, 0, 0);
-  int b = -1, rank = 0;
-  if (c < total) {
-    it = items[c];
-    b = item_bucket(it, q_idx, cap, nq);
-    rank = atomicAdd(&h[b], 1);
-  }
-  __syncthreads();
-  const int n = h[threadIdx.x];
-  base[threadIdx.x] = n ? atomicAdd(&cursor[threadIdx.x], n) : 0;
-  __syncthreads();
-  if (b >= 0) out[base[b] + rank] = it;
-}
-
-// exclusive scan of the bucket counts, in place (one block)
-__global__ __launch_bounds__(kQueryBuckets) void kv_sort_scan(int32_t* __restrict__ counts) {
-  __shared__ int v[kQueryBuckets];
+// Exclusive scan of the key counts (one block, 8 keys per thread): key_start[0..kKvKeys]
+// (key_start[kKvKeys] = the item count) and a copy of the starts as scatter cursors.
+__global__ __launch_bounds__(256) void kv_sort_scan(const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ key_start,
+                                                    int32_t* __restrict__ cursor) {
+  constexpr int kPer = kKvKeys / 256;
+  __shared__ int v[256];
   const int t = threadIdx.x;
-  const int own = counts[t];
+  int c[kPer], own = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    c[k] = counts[t * kPer + k];
+    own += c[k];
+  }
   v[t] = own;
   __syncthreads();
-  for (int d = 1; d < kQueryBuckets; d <<= 1) {
+  for (int d = 1; d < 256; d <<= 1) {
     const int add = t >= d ? v[t - d] : 0;
     __syncthreads();
     v[t] += add;
     __syncthreads();
   }
-  counts[t] = v[t] - own;
+  int run = v[t] - own;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    key_start[t * kPer + k] = run;
+    cursor[t * kPer + k] = run;
+    run += c[k];
+  }
+  if (t == 255) key_start[kKvKeys] = run;
+}
+
+// The item table in key order (a counting sort): each block ranks its 256 items per
+// key in LDS, reserves a range of every key it holds with one atomic on the running
+// cursors, and places its items there. Order inside a key is arbitrary: each item
+// writes its own partials, so the results do not depend on it.
+__global__ __launch_bounds__(256) void kv_sort_scatter(
+    const int4* __restrict__ items, const int32_t* __restrict__ key_start, int Hkv,
+    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ cursor,
+    int4* __restrict__ out) {
+  __shared__ int h[kKvKeys];
+  __shared__ int base[kKvKeys];
+  const int total = key_start[kKvKeys];
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  for (int i = threadIdx.x; i < kKvKeys; i += 256) h[i] = 0;
+  __syncthreads();
+  int4 it = make_int4(0, 0, 0, 0);
+  int key = -1, rank = 0;
+  if (c < total) {
+    it = items[c];
+    key = item_key(it.x, q_idx[it.x * cap + it.z], nq, Hkv);
+    rank = atomicAdd(&h[key], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kKvKeys; i += 256) {
+    const int n = h[i];
+    base[i] = n ? atomicAdd(&cursor[i], n) : 0;
+  }
+  __syncthreads();
+  if (key >= 0) out[base[key] + rank] = it;
 }
 
 template <int QPK>
@@ -454,35 +508,35 @@ void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, hipStream_t stream,
-                           const int32_t* q_idx, long long cap, long long nq,
-                           int32_t* bucket_counts) {
+                           int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
+                           long long nq, int32_t* key_counts, hipStream_t stream) {
   const long long n = static_cast<long long>(Hkv) * nrows;
-  if (bucket_counts && nq <= 0) return hipErrorInvalidValue;
+  if (nq <= 0 || !key_counts) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items, q_idx, cap, nq,
-                     bucket_counts);
+                     key_counts);
   return hipGetLastError();
 }
 
-hipError_t launch_kv_items_by_query(const int4* items, const int32_t* chunk_ptr, int nchunk_rows,
-                                    const int32_t* q_idx, long long cap, long long nq,
-                                    long long max_items, int32_t* counts, int4* out,
-                                    hipStream_t stream) {
+hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_idx, long long cap,
+                                  long long nq, long long max_items, const KvSortBuffers& sb,
+                                  int4* out, hipStream_t stream) {
   if (nq <= 0 || max_items <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((max_items + kQueryBuckets - 1) / kQueryBuckets));
-  const dim3 blk(kQueryBuckets);
-  hipLaunchKernelGGL(kv_sort_scan, dim3(1), blk, 0, stream, counts);
-  hipLaunchKernelGGL(kv_sort_scatter, grid, blk, 0, stream, items, chunk_ptr, nchunk_rows, q_idx,
-                     cap, nq, counts, out);
+  const dim3 grid(static_cast<unsigned>((max_items + 255) / 256));
+  hipLaunchKernelGGL(kv_sort_scan, dim3(1), dim3(256), 0, stream, sb.counts, sb.key_start,
+                     sb.cursor);
+  hipLaunchKernelGGL(kv_sort_scatter, grid, dim3(256), 0, stream, items, sb.key_start, Hkv, q_idx,
+                     cap, nq, sb.cursor, out);
   return hipGetLastError();
 }
 
-hipError_t launch_kvcentric(const KvParams& p, int grid, hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t stream) {
+  if (max_items <= 0) return hipSuccess;
+  // two workgroups per compute unit (the kernel's occupancy), never more than items
+  const long long grid = std::min<long long>(max_items, 2LL * device_cu_count());
   if (p.chunk_entries * p.qpk > kKvChunkRows || p.chunk_entries > kKvMaxEntries)
     return hipErrorInvalidValue;
-  const dim3 g(grid);
+  const dim3 g(static_cast<unsigned>(grid));
   switch (p.qpk) {
     case 1: kv_launch<1>(p, g, stream); break;
     case 2: kv_launch<2>(p, g, stream); break;

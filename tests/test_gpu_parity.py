@@ -340,34 +340,116 @@ def test_paged_equals_contiguous():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads (sampled rows), in the launch configuration the benchmark times
+# full-size workloads, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
+def expected_nonempty(w, q2k: np.ndarray) -> np.ndarray:
+    """[B, Hkv, Sq] bool: the row has at least one key (a valid slot whose block holds a
+    key at or before the causal limit), computed from the index table alone."""
+    nblk = (w.kvlen + w.blk - 1) // w.blk if w.paged else w.Skv // w.blk
+    ok = (q2k >= 0) & (q2k < nblk)
+    if w.causal:
+        lim = np.arange(w.Sq).reshape(1, 1, -1, 1) + w.kvlen - w.Sq  # last visible key
+        ok &= q2k.astype(np.int64) * w.blk <= lim
+    return ok.any(axis=3)
+
+
+def poisoned_workspace(nbytes: int) -> torch.Tensor:
+    """A workspace whose every byte is 0xFF, a NaN pattern for bf16 and fp32: a partial
+    the kernels read without having written it shows up as a non-finite output."""
+    return torch.full((max(nbytes, 256),), 255, dtype=torch.uint8, device="cuda")
+
+
+def check_any_size_properties(w, q2k, o, lse, label):
+    """Properties that hold at any size: O finite everywhere, LSE finite exactly on the
+    rows with a key, and O exactly 0 on the others."""
+    assert torch.isfinite(o.float()).all(), f"{label}: non-finite O"
+    want = torch.as_tensor(np.repeat(expected_nonempty(w, q2k), w.qpk, axis=1), device=o.device)
+    got = torch.isfinite(lse)
+    assert torch.equal(got, want), f"{label}: rows with a finite LSE differ from the index table"
+    assert not torch.isnan(lse).any(), f"{label}: NaN in LSE"
+    if not bool(want.all()):
+        empty = (~want).permute(0, 2, 1)  # [B, Sq, Hq]
+        assert bool((o[empty] == 0).all()), f"{label}: empty rows not zero"
+
+
+# every row against the oracle where it finishes in seconds on the host (c1, c2),
+# sampled rows elsewhere; the at-any-size properties on every row of every workload
+FULL_ROWS = {"c1", "c2"}
+
+
 @pytest.mark.parametrize("key", ["c1", "c2", "c3u", "c3s", "c4a", "c4b"])
-def test_full_size_sampled(key):
+def test_full_size(key):
+    import block_sparse_attention_top_amd as msa
     w = wl.WORKLOADS[key]
     say(f"[full] {key} {w.name}: generating inputs")
     inp = wl.make_inputs(w)
-    say(f"[full] {key}: running GPU (auto path)")
-    o, lse = run_contiguous(inp, w.causal, 0)
-    rows = sample_rows(w.B, w.Sq, 48, seed=1)
-    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
-                                             causal=w.causal, rows=rows)
-    stats = sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, key)
-    # properties that hold at any size: finite, and LSE finite exactly where a key exists
-    assert torch.isfinite(o.float()).all()
+    q, k, v, q2k = (to_dev(inp[n]) for n in ("q", "k", "v", "q2k"))
+    path = msa.msa_sparse_fwd_path(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.topk, 0)
+    ws = poisoned_workspace(msa.msa_sparse_fwd_workspace_size(w.B, w.Sq, w.Skv, w.Hq, w.Hkv,
+                                                              w.D, w.topk, w.blk, path))
+    say(f"[full] {key}: running GPU (auto path = {path}, poisoned workspace)")
+    o, lse = msa.msa_sparse_fwd(q, k, v, q2k, causal=w.causal, path=0, workspace=ws)
+    torch.cuda.synchronize()
+    check_any_size_properties(w, inp["q2k"], o, lse, key)
+    del ws
+    if key in FULL_ROWS:
+        say(f"[full] {key}: oracle on all {w.B * w.Sq} query rows")
+        o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                                 causal=w.causal)
+        stats = full_compare(o, lse, o_ref, lse_ref, key)
+    else:
+        rows = sample_rows(w.B, w.Sq, 48, seed=1)
+        o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                                 causal=w.causal, rows=rows)
+        stats = sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, key)
     say(f"[full] {key}: {stats}")
 
 
-@pytest.mark.parametrize("path", [0, PQ])
-def test_full_size_paged_decode(path):
+@pytest.fixture(scope="module")
+def c5_case():
     w = wl.WORKLOADS["c5"]
-    say(f"[full] c5 {w.name}: generating inputs")
+    say(f"[full] c5 {w.name}: generating inputs and the oracle over all {w.B * w.Sq} rows")
     inp = wl.make_inputs(w)
-    say(f"[full] c5: running GPU (path {path}, auto splits)")
-    o, lse = run_paged(inp, True, path=path)
-    rows = sample_rows(w.B, w.Sq, 64, seed=2)
-    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
-                                                   inp["page_table"], inp["seqused_k"],
-                                                   inp["q2k"], causal=True, rows=rows)
-    stats = sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, "c5")
+    ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                        inp["page_table"], inp["seqused_k"], inp["q2k"],
+                                        causal=True)
+    return w, inp, ref
+
+
+# auto (q-centric, one split), q-centric with a forced split-and-merge, the union decode
+# kernel with its automatic split count and with one split
+@pytest.mark.parametrize("path,splits", [(0, 0), (PQ, 4), (PD, 0), (PD, 1)])
+def test_full_size_paged_decode(c5_case, path, splits):
+    import block_sparse_attention_top_amd as msa
+    w, inp, (o_ref, lse_ref) = c5_case
+    t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k", "q2k")}
+    p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, path)
+    ns = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, splits, p)
+    ws = poisoned_workspace(msa.msa_paged_sparse_fwd_workspace_size(
+        w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk, w.blk, w.max_pages, splits, p))
+    say(f"[full] c5: running GPU (path {p}, {ns} splits, poisoned workspace)")
+    o, lse = msa.msa_paged_sparse_fwd(t["q"], t["k_pool"], t["v_pool"], t["page_table"],
+                                      t["seqused_k"], t["q2k"], causal=True, num_splits=splits,
+                                      path=p, workspace=ws)
+    torch.cuda.synchronize()
+    check_any_size_properties(w, inp["q2k"], o, lse, "c5")
+    stats = full_compare(o, lse, o_ref, lse_ref, f"c5 path {p} splits {ns}")
     say(f"[full] c5: {stats}")
+
+
+def test_kv_centric_at_max_csr_rows():
+    """B * Skv / 128 = 16384 CSR rows, the most the kv-centric path takes: the order-free
+    CSR scatter then keeps exactly 64 KiB of row cursors in LDS."""
+    import block_sparse_attention_top_amd as msa
+    w, inp = contiguous_case(8, 64, 262144, 1, 1, 4, False, wl.MODE_PERM, seed=5)
+    assert w.B * (w.Skv // w.blk) == 16384
+    o, lse = check_contiguous(w, inp, KV, "max-csr-rows")[1]
+    del o, lse
+    # one more block per sequence is too many rows: refused on the host (contents unused)
+    B2, Skv2 = 8, 262144 + 128
+    kv0 = np.zeros((B2, Skv2, 1, 128), dtype=np.uint16)
+    inp2 = dict(q=inp["q"][:, :8].copy(), k=kv0, v=kv0,
+                q2k=np.zeros((B2, 1, 8, 4), dtype=np.int32))
+    inp2["q"] = np.zeros((B2, 8, 1, 128), dtype=np.uint16)
+    with pytest.raises(msa.MsaNotSupportedError):
+        run_contiguous(inp2, False, KV)

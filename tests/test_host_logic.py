@@ -1,0 +1,54 @@
+"""Host-side logic of the library that needs no GPU.
+
+query_bucket (msa_internal.hpp) assigns each kv-centric work item to one of 256
+query ranges by its first query; the item-table and item-order kernels must agree
+on it for every query count the API accepts, including query ids past 2^23, where
+q * 256 no longer fits in 32 bits. The helper is compiled into a host program and
+compared with exact integer arithmetic.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "host", "query_bucket_check.cpp")
+
+
+@pytest.fixture(scope="module")
+def bucket_exe(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("host") / "query_bucket_check")
+    subprocess.check_call(["/opt/rocm/bin/hipcc", "-O1", "-std=c++17", "-x", "hip",
+                           "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+                           "-packed-fp32-ops", SRC, "-o", exe],
+                          stderr=subprocess.DEVNULL)
+    return exe
+
+
+def _run(exe, triples):
+    inp = "".join(f"{q} {nq} {b}\n" for q, nq, b in triples)
+    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    return [int(x) for x in out.split()]
+
+
+def test_query_bucket_exact_past_2_pow_23(bucket_exe):
+    rng = np.random.default_rng(7)
+    triples = []
+    # query counts the API accepts (B*Sq*topk < 2^31 with topk >= 1), around and past 2^23
+    for nq in (1, 3, 8192, 393216, (1 << 23) - 1, 1 << 23, 9_000_000, 134_217_727,
+               (1 << 31) - 1):
+        qs = {0, nq - 1, nq // 2, min(nq - 1, 1 << 23), min(nq - 1, (1 << 23) + 1)}
+        qs |= set(int(x) for x in rng.integers(0, nq, size=16))
+        triples += [(q, nq, 256) for q in sorted(qs)]
+    got = _run(bucket_exe, triples)
+    want = [min(q * b // nq, b - 1) for q, nq, b in triples]
+    assert got == want
+
+
+def test_query_bucket_monotone_and_in_range(bucket_exe):
+    nq = 9_000_000
+    qs = list(range(0, nq, 4099)) + [nq - 1]
+    got = _run(bucket_exe, [(q, nq, 256) for q in qs])
+    assert min(got) == 0 and max(got) == 255
+    assert all(a <= b for a, b in zip(got, got[1:]))
