@@ -90,6 +90,9 @@ def load_library():
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
                                          I, P, P, F, P, P, S, P]
     lib.msa_paged_sparse_fwd.restype = I
+    lib.msa_paged_sparse_fwd_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
+                                                 I, I, I, P, P, F, P, P]
+    lib.msa_paged_sparse_fwd_noalloc.restype = I
     PL = ctypes.POINTER(MsaDecodePlan)
     lib.msa_paged_decode_plan_init.argtypes = [I, I, I, I, I, I, I, I, I, I, PL]
     lib.msa_paged_decode_plan_init.restype = I
@@ -409,6 +412,47 @@ def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causa
     if return_temperature_lse:
         return o, lse, (lse if alias else lse_t)
     return o, lse
+
+
+def msa_paged_sparse_fwd_noalloc(q, k_pool, v_pool, page_table, seqused_k, q2k, *,
+                                 causal: bool, softmax_scale: float = 0.0, num_splits: int = 0,
+                                 path: int = MSA_PATH_AUTO, o=None, lse=None,
+                                 return_temperature_lse: bool = False,
+                                 lse_temperature_scale: Optional[float] = None,
+                                 lse_temperature=None, temperature_fast_path: bool = True,
+                                 stream=None):
+    """msa_paged_sparse_fwd without a workspace: the split partials use the library's
+    own per-GPU scratch array (MSA_NOALLOC_SCRATCH_BYTES). The library allocates
+    nothing; outputs are allocated here only when not given."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16)
+    kv_dtype = _kv_dtype(k_pool, v_pool, ("k_pool", "v_pool"))
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seqused_k, "seqused_k", torch.int32), _dev(q2k, "q2k", torch.int32)
+    B, Sq, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    topk = q2k.shape[-1]
+    if o is None:
+        o = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
+    rc = lib.msa_paged_sparse_fwd_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                          _ptr(seqused_k), _ptr(q2k), B, Sq, Hq, Hkv, D, topk,
+                                          page_size, num_pages, max_pages, int(bool(causal)),
+                                          float(softmax_scale), int(num_splits), int(path),
+                                          kv_dtype, _ptr(o), _ptr(lse), temp, _ptr(lse_t),
+                                          _stream(stream))
+    _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
+    return o, lse
+
+
+MSA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class DecodePlan:

@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 using namespace msa;
@@ -878,6 +879,84 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
     if (e != hipSuccess) return hip_fail(e, "split combine");
   }
   return MSA_OK;
+}
+
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Paged sparse forward for callers that cannot allocate (msa_paged_sparse_fwd_noalloc):
+// the split partials live in a file-scope device array of MSA_NOALLOC_SCRATCH_BYTES.
+// Each GPU the library runs on holds its own copy until the process ends. On the host
+// the name `scratch` is only a stand-in: the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress, that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = MSA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// this device's scratch address (looked up on the first call for the device)
+int scratch_for_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MSA_ERR_NOT_SUPPORTED, "device %d beyond the %d the scratch table keeps", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256))
+      return fail(MSA_ERR_HIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_paged_sparse_fwd_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table, const int32_t* seqused_k,
+                                 const int32_t* q2k, int B, int Sq, int Hq, int Hkv, int D,
+                                 int topk, int page_size, int num_pages, int max_pages, int causal,
+                                 float softmax_scale, int num_splits, int path, int kv_dtype,
+                                 void* o, float* lse, float lse_temperature_scale,
+                                 float* lse_temperature, void* stream) {
+  g_last_error.clear();
+  // The scratch this call needs is the workspace msa_paged_sparse_fwd would take (0 for
+  // one split, and for argument errors, which msa_paged_sparse_fwd reports itself).
+  const size_t need = msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size,
+                                                          max_pages, num_splits, path);
+  if (need > kNoAllocScratchBytes)
+    return fail(MSA_ERR_INVALID_VALUE,
+                "split partials need %zu bytes; the no-allocation entry point holds %zu "
+                "(fewer splits, or msa_paged_sparse_fwd with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "device of the stream");
+    const int rc = scratch_for_device(dev, &ws);
+    if (rc) return rc;
+  }
+  return msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, B, Sq, Hq, Hkv, D,
+                              topk, page_size, num_pages, max_pages, causal, softmax_scale,
+                              num_splits, path, kv_dtype, o, lse, lse_temperature_scale,
+                              lse_temperature, ws, need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 }  // extern "C"

@@ -247,6 +247,35 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * msa_paged_sparse_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. Arguments, results and errors are those of
+ * msa_paged_sparse_fwd, and so are the kernels (results bit for bit equal).
+ *   Scratch: the split partials use a device array inside the library of
+ *   MSA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
+ *   until the process ends. Its device address is looked up on the first call
+ *   on a device (hipGetSymbolAddress, a set-up step that may load the code
+ *   object there); later calls allocate nothing and call no allocating routine.
+ *   Limit: calls whose split partials need more than MSA_NOALLOC_SCRATCH_BYTES
+ *   (msa_paged_sparse_fwd_workspace_size with the same sizes, num_splits and
+ *   path) return MSA_ERR_INVALID_VALUE before any launch. One split (the
+ *   automatic choice on decode batches of 1024 or more (b, hkv, q) rows) needs
+ *   no scratch at all.
+ *   Concurrency: every call on one GPU shares that GPU's array, and each call
+ *   overwrites what the previous one left there; calls that overlap in time on
+ *   one GPU (different streams, or several threads) race and give undefined
+ *   results. Serialise them on one stream.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int msa_paged_sparse_fwd_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table, const int32_t* seqused_k,
+                                 const int32_t* q2k, int B, int Sq, int Hq, int Hkv, int D,
+                                 int topk, int page_size, int num_pages, int max_pages, int causal,
+                                 float softmax_scale, int num_splits, int path, int kv_dtype,
+                                 void* o, float* lse, float lse_temperature_scale,
+                                 float* lse_temperature, void* stream);
+
+/*
  * Dense paged decode with a plan/run split-KV schedule: the q2k = None path of
  * sparse_decode_atten_func and SparseDecodePagedAttentionWrapper.plan / .run on
  * the page "MSA interface.py". Every query row attends to all keys of its

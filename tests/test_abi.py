@@ -278,3 +278,32 @@ def test_decode_plan_and_run_reject_bad_buffers():
                                           ctypes.byref(P16)) == 0
     a = list(run); a[5] = ctypes.byref(P16); a[7] = P16.bytes; a[9] = 1
     assert lib.msa_paged_decode_run(*a) == 2
+
+
+def paged_noalloc(**kw):
+    lib = msa.load_library()
+    a = dict(B=32, Sq=8, Hq=64, Hkv=4, D=128, topk=16, page=128, num_pages=4096, max_pages=128,
+             splits=0, path=1, kvd=0)
+    a.update(kw)
+    return lib.msa_paged_sparse_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Sq"],
+                                            a["Hq"], a["Hkv"], a["D"], a["topk"], a["page"],
+                                            a["num_pages"], a["max_pages"], 1, 0.0, a["splits"],
+                                            a["path"], a["kvd"], FAKE, FAKE, 1.0, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # split partials beyond the scratch array: 16 splits x 16384 rows x 512 B = 128 MiB
+    (dict(splits=16), 1),
+    # argument errors reported as by msa_paged_sparse_fwd
+    (dict(D=64), 2), (dict(topk=33), 2), (dict(Hq=6), 1), (dict(path=2), 1),
+    (dict(splits=-1), 1), (dict(num_pages=0), 1),
+])
+def test_paged_noalloc_rejects_on_host(kw, code):
+    assert paged_noalloc(**kw) == code
+    assert msa.msa_last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    m = re.search(r"#define MSA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == msa.MSA_NOALLOC_SCRATCH_BYTES
