@@ -11,6 +11,7 @@ DIR arguments are rocprofv3 output directories written with --output-format csv:
   --write       rocprofv3 --pmc WRITE_SIZE           on the same bench.py command
   --copy-fetch  rocprofv3 --pmc FETCH_SIZE           on bench.py --copy-calibration MIB
   --copy-write  rocprofv3 --pmc WRITE_SIZE           on bench.py --copy-calibration MIB
+  --util        rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil on the same bench.py command
 
 Writes profiles/kernels_<workload>_<path>.md (per-kernel durations, dominant kernel
 traffic, the exact commands) and profiles/traffic_<workload>_<path>.json (HBM bytes
@@ -77,6 +78,7 @@ def main() -> int:
     ap.add_argument("--commands", help="text file with the commands that produced the dirs")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"])
+    ap.add_argument("--util", help="rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil on the same command")
     args = ap.parse_args()
 
     import bench
@@ -144,6 +146,30 @@ def main() -> int:
                       f"{statistics.median(cw):.0f}; scale {wscale:.1f} B/unit) -> "
                       f"{write_b / 1e9:.3f} GB written",
                       f"- total {traffic / 1e9:.3f} GB per launch"]
+            # every kernel of the step: bytes per launch, and the rate over its traced time
+            lines += ["", "HBM traffic of every kernel per launch (same scaling; rate = bytes / "
+                      "average traced duration):", "",
+                      "| kernel | read GB | written GB | TB/s |", "|---|---|---|---|"]
+            for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+                f = counter_per_dispatch(args.fetch, "FETCH_SIZE", name)
+                wr = counter_per_dispatch(args.write, "WRITE_SIZE", name)
+                if not f or not wr:
+                    continue
+                rb = statistics.median(f) * fscale
+                wb = statistics.median(wr) * wscale
+                lines.append(f"| {short(name)} | {rb / 1e9:.3f} | {wb / 1e9:.3f} | "
+                             f"{(rb + wb) / (statistics.mean(v) * 1e-6) / 1e12:.2f} |")
+    if args.util:
+        lines += ["", "Unit utilisation (rocprofv3 derived metrics, median over dispatches): "
+                  "MfmaUtil = matrix-core busy cycles / (GPU-active cycles x SIMDs); VALUBusy and "
+                  "LdsUtil = VALU- and LDS-active cycles / (GPU-active cycles x CUs).", "",
+                  "| kernel | MfmaUtil % | VALUBusy % | LdsUtil % |", "|---|---|---|---|"]
+        for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            vals = [counter_per_dispatch(args.util, c, name) for c in
+                    ("MfmaUtil", "VALUBusy", "LdsUtil")]
+            if all(vals):
+                lines.append(f"| {short(name)} | " + " | ".join(
+                    f"{statistics.median(x):.1f}" for x in vals) + " |")
     os.makedirs(args.out, exist_ok=True)
     md = os.path.join(args.out, f"kernels_{args.workload}_{args.path}{tag}.md")
     with open(md, "w") as fh:
