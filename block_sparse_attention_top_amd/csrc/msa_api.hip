@@ -115,7 +115,7 @@ int kv_streams(int Hkv) { return Hkv >= 8 ? 8 : (Hkv >= 4 ? 4 : (Hkv >= 2 ? 2 : 
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
 struct KvLayout {
-  size_t row_ptr, q_idx, slot, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, items_by_q,
+  size_t row_ptr, q_idx, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, items_by_q,
       sort_counts, o_part, lse_part, lse_t_part, total;
   long long max_items;
 };
@@ -128,7 +128,6 @@ KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
   size_t off = 0;
   L.row_ptr = off; off += align256(Hkv * (nrows + 1) * 4);
   L.q_idx = off; off += align256(Hkv * cap * 4);
-  L.slot = off; off += align256(Hkv * cap * 4);
   L.csr_ws = off;
   off += align256(csr_workspace_bytes(1, Hkv, static_cast<int>(nq), topk, static_cast<int>(nrows)));
   L.chunk_counts = off; off += align256(nchunk * 4);
@@ -207,18 +206,22 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
   hipError_t e;
+  // q_idx entries hold query * qdiv + slot: the library's own CSR stores each entry as
+  // its index-table position (one int32, half the scatter's stores); a caller's CSR
+  // holds the query ids with the slots beside them
+  int qdiv = 1;
   if (!row_ptr) {
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
     int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
-    int32_t* sl = reinterpret_cast<int32_t*>(ws + L.slot);
     if (vt)
-      e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi, sl,
-                                  ws + L.csr_ws, st, /*ordered=*/false);
+      e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi,
+                                  nullptr, ws + L.csr_ws, st, /*ordered=*/false, /*flat=*/true);
     else
-      e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, sl, ws + L.csr_ws, st,
-                           /*ordered=*/false);
+      e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, nullptr, ws + L.csr_ws,
+                           st, /*ordered=*/false, /*flat=*/true);
     if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
-    row_ptr = rp; q_idx = qi; slot = sl;
+    row_ptr = rp; q_idx = qi; slot = nullptr;
+    qdiv = p.topk;
   }
   const int chunk = chunk_entries_for(p.qpk);
   int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
@@ -244,10 +247,11 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   // marks where its query range starts.
   int4* items = reinterpret_cast<int4*>(ws + L.items);
   e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, q_idx, nq * p.topk, nq,
-                      sb.counts, st);
+                      qdiv, sb.counts, st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
   int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
-  e = launch_kv_items_by_key(items, p.Hkv, q_idx, nq * p.topk, nq, L.max_items, sb, sorted, st);
+  e = launch_kv_items_by_key(items, p.Hkv, q_idx, nq * p.topk, nq, qdiv, L.max_items, sb, sorted,
+                             st);
   if (e != hipSuccess) return hip_fail(e, "kv-centric item order");
   p.items = sorted;
   p.key_start = sb.key_start;

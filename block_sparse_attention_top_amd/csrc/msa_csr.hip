@@ -353,7 +353,9 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
 // LDS: nrows cursors (at most kMaxCsrRows ints = 64 KiB, the dynamic LDS limit).
-template <bool VARLEN, bool I32>
+// FLAT: each entry is stored as its index e = query * topk + slot into the KV head's
+// index table (one int32 instead of a query and a slot); slot is unused.
+template <bool VARLEN, bool I32, bool FLAT>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ q_idx, int32_t* __restrict__ slot, int32_t* __restrict__ row_ptr) {
@@ -389,6 +391,10 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     for (int k = 0; k < kCsrBatch; ++k) {
       if (rows[k] < 0) continue;
       const long long e = rb + 256 * k + threadIdx.x;
+      if (FLAT) {
+        qi[pos[k]] = static_cast<int32_t>(e);
+        continue;
+      }
       const long long q = idx_div<I32>(e, a.topk);
       qi[pos[k]] = static_cast<int32_t>(q);
       if (sl) sl[pos[k]] = static_cast<int32_t>(e - q * a.topk);
@@ -471,6 +477,86 @@ __global__ void zero_ints_kernel(int32_t* __restrict__ p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Exclusive scan of at most kScanOneMax values in one workgroup of 1024 threads. Tile j
+// holds values [4096 j, 4096 (j + 1)); thread t loads and stores its four values of
+// each tile as one 16-byte vector (coalesced across the wave). Each wave scans its
+// 256 values of a tile with lane shuffles; one wave then scans the (tile, wave)
+// totals in order, which gives every wave's run its offset. out[n] = the total.
+constexpr int kScanOneThreads = 1024;
+constexpr int kScanOneTiles = 16;
+constexpr long long kScanOneMax = 4LL * kScanOneThreads * kScanOneTiles;
+__global__ __launch_bounds__(kScanOneThreads) void scan_one_block_kernel(
+    const int32_t* __restrict__ in, int n, int32_t* __restrict__ out) {
+  constexpr int kWaves = kScanOneThreads / 64;
+  __shared__ int blk[kScanOneTiles * kWaves];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int T = (n + 4 * kScanOneThreads - 1) / (4 * kScanOneThreads);
+  int4 v[kScanOneTiles];
+  int pre[kScanOneTiles];
+#pragma unroll
+  for (int j = 0; j < kScanOneTiles; ++j) {
+    v[j] = make_int4(0, 0, 0, 0);
+    pre[j] = 0;
+    if (j < T) {
+      const int k = j * 4 * kScanOneThreads + 4 * t;
+      if (k + 3 < n) {
+        v[j] = *reinterpret_cast<const int4*>(in + k);
+      } else {
+        v[j].x = k < n ? in[k] : 0;
+        v[j].y = k + 1 < n ? in[k + 1] : 0;
+        v[j].z = k + 2 < n ? in[k + 2] : 0;
+      }
+      const int own = v[j].x + v[j].y + v[j].z + v[j].w;
+      int x = own;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      pre[j] = x - own;
+      if (lane == 63) blk[j * kWaves + wave] = x;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scan of the T * kWaves (tile, wave) totals, 4 per lane
+    int a[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = 4 * lane + i < T * kWaves ? blk[4 * lane + i] : 0;
+      own += a[i];
+    }
+    int x = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    int run = x - own;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * lane + i < T * kWaves) blk[4 * lane + i] = run;
+      run += a[i];
+    }
+    if (lane == 63) out[n] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kScanOneTiles; ++j) {
+    if (j < T) {
+      const int k = j * 4 * kScanOneThreads + 4 * t;
+      const int b = blk[j * kWaves + wave] + pre[j];
+      const int4 o = make_int4(b, b + v[j].x, b + v[j].x + v[j].y, b + v[j].x + v[j].y + v[j].z);
+      if (k + 3 < n) {
+        *reinterpret_cast<int4*>(out + k) = o;
+      } else {
+        if (k < n) out[k] = o.x;
+        if (k + 1 < n) out[k + 1] = o.y;
+        if (k + 2 < n) out[k + 2] = o.z;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t scan_tmp_ints(long long n) { return static_cast<size_t>((n + kScanTile - 1) / kScanTile) + 1; }
@@ -478,6 +564,11 @@ size_t scan_tmp_ints(long long n) { return static_cast<size_t>((n + kScanTile - 
 hipError_t launch_exclusive_scan(const int32_t* in, int32_t* out, long long n, int32_t* tmp,
                                  hipStream_t stream) {
   if (n <= 0) return hipErrorInvalidValue;
+  if (n <= kScanOneMax && (reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) % 16 == 0) {
+    hipLaunchKernelGGL(scan_one_block_kernel, dim3(1), dim3(kScanOneThreads), 0, stream, in,
+                       static_cast<int>(n), out);
+    return hipGetLastError();
+  }
   const long long ntiles = (n + kScanTile - 1) / kScanTile;
   if (ntiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(scan_tile_sums, dim3(static_cast<unsigned>(ntiles)), dim3(kScanThreads), 0,
@@ -532,7 +623,7 @@ CsrPlan csr_plan_unordered(int Hkv, long long nq, int topk, int nrows) {
 
 template <bool VARLEN, bool I32>
 hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
-                          void* ws, hipStream_t stream, bool ordered) {
+                          void* ws, hipStream_t stream, bool ordered, bool flat) {
   const int nrows = a.nrows;
   // the plan depends on the query count and the rows only: B * Sq == nq
   const CsrPlan plan = ordered ? csr_plan(1, a.Hkv, static_cast<int>(a.nq), a.topk, nrows)
@@ -564,9 +655,12 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   else if (ordered)
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
-  else  // the order-free scatter also writes the row pointers (from its tile-0 blocks)
-    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32>), grid, dim3(256), lds, stream, a,
-                       plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
+  else if (flat)  // the order-free scatter also writes the row pointers (tile-0 blocks)
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, true>), grid, dim3(256), lds,
+                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
+  else
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, false>), grid, dim3(256), lds,
+                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
   if (ordered) {
     const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
     hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
@@ -577,36 +671,37 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
 
 template <bool VARLEN>
 hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                     hipStream_t stream, bool ordered) {
+                     hipStream_t stream, bool ordered, bool flat) {
+  if (flat && (ordered || a.nq * a.topk >= (1LL << 31))) return hipErrorInvalidValue;
   if (a.nq * a.topk < (1LL << 31))
-    return build_csr_impl<VARLEN, true>(a, row_ptr, q_idx, slot, ws, stream, ordered);
-  return build_csr_impl<VARLEN, false>(a, row_ptr, q_idx, slot, ws, stream, ordered);
+    return build_csr_impl<VARLEN, true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
+  return build_csr_impl<VARLEN, false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
 }
 
 }  // namespace
 
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream, bool ordered) {
+                            hipStream_t stream, bool ordered, bool flat) {
   CsrSrc a{};
   a.q2k = q2k;
   a.Hkv = Hkv; a.Sq = Sq; a.topk = topk; a.nblk = nblk;
   a.nrows = B * nblk;
   a.nq = static_cast<long long>(B) * Sq;
-  return build_csr<false>(a, row_ptr, q_idx, slot, ws, stream, ordered);
+  return build_csr<false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
 }
 
 hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, int Hkv,
                                    int total_q, int topk, int nrows, int32_t* row_ptr,
                                    int32_t* q_idx, int32_t* slot, void* ws, hipStream_t stream,
-                                   bool ordered) {
+                                   bool ordered, bool flat) {
   CsrSrc a{};
   a.q2k = q2k;
   a.q_rows = t.q_rows;
   a.Hkv = Hkv; a.Sq = total_q; a.topk = topk; a.nblk = 0;
   a.nrows = nrows;
   a.nq = total_q;
-  return build_csr<true>(a, row_ptr, q_idx, slot, ws, stream, ordered);
+  return build_csr<true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
 }
 
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,

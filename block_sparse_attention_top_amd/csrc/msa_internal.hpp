@@ -263,8 +263,9 @@ struct KvParams {
   const void* v;
   int kv_fp8;
   const int32_t* row_ptr;    // [Hkv, nrows+1]
-  const int32_t* q_idx;      // [Hkv, cap]
-  const int32_t* slot;       // [Hkv, cap]
+  const int32_t* q_idx;      // [Hkv, cap]: the query of each entry, or (slot == nullptr)
+                             // its index query * topk + slot into the index table
+  const int32_t* slot;       // [Hkv, cap] or nullptr
   const int4* items;         // (hkv, row, first entry, entry count), in key order
   const int32_t* key_start;  // [kKvKeys + 1] first item of each key (the streams' bounds)
   int32_t* stream_next;      // [kKvStreams] items taken from each stream (zero on entry)
@@ -304,15 +305,16 @@ inline KvSortBuffers kv_sort_buffers(int32_t* base) {
   return KvSortBuffers{base, base + kKvKeys, base + kKvSortZeroInts,
                        base + kKvSortZeroInts + kKvKeys};
 }
-// items[c] for every chunk of every row, and the per-key item counts (q_idx [Hkv][cap],
-// nq query rows; key_counts zero on entry)
+// items[c] for every chunk of every row, and the per-key item counts (q_idx [Hkv][cap]
+// holding query * qdiv + slot, qdiv = 1 for plain query ids; nq query rows; key_counts
+// zero on entry)
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
                            int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
-                           long long nq, int32_t* key_counts, hipStream_t stream);
+                           long long nq, int qdiv, int32_t* key_counts, hipStream_t stream);
 // the item table in key order (at most max_items items; the count is read on the device)
 hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_idx, long long cap,
-                                  long long nq, long long max_items, const KvSortBuffers& sb,
-                                  int4* out, hipStream_t stream);
+                                  long long nq, int qdiv, long long max_items,
+                                  const KvSortBuffers& sb, int4* out, hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 
@@ -346,16 +348,19 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows);
 // ordered = true: entries of a row ascending in (query, slot), the unique CSR
 // ordered = false: same rows and entry sets, order inside a row unspecified
 // (used internally by the kv-centric path, whose results do not depend on it)
+// flat (ordered = false only, B*Sq*topk < 2^31): q_idx holds each entry as its index
+// query * topk + slot into the KV head's index table; slot is not written
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream, bool ordered = true);
+                            hipStream_t stream, bool ordered = true, bool flat = false);
 // varlen CSR over nrows rows (q2k [Hkv,total_q,topk]); the tables come from
 // launch_varlen_tables; entries whose row is >= nrows are dropped. Workspace:
 // csr_workspace_bytes(1, Hkv, total_q, topk, nrows).
 hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, int Hkv,
                                    int total_q, int topk,
                                    int nrows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
-                                   void* ws, hipStream_t stream, bool ordered = true);
+                                   void* ws, hipStream_t stream, bool ordered = true,
+                                   bool flat = false);
 // per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix;
 // also sets zero_ints[0, nzero) to 0 when zero_ints is given
 hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,

@@ -80,9 +80,18 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
   const long long blk0 = static_cast<long long>(s) * kBlk;
 
   // stage the chunk's entries and the block's K and V (128 tokens x 256 B each)
-  for (int i = tid; i < ne; i += 256) {
-    ent_q[i] = p.q_idx[hkv * p.cap + e0 + i];
-    ent_t[i] = p.slot[hkv * p.cap + e0 + i];
+  if (p.slot) {
+    for (int i = tid; i < ne; i += 256) {
+      ent_q[i] = p.q_idx[hkv * p.cap + e0 + i];
+      ent_t[i] = p.slot[hkv * p.cap + e0 + i];
+    }
+  } else {  // entries stored as index-table positions query * topk + slot
+    for (int i = tid; i < ne; i += 256) {
+      const int e = p.q_idx[hkv * p.cap + e0 + i];
+      const int q = static_cast<int>(static_cast<uint32_t>(e) / static_cast<uint32_t>(p.topk));
+      ent_q[i] = q;
+      ent_t[i] = e - q * p.topk;
+    }
   }
   {
     // rows past the sequence's last key re-read that key; they are masked out of S.
@@ -391,36 +400,30 @@ __device__ __forceinline__ int item_key(int hkv, long long first_q, long long nq
 }
 
 // items[c] = (hkv, row, first entry, entry count) for every chunk c of every row; each
-// item is also counted under its key (the first queries of 8 chunks loaded together,
-// counts gathered per block in LDS) into key_counts[kKvKeys] (zero on entry).
+// item is also counted under its key (counts gathered per block in LDS) into
+// key_counts[kKvKeys] (zero on entry). One wave per (KV head, row): lane l writes the
+// row's chunks l, l + 64, ..., so that a long row is spread over a wave and every
+// first-query load of a round is in flight together.
 __global__ __launch_bounds__(256) void kv_items_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
     int chunk_entries, int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap,
-    long long nq, int32_t* __restrict__ key_counts) {
+    long long nq, int qdiv, int32_t* __restrict__ key_counts) {
   __shared__ int hist[kKvKeys];
   for (int i = threadIdx.x; i < kKvKeys; i += 256) hist[i] = 0;
   __syncthreads();
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long long idx = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (idx < static_cast<long long>(Hkv) * nrows) {
     const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
     const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
     const int beg = rp[r], end = rp[r + 1];
-    int c = chunk_ptr[idx];
-    constexpr int kB = 8;
-    for (int e0 = beg; e0 < end; e0 += kB * chunk_entries) {
-      int q[kB];
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const int e = e0 + k * chunk_entries;
-        q[k] = q_idx[hkv * cap + (e < end ? e : end - 1)];
-      }
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const int e = e0 + k * chunk_entries;
-        if (e >= end) break;
-        items[c++] = make_int4(hkv, r, e, min(chunk_entries, end - e));
-        atomicAdd(&hist[item_key(hkv, q[k], nq, Hkv)], 1);
-      }
+    const int c0 = chunk_ptr[idx];
+    const int nch = (end - beg + chunk_entries - 1) / chunk_entries;
+    for (int j = lane; j < nch; j += 64) {
+      const int e = beg + j * chunk_entries;
+      const int q = q_idx[hkv * cap + e] / qdiv;
+      items[c0 + j] = make_int4(hkv, r, e, min(chunk_entries, end - e));
+      atomicAdd(&hist[item_key(hkv, q, nq, Hkv)], 1);
     }
   }
   __syncthreads();
@@ -468,8 +471,8 @@ __global__ __launch_bounds__(256) void kv_sort_scan(const int32_t* __restrict__ 
 // writes its own partials, so the results do not depend on it.
 __global__ __launch_bounds__(256) void kv_sort_scatter(
     const int4* __restrict__ items, const int32_t* __restrict__ key_start, int Hkv,
-    const int32_t* __restrict__ q_idx, long long cap, long long nq, int32_t* __restrict__ cursor,
-    int4* __restrict__ out) {
+    const int32_t* __restrict__ q_idx, long long cap, long long nq, int qdiv,
+    int32_t* __restrict__ cursor, int4* __restrict__ out) {
   __shared__ int h[kKvKeys];
   __shared__ int base[kKvKeys];
   const int total = key_start[kKvKeys];
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(256) void kv_sort_scatter(
   int key = -1, rank = 0;
   if (c < total) {
     it = items[c];
-    key = item_key(it.x, q_idx[it.x * cap + it.z], nq, Hkv);
+    key = item_key(it.x, q_idx[it.x * cap + it.z] / qdiv, nq, Hkv);
     rank = atomicAdd(&h[key], 1);
   }
   __syncthreads();
@@ -509,24 +512,24 @@ void kv_launch(const KvParams& p, dim3 grid, hipStream_t stream) {
 
 hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
                            int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
-                           long long nq, int32_t* key_counts, hipStream_t stream) {
+                           long long nq, int qdiv, int32_t* key_counts, hipStream_t stream) {
   const long long n = static_cast<long long>(Hkv) * nrows;
   if (nq <= 0 || !key_counts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
                      stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items, q_idx, cap, nq,
-                     key_counts);
+                     qdiv, key_counts);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_idx, long long cap,
-                                  long long nq, long long max_items, const KvSortBuffers& sb,
-                                  int4* out, hipStream_t stream) {
+                                  long long nq, int qdiv, long long max_items,
+                                  const KvSortBuffers& sb, int4* out, hipStream_t stream) {
   if (nq <= 0 || max_items <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((max_items + 255) / 256));
   hipLaunchKernelGGL(kv_sort_scan, dim3(1), dim3(256), 0, stream, sb.counts, sb.key_start,
                      sb.cursor);
   hipLaunchKernelGGL(kv_sort_scatter, grid, dim3(256), 0, stream, items, sb.key_start, Hkv, q_idx,
-                     cap, nq, sb.cursor, out);
+                     cap, nq, qdiv, sb.cursor, out);
   return hipGetLastError();
 }
 
