@@ -180,6 +180,7 @@ __device__ __forceinline__ void rank_in_batch(int row, int& rank, int& cnt) {
 }
 
 constexpr int kCsrBatch = 8;  // entries per thread whose index loads are in flight together
+constexpr size_t kCsrMaskLdsMax = 150 * 1024;  // LDS of the mask-ranked scatter, at most
 
 // Query tile of workgroup x. Workgroups are dealt round-robin over the 8 XCDs, and
 // consecutive tiles write adjacent counts and adjacent runs of a row's entries, so
@@ -284,12 +285,18 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
 // wave, per row, the position after the entries of the lower quarters; each wave
 // finally runs the ballot-ranked scatter above on its quarter. Same output bits,
 // four times the waves. LDS: 4 * nrows ints.
-template <bool VARLEN, bool I32>
+//
+// MASK: the lanes of a batch find the peers holding their row through a per-wave
+// table of 64-bit lane masks in LDS (each lane ORs its bit into its row's mask and
+// reads it back; the row's last lane clears it), in a constant number of steps
+// instead of one ballot pass per distinct row of the batch: on wide tables nearly
+// every entry of a batch has a row of its own. LDS: 4 * nrows * (4 + 8) bytes.
+template <bool VARLEN, bool I32, bool MASK>
 __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q, int ntiles,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ q_idx,
                                                            int32_t* __restrict__ slot) {
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(8))) int lds[];
   constexpr int kPer = 16;  // entries per lane per round
   const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -301,7 +308,15 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
   const long long sub = (g1 - g0 + 3) / 4;
   const long long w0 = std::min(g1, g0 + wave * sub), w1 = std::min(g1, w0 + sub);
   int* cursor = lds + wave * nrows;
+  // MASK: the waves' mask tables follow the 4 * nrows cursors (8-byte aligned: nrows
+  // is rounded up to even)
+  unsigned long long* mask =
+      reinterpret_cast<unsigned long long*>(lds + 4 * ((nrows + 1) & ~1)) + wave * nrows;
   for (int r = tid; r < 4 * nrows; r += 256) lds[r] = 0;
+  if (MASK) {
+    unsigned long long* all = reinterpret_cast<unsigned long long*>(lds + 4 * ((nrows + 1) & ~1));
+    for (int r = tid; r < 4 * nrows; r += 256) all[r] = 0;
+  }
   __syncthreads();
   for (long long rb = w0 * a.topk; rb < w1 * a.topk; rb += 64 * kCsrBatch) {
     int rows[kCsrBatch];
@@ -333,13 +348,27 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
       const long long e = rb + 64 * k + lane;
       const int row = rows[k];
       int rank = 0, cnt = 0;
-      rank_in_batch(row, rank, cnt);
+      if (MASK) {
+        // one wave, LDS accesses in program order: every OR lands before the reads
+        if (row >= 0) atomicOr(&mask[row], 1ull << lane);
+        __builtin_amdgcn_wave_barrier();
+        if (row >= 0) {
+          const unsigned long long peers = mask[row];
+          rank = __popcll(peers & __lanemask_lt());
+          cnt = __popcll(peers);
+        }
+      } else {
+        rank_in_batch(row, rank, cnt);
+      }
       // this wave's cursors only: its lanes read before the last-ranked lane of a row
       // writes (one wave, LDS accesses in program order)
       int pos = 0;
       if (row >= 0) pos = cursor[row] + rank;
       __builtin_amdgcn_wave_barrier();
-      if (row >= 0 && rank == cnt - 1) cursor[row] = pos + 1;
+      if (row >= 0 && rank == cnt - 1) {
+        cursor[row] = pos + 1;
+        if (MASK) mask[row] = 0;
+      }
       if (row >= 0) {
         const long long q = idx_div<I32>(e, a.topk);
         qi[pos] = static_cast<int32_t>(q);
@@ -649,9 +678,23 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
-  if (ordered && 4 * lds <= 64 * 1024)  // within the default dynamic LDS limit
-    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32>), grid, dim3(256), 4 * lds, stream, a,
-                       plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  // the mask-ranked scatter where its tables fit the LDS (a workgroup may take up to
+  // 160 KiB on gfx950; above 64 KiB the kernel must be allowed to), else ballot ranks
+  const size_t lds_mask = 4 * (static_cast<size_t>((nrows + 1) & ~1) * 4 +
+                               static_cast<size_t>(nrows) * 8);
+  bool mask_ok = ordered && lds_mask <= kCsrMaskLdsMax;
+  if (mask_ok && lds_mask > 64 * 1024)
+    mask_ok = hipFuncSetAttribute(
+                  reinterpret_cast<const void*>(&csr_scatter4_kernel<VARLEN, I32, true>),
+                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                  static_cast<int>(lds_mask)) == hipSuccess;
+  (void)hipGetLastError();  // a refused attribute leaves the ballot-ranked scatter
+  if (mask_ok)
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, true>), grid, dim3(256), lds_mask, stream,
+                       a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  else if (ordered && 4 * lds <= 64 * 1024)  // within the default dynamic LDS limit
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, false>), grid, dim3(256), 4 * lds, stream,
+                       a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   else if (ordered)
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);

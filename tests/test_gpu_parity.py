@@ -405,6 +405,23 @@ def test_full_size(key):
     say(f"[full] {key}: {stats}")
 
 
+@pytest.mark.parametrize("key", ["c2", "c4b"])
+def test_full_size_prebuilt_csr_bit_identical(key):
+    """The forward given the public ordered CSR equals the forward that builds its own
+    order-free CSR (entries stored as index-table positions), bit for bit: every
+    (query, slot) partial depends only on its own row, whatever the item it runs in."""
+    import block_sparse_attention_top_amd as msa
+    w = wl.WORKLOADS[key]
+    say(f"[full] {key} {w.name}: own CSR against the public ordered CSR")
+    inp = wl.make_inputs(w)
+    q, k, v, q2k = (to_dev(inp[n]) for n in ("q", "k", "v", "q2k"))
+    o1, l1 = msa.msa_sparse_fwd(q, k, v, q2k, causal=w.causal, path=KV)
+    csr = msa.msa_build_k2q_csr(q2k, w.Skv // w.blk)
+    o2, l2 = msa.msa_sparse_fwd(q, k, v, q2k, *csr, causal=w.causal, path=KV)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 @pytest.fixture(scope="module")
 def c5_case():
     w = wl.WORKLOADS["c5"]

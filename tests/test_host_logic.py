@@ -52,3 +52,41 @@ def test_query_bucket_monotone_and_in_range(bucket_exe):
     got = _run(bucket_exe, [(q, nq, 256) for q in qs])
     assert min(got) == 0 and max(got) == 255
     assert all(a <= b for a, b in zip(got, got[1:]))
+
+
+def test_bench_skew_diagnostics_brute_force():
+    """bench.py's index-skew summary (CSR row lengths, block-0 share, per-query fan-out)
+    against a brute-force count over a small table with -1 and out-of-range ids."""
+    import sys
+    sys.path.insert(0, os.path.dirname(HERE))
+    import bench
+    import workloads as wl
+    w = wl.Workload("tiny", B=2, Sq=40, Skv=640, Hkv=2, qpk=2, topk=4, causal=True,
+                    mode=wl.MODE_CAUSAL)
+    rng = np.random.default_rng(3)
+    q2k = rng.integers(-2, 7, size=(w.B, w.Hkv, w.Sq, w.topk)).astype(np.int32)  # 5 blocks
+    d = bench.skew_diagnostics(w, q2k)
+    nblk = w.Skv // w.blk
+    counts = {}
+    per_row = []
+    b0 = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for q in range(w.Sq):
+                n = 0
+                for t in range(w.topk):
+                    s = int(q2k[b, h, q, t])
+                    if 0 <= s < nblk:
+                        counts[(h, b * nblk + s)] = counts.get((h, b * nblk + s), 0) + 1
+                        n += 1
+                        b0 += s == 0
+                per_row.append(n)
+    allc = [counts.get((h, r), 0) for h in range(w.Hkv) for r in range(w.B * nblk)]
+    assert d["valid_entries"] == sum(allc) == sum(per_row)
+    assert d["csr_rows"] == len(allc)
+    assert d["row_len_max"] == max(allc)
+    assert d["empty_rows"] == sum(c == 0 for c in allc)
+    assert abs(d["row_len_mean"] - np.mean(allc)) < 0.06
+    assert d["block0_share"] == round(b0 / sum(allc), 4)
+    assert d["fanout_min"] == min(per_row)
+    assert d["queries_with_no_slot"] == sum(n == 0 for n in per_row)
