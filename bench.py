@@ -46,15 +46,42 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed: what the compiler
+    sees, so that an edit of a comment does not count as a change of the kernel."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest(kernel: str) -> str:
-    """Hash of a kernel's source and the shared header: a counter summary is reused
-    only while the kernel it measured is unchanged."""
+    """Hash of the code (comments and layout stripped) of a kernel's sources and the
+    shared header: a counter summary is reused only while the kernel it measured is
+    unchanged."""
     import hashlib
     srcs = next(f for k, f in KERNEL_SOURCES.items() if kernel.startswith(k))
     h = hashlib.sha256()
     for f in srcs + ("msa_internal.hpp",):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
