@@ -296,23 +296,30 @@ class Case:
             fwd = lambda: msa.msa_sparse_fwd(t["q"], t["k"], t["v"], t["q2k"], *csr,
                                              causal=w.causal, path=2, o=self.o, lse=self.lse)
 
-        def timed(fn):
+        def timed(fn, n):
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            for _ in range(steps):
+            for _ in range(n):
                 fn()
             b.record()
             b.synchronize()
-            return a.elapsed_time(b) / steps
+            return a.elapsed_time(b) / n
 
-        csr_ms = timed(build)
-        fwd_ms = timed(fwd)
-        both_ms = timed(self.step)
-        return {"csr_ms": csr_ms, "fwd_ms": fwd_ms, "csr_plus_fwd_ms": both_ms,
-                "fwd_TFLOP_per_s": self.flops / (fwd_ms * 1e-3) / 1e12}
+        # The three loops alternate over several rounds and each reports its median: a
+        # fixed order (build, then forward, then step) let the clock's drift under
+        # sustained load favour whichever loop ran later.
+        rounds, n = 3, max(3, steps // 2)
+        res = {"csr": [], "fwd": [], "both": []}
+        for _ in range(rounds):
+            res["csr"].append(timed(build, n))
+            res["fwd"].append(timed(fwd, n))
+            res["both"].append(timed(self.step, n))
+        med = {k: float(np.median(v)) for k, v in res.items()}
+        return {"csr_ms": med["csr"], "fwd_ms": med["fwd"], "csr_plus_fwd_ms": med["both"],
+                "fwd_TFLOP_per_s": self.flops / (med["fwd"] * 1e-3) / 1e12}
 
     def metric(self, ms: float, kernel_ms: float) -> dict:
         if self.w.paged:
