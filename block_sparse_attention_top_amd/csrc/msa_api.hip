@@ -115,25 +115,21 @@ int kv_streams(int Hkv) { return Hkv >= 8 ? 8 : (Hkv >= 4 ? 4 : (Hkv >= 2 ? 2 : 
 int chunk_entries_for(int qpk) { return std::min(kKvMaxEntries, kKvChunkRows / qpk); }
 
 struct KvLayout {
-  size_t row_ptr, q_idx, csr_ws, chunk_counts, chunk_ptr, scan_tmp, items, items_by_q,
-      sort_counts, o_part, lse_part, lse_t_part, total;
+  size_t row_ptr, q_idx, csr_ws, items, items_by_q, sort_counts, o_part, lse_part, lse_t_part,
+      total;
   long long max_items;
 };
 
 // nq query rows (B * Sq, or total_q), nrows CSR rows
 KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
   const long long cap = nq * topk;
-  const long long nchunk = static_cast<long long>(Hkv) * nrows;
   KvLayout L;
   size_t off = 0;
   L.row_ptr = off; off += align256(Hkv * (nrows + 1) * 4);
   L.q_idx = off; off += align256(Hkv * cap * 4);
   L.csr_ws = off;
   off += align256(csr_workspace_bytes(1, Hkv, static_cast<int>(nq), topk, static_cast<int>(nrows)));
-  L.chunk_counts = off; off += align256(nchunk * 4);
-  L.chunk_ptr = off; off += align256((nchunk + 1) * 4);
-  L.scan_tmp = off; off += align256(scan_tmp_ints(nchunk) * 4);
-  // sum over rows of ceil(len / chunk) <= nnz / chunk + rows
+  // one slot per possible item (kv_item_slot): per KV head cap / chunk + nrows + 1
   L.max_items = static_cast<long long>(Hkv) * (cap / chunk_entries_for(Hq / Hkv) + nrows + 1);
   L.items = off; off += align256(L.max_items * 16);
   L.items_by_q = off; off += align256(L.max_items * 16);
@@ -192,8 +188,8 @@ size_t paged_workspace(int B, int Sq, int Hq, int splits) {
   return align256(splits * rows * kD * 4) + 2 * align256(splits * rows * 4);
 }
 
-// The kv-centric pipeline: k2q CSR (unless given), chunk schedule, item table,
-// per-block partials, slot combine. `p` carries the problem (and, for a varlen
+// The kv-centric pipeline: k2q CSR (unless given) and the work items, items in key
+// order, per-block partials, slot combine. `p` carries the problem (and, for a varlen
 // batch, cu_q / cu_k / total sizes); vt != nullptr selects the varlen layout,
 // its tables already built on the stream.
 int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
@@ -206,31 +202,39 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
   hipError_t e;
+  const int chunk = chunk_entries_for(p.qpk);  // a power of two
+  int chunk_shift = 0;
+  while ((1 << chunk_shift) < chunk) ++chunk_shift;
+  const KvSortBuffers sb = kv_sort_buffers(reinterpret_cast<int32_t*>(ws + L.sort_counts));
+  int4* items = reinterpret_cast<int4*>(ws + L.items);
   // q_idx entries hold query * qdiv + slot: the library's own CSR stores each entry as
   // its index-table position (one int32, half the scatter's stores); a caller's CSR
   // holds the query ids with the slots beside them
   int qdiv = 1;
   if (!row_ptr) {
+    // the order-free CSR lists the work items (one per chunk of each row) while it
+    // scatters; its count pass clears the item counters
     int32_t* rp = reinterpret_cast<int32_t*>(ws + L.row_ptr);
     int32_t* qi = reinterpret_cast<int32_t*>(ws + L.q_idx);
+    const KvItemEmit emit{items, L.max_items / p.Hkv, L.max_items, sb, chunk_shift};
     if (vt)
       e = launch_build_csr_varlen(q2k, *vt, p.Hkv, static_cast<int>(nq), p.topk, nrows, rp, qi,
-                                  nullptr, ws + L.csr_ws, st, /*ordered=*/false, /*flat=*/true);
+                                  nullptr, ws + L.csr_ws, st, /*ordered=*/false, /*flat=*/true,
+                                  &emit);
     else
       e = launch_build_csr(q2k, p.B, p.Hkv, p.Sq, p.topk, p.nblk, rp, qi, nullptr, ws + L.csr_ws,
-                           st, /*ordered=*/false, /*flat=*/true);
+                           st, /*ordered=*/false, /*flat=*/true, &emit);
     if (e != hipSuccess) return hip_fail(e, "k2q CSR build");
     row_ptr = rp; q_idx = qi; slot = nullptr;
     qdiv = p.topk;
+  } else {
+    e = launch_zero_ints(sb.counts, kKvSortZeroInts, reinterpret_cast<int32_t*>(items),
+                         4 * L.max_items, st);
+    if (e == hipSuccess)
+      e = launch_kv_items(row_ptr, p.Hkv, nrows, chunk_shift, L.max_items / p.Hkv, items, q_idx,
+                          nq * p.topk, nq, qdiv, sb, st);
+    if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
   }
-  const int chunk = chunk_entries_for(p.qpk);
-  int32_t* chunk_ptr = reinterpret_cast<int32_t*>(ws + L.chunk_ptr);
-  const KvSortBuffers sb = kv_sort_buffers(reinterpret_cast<int32_t*>(ws + L.sort_counts));
-  e = launch_chunk_schedule(row_ptr, p.Hkv, nrows, chunk,
-                            reinterpret_cast<int32_t*>(ws + L.chunk_counts), chunk_ptr,
-                            reinterpret_cast<int32_t*>(ws + L.scan_tmp), st, sb.counts,
-                            kKvSortZeroInts);
-  if (e != hipSuccess) return hip_fail(e, "kv-centric schedule");
   p.row_ptr = row_ptr; p.q_idx = q_idx; p.slot = slot;
   p.chunk_entries = chunk;
   p.o_part = reinterpret_cast<uint16_t*>(ws + L.o_part);
@@ -240,15 +244,11 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
     p.rowbase = vt->rowbase;
     p.row_seq = vt->row_seq;
   }
-  // The item table, then the same items ordered by (KV head, first query) and cut into
-  // one stream per XCD: the items running together on an XCD then gather Q rows from
-  // one narrow query range of one KV head, which stays in that XCD's L2. The order-free
-  // CSR lists each row's entries in ascending query tiles, so an item's first query
-  // marks where its query range starts.
-  int4* items = reinterpret_cast<int4*>(ws + L.items);
-  e = launch_kv_items(row_ptr, chunk_ptr, p.Hkv, nrows, chunk, items, q_idx, nq * p.topk, nq,
-                      qdiv, sb.counts, st);
-  if (e != hipSuccess) return hip_fail(e, "kv-centric item table");
+  // The items ordered by (KV head, first query) and cut into one stream per XCD: the
+  // items running together on an XCD then gather Q rows from one narrow query range of
+  // one KV head, which stays in that XCD's L2. The order-free CSR lists each row's
+  // entries in ascending query tiles, so an item's first query marks where its query
+  // range starts.
   int4* sorted = reinterpret_cast<int4*>(ws + L.items_by_q);
   e = launch_kv_items_by_key(items, p.Hkv, q_idx, nq * p.topk, nq, qdiv, L.max_items, sb, sorted,
                              st);

@@ -206,12 +206,33 @@ __device__ __forceinline__ void load_rows(const CsrSrc& a, int hkv, long long e0
   }
 }
 
+// Fill of zeros over two int ranges, shared out over all workgroups of the grid.
+__device__ __forceinline__ void grid_zero2(int32_t* p0, long long n0, int32_t* p1, long long n1) {
+  const long long nb = static_cast<long long>(gridDim.x) * gridDim.y;
+  const long long b = static_cast<long long>(blockIdx.y) * gridDim.x + blockIdx.x;
+  for (long long i = b * blockDim.x + threadIdx.x; i < n0 + n1; i += nb * blockDim.x) {
+    if (i < n0) p0[i] = 0;
+    else p1[i - n0] = 0;
+  }
+}
+
+// z: ranges the grid also clears (the kv-centric item table and its counters, filled
+// by the scatter that follows)
+struct ZeroRanges {
+  int32_t* p0;
+  long long n0;
+  int32_t* p1;
+  long long n1;
+};
+
 template <bool VARLEN, bool I32, int NT>
 __global__ __launch_bounds__(NT) void csr_count_kernel(CsrSrc a, int tile_q, int ntiles,
-                                                        int32_t* __restrict__ counts) {
+                                                        int32_t* __restrict__ counts,
+                                                        ZeroRanges z) {
   extern __shared__ int cnt[];
   const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int nrows = a.nrows;
+  if (z.n0 + z.n1 > 0) grid_zero2(z.p0, z.n0, z.p1, z.n1);
   for (int r = threadIdx.x; r < nrows; r += blockDim.x) cnt[r] = 0;
   __syncthreads();
   const long long g0 = static_cast<long long>(tile) * tile_q;
@@ -381,24 +402,34 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
 
 // Unordered scatter: every entry of a (row, tile) segment lands inside that
 // segment, slot claimed with an LDS atomic (order within a segment unspecified).
-// LDS: nrows cursors (at most kMaxCsrRows ints = 64 KiB, the dynamic LDS limit).
+// LDS: nrows cursors (at most kMaxCsrRows ints), and with ITEMS each row's first
+// position and a histogram of the listed items' keys beside them.
 // FLAT: each entry is stored as its index e = query * topk + slot into the KV head's
 // index table (one int32 instead of a query and a slot); slot is unused.
-template <bool VARLEN, bool I32, bool FLAT>
+// ITEMS: the entry that lands on the first position of a chunk of 2^chunk_shift
+// entries of its row writes the chunk's kv-centric work item to its slot (KvItemEmit);
+// the workgroup's item counts per key go out at its end, one atomic per key used.
+template <bool VARLEN, bool I32, bool FLAT, bool ITEMS>
 __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     CsrSrc a, int tile_q, int ntiles, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ q_idx, int32_t* __restrict__ slot, int32_t* __restrict__ row_ptr) {
+    int32_t* __restrict__ q_idx, int32_t* __restrict__ slot, int32_t* __restrict__ row_ptr,
+    KvItemEmit emit) {
   extern __shared__ int cursor[];
   const int tile = csr_tile_of(blockIdx.x, ntiles), hkv = blockIdx.y;
   const int nrows = a.nrows;
+  int* rowbeg = cursor + nrows;  // ITEMS only
+  int* hist = rowbeg + nrows;    // ITEMS only: [kKvKeys]
   const long long cap = a.nq * a.topk;
   const long long seg = static_cast<long long>(hkv) * nrows * ntiles;
   const int base_h = offsets[seg];
   for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
     cursor[r] = offsets[seg + static_cast<long long>(r) * ntiles + tile] - base_h;
+    if (ITEMS) rowbeg[r] = offsets[seg + static_cast<long long>(r) * ntiles] - base_h;
     // tile 0 holds each row's first position: the row pointers of this KV head
     if (row_ptr && tile == 0) row_ptr[static_cast<long long>(hkv) * (nrows + 1) + r] = cursor[r];
   }
+  if (ITEMS)
+    for (int i = threadIdx.x; i < kKvKeys; i += blockDim.x) hist[i] = 0;
   if (row_ptr && tile == 0 && threadIdx.x == 0)
     row_ptr[static_cast<long long>(hkv) * (nrows + 1) + nrows] =
         offsets[seg + static_cast<long long>(nrows) * ntiles] - base_h;
@@ -408,6 +439,7 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
   int32_t* qi = q_idx + hkv * cap;
   int32_t* sl = slot ? slot + hkv * cap : nullptr;
   const long long e1 = g1 * a.topk;
+  const int cmask = ITEMS ? (1 << emit.chunk_shift) - 1 : 0;
   for (long long rb = g0 * a.topk; rb < e1; rb += 256 * kCsrBatch) {
     int rows[kCsrBatch], pos[kCsrBatch];
     load_rows<VARLEN, I32>(a, hkv, rb + threadIdx.x, 256, e1, rows);
@@ -420,6 +452,15 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
     for (int k = 0; k < kCsrBatch; ++k) {
       if (rows[k] < 0) continue;
       const long long e = rb + 256 * k + threadIdx.x;
+      if (ITEMS && ((pos[k] - rowbeg[rows[k]]) & cmask) == 0) {
+        // first entry of a chunk: the chunk's work item (the row ends where the next
+        // row's tile 0 begins)
+        const int end =
+            offsets[seg + static_cast<long long>(rows[k] + 1) * ntiles] - base_h;
+        emit.items[kv_item_slot(hkv, emit.per_head, pos[k], emit.chunk_shift, rows[k])] =
+            make_int4(hkv, rows[k], pos[k], min(cmask + 1, end - pos[k]));
+        atomicAdd(&hist[kv_item_key(hkv, idx_div<I32>(e, a.topk), a.nq, a.Hkv)], 1);
+      }
       if (FLAT) {
         qi[pos[k]] = static_cast<int32_t>(e);
         continue;
@@ -427,6 +468,13 @@ __global__ __launch_bounds__(256) void csr_scatter_unordered_kernel(
       const long long q = idx_div<I32>(e, a.topk);
       qi[pos[k]] = static_cast<int32_t>(q);
       if (sl) sl[pos[k]] = static_cast<int32_t>(e - q * a.topk);
+    }
+  }
+  if (ITEMS) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kKvKeys; i += blockDim.x) {
+      const int n = hist[i];
+      if (n) atomicAdd(&emit.sb.counts[i], n);
     }
   }
 }
@@ -440,70 +488,11 @@ __global__ void csr_row_ptr_kernel(const int32_t* __restrict__ offsets, int Hkv,
   row_ptr[idx] = offsets[seg + static_cast<long long>(r) * ntiles] - offsets[seg];
 }
 
-__global__ void chunk_count_kernel(const int32_t* __restrict__ row_ptr, int Hkv, int nrows,
-                                   int chunk_entries, int32_t* __restrict__ counts) {
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long long>(Hkv) * nrows) return;
-  const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
-  const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
-  const int len = rp[r + 1] - rp[r];
-  counts[idx] = (len + chunk_entries - 1) / chunk_entries;
-}
-
 inline unsigned blocks_for(long long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
 
-// The whole chunk schedule in one workgroup when there are at most
-// kSmallSchedThreads * kSmallSchedPer (KV head, row) pairs: each thread counts the
-// chunks of kSmallSchedPer consecutive rows, one block-wide scan turns the counts
-// into chunk_ptr (exclusive, with the total at [n]). It also clears `zero_ints`
-// (a caller's counters), saving the launches of the separate count, scan and clear.
-constexpr int kSmallSchedThreads = 1024;
-constexpr int kSmallSchedPer = 16;
-__global__ __launch_bounds__(kSmallSchedThreads) void chunk_schedule_small_kernel(
-    const int32_t* __restrict__ row_ptr, int Hkv, int nrows, int chunk_entries,
-    int32_t* __restrict__ chunk_ptr, int32_t* __restrict__ zero_ints, int nzero) {
-  __shared__ int sum[kSmallSchedThreads];
-  const int t = threadIdx.x;
-  const int n = Hkv * nrows;
-  int cnt[kSmallSchedPer];
-  int local = 0;
-  // indices clamped into range so that all loads are unconditional and in flight together
-  int len[kSmallSchedPer];
-#pragma unroll
-  for (int k = 0; k < kSmallSchedPer; ++k) {
-    const int idx = min(t * kSmallSchedPer + k, n - 1);
-    const int hkv = idx / nrows, r = idx % nrows;
-    const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
-    len[k] = rp[r + 1] - rp[r];
-  }
-#pragma unroll
-  for (int k = 0; k < kSmallSchedPer; ++k) {
-    const int c = t * kSmallSchedPer + k < n ? (len[k] + chunk_entries - 1) / chunk_entries : 0;
-    cnt[k] = c;
-    local += c;
-  }
-  sum[t] = local;
-  __syncthreads();
-  for (int d = 1; d < kSmallSchedThreads; d <<= 1) {
-    const int add = t >= d ? sum[t - d] : 0;
-    __syncthreads();
-    sum[t] += add;
-    __syncthreads();
-  }
-  int run = sum[t] - local;
-#pragma unroll
-  for (int k = 0; k < kSmallSchedPer; ++k) {
-    const int idx = t * kSmallSchedPer + k;
-    if (idx < n) chunk_ptr[idx] = run;
-    run += cnt[k];
-  }
-  if (t == kSmallSchedThreads - 1) chunk_ptr[n] = sum[t];
-  for (int i = t; i < nzero; i += kSmallSchedThreads) zero_ints[i] = 0;
-}
-
-__global__ void zero_ints_kernel(int32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+__global__ void zero_ints_kernel(int32_t* __restrict__ p0, long long n0, int32_t* __restrict__ p1,
+                                 long long n1) {
+  grid_zero2(p0, n0, p1, n1);
 }
 
 // Exclusive scan of at most kScanOneMax values in one workgroup of 1024 threads. Tile j
@@ -652,7 +641,8 @@ CsrPlan csr_plan_unordered(int Hkv, long long nq, int topk, int nrows) {
 
 template <bool VARLEN, bool I32>
 hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
-                          void* ws, hipStream_t stream, bool ordered, bool flat) {
+                          void* ws, hipStream_t stream, bool ordered, bool flat,
+                          const KvItemEmit* emit) {
   const int nrows = a.nrows;
   // the plan depends on the query count and the rows only: B * Sq == nq
   const CsrPlan plan = ordered ? csr_plan(1, a.Hkv, static_cast<int>(a.nq), a.topk, nrows)
@@ -668,12 +658,15 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   // With at most one tile per compute unit (long order-free tiles on the largest
   // problems), the count runs 1024 threads per tile so that 16 waves per compute unit
   // keep index loads in flight; otherwise 256.
+  ZeroRanges z{};
+  if (emit) z = ZeroRanges{emit->sb.counts, kKvSortZeroInts, reinterpret_cast<int32_t*>(emit->items),
+                           4 * emit->max_items};
   if (static_cast<long long>(plan.ntiles) * a.Hkv <= device_cu_count())
     hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32, 1024>), grid, dim3(1024), lds, stream, a,
-                       plan.tile_q, plan.ntiles, counts);
+                       plan.tile_q, plan.ntiles, counts, z);
   else
     hipLaunchKernelGGL((csr_count_kernel<VARLEN, I32, 256>), grid, dim3(256), lds, stream, a,
-                       plan.tile_q, plan.ntiles, counts);
+                       plan.tile_q, plan.ntiles, counts, z);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
@@ -698,12 +691,26 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   else if (ordered)
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);
-  else if (flat)  // the order-free scatter also writes the row pointers (tile-0 blocks)
-    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, true>), grid, dim3(256), lds,
-                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
-  else
-    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, false>), grid, dim3(256), lds,
-                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr);
+  else if (flat && emit) {  // with the kv-centric items; LDS: cursors, row starts, keys
+    const auto kern = &csr_scatter_unordered_kernel<VARLEN, I32, true, true>;
+    const size_t lds_items = 2 * lds + kKvKeys * sizeof(int);
+    if (lds_items > 64 * 1024) {
+      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                static_cast<int>(lds_items));
+      if (ea != hipSuccess) return ea;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds_items, stream, a, plan.tile_q, plan.ntiles,
+                       offsets, q_idx, slot, row_ptr, *emit);
+  } else if (flat) {  // the order-free scatter also writes the row pointers (tile-0 blocks)
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, true, false>), grid, dim3(256),
+                       lds, stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr,
+                       KvItemEmit{});
+  } else {
+    hipLaunchKernelGGL((csr_scatter_unordered_kernel<VARLEN, I32, false, false>), grid, dim3(256),
+                       lds, stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot, row_ptr,
+                       KvItemEmit{});
+  }
   if (ordered) {
     const long long nrp = static_cast<long long>(a.Hkv) * (nrows + 1);
     hipLaunchKernelGGL(csr_row_ptr_kernel, dim3(blocks_for(nrp, 256)), dim3(256), 0, stream,
@@ -714,57 +721,47 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
 
 template <bool VARLEN>
 hipError_t build_csr(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                     hipStream_t stream, bool ordered, bool flat) {
+                     hipStream_t stream, bool ordered, bool flat, const KvItemEmit* emit) {
   if (flat && (ordered || a.nq * a.topk >= (1LL << 31))) return hipErrorInvalidValue;
+  if (emit && (!flat || emit->chunk_shift < 0 || emit->chunk_shift > 20)) return hipErrorInvalidValue;
   if (a.nq * a.topk < (1LL << 31))
-    return build_csr_impl<VARLEN, true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
-  return build_csr_impl<VARLEN, false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
+    return build_csr_impl<VARLEN, true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat, emit);
+  return build_csr_impl<VARLEN, false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat, emit);
 }
 
 }  // namespace
 
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream, bool ordered, bool flat) {
+                            hipStream_t stream, bool ordered, bool flat, const KvItemEmit* emit) {
   CsrSrc a{};
   a.q2k = q2k;
   a.Hkv = Hkv; a.Sq = Sq; a.topk = topk; a.nblk = nblk;
   a.nrows = B * nblk;
   a.nq = static_cast<long long>(B) * Sq;
-  return build_csr<false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
+  return build_csr<false>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat, emit);
 }
 
 hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, int Hkv,
                                    int total_q, int topk, int nrows, int32_t* row_ptr,
                                    int32_t* q_idx, int32_t* slot, void* ws, hipStream_t stream,
-                                   bool ordered, bool flat) {
+                                   bool ordered, bool flat, const KvItemEmit* emit) {
   CsrSrc a{};
   a.q2k = q2k;
   a.q_rows = t.q_rows;
   a.Hkv = Hkv; a.Sq = total_q; a.topk = topk; a.nblk = 0;
   a.nrows = nrows;
   a.nq = total_q;
-  return build_csr<true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat);
+  return build_csr<true>(a, row_ptr, q_idx, slot, ws, stream, ordered, flat, emit);
 }
 
-hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
-                                 int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
-                                 hipStream_t stream, int32_t* zero_ints, int nzero) {
-  const long long n = static_cast<long long>(Hkv) * nrows;
-  if (n <= static_cast<long long>(kSmallSchedThreads) * kSmallSchedPer) {
-    hipLaunchKernelGGL(chunk_schedule_small_kernel, dim3(1), dim3(kSmallSchedThreads), 0, stream,
-                       row_ptr, Hkv, nrows, chunk_entries, chunk_ptr, zero_ints,
-                       zero_ints ? nzero : 0);
-    return hipGetLastError();
-  }
-  if (zero_ints && nzero > 0)
-    hipLaunchKernelGGL(zero_ints_kernel, dim3(blocks_for(nzero, 256)), dim3(256), 0, stream,
-                       zero_ints, nzero);
-  hipLaunchKernelGGL(chunk_count_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, stream, row_ptr,
-                     Hkv, nrows, chunk_entries, chunk_counts);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_exclusive_scan(chunk_counts, chunk_ptr, n, scan_tmp, stream);
+hipError_t launch_zero_ints(int32_t* p0, long long n0, int32_t* p1, long long n1,
+                            hipStream_t stream) {
+  if (n0 + n1 <= 0) return hipSuccess;
+  const long long blocks = std::min<long long>((n0 + n1 + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     p0, n0, p1, n1);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -296,25 +296,49 @@ hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t 
 struct KvSortBuffers {
   int32_t* counts;     // [kKvKeys] items per key
   int32_t* next;       // [kKvStreams] items taken from each stream (KvParams::stream_next)
-  int32_t* cursor;     // [kKvKeys] scatter cursors
-  int32_t* key_start;  // [kKvKeys + 1] first item of each key
+  int32_t* cursor;     // [kKvKeys] items placed per key by the sort
+  int32_t* key_start;  // [kKvKeys + 1] first item of each key (written by the sort)
 };
-constexpr int kKvSortZeroInts = kKvKeys + 16;
-constexpr int kKvSortInts = kKvSortZeroInts + kKvKeys + kKvKeys + 1;
+// counts, next and cursor lie in the first kKvSortZeroInts ints, which must be zero
+// before the item table is built
+constexpr int kKvSortZeroInts = kKvKeys + 16 + kKvKeys;
+constexpr int kKvSortInts = kKvSortZeroInts + kKvKeys + 1;
 inline KvSortBuffers kv_sort_buffers(int32_t* base) {
-  return KvSortBuffers{base, base + kKvKeys, base + kKvSortZeroInts,
-                       base + kKvSortZeroInts + kKvKeys};
+  return KvSortBuffers{base, base + kKvKeys, base + kKvKeys + 16, base + kKvSortZeroInts};
 }
-// items[c] for every chunk of every row, and the per-key item counts (q_idx [Hkv][cap]
-// holding query * qdiv + slot, qdiv = 1 for plain query ids; nq query rows; key_counts
-// zero on entry)
-hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
-                           long long nq, int qdiv, int32_t* key_counts, hipStream_t stream);
-// the item table in key order (at most max_items items; the count is read on the device)
+// The unsorted item table has a fixed slot for every possible item: item j of row r
+// of KV head hkv starts at row position p = row start + j * chunk, and
+//   slot = hkv * per_head + floor(p / chunk) + r,  per_head = cap / chunk + nrows + 1,
+// which grows strictly with (r, j) (a row's first chunk starts at or after its
+// predecessor's last one) and stays below per_head. Unused slots hold entry count 0:
+// the table is cleared (as ints) before it is filled.
+__host__ __device__ inline long long kv_item_slot(int hkv, long long per_head, int pos,
+                                                  int chunk_shift, int row) {
+  return static_cast<long long>(hkv) * per_head + (pos >> chunk_shift) + row;
+}
+// Key of a kv-centric work item: its KV head and first query as one coordinate
+// c = hkv * nq + first query, bucketed into kKvKeys equal ranges; stream s of the
+// kernel holds keys [s * kKvKeys / streams, (s + 1) * kKvKeys / streams).
+__device__ __forceinline__ int kv_item_key(int hkv, long long first_q, long long nq, int Hkv) {
+  return query_bucket(static_cast<long long>(hkv) * nq + first_q, static_cast<long long>(Hkv) * nq,
+                      kKvKeys);
+}
+// items for every chunk of 2^chunk_shift entries of every CSR row of a caller's CSR,
+// each at its slot (kv_item_slot), and the per-key item counts (q_idx [Hkv][cap]
+// holding query * qdiv + slot, qdiv = 1 for plain query ids; nq query rows; the
+// table and the sort buffers' zero region cleared beforehand)
+hipError_t launch_kv_items(const int32_t* row_ptr, int Hkv, int nrows, int chunk_shift,
+                           long long per_head, int4* items, const int32_t* q_idx, long long cap,
+                           long long nq, int qdiv, const KvSortBuffers& sb, hipStream_t stream);
+// the item table (max_items slots, unused ones with entry count 0) in key order; the
+// item count and key_start are computed on the device from sb.counts
 hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_idx, long long cap,
                                   long long nq, int qdiv, long long max_items,
                                   const KvSortBuffers& sb, int4* out, hipStream_t stream);
+// zero n0 ints at p0 and n1 at p1 (a fill kernel, so that a captured graph holds no
+// memset node)
+hipError_t launch_zero_ints(int32_t* p0, long long n0, int32_t* p1, long long n1,
+                            hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 
@@ -350,9 +374,22 @@ size_t csr_workspace_bytes(int B, int Hkv, int Sq, int topk, int nrows);
 // (used internally by the kv-centric path, whose results do not depend on it)
 // flat (ordered = false only, B*Sq*topk < 2^31): q_idx holds each entry as its index
 // query * topk + slot into the KV head's index table; slot is not written
+// The kv-centric work items, listed by the order-free flat build while it scatters:
+// the entry that lands first in a chunk of 2^chunk_shift entries of its row writes the
+// chunk's item (hkv, row, position, entry count) to its slot (kv_item_slot) and counts
+// it under its key (kv_item_key of the entry's query) in sb.counts. The count pass
+// clears the table (max_items int4) and the sort buffers' zero region first.
+struct KvItemEmit {
+  int4* items;
+  long long per_head;
+  long long max_items;
+  KvSortBuffers sb;
+  int chunk_shift;
+};
 hipError_t launch_build_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int nblk,
                             int32_t* row_ptr, int32_t* q_idx, int32_t* slot, void* ws,
-                            hipStream_t stream, bool ordered = true, bool flat = false);
+                            hipStream_t stream, bool ordered = true, bool flat = false,
+                            const KvItemEmit* emit = nullptr);
 // varlen CSR over nrows rows (q2k [Hkv,total_q,topk]); the tables come from
 // launch_varlen_tables; entries whose row is >= nrows are dropped. Workspace:
 // csr_workspace_bytes(1, Hkv, total_q, topk, nrows).
@@ -360,11 +397,6 @@ hipError_t launch_build_csr_varlen(const int32_t* q2k, const VarlenTables& t, in
                                    int total_q, int topk,
                                    int nrows, int32_t* row_ptr, int32_t* q_idx, int32_t* slot,
                                    void* ws, hipStream_t stream, bool ordered = true,
-                                   bool flat = false);
-// per (hkv,row) chunk counts ceil(len / chunk_entries) -> chunk_ptr exclusive prefix;
-// also sets zero_ints[0, nzero) to 0 when zero_ints is given
-hipError_t launch_chunk_schedule(const int32_t* row_ptr, int Hkv, int nrows, int chunk_entries,
-                                 int32_t* chunk_counts, int32_t* chunk_ptr, int32_t* scan_tmp,
-                                 hipStream_t stream, int32_t* zero_ints = nullptr, int nzero = 0);
+                                   bool flat = false, const KvItemEmit* emit = nullptr);
 
 }  // namespace msa

@@ -403,105 +403,100 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   }
 }
 
-// Key of a work item: its KV head and first query as one coordinate
-// c = hkv * nq + first query, bucketed into kKvKeys equal ranges. Stream s holds
-// keys [s * kKvBucketsPerStream, (s + 1) * kKvBucketsPerStream).
-__device__ __forceinline__ int item_key(int hkv, long long first_q, long long nq, int Hkv) {
-  return query_bucket(static_cast<long long>(hkv) * nq + first_q, static_cast<long long>(Hkv) * nq,
-                      kKvKeys);
-}
-
-// items[c] = (hkv, row, first entry, entry count) for every chunk c of every row; each
-// item is also counted under its key (counts gathered per block in LDS) into
-// key_counts[kKvKeys] (zero on entry). One wave per (KV head, row): lane l writes the
-// row's chunks l, l + 64, ..., so that a long row is spread over a wave and every
-// first-query load of a round is in flight together.
+// items for the chunks of 2^chunk_shift entries of every row of a caller's CSR, each
+// at its slot (kv_item_slot), and the per-key item counts (counts gathered per
+// workgroup in LDS). One wave per (KV head, row): lane l writes the row's chunks l,
+// l + 64, ..., so that a long row is spread over a wave and every first-query load of
+// a round is in flight together. The order-free CSR that the library builds itself
+// lists its items while it scatters (KvItemEmit), so this kernel runs only for a
+// caller's CSR.
 __global__ __launch_bounds__(256) void kv_items_kernel(
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ chunk_ptr, int Hkv, int nrows,
-    int chunk_entries, int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap,
-    long long nq, int qdiv, int32_t* __restrict__ key_counts) {
+    const int32_t* __restrict__ row_ptr, int Hkv, int nrows, int chunk_shift, long long per_head,
+    int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap, long long nq,
+    int qdiv, KvSortBuffers sb) {
   __shared__ int hist[kKvKeys];
   for (int i = threadIdx.x; i < kKvKeys; i += 256) hist[i] = 0;
   __syncthreads();
   const long long idx = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int chunk = 1 << chunk_shift;
   if (idx < static_cast<long long>(Hkv) * nrows) {
     const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
     const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
     const int beg = rp[r], end = rp[r + 1];
-    const int c0 = chunk_ptr[idx];
-    const int nch = (end - beg + chunk_entries - 1) / chunk_entries;
+    const int nch = end > beg ? (end - beg + chunk - 1) >> chunk_shift : 0;
     for (int j = lane; j < nch; j += 64) {
-      const int e = beg + j * chunk_entries;
+      const int e = beg + j * chunk;
       const int q = q_idx[hkv * cap + e] / qdiv;
-      items[c0 + j] = make_int4(hkv, r, e, min(chunk_entries, end - e));
-      atomicAdd(&hist[item_key(hkv, q, nq, Hkv)], 1);
+      items[kv_item_slot(hkv, per_head, e, chunk_shift, r)] =
+          make_int4(hkv, r, e, min(chunk, end - e));
+      atomicAdd(&hist[kv_item_key(hkv, q, nq, Hkv)], 1);
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kKvKeys; i += 256) {
     const int n = hist[i];
-    if (n) atomicAdd(&key_counts[i], n);
+    if (n) atomicAdd(&sb.counts[i], n);
   }
 }
 
-// Exclusive scan of the key counts (one block, 8 keys per thread): key_start[0..kKvKeys]
-// (key_start[kKvKeys] = the item count) and a copy of the starts as scatter cursors.
-__global__ __launch_bounds__(256) void kv_sort_scan(const int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ key_start,
-                                                    int32_t* __restrict__ cursor) {
+// The item table in key order (a counting sort). Every workgroup scans the key counts
+// itself (8 keys per thread), so no separate scan launch is needed; workgroup 0
+// publishes the starts in sb.key_start (key_start[kKvKeys] = the item count) for the
+// forward kernel. Each workgroup then ranks the items of its 256 table slots (unused
+// slots hold entry count 0) per key in LDS, reserves a range of every key it holds
+// with one atomic on the key's cursor, and places its items there. Order inside a key
+// is arbitrary: each item writes its own partials, so the results do not depend on it.
+__global__ __launch_bounds__(256) void kv_sort_scatter(
+    const int4* __restrict__ items, long long nslots, KvSortBuffers sb, int Hkv,
+    const int32_t* __restrict__ q_idx, long long cap, long long nq, int qdiv,
+    int4* __restrict__ out) {
   constexpr int kPer = kKvKeys / 256;
-  __shared__ int v[256];
-  const int t = threadIdx.x;
+  __shared__ int h[kKvKeys];
+  __shared__ int base[kKvKeys];
+  __shared__ int wsum[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int c[kPer], own = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    c[k] = counts[t * kPer + k];
+    c[k] = sb.counts[t * kPer + k];
     own += c[k];
   }
-  v[t] = own;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const int add = t >= d ? v[t - d] : 0;
-    __syncthreads();
-    v[t] += add;
-    __syncthreads();
+  int x = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  int run = v[t] - own;
+  if (lane == 63) wsum[wave] = x;
+  for (int i = t; i < kKvKeys; i += 256) h[i] = 0;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
+  int run = before + x - own;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    key_start[t * kPer + k] = run;
-    cursor[t * kPer + k] = run;
+    base[t * kPer + k] = run;
+    if (blockIdx.x == 0) sb.key_start[t * kPer + k] = run;
     run += c[k];
   }
-  if (t == 255) key_start[kKvKeys] = run;
-}
-
-// The item table in key order (a counting sort): each block ranks its 256 items per
-// key in LDS, reserves a range of every key it holds with one atomic on the running
-// cursors, and places its items there. Order inside a key is arbitrary: each item
-// writes its own partials, so the results do not depend on it.
-__global__ __launch_bounds__(256) void kv_sort_scatter(
-    const int4* __restrict__ items, const int32_t* __restrict__ key_start, int Hkv,
-    const int32_t* __restrict__ q_idx, long long cap, long long nq, int qdiv,
-    int32_t* __restrict__ cursor, int4* __restrict__ out) {
-  __shared__ int h[kKvKeys];
-  __shared__ int base[kKvKeys];
-  const int total = key_start[kKvKeys];
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  for (int i = threadIdx.x; i < kKvKeys; i += 256) h[i] = 0;
+  if (t == 255 && blockIdx.x == 0) sb.key_start[kKvKeys] = run;
   __syncthreads();
+  const long long ci = static_cast<long long>(blockIdx.x) * 256 + t;
   int4 it = make_int4(0, 0, 0, 0);
   int key = -1, rank = 0;
-  if (c < total) {
-    it = items[c];
-    key = item_key(it.x, q_idx[it.x * cap + it.z] / qdiv, nq, Hkv);
-    rank = atomicAdd(&h[key], 1);
+  if (ci < nslots) {
+    it = items[ci];
+    if (it.w > 0) {
+      key = kv_item_key(it.x, q_idx[it.x * cap + it.z] / qdiv, nq, Hkv);
+      rank = atomicAdd(&h[key], 1);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kKvKeys; i += 256) {
+  for (int i = t; i < kKvKeys; i += 256) {
     const int n = h[i];
-    base[i] = n ? atomicAdd(&cursor[i], n) : 0;
+    if (n) base[i] += atomicAdd(&sb.cursor[i], n);
   }
   __syncthreads();
   if (key >= 0) out[base[key] + rank] = it;
@@ -527,14 +522,14 @@ void kv_launch(const KvParams& p, long long max_items, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_kv_items(const int32_t* row_ptr, const int32_t* chunk_ptr, int Hkv, int nrows,
-                           int chunk_entries, int4* items, const int32_t* q_idx, long long cap,
-                           long long nq, int qdiv, int32_t* key_counts, hipStream_t stream) {
+hipError_t launch_kv_items(const int32_t* row_ptr, int Hkv, int nrows, int chunk_shift,
+                           long long per_head, int4* items, const int32_t* q_idx, long long cap,
+                           long long nq, int qdiv, const KvSortBuffers& sb, hipStream_t stream) {
   const long long n = static_cast<long long>(Hkv) * nrows;
-  if (nq <= 0 || !key_counts) return hipErrorInvalidValue;
+  if (nq <= 0 || n <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_items_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
-                     stream, row_ptr, chunk_ptr, Hkv, nrows, chunk_entries, items, q_idx, cap, nq,
-                     qdiv, key_counts);
+                     stream, row_ptr, Hkv, nrows, chunk_shift, per_head, items, q_idx, cap, nq,
+                     qdiv, sb);
   return hipGetLastError();
 }
 
@@ -543,10 +538,8 @@ hipError_t launch_kv_items_by_key(const int4* items, int Hkv, const int32_t* q_i
                                   const KvSortBuffers& sb, int4* out, hipStream_t stream) {
   if (nq <= 0 || max_items <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((max_items + 255) / 256));
-  hipLaunchKernelGGL(kv_sort_scan, dim3(1), dim3(256), 0, stream, sb.counts, sb.key_start,
-                     sb.cursor);
-  hipLaunchKernelGGL(kv_sort_scatter, grid, dim3(256), 0, stream, items, sb.key_start, Hkv, q_idx,
-                     cap, nq, qdiv, sb.cursor, out);
+  hipLaunchKernelGGL(kv_sort_scatter, grid, dim3(256), 0, stream, items, max_items, sb, Hkv, q_idx,
+                     cap, nq, qdiv, out);
   return hipGetLastError();
 }
 

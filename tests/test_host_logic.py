@@ -5,6 +5,10 @@ query ranges by its first query; the item-table and item-order kernels must agre
 on it for every query count the API accepts, including query ids past 2^23, where
 q * 256 no longer fits in 32 bits. The helper is compiled into a host program and
 compared with exact integer arithmetic.
+
+kv_item_slot (msa_internal.hpp) gives each kv-centric work item (a chunk of a CSR row)
+a fixed slot in the unsorted item table, so that the scatter can list items without a
+shared counter; two items must never share a slot, and every slot must fit the table.
 """
 import os
 import subprocess
@@ -16,14 +20,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "host", "query_bucket_check.cpp")
 
 
-@pytest.fixture(scope="module")
-def bucket_exe(tmp_path_factory):
-    exe = str(tmp_path_factory.mktemp("host") / "query_bucket_check")
+def _build(tmp_path_factory, src, name):
+    exe = str(tmp_path_factory.mktemp("host") / name)
     subprocess.check_call(["/opt/rocm/bin/hipcc", "-O1", "-std=c++17", "-x", "hip",
                            "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-                           "-packed-fp32-ops", SRC, "-o", exe],
+                           "-packed-fp32-ops", src, "-o", exe],
                           stderr=subprocess.DEVNULL)
     return exe
+
+
+@pytest.fixture(scope="module")
+def bucket_exe(tmp_path_factory):
+    return _build(tmp_path_factory, SRC, "query_bucket_check")
+
+
+@pytest.fixture(scope="module")
+def slot_exe(tmp_path_factory):
+    return _build(tmp_path_factory, os.path.join(HERE, "host", "kv_item_slot_check.cpp"),
+                  "kv_item_slot_check")
 
 
 def _run(exe, triples):
@@ -52,6 +66,27 @@ def test_query_bucket_monotone_and_in_range(bucket_exe):
     got = _run(bucket_exe, [(q, nq, 256) for q in qs])
     assert min(got) == 0 and max(got) == 255
     assert all(a <= b for a, b in zip(got, got[1:]))
+
+
+@pytest.mark.parametrize("Hkv,shift,nrows,seed", [(1, 7, 64, 0), (4, 7, 200, 1), (2, 9, 300, 2),
+                                                   (3, 8, 50, 3), (1, 9, 3072, 4)])
+def test_kv_item_slots_distinct_and_in_range(slot_exe, Hkv, shift, nrows, seed):
+    rng = np.random.default_rng(seed)
+    chunk = 1 << shift
+    # rows of every kind: empty, one entry, a chunk and one more (a last chunk of one
+    # entry, followed at once by the next row's first chunk), exact multiples, long rows
+    kinds = [0, 1, chunk, chunk + 1, 2 * chunk - 1, 3 * chunk]
+    lens = [int(rng.choice(kinds)) if rng.random() < 0.5 else int(rng.integers(0, 6 * chunk))
+            for _ in range(Hkv * nrows)]
+    inp = f"{Hkv} {shift} {nrows}\n" + " ".join(map(str, lens)) + "\n"
+    out = subprocess.run([slot_exe], input=inp, capture_output=True, text=True,
+                         check=True).stdout.split()
+    per_head = int(out[0])
+    slots = [int(x) for x in out[1:]]
+    n_items = sum((n + chunk - 1) // chunk for n in lens)
+    assert len(slots) == n_items
+    assert len(set(slots)) == n_items
+    assert min(slots, default=0) >= 0 and max(slots, default=0) < Hkv * per_head
 
 
 def test_bench_skew_diagnostics_brute_force():
