@@ -106,22 +106,29 @@ def main() -> int:
         lines += ["Commands (run from the repository root on one MI355X):", "", "```"]
         lines += open(args.commands).read().strip().splitlines()
         lines += ["```", ""]
-    lines += ["| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    lines += ["| kernel | calls | avg us | median us | min us | max us | total ms |",
+              "|---|---|---|---|---|---|---|"]
     total = 0.0
     for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
         if "elementwise" in name or "distribution" in name:
             continue
         total += sum(v)
-        lines.append(f"| {short(name)} | {len(v)} | {statistics.mean(v):.1f} | {min(v):.1f} | "
-                     f"{max(v):.1f} | {sum(v) / 1e3:.3f} |")
+        lines.append(f"| {short(name)} | {len(v)} | {statistics.mean(v):.1f} | "
+                     f"{statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{sum(v) / 1e3:.3f} |")
     dom_durs = [x for n, v in durs.items() if dom in n for x in v]
     dom_avg = statistics.mean(dom_durs) if dom_durs else None
+    dom_med = statistics.median(dom_durs) if dom_durs else None
     full = [short(n) for n in durs if dom in n]
     if full:  # the instance as the trace names it
         dom_name = full[0]
     else:
         dom_name = dom
-    lines += ["", f"Dominant kernel: `{dom_name}`, average {dom_avg:.1f} us per launch." if dom_avg
+    lines += ["", f"Dominant kernel: `{dom_name}`, average {dom_avg:.1f} us per launch, median "
+              f"{dom_med:.1f} us. Launch durations vary within one run: the first launches, and "
+              "the first after each of bench.py's host-side phases, warm up, and the clock moves "
+              "under sustained load; the median is the typical launch (under the profiler, a "
+              "few per cent slower than without)." if dom_avg
               else f"Dominant kernel `{dom}` not found in the trace."]
 
     traffic = None
@@ -180,6 +187,7 @@ def main() -> int:
         with open(js, "w") as fh:
             json.dump({"workload": w.name, "path": args.path, "kernel": dom_name,
                        "hbm_bytes_per_launch": traffic, "kernel_avg_us": dom_avg,
+                       "kernel_median_us": dom_med,
                        "source_digest": bench.source_digest(dom)}, fh, indent=1)
             fh.write("\n")
         print("wrote", js)
