@@ -1,5 +1,5 @@
-// kv-block -> query CSR builder, device exclusive scan and the kv-centric
-// work schedule.
+// kv-block -> query CSR builder and device exclusive scan; the order-free build
+// also lists the kv-centric work items (one per chunk of each row) as it scatters.
 //
 // The CSR is the one `build_k2q_csr` produces on the page "MSA interface.py"
 // (row r = b * nblk + s of each KV head lists the global query ids b*Sq + q

@@ -291,8 +291,9 @@ struct KvParams {
 // persistent grid (two workgroups per compute unit, at most max_items) over the
 // streams of the key-ordered item table
 hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t stream);
-// The item order's counters: counts[kKvKeys] and next[kKvStreams] must be zero on entry
-// (the chunk schedule clears kKvSortZeroInts ints from `counts`, which `next` follows).
+// The item order's counters: counts, next and cursor must be zero before the item table
+// is filled (the CSR count pass, or a fill kernel for a caller's CSR, clears the first
+// kKvSortZeroInts ints, which hold all three).
 struct KvSortBuffers {
   int32_t* counts;     // [kKvKeys] items per key
   int32_t* next;       // [kKvStreams] items taken from each stream (KvParams::stream_next)

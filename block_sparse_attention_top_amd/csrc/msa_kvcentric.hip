@@ -26,9 +26,9 @@
 // and may end inside it, and the causal limit uses the sequence's own lengths.
 //
 // Layout on gfx950. A work item is (KV head, CSR row = (b, block), a chunk of
-// up to `chunk_entries` CSR entries), listed in an item table by the schedule
-// kernels and ordered by (KV head, first query) into one stream per KV head (see
-// kvcentric_kernel). A workgroup of 4 waves stages the block's K and V tiles
+// up to `chunk_entries` CSR entries), listed in an item table by the CSR scatter
+// (or kv_items_kernel for a caller's CSR) and ordered by (KV head, first query) into
+// one stream per KV head (see kvcentric_kernel). A workgroup of 4 waves stages the block's K and V tiles
 // (128 x 128 bf16, padded rows) and the chunk's (query, slot) entries in LDS;
 // two workgroups share a CU, so one wave's softmax (VALU) overlaps the other
 // wave's matrix work on each SIMD, and one workgroup's tile load overlaps the
