@@ -202,6 +202,7 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   const int32_t* q_idx = csr_q_idx;
   const int32_t* slot = csr_slot;
   hipError_t e;
+  if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
   const int chunk = chunk_entries_for(p.qpk);  // a power of two
   int chunk_shift = 0;
   while ((1 << chunk_shift) < chunk) ++chunk_shift;
@@ -257,7 +258,6 @@ int run_kvcentric(KvParams p, const int32_t* q2k, const int32_t* csr_row_ptr,
   p.key_start = sb.key_start;
   p.stream_next = sb.next;
   p.streams = kv_streams(p.Hkv);
-  if (L.max_items > 0x7FFFFFFFLL) return fail(MSA_ERR_INVALID_VALUE, "problem too large");
   prof_mark(g_prof_before, st);
   e = launch_kvcentric(p, L.max_items, st);
   prof_mark(g_prof_after, st);
