@@ -254,14 +254,24 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (hf == 0) {
         m_ref = mx;
-      } else if (__any((mx - m_ref) * c2m > 8.f)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
-        ps *= alpha;
-        if (TEMP) pst *= m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2t);
+      } else {
+        // The rescale is decided per row: a row moves its reference max only when its
+        // own second half exceeds it by the gap, and every other row keeps it and
+        // multiplies by exactly 1. A row's result then depends on its own scores
+        // alone, not on which rows share its wave step (the library's own CSR is
+        // order-free, so that grouping changes from call to call).
+        const bool resc = (mx - m_ref) * c2m > 8.f;
+        if (__any(resc)) {
+          const float m_new = resc ? mx : m_ref;
+          const float alpha =
+              !resc ? 1.f : m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2);
+          ps *= alpha;
+          if (TEMP)
+            pst *= !resc ? 1.f : m_ref == -INFINITY ? 0.f : fast_exp2((m_ref - m_new) * c2t);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
-        m_ref = m_new;
+          for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+          m_ref = m_new;
+        }
       }
       const float nmc = -(m_ref == -INFINITY ? 0.f : m_ref) * c2;
       uint32_t pk[2][8];

@@ -51,6 +51,18 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     return {"o_err": o_err, "lse_err": lse_err}
 
 
+def check_lse_t(lt_gpu, lt_ref, label):
+    """Temperature-scaled LSE against the oracle: the test page's rule for it,
+    |d| <= 1e-3 + 1e-3 |ref| on finite entries, with identical empty-row masks."""
+    lt_gpu = np.asarray(lt_gpu, dtype=np.float64)
+    fin = np.isfinite(lt_ref)
+    assert np.array_equal(np.isneginf(lt_gpu), ~fin), f"{label}: empty-row mask differs"
+    err = np.abs(lt_gpu[fin] - lt_ref[fin])
+    bound = 1e-3 + 1e-3 * np.abs(lt_ref[fin])
+    assert np.all(err <= bound), f"{label}: temperature LSE error {err.max()}"
+    return float(err.max()) if err.size else 0.0
+
+
 def run_contiguous(inp: dict, causal: bool, path: int, softmax_scale: float = 0.0, csr=None):
     import block_sparse_attention_top_amd as msa
     q, k, v, q2k = (to_dev(inp[n]) for n in ("q", "k", "v", "q2k"))

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import bf16_dev_to_f64, compare, sample_rows, say, to_dev
+from parity_util import bf16_dev_to_f64, check_lse_t, compare, sample_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,62 @@ def test_paged_fp8(splits):
                                                    causal=True)
     compare(bf16_dev_to_f64(o8), l8.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
             lse_ref.transpose(0, 2, 1), "paged")
+
+
+@pytest.mark.parametrize("path", [Q, KV])
+def test_varlen_fp8_temperature(path):
+    """fp8 cache with the temperature-scaled LSE on a ragged batch (the fp8 and
+    temperature variants of both varlen kernels together): bit for bit the bf16 run on
+    the dequantized K/V, and the oracle on the fp8 inputs."""
+    import block_sparse_attention_top_amd as msa
+    inp = wl.make_varlen_inputs(87, [150, 3, 260, 0, 64], [800, 129, 300, 256, 1000], 2, 8, 8,
+                                wl.MODE_CAUSAL)
+    f8 = wl.with_fp8_kv(inp)
+    say(f"[fp8] varlen + temperature path={path}")
+    q, q2k = to_dev(inp["q"]), to_dev(inp["q2k"])
+    cu = (to_dev(inp["cu_seqlens_q"]), to_dev(inp["cu_seqlens_k"]))
+    k8, v8 = fp8_dev(f8["k"]), fp8_dev(f8["v"])
+    tk = dict(return_temperature_lse=True, lse_temperature_scale=0.5)
+    o8, l8, t8 = msa.msa_sparse_fwd_varlen(q, k8, v8, q2k, *cu, causal=True, path=path, **tk)
+    od, ld, td = msa.msa_sparse_fwd_varlen(q, k8.to(torch.bfloat16).contiguous(),
+                                           v8.to(torch.bfloat16).contiguous(), q2k, *cu,
+                                           causal=True, path=path, **tk)
+    torch.cuda.synchronize()
+    assert bits_equal(o8, od) and bits_equal(l8, ld) and bits_equal(t8, td)
+    o_ref, lse_ref, lt_ref = oracle.sparse_attention_varlen(
+        f8["q"], f8["k"], f8["v"], f8["q2k"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+        causal=True, temperature=0.5)
+    compare(bf16_dev_to_f64(o8), l8.cpu().numpy().astype(np.float64), o_ref, lse_ref, "varlen")
+    check_lse_t(t8.cpu().numpy(), lt_ref, f"varlen-fp8-T0.5-path{path}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_paged_fp8_temperature(splits):
+    """fp8 cache with the temperature-scaled LSE on the paged q-centric kernel, one split
+    and four (the split combine merges both LSEs)."""
+    import block_sparse_attention_top_amd as msa
+    w = wl.Workload("fpt", B=3, Sq=8, Skv=4096, Hkv=2, qpk=16, topk=8, causal=True,
+                    mode=wl.MODE_CAUSAL, paged=True, seqused_trim=60, seed=88)
+    inp = wl.make_inputs(w)
+    f8 = wl.with_fp8_kv(inp)
+    say(f"[fp8] paged + temperature splits={splits}")
+    t = {n: to_dev(inp[n]) for n in ("q", "page_table", "seqused_k", "q2k")}
+    k8, v8 = fp8_dev(f8["k_pool"]), fp8_dev(f8["v_pool"])
+    args = (t["page_table"], t["seqused_k"], t["q2k"])
+    tk = dict(return_temperature_lse=True, lse_temperature_scale=2.0)
+    o8, l8, t8 = msa.msa_paged_sparse_fwd(t["q"], k8, v8, *args, causal=True,
+                                          num_splits=splits, path=Q, **tk)
+    od, ld, td = msa.msa_paged_sparse_fwd(t["q"], k8.to(torch.bfloat16).contiguous(),
+                                          v8.to(torch.bfloat16).contiguous(), *args, causal=True,
+                                          num_splits=splits, path=Q, **tk)
+    torch.cuda.synchronize()
+    assert bits_equal(o8, od) and bits_equal(l8, ld) and bits_equal(t8, td)
+    o_ref, lse_ref, lt_ref = oracle.paged_sparse_attention(
+        f8["q"], f8["k_pool"], f8["v_pool"], f8["page_table"], f8["seqused_k"], f8["q2k"],
+        causal=True, temperature=2.0)
+    compare(bf16_dev_to_f64(o8), l8.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
+            lse_ref.transpose(0, 2, 1), "paged")
+    check_lse_t(t8.cpu().numpy(), lt_ref, f"paged-fp8-T2-splits{splits}")
 
 
 def test_fp8_rejected_by_the_bf16_only_paths():

@@ -8,21 +8,11 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import bf16_dev_to_f64, compare, say, to_dev
+from parity_util import bf16_dev_to_f64, check_lse_t, compare, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
 Q, KV, DEC, TILE = 1, 2, 3, 4
-
-
-def check_lse_t(lt_gpu, lt_ref, label):
-    lt_gpu = np.asarray(lt_gpu, dtype=np.float64)
-    fin = np.isfinite(lt_ref)
-    assert np.array_equal(np.isneginf(lt_gpu), ~fin), f"{label}: empty-row mask differs"
-    err = np.abs(lt_gpu[fin] - lt_ref[fin])
-    bound = 1e-3 + 1e-3 * np.abs(lt_ref[fin])
-    assert np.all(err <= bound), f"{label}: temperature LSE error {err.max()}"
-    return float(err.max()) if err.size else 0.0
 
 
 def contiguous(B, Sq, Skv, Hkv, qpk, topk, causal, mode, seed):
