@@ -53,8 +53,9 @@ def run_fp8(inp, w, max_kv, causal=True, **kw):
     return out
 
 
-def check(o_gpu, lse_gpu, o_ref, lse_ref, label):
-    """o_* [rows, Hq, D], lse_* [rows, Hq]; the page's fp8 rule plus a 1e-3 LSE bound."""
+def check(o_gpu, lse_gpu, o_ref, lse_ref, label, lse_abs=1e-3):
+    """o_* [rows, Hq, D], lse_* [rows, Hq]; the page's fp8 rule plus an absolute LSE
+    bound (lse_abs; None keeps the page's relative rule alone)."""
     o_g = np.asarray(o_gpu, dtype=np.float64)
     o_bf = torch.from_numpy(o_ref).to(torch.bfloat16).double().numpy()
     floor = np.abs(o_bf - o_ref).max()
@@ -66,7 +67,8 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, label):
     say(f"[{label}] O max-abs {o_err:.4f} (bf16 floor {floor:.4f}), LSE max-abs {lse_err:.2e}")
     assert o_err <= max(0.125, 4 * floor), f"{label}: O error {o_err}"
     assert np.all(np.abs(lse_g[fin] - lse_ref[fin]) <= 2e-3 + 2e-3 * np.abs(lse_ref[fin]))
-    assert lse_err <= 1e-3, f"{label}: LSE error {lse_err}"
+    if lse_abs is not None:
+        assert lse_err <= lse_abs, f"{label}: LSE error {lse_err}"
     assert not np.any(o_g[~fin]), f"{label}: empty rows must be zero"
 
 
@@ -191,3 +193,25 @@ def test_fp8_decode_bad_pages_and_nan_tails():
     o, lse = run_fp8(inp, w, 1024)
     check(*as_rows(o, lse), *oracle_rows(inp), "fp8-bad-pages")
     assert torch.isfinite(o.float()).all()
+
+
+def test_fp8_decode_peaked():
+    """Peaked scores (Q x 16 and V / 4, applied before the e4m3 rounding): the decode's
+    lazy reference max moves often, which is where its rounding of P against the running
+    max departs most from the reference's rounding against the final max. Still within
+    the page's fp8 rule. The LSEs here are ~50: the fp32 accumulation of dot products
+    of that size alone is ~1e-3 in natural-log units, so the test keeps the page's
+    relative LSE rule (2e-3 + 2e-3 |LSE|) without the absolute 1e-3 bound of the
+    N(0, 1) cases."""
+    from test_gpu_peaked import scaled
+    w = wl.Workload("df8p", B=3, Sq=SQ, Skv=3072, Hkv=2, qpk=16, topk=1, causal=True,
+                    mode=wl.MODE_CAUSAL, paged=True, seed=96)
+    inp = wl.make_inputs(w)
+    inp["seqused_k"] = np.asarray([3000, 1, 2500], dtype=np.int32)
+    inp["q"] = scaled(inp["q"], 16)
+    inp["v_pool"] = scaled(inp["v_pool"], 0.25)
+    for n in ("q", "k_pool", "v_pool"):
+        inp[n] = wl.bf16_bits_to_fp8(inp[n])
+    say("[fp8 dense] peaked scores")
+    o, lse = run_fp8(inp, w, 3000)
+    check(*as_rows(o, lse), *oracle_rows(inp), "fp8-peaked", lse_abs=None)
