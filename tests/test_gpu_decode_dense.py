@@ -94,7 +94,7 @@ def run_dense(inp, w, max_kv, causal=True, **kw):
     import block_sparse_attention_top_amd as msa
     t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k")}
     tk = {k: kw.pop(k) for k in list(kw) if k in ("return_temperature_lse",
-                                                  "lse_temperature_scale")}
+                                                  "lse_temperature_scale", "softmax_scale")}
     p = msa.msa_paged_decode_plan(t["page_table"], t["seqused_k"], seqlen_q=w.Sq,
                                   max_seqlen_k=max_kv, num_qo_heads=w.Hq, num_kv_heads=w.Hkv,
                                   **kw)

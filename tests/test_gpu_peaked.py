@@ -66,3 +66,33 @@ def test_dense_decode_peaked():
     o_ref, lse_ref = oracle_dense(inp, w)
     compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
             lse_ref.transpose(0, 2, 1), "peaked-dense")
+
+
+@pytest.mark.parametrize("path,splits", [(Q, 1), (Q, 3), (DEC, 0)])
+def test_paged_softmax_scale(path, splits):
+    """An explicit softmax scale (0.2, above the default D^-0.5 = 0.088) on both paged
+    kernels; the contiguous paths take one in test_unused_slots_invalid_ids_and_empty_blocks."""
+    w = wl.Workload("pks", B=2, Sq=4, Skv=2048, Hkv=2, qpk=8, topk=8, causal=True,
+                    mode=wl.MODE_CAUSAL, paged=True, seqused_trim=5, seed=97)
+    inp = wl.make_inputs(w)
+    say(f"[scale] paged path={path} splits={splits}")
+    o, lse = run_paged(inp, True, num_splits=splits, softmax_scale=0.2, path=path)
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   inp["q2k"], causal=True, softmax_scale=0.2)
+    full_compare(o, lse, o_ref, lse_ref, f"scale-paged-{path}-{splits}")
+
+
+def test_dense_decode_softmax_scale():
+    from test_gpu_decode_dense import dense_inputs, run_dense
+    w, inp = dense_inputs(98, 2, 2000, [2000, 700])
+    say("[scale] dense decode")
+    _, (o, lse) = run_dense(inp, w, 2000, softmax_scale=0.2)
+    full = np.broadcast_to(np.arange(w.max_pages, dtype=np.int32),
+                           (w.B, w.Hkv, w.Sq, w.max_pages))
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   np.ascontiguousarray(full), causal=True,
+                                                   softmax_scale=0.2)
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
+            lse_ref.transpose(0, 2, 1), "scale-dense")
