@@ -62,6 +62,16 @@ def test_contiguous_small(path, name, B, Sq, Skv, Hkv, qpk, topk, causal, mode):
     check_contiguous(w, inp, path, name)
 
 
+@pytest.mark.parametrize("path", [Q, KV])
+@pytest.mark.parametrize("Hkv", [3, 5, 12, 16])
+def test_kv_head_counts(path, Hkv):
+    """KV head counts whose item streams do not line up with the heads: the kv-centric
+    items are cut into 1, 2, 4 or 8 streams of equal key ranges, so 3, 5 and 12 heads
+    put stream boundaries inside a head's query range, and 16 heads share streams."""
+    w, inp = contiguous_case(2, 300, 1024, Hkv, 2, 4, True, wl.MODE_CAUSAL, seed=8 + Hkv)
+    check_contiguous(w, inp, path, f"hkv{Hkv}")
+
+
 @pytest.mark.parametrize("path", [Q, KV, TILE])
 @pytest.mark.parametrize("qpk", [1, 2, 4, 8, 16])
 def test_qhead_per_kv_sweep(path, qpk):
