@@ -291,21 +291,24 @@ struct KvParams {
 // persistent grid (two workgroups per compute unit, at most max_items) over the
 // streams of the key-ordered item table
 hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t stream);
-// The item order's counters: counts, next and cursor must be zero before the item table
-// is filled (the CSR count pass, or a fill kernel for a caller's CSR, clears the first
-// kKvSortZeroInts ints, which hold all three).
+// The item order's counters: counts, next, bad and cursor must be zero before the item
+// table is filled (the CSR count pass, or a fill kernel for a caller's CSR, clears the
+// first kKvSortZeroInts ints, which hold all four).
 struct KvSortBuffers {
   int32_t* counts;     // [kKvKeys] items per key
   int32_t* next;       // [kKvStreams] items taken from each stream (KvParams::stream_next)
+  int32_t* bad;        // [1] set when a caller's CSR row_ptr is not non-decreasing in [0, cap]
   int32_t* cursor;     // [kKvKeys] items placed per key by the sort
   int32_t* key_start;  // [kKvKeys + 1] first item of each key (written by the sort)
 };
-// counts, next and cursor lie in the first kKvSortZeroInts ints, which must be zero
+// counts, next, bad and cursor lie in the first kKvSortZeroInts ints, which must be zero
 // before the item table is built
+static_assert(kKvStreams < 16, "next and bad share 16 ints");
 constexpr int kKvSortZeroInts = kKvKeys + 16 + kKvKeys;
 constexpr int kKvSortInts = kKvSortZeroInts + kKvKeys + 1;
 inline KvSortBuffers kv_sort_buffers(int32_t* base) {
-  return KvSortBuffers{base, base + kKvKeys, base + kKvKeys + 16, base + kKvSortZeroInts};
+  return KvSortBuffers{base, base + kKvKeys, base + kKvKeys + kKvStreams, base + kKvKeys + 16,
+                       base + kKvSortZeroInts};
 }
 // The unsorted item table has a fixed slot for every possible item: item j of row r
 // of KV head hkv starts at row position p = row start + j * chunk, and
@@ -316,6 +319,13 @@ inline KvSortBuffers kv_sort_buffers(int32_t* base) {
 __host__ __device__ inline long long kv_item_slot(int hkv, long long per_head, int pos,
                                                   int chunk_shift, int row) {
   return static_cast<long long>(hkv) * per_head + (pos >> chunk_shift) + row;
+}
+// A row [rb, re) of a caller's CSR is used only if 0 <= rb <= re <= cap. Each used row
+// then reads and slots inside the tables, and when every row of a KV head passes, its
+// row starts are non-decreasing within [0, cap], so kv_item_slot's slots are distinct
+// and each key's count is exact; a failing row voids the whole item order (sb.bad).
+__host__ __device__ inline bool kv_row_ok(long long rb, long long re, long long cap) {
+  return rb >= 0 && rb <= re && re <= cap;
 }
 // Key of a kv-centric work item: its KV head and first query as one coordinate
 // c = hkv * nq + first query, bucketed into kKvKeys equal ranges; stream s of the

@@ -82,9 +82,15 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
 
   // stage the chunk's entries and the block's K and V (128 tokens x 256 B each)
   if (p.slot) {
+    // a caller's CSR: an entry whose query is not in the row's sequence or whose slot
+    // is outside [0, topk) is kept as padding (slot -1, query 0: nothing gathered out
+    // of bounds, nothing stored)
     for (int i = tid; i < ne; i += 256) {
-      ent_q[i] = p.q_idx[hkv * p.cap + e0 + i];
-      ent_t[i] = p.slot[hkv * p.cap + e0 + i];
+      const int q = p.q_idx[hkv * p.cap + e0 + i];
+      const int t = p.slot[hkv * p.cap + e0 + i];
+      const bool v = q >= qbeg && q < qbeg + sq_b && t >= 0 && t < p.topk;
+      ent_q[i] = v ? q : 0;
+      ent_t[i] = v ? t : -1;
     }
   } else {  // entries stored as index-table positions query * topk + slot
     for (int i = tid; i < ne; i += 256) {
@@ -160,10 +166,10 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
   };
   auto fetch = [&](int step, Rows& R) {
     const int i = step * EPW + ent;
-    R.ok = i < ne;
-    const int ii = R.ok ? i : 0;
+    const int ii = i < ne ? i : 0;
     R.gq = ent_q[ii];
     R.t = ent_t[ii];
+    R.ok = i < ne && R.t >= 0;
     const uint16_t* qrow = p.q + (static_cast<long long>(R.gq) * p.Hq + head) * kD + 8 * h;
 #pragma unroll
     for (int kq = 0; kq < 8; ++kq)
@@ -419,7 +425,10 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
 // l + 64, ..., so that a long row is spread over a wave and every first-query load of
 // a round is in flight together. The order-free CSR that the library builds itself
 // lists its items while it scatters (KvItemEmit), so this kernel runs only for a
-// caller's CSR.
+// caller's CSR. Its row_ptr is not trusted: a row is used only if kv_row_ok, which
+// keeps every read and slot in bounds; any other row raises sb.bad, and the sort then
+// places no item at all (with a row out of order, rows may overlap, their slots collide
+// and the counts overshoot).
 __global__ __launch_bounds__(256) void kv_items_kernel(
     const int32_t* __restrict__ row_ptr, int Hkv, int nrows, int chunk_shift, long long per_head,
     int4* __restrict__ items, const int32_t* __restrict__ q_idx, long long cap, long long nq,
@@ -433,7 +442,10 @@ __global__ __launch_bounds__(256) void kv_items_kernel(
   if (idx < static_cast<long long>(Hkv) * nrows) {
     const int hkv = static_cast<int>(idx / nrows), r = static_cast<int>(idx % nrows);
     const int32_t* rp = row_ptr + static_cast<long long>(hkv) * (nrows + 1);
-    const int beg = rp[r], end = rp[r + 1];
+    const int rb = rp[r], re = rp[r + 1];
+    const bool ok = kv_row_ok(rb, re, cap);
+    if (!ok && lane == 0) atomicOr(sb.bad, 1);
+    const int beg = ok ? rb : 0, end = ok ? re : 0;
     const int nch = end > beg ? (end - beg + chunk - 1) >> chunk_shift : 0;
     for (int j = lane; j < nch; j += 64) {
       const int e = beg + j * chunk;
@@ -457,6 +469,7 @@ __global__ __launch_bounds__(256) void kv_items_kernel(
 // slots hold entry count 0) per key in LDS, reserves a range of every key it holds
 // with one atomic on the key's cursor, and places its items there. Order inside a key
 // is arbitrary: each item writes its own partials, so the results do not depend on it.
+// With sb.bad set every count reads as zero: no item is placed and the starts are 0.
 __global__ __launch_bounds__(256) void kv_sort_scatter(
     const int4* __restrict__ items, long long nslots, KvSortBuffers sb, int Hkv,
     const int32_t* __restrict__ q_idx, long long cap, long long nq, int qdiv,
@@ -466,10 +479,12 @@ __global__ __launch_bounds__(256) void kv_sort_scatter(
   __shared__ int base[kKvKeys];
   __shared__ int wsum[4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // a caller's CSR whose row_ptr failed the item kernel's check: no items at all
+  const bool bad = *sb.bad != 0;
   int c[kPer], own = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    c[k] = sb.counts[t * kPer + k];
+    c[k] = bad ? 0 : sb.counts[t * kPer + k];
     own += c[k];
   }
   int x = own;
@@ -496,7 +511,7 @@ __global__ __launch_bounds__(256) void kv_sort_scatter(
   const long long ci = static_cast<long long>(blockIdx.x) * 256 + t;
   int4 it = make_int4(0, 0, 0, 0);
   int key = -1, rank = 0;
-  if (ci < nslots) {
+  if (ci < nslots && !bad) {
     it = items[ci];
     if (it.w > 0) {
       key = kv_item_key(it.x, q_idx[it.x * cap + it.z] / qdiv, nq, Hkv);

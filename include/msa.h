@@ -35,6 +35,13 @@
  *     [0, num_pages) are treated as unused slots (no device-side error).
  *     The slots of one index row must name distinct blocks; repeated ids
  *     give unspecified results.
+ *   - A prebuilt k2q CSR given to a forward must be what the matching
+ *     msa_build_k2q_csr* call wrote for the same q2k and sizes. Any other
+ *     contents give unspecified results, but every access stays inside the
+ *     tensors: a row_ptr that is not non-decreasing within [0, rows * topk]
+ *     (rows = B * Sq, or total_q) makes the kv-centric pass compute no partial
+ *     at all, and an entry whose query lies outside its row's sequence, or
+ *     whose slot lies outside [0, topk), is skipped.
  *   - Every forward entry point takes (lse_temperature_scale, lse_temperature):
  *     lse_temperature NULL skips the temperature-scaled LSE; otherwise it is an
  *     fp32 output in the layout of lse and lse_temperature_scale = T must be

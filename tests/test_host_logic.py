@@ -78,7 +78,7 @@ def test_kv_item_slots_distinct_and_in_range(slot_exe, Hkv, shift, nrows, seed):
     kinds = [0, 1, chunk, chunk + 1, 2 * chunk - 1, 3 * chunk]
     lens = [int(rng.choice(kinds)) if rng.random() < 0.5 else int(rng.integers(0, 6 * chunk))
             for _ in range(Hkv * nrows)]
-    inp = f"{Hkv} {shift} {nrows}\n" + " ".join(map(str, lens)) + "\n"
+    inp = f"len {Hkv} {shift} {nrows}\n" + " ".join(map(str, lens)) + "\n"
     out = subprocess.run([slot_exe], input=inp, capture_output=True, text=True,
                          check=True).stdout.split()
     per_head = int(out[0])
@@ -87,6 +87,53 @@ def test_kv_item_slots_distinct_and_in_range(slot_exe, Hkv, shift, nrows, seed):
     assert len(slots) == n_items
     assert len(set(slots)) == n_items
     assert min(slots, default=0) >= 0 and max(slots, default=0) < Hkv * per_head
+
+
+@pytest.mark.parametrize("kind", ["valid", "descent", "negative", "past_cap", "huge",
+                                  "random"])
+def test_kv_caller_row_ptr_checked(slot_exe, kind):
+    """A caller's CSR row_ptr is not trusted by the kv-centric item kernel: a row is
+    listed only if 0 <= row_ptr[r] <= row_ptr[r + 1] <= cap (kv_row_ok), any failing
+    row voids the item order, and every listed chunk must then lie in [0, cap) with
+    its slot inside the table; with no failing row the slots must be distinct."""
+    rng = np.random.default_rng(11)
+    Hkv, shift, nrows, cap = 3, 7, 60, 60 * 200
+    chunk = 1 << shift
+    rp = []
+    for _ in range(Hkv):
+        lens = rng.integers(0, 4 * chunk, size=nrows)
+        lens = (lens * cap // max(int(lens.sum()), cap)).astype(np.int64)
+        rp.append(np.concatenate([[0], np.cumsum(lens)]))
+    rp = np.stack(rp)
+    if kind == "descent":
+        rp[1, 17], rp[1, 18] = rp[1, 18] + 5, rp[1, 17]
+    elif kind == "negative":
+        rp[0, 0] = -5
+    elif kind == "past_cap":
+        rp[2, nrows] = cap + 1
+    elif kind == "huge":
+        rp[1, 30:] = (1 << 31) - 1
+    elif kind == "random":
+        rp = rng.integers(-cap, 2 * cap, size=rp.shape)
+    want_bad = any(not (0 <= rp[h, r] <= rp[h, r + 1] <= cap)
+                   for h in range(Hkv) for r in range(nrows))
+    assert want_bad == (kind != "valid")
+    inp = f"ptr {Hkv} {shift} {nrows} {cap}\n" + " ".join(map(str, rp.ravel())) + "\n"
+    out = subprocess.run([slot_exe], input=inp, capture_output=True, text=True,
+                         check=True).stdout.split()
+    per_head, bad = int(out[0]), int(out[1])
+    assert per_head == cap // chunk + nrows + 1
+    assert bad == int(want_bad)
+    items = np.array([int(x) for x in out[2:]], dtype=np.int64).reshape(-1, 3)
+    if len(items):
+        slot, beg, end = items[:, 0], items[:, 1], items[:, 2]
+        assert slot.min() >= 0 and slot.max() < Hkv * per_head
+        assert beg.min() >= 0 and end.max() <= cap and (beg < end).all()
+    if not want_bad:
+        assert len(set(items[:, 0].tolist())) == len(items)
+        n_items = sum(-(-int(rp[h, r + 1] - rp[h, r]) // chunk)
+                      for h in range(Hkv) for r in range(nrows))
+        assert len(items) == n_items
 
 
 def test_bench_skew_diagnostics_brute_force():
