@@ -303,7 +303,11 @@ int msa_paged_sparse_fwd_noalloc(const void* q, const void* k_pool, const void* 
  *   disable_split_kv   one chunk per sequence (needs max_seqlen_k <= 512 pages)
  * msa_paged_decode_plan builds the schedule on the device from seqused_k on
  * `stream`, into the plan buffer; it stays valid while seqused_k does not change,
- * and any number of runs may use it. msa_paged_decode_run runs the decode.
+ * and any number of runs may use it. msa_paged_decode_run runs the decode. A run
+ * with a seqused_k changed since the plan stays inside the tensors (page counts
+ * are clamped to max_pages when planned, key counts when run) but its results
+ * are unspecified; a run on a buffer that msa_paged_decode_plan has not filled
+ * for this plan reads garbage indices and is undefined behaviour.
  * The schedule arrays (int32, at the byte offsets in the plan): kv_pages[B]
  * (ceil(seqused / 128)), split_counts[B] (chunks of each sequence), o_indptr[B+1]
  * (first partial row of each sequence; it advances by Sq * chunks),
