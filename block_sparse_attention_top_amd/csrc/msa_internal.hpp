@@ -32,11 +32,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
-// bf16 <-> fp32
+// fp32 -> bf16
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
 // Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -85,12 +82,6 @@ __device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-// c + a.lo * b.lo + a.hi * b.hi with a, b packed bf16 pairs (v_dot2c_f32_bf16)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as packed bf16
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // fp8 e4m3fn K/V cache: 16 fp8 bytes -> 16 bf16 values (exact; e4m3fn is a subset
@@ -118,12 +109,6 @@ constexpr float kLog2e = 1.442695040888963407359f;
 __host__ __device__ __forceinline__ int query_bucket(long long q, long long nq, int buckets) {
   const long long b = q * buckets / nq;
   return static_cast<int>(b < 0 ? 0 : (b >= buckets ? buckets - 1 : b));
-}
-
-// floor(a / b) for b > 0
-__host__ __device__ __forceinline__ long long floor_div(long long a, long long b) {
-  long long q = a / b;
-  return (a % b != 0 && a < 0) ? q - 1 : q;
 }
 
 // ---------------------------------------------------------------------------

@@ -8,7 +8,6 @@ it writes out and the passages of the pages it follows.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import subprocess
 from typing import Optional
@@ -287,5 +286,3 @@ def k2q_csr_varlen(q2k, cu_seqlens_q, cu_seqlens_k, *, blk: int = 128, with_slot
     return row_ptr, q_idx, slot
 
 
-def default_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)

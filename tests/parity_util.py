@@ -12,9 +12,6 @@ import sys
 import numpy as np
 import torch
 
-import oracle
-import workloads as wl
-
 O_ATOL = 2e-2
 LSE_ATOL = 1e-3
 

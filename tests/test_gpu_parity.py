@@ -6,8 +6,8 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import (compare, full_compare, run_contiguous, run_paged, sample_rows,
-                         sampled_compare, say, to_dev)
+from parity_util import (full_compare, run_contiguous, run_paged, sample_rows, sampled_compare,
+                         say, to_dev)
 
 pytestmark = pytest.mark.gpu
 

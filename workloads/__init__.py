@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np
@@ -229,9 +229,6 @@ def make_varlen_inputs(seed: int, q_lens, k_lens, Hkv: int, qpk: int, topk: int,
     out["q2k"] = q2k
     return out
 
-
-def varlen_effective_flops(q_lens, Hq: int, topk: int, D: int = 128, blk: int = 128) -> float:
-    return 4.0 * sum(q_lens) * Hq * topk * blk * D
 
 
 @dataclass
