@@ -17,12 +17,16 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msa_oracle.c")
 _HDR = os.path.join(_HERE, "msa_oracle.h")
-_LIB = os.path.join(_HERE, "libmsa_oracle.so")
+# MSA_ORACLE_LIB names an already built oracle library to load instead of this one; the
+# oracle's mutation test uses it to run the pins against deliberately broken copies
+_LIB = os.environ.get("MSA_ORACLE_LIB") or os.path.join(_HERE, "libmsa_oracle.so")
 _lib = None
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if os.environ.get("MSA_ORACLE_LIB"):
+        return _LIB  # given prebuilt
     newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
         tmp = _LIB + ".tmp%d" % os.getpid()

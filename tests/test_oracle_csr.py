@@ -48,6 +48,30 @@ def test_csr_matches_brute_force(mode, B, Hkv, Sq, Skv, topk):
             assert list(zip(q_idx[h, lo:hi].tolist(), slot[h, lo:hi].tolist())) == entries
 
 
+def test_csr_duplicate_ids_in_slot_order():
+    """A block named twice in one index row gives that CSR row two entries of the query,
+    in slot order: the CSR lists every valid (q, t) slot in ascending (q, t) order."""
+    B, Hkv, Sq, Skv, topk = 2, 2, 60, 1024, 6
+    nblk = Skv // 128
+    q2k = wl.q2k_table(13, wl.MODE_PERM, B, Hkv, Sq, Skv, 128, topk)
+    rng = np.random.default_rng(1)
+    rows = rng.random((B, Hkv, Sq)) < 0.4
+    for b, h, q in zip(*np.nonzero(rows)):
+        t1, t2 = sorted(rng.choice(topk, size=2, replace=False))
+        q2k[b, h, q, t2] = q2k[b, h, q, t1]
+    row_ptr, q_idx, slot = oracle.k2q_csr(q2k, nblk)
+    ref = brute_force_csr(q2k, nblk)
+    repeats = 0
+    for h in range(Hkv):
+        for r, entries in enumerate(ref[h]):
+            lo, hi = row_ptr[h, r], row_ptr[h, r + 1]
+            got = list(zip(q_idx[h, lo:hi].tolist(), slot[h, lo:hi].tolist()))
+            assert got == entries
+            qs = [e[0] for e in entries]
+            repeats += len(qs) - len(set(qs))
+    assert repeats == int(rows.sum())  # every planted repeat shows up as a second entry
+
+
 def test_csr_invariants_and_empty_rows():
     B, Hkv, Sq, Skv, topk = 2, 2, 200, 2048, 4
     nblk = Skv // 128
