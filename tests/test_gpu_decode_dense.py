@@ -104,13 +104,13 @@ def run_dense(inp, w, max_kv, causal=True, **kw):
     return p, out
 
 
-def oracle_dense(inp, w, causal=True, rows=None, temperature=None):
+def oracle_dense(inp, w, causal=True, rows=None, temperature=None, softmax_scale=None):
     full = np.broadcast_to(np.arange(w.max_pages, dtype=np.int32),
                            (w.B, w.Hkv, w.Sq, w.max_pages))
     return oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
                                          inp["page_table"], inp["seqused_k"],
                                          np.ascontiguousarray(full), causal=causal, rows=rows,
-                                         temperature=temperature)
+                                         temperature=temperature, softmax_scale=softmax_scale)
 
 
 @pytest.mark.parametrize("kv_tokens", [1, 8, 127, 128, 1000, 4096])
@@ -223,3 +223,60 @@ def test_dense_decode_wide_columns(sq):
     o_ref, lse_ref = oracle_dense(inp, w)
     compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
             lse_ref.transpose(0, 2, 1), f"dense-wide-{sq}")
+
+
+def draw_dense_cases(n=24, seed=2028, fp8=False):
+    """Seeded random dense decodes: KV heads, qhead_per_kv, query count, batch, ragged
+    seqused_k (zero included), split mode, causality, temperature and scale. The fp8
+    decode serves at most 128 (query, head) columns per KV head; bf16 takes wider
+    ones through the union kernel's dense mode."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        c = dict(hkv=int(rng.choice([1, 2, 3, 4, 8])), qpk=int(rng.choice([1, 2, 4, 8, 16])),
+                 sq=int(rng.integers(1, 17)), batch=int(rng.integers(1, 9)),
+                 max_kv=int(rng.integers(1, 4000)), causal=bool(rng.random() < 0.7),
+                 temp=[None, None, 0.5, 2.0][int(rng.integers(4))],
+                 scale=0.0 if rng.random() < 0.7 else float(rng.uniform(0.02, 0.2)),
+                 seed=int(rng.integers(1, 1 << 30)))
+        if fp8 and c["sq"] * c["qpk"] > 128:
+            continue
+        if not fp8 and rng.random() < 0.25:  # wider than 128 columns: the union kernel
+            c["qpk"], c["sq"] = 16, int(rng.integers(9, 17))
+        lens = [0 if rng.random() < 0.15 else int(rng.integers(1, c["max_kv"] + 1))
+                for _ in range(c["batch"])]
+        lens[int(rng.integers(c["batch"]))] = c["max_kv"]
+        c["lens"] = lens
+        c["split"] = [{}, {"fixed_split_size": int(rng.integers(1, 9))},
+                      {"disable_split_kv": True},
+                      {"max_grid_size": int(rng.choice([16, 64, 256]))}][int(rng.integers(4))]
+        if c["batch"] * c["sq"] * c["hkv"] * c["qpk"] * c["max_kv"] * 128 * 4 > 5e9:
+            continue
+        cases.append(c)
+    return cases
+
+
+DENSE_CASES = draw_dense_cases()
+
+
+@pytest.mark.parametrize("i", range(len(DENSE_CASES)))
+def test_dense_decode_random(i):
+    c = DENSE_CASES[i]
+    say(f"[dense sweep] case {i}: { {k: v for k, v in c.items() if k != 'seed'} }")
+    w, inp = dense_inputs(c["seed"], c["batch"], c["max_kv"], c["lens"], hkv=c["hkv"],
+                          qpk=c["qpk"], sq=c["sq"])
+    kw = dict(c["split"], softmax_scale=c["scale"])
+    if c["temp"]:
+        kw.update(return_temperature_lse=True, lse_temperature_scale=c["temp"])
+    p, out = run_dense(inp, w, c["max_kv"], causal=c["causal"], **kw)
+    ref = oracle_dense(inp, w, causal=c["causal"], temperature=c["temp"],
+                       softmax_scale=c["scale"] if c["scale"] > 0 else None)
+    o, lse = out[0], out[1]
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().transpose(0, 2, 1).astype(np.float64), ref[0],
+            ref[1].transpose(0, 2, 1), f"dense-random-{i}")
+    if c["temp"]:
+        lt_g = out[2].cpu().numpy().astype(np.float64)
+        lt_ref = ref[2]
+        fin = np.isfinite(lt_ref)
+        assert np.array_equal(np.isfinite(lt_g), fin)
+        assert np.all(np.abs(lt_g[fin] - lt_ref[fin]) <= 1e-3 + 1e-3 * np.abs(lt_ref[fin]))

@@ -215,3 +215,36 @@ def test_fp8_decode_peaked():
     say("[fp8 dense] peaked scores")
     o, lse = run_fp8(inp, w, 3000)
     check(*as_rows(o, lse), *oracle_rows(inp), "fp8-peaked", lse_abs=None)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_fp8_decode_random(i):
+    """Seeded random fp8 decodes (the bf16 sweep's generator, limited to the fp8
+    decode's 128 columns per KV head) under the page's fp8 rule."""
+    import block_sparse_attention_top_amd as msa
+    from test_gpu_decode_dense import draw_dense_cases
+    c = draw_dense_cases(seed=2029, fp8=True)[i]
+    say(f"[fp8 dense sweep] case {i}: { {k: v for k, v in c.items() if k != 'seed'} }")
+    w, inp = fp8_inputs(c["seed"], c["batch"], c["max_kv"], c["lens"], hkv=c["hkv"],
+                        qpk=c["qpk"], sq=c["sq"])
+    pt, seq = to_dev(inp["page_table"]), to_dev(inp["seqused_k"])
+    p = msa.msa_paged_decode_plan(pt, seq, seqlen_q=w.Sq, max_seqlen_k=c["max_kv"],
+                                  num_qo_heads=w.Hq, num_kv_heads=w.Hkv, **c["split"])
+    tk = dict(return_temperature_lse=True, lse_temperature_scale=c["temp"]) if c["temp"] else {}
+    out = msa.msa_paged_decode_run(p, fp8_dev(inp["q"]), fp8_dev(inp["k_pool"]),
+                                   fp8_dev(inp["v_pool"]), pt, seq, causal=c["causal"],
+                                   softmax_scale=c["scale"], **tk)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_fp8(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                  inp["seqused_k"], causal=c["causal"],
+                                  softmax_scale=c["scale"] if c["scale"] > 0 else None,
+                                  temperature=c["temp"])
+    o, lse = as_rows(out[0], out[1])
+    B, Sq, Hq, D = ref[0].shape
+    check(o, lse, ref[0].reshape(B * Sq, Hq, D), ref[1].transpose(0, 2, 1).reshape(B * Sq, Hq),
+          f"fp8-random-{i}")
+    if c["temp"]:
+        lt_g = out[2].cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref[2])
+        assert np.array_equal(np.isfinite(lt_g), fin)
+        assert np.all(np.abs(lt_g[fin] - ref[2][fin]) <= 1e-3 + 1e-3 * np.abs(ref[2][fin]))
