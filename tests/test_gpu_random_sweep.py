@@ -265,3 +265,77 @@ def test_random_large_case(i):
     compare(og, lg, ref[0], ref[1], f"large case {i}")
     if c["temp"]:
         check_lse_t(lt, ref[2], f"large case {i} temperature")
+
+
+def draw_csr_cases(n=24, seed=2030):
+    """Random index tables for the public k2q CSR builders: ids uniform with
+    replacement (so repeats within a row occur), holes (-1) and ids past the blocks,
+    CSR row counts on both sides of the builder's 3200-row switch between LDS mask
+    tables and ballot ranking; contiguous or varlen (empty sequences included)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        c = dict(varlen=bool(rng.random() < 0.35), Hkv=int(rng.integers(1, 5)),
+                 topk=int(rng.integers(1, 33)), p_hole=float(rng.choice([0.0, 0.05, 0.3])),
+                 p_oob=float(rng.choice([0.0, 0.02])), seed=int(rng.integers(1, 1 << 30)))
+        if c["varlen"]:
+            B = int(rng.integers(1, 7))
+            c["q_lens"] = [0 if rng.random() < 0.15 else int(rng.integers(1, 1500))
+                           for _ in range(B)]
+            c["k_lens"] = [0 if rng.random() < 0.15 else int(rng.integers(1, 150000))
+                           for _ in range(B)]
+            c["k_lens"][0] = max(c["k_lens"][0], 1)
+            entries = sum(c["q_lens"]) * c["Hkv"] * c["topk"]
+        else:
+            c["B"], c["Sq"] = int(rng.integers(1, 5)), int(rng.integers(1, 3000))
+            # 40% past 3200 CSR rows (B * nblk), where the builder ranks by ballots
+            c["nblk"] = (int(rng.integers(1, 1600)) if rng.random() < 0.6 else
+                         int(rng.integers(3300, 6500)) // c["B"] + 1)
+            entries = c["B"] * c["Sq"] * c["Hkv"] * c["topk"]
+        if entries == 0 or entries > (2 << 20):
+            continue
+        out.append(c)
+    return out
+
+
+CSR_CASES = draw_csr_cases()
+
+
+def _holes(rng, q2k, c, nblk_max):
+    q2k[rng.random(q2k.shape) < c["p_hole"]] = -1
+    q2k[rng.random(q2k.shape) < c["p_oob"]] = nblk_max + int(rng.integers(0, 5))
+    return q2k
+
+
+@pytest.mark.parametrize("i", range(len(CSR_CASES)))
+def test_random_csr(i):
+    import block_sparse_attention_top_amd as msa
+    c = CSR_CASES[i]
+    say(f"[sweep-csr] case {i}: { {k: v for k, v in c.items() if k != 'seed'} }")
+    rng = np.random.default_rng(c["seed"])
+    if c["varlen"]:
+        cu_q, cu_k = wl.cu_seqlens(c["q_lens"]), wl.cu_seqlens(c["k_lens"])
+        total_q = int(cu_q[-1])
+        q2k = np.full((c["Hkv"], total_q, c["topk"]), -1, dtype=np.int32)
+        for b in range(len(c["q_lens"])):
+            nb = -(-c["k_lens"][b] // 128)
+            if nb and c["q_lens"][b]:
+                q2k[:, cu_q[b]:cu_q[b + 1]] = rng.integers(0, nb, (c["Hkv"], c["q_lens"][b],
+                                                                   c["topk"]))
+        q2k = _holes(rng, q2k, c, max(-(-k // 128) for k in c["k_lens"]))
+        total_rows = oracle.varlen_total_rows(cu_k)
+        rp, qi, sl = msa.msa_build_k2q_csr_varlen(to_dev(q2k), to_dev(cu_q), to_dev(cu_k),
+                                                  int(cu_k[-1]), total_rows)
+        ref = oracle.k2q_csr_varlen(q2k, cu_q, cu_k)
+    else:
+        q2k = rng.integers(0, c["nblk"], (c["B"], c["Hkv"], c["Sq"], c["topk"])).astype(np.int32)
+        q2k = _holes(rng, q2k, c, c["nblk"])
+        rp, qi, sl = msa.msa_build_k2q_csr(to_dev(q2k), c["nblk"])
+        ref = oracle.k2q_csr(q2k, c["nblk"])
+    torch.cuda.synchronize()
+    rp, qi, sl = rp.cpu().numpy(), qi.cpu().numpy(), sl.cpu().numpy()
+    assert np.array_equal(rp, ref[0]), "row_ptr differs"
+    for h in range(c["Hkv"]):
+        n = ref[0][h, -1]
+        assert np.array_equal(qi[h, :n], ref[1][h, :n]), f"q_idx differs (h={h})"
+        assert np.array_equal(sl[h, :n], ref[2][h, :n]), f"slot differs (h={h})"
