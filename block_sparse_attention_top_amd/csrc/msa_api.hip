@@ -58,29 +58,41 @@ int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
   return MSA_OK;
 }
 
-// Automatic choice: the kv-centric path reads each selected K/V block once per
-// chunk of ~2048 (query, head) rows and pays a bf16 partial round trip; the
-// q-centric path re-reads a 64 KiB K/V block per (query, KV head) pair but
-// needs no CSR, schedule or combine launches. Small problems (launch-bound) and
-// problems with more CSR rows than the LDS-resident CSR passes take the
+// Automatic choice. The q-centric kernel works through (query, KV head, block) units,
+// each a 64 KiB K/V block read through the caches and multiplied for the qhead_per_kv
+// heads (padded to 16 matrix columns), so its time grows with the unit count whatever
+// qhead_per_kv is. The kv-centric path reads each selected block once per chunk of
+// ~2048 (query, head) rows and pays a bf16 partial round trip per (query, head, slot),
+// after a fixed chain of ~45 us of CSR, item and combine launches. Measured on one
+// MI355X (B 1, Hkv 4, Sq = Skv 256-8192, qhead_per_kv 1/4/16, topk 8/16, causal or
+// not), the kv-centric path is the faster one from 32768 units on, by up to 12x at
+// qhead_per_kv 1, and at most 17% slower just past that point at qhead_per_kv 16.
+// Problems with more CSR rows than the LDS-resident CSR passes hold take the
 // q-centric path.
+constexpr long long kKvMinUnits = 32768;
+long long qcentric_units(long long nq, int Hkv, int topk, long long nblk) {
+  return nq * Hkv * std::min<long long>(topk, nblk);  // blocks past the last one are unused
+}
 int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC || path == MSA_PATH_TILE) return path;
-  const long long nrows = static_cast<long long>(B) * (Skv / kBlk);
-  const long long work = static_cast<long long>(B) * Sq * Hq * topk;  // (query, head, slot) triples
-  if (nrows > kMaxCsrRows || work < (1LL << 20)) return MSA_PATH_QCENTRIC;
-  (void)Hkv;
+  (void)Hq;
+  const long long nblk = Skv / kBlk;
+  const long long nrows = static_cast<long long>(B) * nblk;
+  if (nrows > kMaxCsrRows ||
+      qcentric_units(static_cast<long long>(B) * Sq, Hkv, topk, nblk) < kKvMinUnits)
+    return MSA_PATH_QCENTRIC;
   return MSA_PATH_KVCENTRIC;
 }
 
-// Varlen batches: the same rule with the packed sizes; the CSR row count is
-// bounded on the host by floor(total_k / 128) + B (each sequence adds at most
-// one partial block), since the lengths themselves are on the device.
+// Varlen batches: the same rule with the packed sizes. The lengths are on the device,
+// so the host bounds a sequence's blocks by ceil(total_k / 128) and the CSR row count
+// by floor(total_k / 128) + B (each sequence adds at most one partial block).
 long long varlen_rows_bound(int B, long long total_k) { return total_k / kBlk + B; }
-int resolve_varlen_path(int path, int B, long long total_q, long long total_k, int Hq, int topk) {
+int resolve_varlen_path(int path, int B, long long total_q, long long total_k, int Hkv,
+                        int topk) {
   if (path != MSA_PATH_AUTO) return path;
-  const long long work = total_q * Hq * topk;
-  if (total_k == 0 || varlen_rows_bound(B, total_k) > kMaxCsrRows || work < (1LL << 20))
+  if (total_k == 0 || varlen_rows_bound(B, total_k) > kMaxCsrRows ||
+      qcentric_units(total_q, Hkv, topk, (total_k + kBlk - 1) / kBlk) < kKvMinUnits)
     return MSA_PATH_QCENTRIC;
   return MSA_PATH_KVCENTRIC;
 }
@@ -455,8 +467,8 @@ int msa_build_k2q_csr(const int32_t* q2k, int B, int Hkv, int Sq, int topk, int 
 // ---------------------------------------------------------------------------
 int msa_sparse_fwd_varlen_path(int B, int total_q, int total_k, int Hq, int Hkv, int topk,
                                int path) {
-  (void)Hkv;
-  return resolve_varlen_path(path, B, total_q, total_k, Hq, topk);
+  (void)Hq;
+  return resolve_varlen_path(path, B, total_q, total_k, Hkv, topk);
 }
 
 static bool varlen_sizes_ok(int B, int total_q, int total_k, int Hq, int Hkv, int D, int topk,
@@ -468,7 +480,7 @@ static bool varlen_sizes_ok(int B, int total_q, int total_k, int Hq, int Hkv, in
 size_t msa_sparse_fwd_varlen_workspace_size(int B, int total_q, int total_k, int Hq, int Hkv,
                                             int D, int topk, int blk_kv, int path) {
   if (!varlen_sizes_ok(B, total_q, total_k, Hq, Hkv, D, topk, blk_kv) || total_k == 0) return 0;
-  if (resolve_varlen_path(path, B, total_q, total_k, Hq, topk) != MSA_PATH_KVCENTRIC) return 0;
+  if (resolve_varlen_path(path, B, total_q, total_k, Hkv, topk) != MSA_PATH_KVCENTRIC) return 0;
   const long long nrows = varlen_rows_bound(B, total_k);
   return align256(varlen_tables_bytes(B, total_q, nrows)) +
          kv_layout(total_q, nrows, Hq, Hkv, topk).total;
@@ -516,7 +528,7 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
   const int qpk = Hq / Hkv;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  int which = resolve_varlen_path(path, B, total_q, total_k, Hq, topk);
+  int which = resolve_varlen_path(path, B, total_q, total_k, Hkv, topk);
   if (total_k == 0) which = MSA_PATH_QCENTRIC;  // no keys: every row is empty
   rc = check_kv_dtype(kv_dtype, which);
   if (rc) return rc;

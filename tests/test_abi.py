@@ -140,6 +140,13 @@ def test_auto_path_resolution():
     # small problems take the q-centric path, large ones the kv-centric path
     assert msa.msa_sparse_fwd_path(1, 1024, 1024, 2, 1, 4, 0) == 1
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 0) == 2
+    # the switch is at 32768 (query, KV head, block) units, B * Sq * Hkv * min(topk, nblk),
+    # whatever qhead_per_kv is
+    assert msa.msa_sparse_fwd_path(1, 1024, 1024, 4, 4, 8, 0) == 2    # 1024 * 4 * 8
+    assert msa.msa_sparse_fwd_path(1, 1023, 1024, 4, 4, 8, 0) == 1    # one query fewer
+    assert msa.msa_sparse_fwd_path(1, 1024, 1024, 64, 4, 16, 0) == 2  # min(16, 8 blocks)
+    assert msa.msa_sparse_fwd_path(1, 512, 512, 64, 4, 16, 0) == 1    # 512 * 4 * 4
+    assert msa.msa_sparse_fwd_path(1, 8192, 8192, 4, 4, 16, 0) == 2   # qhead_per_kv 1
     # more CSR rows than the kv-centric passes hold -> q-centric
     assert msa.msa_sparse_fwd_path(1, 8192, 128 * 20000, 64, 4, 16, 0) == 1
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 1) == 1
@@ -192,6 +199,10 @@ def test_varlen_workspace_and_paths():
     # small batches run q-centric (no workspace), large ones kv-centric
     assert msa.msa_sparse_fwd_varlen_path(3, 300, 900, 16, 1, 4) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(4, 32768, 32768, 64, 4, 16) == msa.MSA_PATH_KVCENTRIC
+    # units: total_q * Hkv * min(topk, ceil(total_k / 128))
+    assert msa.msa_sparse_fwd_varlen_path(2, 2048, 4096, 4, 4, 4, 0) == msa.MSA_PATH_KVCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(2, 2047, 4096, 4, 4, 4, 0) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(2, 2048, 384, 4, 4, 16, 0) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(4, 32768, 0, 64, 4, 16) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(2, 8192, 128 * 20000, 64, 4, 16) == \
         msa.MSA_PATH_QCENTRIC
