@@ -318,8 +318,13 @@ class Case:
             res["fwd"].append(timed(fwd, n))
             res["both"].append(timed(self.step, n))
         med = {k: float(np.median(v)) for k, v in res.items()}
+        # the CSR build's algorithmic bytes: the index table read, row_ptr written, and
+        # q_idx and slot written for every valid entry
+        nnz = int(csr[0][:, -1].sum().item())
+        csr_bytes = t["q2k"].numel() * 4 + csr[0].numel() * 4 + 2 * nnz * 4
         return {"csr_ms": med["csr"], "fwd_ms": med["fwd"], "csr_plus_fwd_ms": med["both"],
-                "fwd_TFLOP_per_s": self.flops / (med["fwd"] * 1e-3) / 1e12}
+                "fwd_TFLOP_per_s": self.flops / (med["fwd"] * 1e-3) / 1e12,
+                "csr_bytes": csr_bytes, "csr_GB_per_s": csr_bytes / (med["csr"] * 1e-3) / 1e9}
 
     def metric(self, ms: float, kernel_ms: float) -> dict:
         if self.w.paged:
