@@ -67,8 +67,8 @@ int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
 // MI355X (B 1, Hkv 4, Sq = Skv 256-8192, qhead_per_kv 1/4/16, topk 8/16, causal or
 // not), the kv-centric path is the faster one from 32768 units on, by up to 12x at
 // qhead_per_kv 1, and at most 17% slower just past that point at qhead_per_kv 16.
-// Problems with more CSR rows than the LDS-resident CSR passes hold take the
-// q-centric path.
+// A sequence with more blocks than the LDS-resident CSR passes hold takes the q-centric
+// path; a batch with more rows in all runs the kv-centric path in sub-batches.
 constexpr long long kKvMinUnits = 32768;
 long long qcentric_units(long long nq, int Hkv, int topk, long long nblk) {
   return nq * Hkv * std::min<long long>(topk, nblk);  // blocks past the last one are unused
@@ -77,11 +77,18 @@ int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC || path == MSA_PATH_TILE) return path;
   (void)Hq;
   const long long nblk = Skv / kBlk;
-  const long long nrows = static_cast<long long>(B) * nblk;
-  if (nrows > kMaxCsrRows ||
+  if (nblk > kMaxCsrRows ||
       qcentric_units(static_cast<long long>(B) * Sq, Hkv, topk, nblk) < kKvMinUnits)
     return MSA_PATH_QCENTRIC;
   return MSA_PATH_KVCENTRIC;
+}
+
+// The kv-centric passes hold one int per CSR row in LDS, so a batch of more than
+// kMaxCsrRows rows (B * Skv / 128) runs as consecutive sub-batches of this many whole
+// sequences (a sequence's queries select only its own blocks); 0 when one sequence alone
+// has too many blocks.
+int kv_sub_batch(int B, int nblk) {
+  return nblk > kMaxCsrRows ? 0 : std::min(B, kMaxCsrRows / nblk);
 }
 
 // Varlen batches: the same rule with the packed sizes. The lengths are on the device,
@@ -325,8 +332,10 @@ size_t msa_sparse_fwd_workspace_size(int B, int Sq, int Skv, int Hq, int Hkv, in
     return 0;
   const int which = resolve_path(path, B, Sq, Skv, Hq, Hkv, topk);
   if (which == MSA_PATH_QCENTRIC || which == MSA_PATH_TILE) return 0;
-  return kv_layout(static_cast<long long>(B) * Sq, static_cast<long long>(B) * (Skv / kBlk), Hq, Hkv,
-                   topk).total;
+  const int bc = kv_sub_batch(B, Skv / kBlk);  // the largest sub-batch
+  if (bc == 0) return 0;
+  return kv_layout(static_cast<long long>(bc) * Sq, static_cast<long long>(bc) * (Skv / kBlk), Hq,
+                   Hkv, topk).total;
 }
 
 int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q2k,
@@ -407,30 +416,48 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric forward");
   }
 
-  // kv-centric
+  // kv-centric, in sub-batches of whole sequences when the batch has more CSR rows than
+  // the CSR passes hold (a caller's CSR covers the whole batch, so it must fit)
   const long long nrows = static_cast<long long>(B) * nblk;
-  if (nrows > kMaxCsrRows)
-    return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: B*Skv/128 = %lld exceeds %d", nrows,
+  const int bc = kv_sub_batch(B, nblk);
+  if (bc == 0)
+    return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: Skv/128 = %d exceeds %d", nblk,
                 kMaxCsrRows);
-  const KvLayout L = kv_layout(static_cast<long long>(B) * Sq, nrows, Hq, Hkv, topk);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu", L.total,
+  if (have_csr && nrows > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED, "prebuilt CSR: B*Skv/128 = %lld exceeds %d", nrows,
+                kMaxCsrRows);
+  const size_t need = kv_layout(static_cast<long long>(bc) * Sq, static_cast<long long>(bc) * nblk,
+                                Hq, Hkv, topk).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
   if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
-  KvParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = k;
-  p.v = v;
-  p.kv_fp8 = kv_fp8;
-  p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
-  p.nblk = nblk; p.nrows = static_cast<int>(nrows);
-  p.cap = static_cast<long long>(B) * Sq * topk;
-  p.causal = causal ? 1 : 0;
-  p.scale_log2 = scale * kLog2e;
-  p.inv_temp = inv_temp;
-  return run_kvcentric(p, q2k, have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
-                       static_cast<char*>(workspace), nullptr, static_cast<uint16_t*>(o), lse,
-                       lse_temperature, st);
+  const size_t kv_elem = kv_fp8 ? 1 : 2;
+  for (int b0 = 0; b0 < B; b0 += bc) {
+    const int nb = std::min(bc, B - b0);
+    const long long q_off = static_cast<long long>(b0) * Sq * Hq * D;  // elements
+    const long long kv_off = static_cast<long long>(b0) * Skv * Hkv * D;
+    const long long l_off = static_cast<long long>(b0) * Hq * Sq;
+    const KvLayout L = kv_layout(static_cast<long long>(nb) * Sq, static_cast<long long>(nb) * nblk,
+                                 Hq, Hkv, topk);
+    KvParams p{};
+    p.q = static_cast<const uint16_t*>(q) + q_off;
+    p.k = static_cast<const char*>(k) + kv_off * kv_elem;
+    p.v = static_cast<const char*>(v) + kv_off * kv_elem;
+    p.kv_fp8 = kv_fp8;
+    p.B = nb; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+    p.nblk = nblk; p.nrows = nb * nblk;
+    p.cap = static_cast<long long>(nb) * Sq * topk;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.inv_temp = inv_temp;
+    rc = run_kvcentric(p, q2k + static_cast<long long>(b0) * Hkv * Sq * topk,
+                       have_csr ? csr_row_ptr : nullptr, csr_q_idx, csr_slot, L,
+                       static_cast<char*>(workspace), nullptr, static_cast<uint16_t*>(o) + q_off,
+                       lse + l_off, lse_temperature ? lse_temperature + l_off : nullptr, st);
+    if (rc) return rc;
+  }
+  return MSA_OK;
 }
 
 size_t msa_build_k2q_csr_workspace_size(int B, int Hkv, int Sq, int topk, int num_kv_blocks) {

@@ -106,7 +106,13 @@ enum msa_dtype {
  *            one. When NULL the kv-centric path builds it in the workspace.
  *   causal   0 none, 1 bottom-right (limit q + Skv - Sq)
  *   softmax_scale  <= 0 selects D^-0.5
- *   path     enum msa_path
+ *   path     enum msa_path. The kv-centric path keeps one int per CSR row
+ *            (B * nblk rows per KV head) in LDS, at most 16384: a longer batch
+ *            runs in sub-batches of floor(16384 / nblk) whole sequences (the
+ *            workspace covers one), a prebuilt CSR is then refused, and a
+ *            single sequence of more than 16384 blocks returns
+ *            MSA_ERR_NOT_SUPPORTED (the automatic path then takes the
+ *            q-centric one).
  *   kv_dtype enum msa_dtype
  *   o        bf16 [B, Sq, Hq, D]   (out)
  *   lse      fp32 [B, Hq, Sq]      (out)

@@ -147,8 +147,14 @@ def test_auto_path_resolution():
     assert msa.msa_sparse_fwd_path(1, 1024, 1024, 64, 4, 16, 0) == 2  # min(16, 8 blocks)
     assert msa.msa_sparse_fwd_path(1, 512, 512, 64, 4, 16, 0) == 1    # 512 * 4 * 4
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 4, 4, 16, 0) == 2   # qhead_per_kv 1
-    # more CSR rows than the kv-centric passes hold -> q-centric
+    # one sequence with more blocks than the kv-centric passes hold -> q-centric; a batch
+    # with more rows in all stays kv-centric (sub-batches of whole sequences)
     assert msa.msa_sparse_fwd_path(1, 8192, 128 * 20000, 64, 4, 16, 0) == 1
+    assert msa.msa_sparse_fwd_path(4, 4096, 128 * 8192, 64, 4, 16, 0) == 2
+    ws4 = msa.msa_sparse_fwd_workspace_size(4, 4096, 128 * 8192, 64, 4, 128, 16, 128, 2)
+    ws2 = msa.msa_sparse_fwd_workspace_size(2, 4096, 128 * 8192, 64, 4, 128, 16, 128, 2)
+    assert ws4 == ws2 > 0  # sized for one sub-batch of two sequences
+    assert msa.msa_sparse_fwd_workspace_size(1, 8192, 128 * 20000, 64, 4, 128, 16, 128, 2) == 0
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 1) == 1
     # paged: automatic is the q-centric kernel; the decode kernel is asked for
     assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16) == msa.MSA_PATH_QCENTRIC

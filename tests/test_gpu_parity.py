@@ -6,8 +6,8 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import (full_compare, run_contiguous, run_paged, sample_rows, sampled_compare,
-                         say, to_dev)
+from parity_util import (bf16_dev_to_f64, full_compare, run_contiguous, run_paged, sample_rows,
+                         sampled_compare, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -508,11 +508,37 @@ def test_kv_centric_at_max_csr_rows():
     assert w.B * (w.Skv // w.blk) == 16384
     o, lse = check_contiguous(w, inp, KV, "max-csr-rows")[1]
     del o, lse
-    # one more block per sequence is too many rows: refused on the host (contents unused)
-    B2, Skv2 = 8, 262144 + 128
-    kv0 = np.zeros((B2, Skv2, 1, 128), dtype=np.uint16)
-    inp2 = dict(q=inp["q"][:, :8].copy(), k=kv0, v=kv0,
-                q2k=np.zeros((B2, 1, 8, 4), dtype=np.int32))
-    inp2["q"] = np.zeros((B2, 8, 1, 128), dtype=np.uint16)
+    # one sequence of 16385 blocks is too many rows for the kv-centric passes: refused on
+    # the host before any launch (contents unused); the automatic path takes q-centric
+    Skv2 = (16384 + 1) * 128
+    kv0 = torch.zeros((1, Skv2, 1, 128), dtype=torch.bfloat16, device="cuda")
+    q0 = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    q2k0 = torch.zeros((1, 1, 8, 4), dtype=torch.int32, device="cuda")
     with pytest.raises(msa.MsaNotSupportedError):
-        run_contiguous(inp2, False, KV)
+        msa.msa_sparse_fwd(q0, kv0, kv0, q2k0, causal=False, path=KV)
+    assert msa.msa_sparse_fwd_path(1, 8, Skv2, 1, 1, 4, 0) == Q
+    del kv0
+
+
+def test_kv_centric_sub_batches():
+    """B * Skv / 128 = 3 x 5500 = 16500 CSR rows, past the 16384 the kv-centric passes
+    hold: the path runs sub-batches of two sequences and one. Sampled rows of every
+    sequence against the oracle, and every row against the q-centric path."""
+    import block_sparse_attention_top_amd as msa
+    w, inp = contiguous_case(3, 64, 5500 * 128, 1, 2, 8, True, wl.MODE_CAUSAL, seed=6)
+    assert w.B * (w.Skv // w.blk) == 16500
+    say(f"[sub-batch] {w.B} x {w.Skv // w.blk} blocks: kv-centric in sub-batches")
+    o, lse = run_contiguous(inp, True, KV)
+    rows = np.array([0, 1, 31, 63, 64, 100, 127, 128, 150, 191])  # all three sequences
+    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                             causal=True, rows=rows)
+    sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, "sub-batches")
+    oq, lq = run_contiguous(inp, True, Q)
+    full_compare(o, lse, bf16_dev_to_f64(oq).astype(np.float64),
+                 lq.cpu().numpy().astype(np.float64), "sub-batches vs q-centric")
+    # a prebuilt CSR covers the whole batch, so it must fit the CSR passes: refused
+    nr = w.B * (w.Skv // w.blk)
+    rp = torch.zeros((1, nr + 1), dtype=torch.int32, device="cuda")
+    qi = torch.zeros((1, w.B * w.Sq * w.topk), dtype=torch.int32, device="cuda")
+    with pytest.raises(msa.MsaNotSupportedError):
+        run_contiguous(inp, True, KV, csr=(rp, qi, qi))
