@@ -182,6 +182,18 @@ __device__ __forceinline__ void rank_in_batch(int row, int& rank, int& cnt) {
 constexpr int kCsrBatch = 8;  // entries per thread whose index loads are in flight together
 constexpr size_t kCsrMaskLdsMax = 150 * 1024;  // LDS of the mask-ranked scatter, at most
 
+// How the ordered scatter ranks a wave's 64-entry batch: by ballots per distinct row; with
+// a per-row table of lane masks in LDS; or with a small per-wave hash table of (row, mask)
+// slots, which needs no per-row table, so that wide tables leave room for more
+// workgroups per compute unit.
+enum CsrRank { kRankBallot = 0, kRankMask = 1, kRankHash = 2 };
+constexpr int kCsrHashSlots = 128;  // per wave; a batch holds at most 64 distinct rows
+// Tables of more rows than this rank by hash. Public build, ms, mask / hash ranking (the
+// same bits): 64 rows 0.024 / 0.026, 256 rows 0.045 / 0.047, 384 rows 0.035 / 0.037,
+// 3072 rows 0.219 / 0.189 (one workgroup per compute unit with the masks, two with the
+// slots), 8000 rows 0.250 / 0.059 (past the mask tables' LDS the one-wave scatter ran).
+constexpr int kCsrHashAboveRows = 2048;
+
 // Query tile of workgroup x. Workgroups are dealt round-robin over the 8 XCDs, and
 // consecutive tiles write adjacent counts and adjacent runs of a row's entries, so
 // the tiles are permuted to run in groups of ntiles / 8 consecutive tiles per XCD:
@@ -307,12 +319,14 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(CsrSrc a, int tile_q, i
 // finally runs the ballot-ranked scatter above on its quarter. Same output bits,
 // four times the waves. LDS: 4 * nrows ints.
 //
-// MASK: the lanes of a batch find the peers holding their row through a per-wave
-// table of 64-bit lane masks in LDS (each lane ORs its bit into its row's mask and
-// reads it back; the row's last lane clears it), in a constant number of steps
-// instead of one ballot pass per distinct row of the batch: on wide tables nearly
-// every entry of a batch has a row of its own. LDS: 4 * nrows * (4 + 8) bytes.
-template <bool VARLEN, bool I32, bool MASK>
+// kRankMask: the lanes of a batch find the peers holding their row through a
+// per-wave table of 64-bit lane masks in LDS (each lane ORs its bit into its row's
+// mask and reads it back; the row's last lane clears it), in a constant number of
+// steps instead of one ballot pass per distinct row of the batch: on wide tables
+// nearly every entry of a batch has a row of its own. LDS: 4 * nrows * (4 + 8) bytes.
+// kRankHash: the same masks kept in kCsrHashSlots (row, mask) slots per wave instead
+// of one per row. LDS: 4 * nrows * 4 + 4 * kCsrHashSlots * (8 + 4) bytes.
+template <bool VARLEN, bool I32, int RANK>
 __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q, int ntiles,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ q_idx,
@@ -329,15 +343,21 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
   const long long sub = (g1 - g0 + 3) / 4;
   const long long w0 = std::min(g1, g0 + wave * sub), w1 = std::min(g1, w0 + sub);
   int* cursor = lds + wave * nrows;
-  // MASK: the waves' mask tables follow the 4 * nrows cursors (8-byte aligned: nrows
-  // is rounded up to even)
-  unsigned long long* mask =
-      reinterpret_cast<unsigned long long*>(lds + 4 * ((nrows + 1) & ~1)) + wave * nrows;
+  // kRankMask: the waves' mask tables follow the 4 * nrows cursors (8-byte aligned:
+  // nrows is rounded up to even); kRankHash: there the waves' hash slots instead, each
+  // a row (-1 = empty) and a lane mask
+  unsigned long long* tables = reinterpret_cast<unsigned long long*>(lds + 4 * ((nrows + 1) & ~1));
+  unsigned long long* mask = tables + wave * nrows;
+  unsigned long long* hmask = tables + wave * kCsrHashSlots;
+  int* hkey = reinterpret_cast<int*>(tables + 4 * kCsrHashSlots) + wave * kCsrHashSlots;
   for (int r = tid; r < 4 * nrows; r += 256) lds[r] = 0;
-  if (MASK) {
-    unsigned long long* all = reinterpret_cast<unsigned long long*>(lds + 4 * ((nrows + 1) & ~1));
-    for (int r = tid; r < 4 * nrows; r += 256) all[r] = 0;
-  }
+  if (RANK == kRankMask)
+    for (int r = tid; r < 4 * nrows; r += 256) tables[r] = 0;
+  if (RANK == kRankHash)
+    for (int r = tid; r < 4 * kCsrHashSlots; r += 256) {
+      tables[r] = 0;
+      reinterpret_cast<int*>(tables + 4 * kCsrHashSlots)[r] = -1;
+    }
   __syncthreads();
   for (long long rb = w0 * a.topk; rb < w1 * a.topk; rb += 64 * kCsrBatch) {
     int rows[kCsrBatch];
@@ -368,13 +388,32 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
     for (int k = 0; k < kPer; ++k) {
       const long long e = rb + 64 * k + lane;
       const int row = rows[k];
-      int rank = 0, cnt = 0;
-      if (MASK) {
+      int rank = 0, cnt = 0, hs = 0;
+      if (RANK == kRankMask) {
         // one wave, LDS accesses in program order: every OR lands before the reads
         if (row >= 0) atomicOr(&mask[row], 1ull << lane);
         __builtin_amdgcn_wave_barrier();
         if (row >= 0) {
           const unsigned long long peers = mask[row];
+          rank = __popcll(peers & __lanemask_lt());
+          cnt = __popcll(peers);
+        }
+      } else if (RANK == kRankHash) {
+        // claim the row's slot (linear probing from a multiplicative hash; the table
+        // never holds more than 64 rows, so every lane finds its row or an empty slot
+        // within kCsrHashSlots probes), then OR the lane into the slot's mask
+        if (row >= 0) {
+          hs = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 25);
+          for (int probe = 0; probe < kCsrHashSlots; ++probe) {
+            const int prev = atomicCAS(&hkey[hs], -1, row);
+            if (prev == -1 || prev == row) break;
+            hs = (hs + 1) & (kCsrHashSlots - 1);
+          }
+          atomicOr(&hmask[hs], 1ull << lane);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (row >= 0) {
+          const unsigned long long peers = hmask[hs];
           rank = __popcll(peers & __lanemask_lt());
           cnt = __popcll(peers);
         }
@@ -388,7 +427,11 @@ __global__ __launch_bounds__(256) void csr_scatter4_kernel(CsrSrc a, int tile_q,
       __builtin_amdgcn_wave_barrier();
       if (row >= 0 && rank == cnt - 1) {
         cursor[row] = pos + 1;
-        if (MASK) mask[row] = 0;
+        if (RANK == kRankMask) mask[row] = 0;
+        if (RANK == kRankHash) {  // every lane of the row has read the mask: free the slot
+          hmask[hs] = 0;
+          hkey[hs] = -1;
+        }
       }
       if (row >= 0) {
         const long long q = idx_div<I32>(e, a.topk);
@@ -686,23 +729,34 @@ hipError_t build_csr_impl(const CsrSrc& a, int32_t* row_ptr, int32_t* q_idx, int
   if (err != hipSuccess) return err;
   err = launch_exclusive_scan(counts, offsets, plan.counts, tmp, stream);
   if (err != hipSuccess) return err;
-  // the mask-ranked scatter where its tables fit the LDS (a workgroup may take up to
-  // 160 KiB on gfx950; above 64 KiB the kernel must be allowed to), else ballot ranks
-  const size_t lds_mask = 4 * (static_cast<size_t>((nrows + 1) & ~1) * 4 +
-                               static_cast<size_t>(nrows) * 8);
-  bool mask_ok = ordered && lds_mask <= kCsrMaskLdsMax;
-  if (mask_ok && lds_mask > 64 * 1024)
-    mask_ok = hipFuncSetAttribute(
-                  reinterpret_cast<const void*>(&csr_scatter4_kernel<VARLEN, I32, true>),
-                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                  static_cast<int>(lds_mask)) == hipSuccess;
-  (void)hipGetLastError();  // a refused attribute leaves the ballot-ranked scatter
-  if (mask_ok)
-    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, true>), grid, dim3(256), lds_mask, stream,
-                       a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  // The ordered scatter ranks with hash slots on tables wider than kCsrHashAboveRows,
+  // else with per-row mask tables, where either fits the LDS (a workgroup may take up to
+  // 160 KiB on gfx950; above 64 KiB the kernel must be allowed to), else with ballots.
+  const size_t lds_cursors = 4 * static_cast<size_t>((nrows + 1) & ~1) * 4;
+  const size_t lds_mask = lds_cursors + 4 * static_cast<size_t>(nrows) * 8;
+  const size_t lds_hash = lds_cursors + 4 * kCsrHashSlots * (8 + 4);
+  const auto allow = [](const void* kern, size_t bytes) {
+    if (bytes <= 64 * 1024) return true;
+    const bool ok = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(bytes)) == hipSuccess;
+    (void)hipGetLastError();  // a refused attribute leaves the next ranking
+    return ok;
+  };
+  const bool hash_ok =
+      ordered && nrows > kCsrHashAboveRows && lds_hash <= kCsrMaskLdsMax &&
+      allow(reinterpret_cast<const void*>(&csr_scatter4_kernel<VARLEN, I32, kRankHash>), lds_hash);
+  const bool mask_ok =
+      ordered && !hash_ok && lds_mask <= kCsrMaskLdsMax &&
+      allow(reinterpret_cast<const void*>(&csr_scatter4_kernel<VARLEN, I32, kRankMask>), lds_mask);
+  if (hash_ok)
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, kRankHash>), grid, dim3(256), lds_hash,
+                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+  else if (mask_ok)
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, kRankMask>), grid, dim3(256), lds_mask,
+                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   else if (ordered && 4 * lds <= 64 * 1024)  // within the default dynamic LDS limit
-    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, false>), grid, dim3(256), 4 * lds, stream,
-                       a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
+    hipLaunchKernelGGL((csr_scatter4_kernel<VARLEN, I32, kRankBallot>), grid, dim3(256), 4 * lds,
+                       stream, a, plan.tile_q, plan.ntiles, offsets, q_idx, slot);
   else if (ordered)
     hipLaunchKernelGGL((csr_scatter_kernel<VARLEN, I32>), grid, dim3(64), lds, stream, a, plan.tile_q,
                        plan.ntiles, offsets, q_idx, slot);

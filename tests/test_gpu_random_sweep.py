@@ -270,8 +270,9 @@ def test_random_large_case(i):
 def draw_csr_cases(n=24, seed=2030):
     """Random index tables for the public k2q CSR builders: ids uniform with
     replacement (so repeats within a row occur), holes (-1) and ids past the blocks,
-    CSR row counts on both sides of the builder's 3200-row switch between LDS mask
-    tables and ballot ranking; contiguous or varlen (empty sequences included)."""
+    CSR row counts in each of the ordered builder's three scatters (per-row lane masks
+    in LDS up to 2048 rows, per-wave hash slots up to 9216, one wave per tile up to
+    the builders' 16384); contiguous or varlen (empty sequences included)."""
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -288,9 +289,12 @@ def draw_csr_cases(n=24, seed=2030):
             entries = sum(c["q_lens"]) * c["Hkv"] * c["topk"]
         else:
             c["B"], c["Sq"] = int(rng.integers(1, 5)), int(rng.integers(1, 3000))
-            # 40% past 3200 CSR rows (B * nblk), where the builder ranks by ballots
-            c["nblk"] = (int(rng.integers(1, 1600)) if rng.random() < 0.6 else
-                         int(rng.integers(3300, 6500)) // c["B"] + 1)
+            # CSR rows (B * nblk): 45% ranked by masks, 40% by hash slots, 15% past both
+            u = rng.random()
+            rows = (int(rng.integers(1, 2049)) if u < 0.45 else
+                    int(rng.integers(2049 + c["B"], 9217)) if u < 0.85 else
+                    int(rng.integers(9217 + c["B"], 16385)))  # the builders take 16384 rows
+            c["nblk"] = max(1, rows // c["B"])
             entries = c["B"] * c["Sq"] * c["Hkv"] * c["topk"]
         if entries == 0 or entries > (2 << 20):
             continue
