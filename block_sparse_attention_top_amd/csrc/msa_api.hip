@@ -67,18 +67,32 @@ int check_common(int B, int Sq, int Hq, int Hkv, int D, int topk, int blk) {
 // MI355X (B 1, Hkv 4, Sq = Skv 256-8192, qhead_per_kv 1/4/16, topk 8/16, causal or
 // not), the kv-centric path is the faster one from 32768 units on, by up to 12x at
 // qhead_per_kv 1, and at most 17% slower just past that point at qhead_per_kv 16.
+// That needs each selected block to serve several queries: a kv-centric item reads its
+// block once for the queries that selected it. Batches of short query sets over long
+// keys select each block about once (entries per CSR row = Sq * topk / blocks), and
+// there the q-centric kernel was faster (Hkv 4, 64 query heads, topk 16, causal): 0.38
+// against 0.64 ms at 0.25 entries per row (64 sequences of 8 queries over 65 536
+// keys), 1.27 against 1.55 ms at 1 (64 of 32 over 65 536); from 2 entries per row on
+// the kv-centric path was as fast or faster (0.34 against 0.32 ms for 64 of 8 over
+// 8192, 1.15 against 0.80 ms for 16 of 128 over 65 536, at 4).
 // A sequence with more blocks than the LDS-resident CSR passes hold takes the q-centric
 // path; a batch with more rows in all runs the kv-centric path in sub-batches.
 constexpr long long kKvMinUnits = 32768;
+constexpr long long kKvMinEntriesPerRow = 2;
 long long qcentric_units(long long nq, int Hkv, int topk, long long nblk) {
   return nq * Hkv * std::min<long long>(topk, nblk);  // blocks past the last one are unused
+}
+// nq query rows selecting among nrows CSR rows of nblk blocks per sequence (per KV head)
+bool kv_pays(long long nq, int Hkv, int topk, long long nblk, long long nrows) {
+  return qcentric_units(nq, Hkv, topk, nblk) >= kKvMinUnits &&
+         nq * std::min<long long>(topk, nblk) >= kKvMinEntriesPerRow * nrows;
 }
 int resolve_path(int path, int B, int Sq, int Skv, int Hq, int Hkv, int topk) {
   if (path == MSA_PATH_QCENTRIC || path == MSA_PATH_KVCENTRIC || path == MSA_PATH_TILE) return path;
   (void)Hq;
   const long long nblk = Skv / kBlk;
   if (nblk > kMaxCsrRows ||
-      qcentric_units(static_cast<long long>(B) * Sq, Hkv, topk, nblk) < kKvMinUnits)
+      !kv_pays(static_cast<long long>(B) * Sq, Hkv, topk, nblk, static_cast<long long>(B) * nblk))
     return MSA_PATH_QCENTRIC;
   return MSA_PATH_KVCENTRIC;
 }
@@ -99,7 +113,7 @@ int resolve_varlen_path(int path, int B, long long total_q, long long total_k, i
                         int topk) {
   if (path != MSA_PATH_AUTO) return path;
   if (total_k == 0 || varlen_rows_bound(B, total_k) > kMaxCsrRows ||
-      qcentric_units(total_q, Hkv, topk, (total_k + kBlk - 1) / kBlk) < kKvMinUnits)
+      !kv_pays(total_q, Hkv, topk, (total_k + kBlk - 1) / kBlk, varlen_rows_bound(B, total_k)))
     return MSA_PATH_QCENTRIC;
   return MSA_PATH_KVCENTRIC;
 }

@@ -70,7 +70,8 @@ enum msa_status {
 };
 
 enum msa_path {
-  MSA_PATH_AUTO = 0,      /* kv-centric for large problems, else q-centric */
+  MSA_PATH_AUTO = 0,      /* kv-centric for large problems whose selected blocks each serve
+                             two or more (query, slot) entries on average, else q-centric */
   MSA_PATH_QCENTRIC = 1,  /* one fused pass per (b, hkv, q) index row */
   MSA_PATH_KVCENTRIC = 2, /* CSR-driven per-block partials + LSE merge kernel */
   MSA_PATH_DECODE = 3,    /* paged only: one pass over the union of the blocks that

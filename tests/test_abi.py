@@ -151,6 +151,12 @@ def test_auto_path_resolution():
     # with more rows in all stays kv-centric (sub-batches of whole sequences)
     assert msa.msa_sparse_fwd_path(1, 8192, 128 * 20000, 64, 4, 16, 0) == 1
     assert msa.msa_sparse_fwd_path(4, 4096, 128 * 8192, 64, 4, 16, 0) == 2
+    # short query sets over long keys: each block serves about Sq * topk / nblk entries,
+    # and the kv-centric path needs two or more per block on average
+    assert msa.msa_sparse_fwd_path(64, 8, 65536, 64, 4, 16, 0) == 1    # 0.25 per block
+    assert msa.msa_sparse_fwd_path(16, 32, 65536, 64, 4, 16, 0) == 1   # 1
+    assert msa.msa_sparse_fwd_path(8, 64, 65536, 64, 4, 16, 0) == 2    # 2
+    assert msa.msa_sparse_fwd_path(64, 8, 8192, 64, 4, 16, 0) == 2     # 2
     ws4 = msa.msa_sparse_fwd_workspace_size(4, 4096, 128 * 8192, 64, 4, 128, 16, 128, 2)
     ws2 = msa.msa_sparse_fwd_workspace_size(2, 4096, 128 * 8192, 64, 4, 128, 16, 128, 2)
     assert ws4 == ws2 > 0  # sized for one sub-batch of two sequences
@@ -210,6 +216,9 @@ def test_varlen_workspace_and_paths():
     assert msa.msa_sparse_fwd_varlen_path(2, 2047, 4096, 4, 4, 4, 0) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(2, 2048, 384, 4, 4, 16, 0) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(4, 32768, 0, 64, 4, 16) == msa.MSA_PATH_QCENTRIC
+    # 512 queries over 8208 rows (bound): 8192 entries, fewer than 2 per row
+    assert msa.msa_sparse_fwd_varlen_path(16, 512, 16 * 65536, 64, 4, 16) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_sparse_fwd_varlen_path(4, 2048, 4 * 65536, 64, 4, 16) == msa.MSA_PATH_KVCENTRIC
     assert msa.msa_sparse_fwd_varlen_path(2, 8192, 128 * 20000, 64, 4, 16) == \
         msa.MSA_PATH_QCENTRIC
     assert msa.msa_sparse_fwd_varlen_workspace_size(3, 300, 900, 16, 1, 128, 4, 128, 1) == 0
