@@ -215,19 +215,20 @@ class Case:
                 causal=w.causal, o=self.o, lse=self.lse, **tk)
             self.bytes = dense_decode_algorithmic_bytes(w, self.inp)
         elif w.paged:
-            p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, PATHS[path])
-            if p not in (1, 3):
+            p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, w.max_pages, PATHS[path])
+            if p not in (1, 2, 3):
                 raise SystemExit(f"path {path} does not apply to the paged workload {key}")
             nb = msa.msa_paged_sparse_fwd_workspace_size(w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk,
                                                         w.blk, w.max_pages, splits, p)
             ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
-            self.path_name = {1: "paged-qcentric", 3: "paged-decode"}[p]
-            self.splits = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, splits, p)
+            self.path_name = {1: "paged-qcentric", 2: "paged-kv-centric", 3: "paged-decode"}[p]
+            self.splits = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, w.max_pages,
+                                                          splits, p)
             self.step = lambda: msa.msa_paged_sparse_fwd(
                 t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"],
                 causal=w.causal, num_splits=splits, path=p, o=self.o, lse=self.lse,
                 workspace=ws, **tk)
-            self.bytes = decode_algorithmic_bytes(w, self.inp)
+            self.bytes = decode_algorithmic_bytes(w, self.inp) if w.decode else None
         else:
             p = msa.msa_sparse_fwd_path(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.topk, PATHS[path])
             nb = msa.msa_sparse_fwd_workspace_size(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, w.topk,
@@ -327,7 +328,7 @@ class Case:
                 "csr_bytes": csr_bytes, "csr_GB_per_s": csr_bytes / (med["csr"] * 1e-3) / 1e9}
 
     def metric(self, ms: float, kernel_ms: float) -> dict:
-        if self.w.paged:
+        if self.w.decode:
             gbs = self.bytes / (ms * 1e-3) / 1e9
             return {"ms": ms, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                     "kernel_ms": kernel_ms,
@@ -354,10 +355,12 @@ class Case:
             waves = 2 if items < 8 * cus else 1
             paged = "true" if w.paged else "false"
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
+        if self.path_name in ("kv-centric", "paged-kv-centric"):
+            paged = "true" if w.paged else "false"
+            return f"kvcentric_kernel<{w.qpk}, {t}, {f}, {paged}>"
         if w.paged:
             return decode_instance(w, fp8).replace("TEMP", t)
-        return {"kv-centric": f"kvcentric_kernel<{w.qpk}, {t}, {f}>",
-                "query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
+        return {"query-tile": f"tile_kernel<{w.qpk}, {t}>"}[self.path_name]
 
 
 def decode_instance(w, fp8: bool = False) -> str:
@@ -484,7 +487,7 @@ def cpu_baseline(case: Case, budget_s: float = 12.0) -> dict:
     if n_target > n:
         n, dt = run(n_target)
     frac = n / total_rows
-    if w.paged:
+    if w.decode:
         value = case.bytes * frac / dt / 1e9
         unit = "GB/s"
     else:
@@ -506,9 +509,9 @@ def main() -> int:
     ap.add_argument("--path", default="auto", choices=sorted(PATHS))
     ap.add_argument("--splits", type=int, default=0,
                     help="KV splits of the paged workload (0 = the library's choice)")
-    ap.add_argument("--extra", default="c5",
+    ap.add_argument("--extra", default="c5,c3p",
                     help="comma-separated workloads reported beside (default: the paged decode "
-                         "batch c5; '' for none)")
+                         "batch c5 and the paged prefill c3p; '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="K/V element type (fp8 = the e4m3fn cache)")
@@ -544,7 +547,7 @@ def main() -> int:
     log(f"[bench] {args.workload}: {m}")
     w = case.w
     traffic = measured_traffic(case) if args.lse_temperature is None else None
-    if w.paged:
+    if w.decode:
         value, unit = m["GB_per_s"], "GB/s"
         metric = "paged dense decode GB/s" if w.dense else "paged sparse decode GB/s"
         ach = m["kernel_GB_per_s"]
@@ -558,7 +561,7 @@ def main() -> int:
                 "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     # the whole step (every launch of the call) against the same peak, beside the
     # dominant kernel's own fraction
-    roof["step_frac"] = (m["hbm_frac"] if w.paged else m["mfma_frac"])
+    roof["step_frac"] = (m["hbm_frac"] if w.decode else m["mfma_frac"])
     roof["kernel"] = case.dominant_kernel()
     if args.lse_temperature is not None or args.kv_dtype == "fp8":  # the kernels' variants
         roof["kernel"] = case.dominant_kernel(args.lse_temperature is not None,

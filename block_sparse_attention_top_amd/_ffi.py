@@ -83,9 +83,9 @@ def load_library():
     lib.msa_build_k2q_csr_varlen.restype = I
     lib.msa_paged_sparse_fwd_workspace_size.argtypes = [I] * 10
     lib.msa_paged_sparse_fwd_workspace_size.restype = S
-    lib.msa_paged_sparse_fwd_path.argtypes = [I] * 5
+    lib.msa_paged_sparse_fwd_path.argtypes = [I] * 6
     lib.msa_paged_sparse_fwd_path.restype = I
-    lib.msa_paged_sparse_fwd_splits.argtypes = [I] * 6
+    lib.msa_paged_sparse_fwd_splits.argtypes = [I] * 7
     lib.msa_paged_sparse_fwd_splits.restype = I
     lib.msa_paged_sparse_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, I,
                                          I, P, P, F, P, P, S, P]
@@ -369,12 +369,14 @@ def msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size, max_
                                                                   num_splits, path))
 
 
-def msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, path=MSA_PATH_AUTO) -> int:
-    return int(load_library().msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, path))
+def msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, max_pages, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, max_pages, path))
 
 
-def msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, num_splits=0, path=MSA_PATH_AUTO) -> int:
-    return int(load_library().msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, num_splits, path))
+def msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, max_pages, num_splits=0,
+                                path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_splits(B, Sq, Hkv, topk, max_pages,
+                                                          num_splits, path))
 
 
 def msa_paged_sparse_fwd(q, k_pool, v_pool, page_table, seqused_k, q2k, *, causal: bool,

@@ -175,10 +175,12 @@ KvLayout kv_layout(long long nq, long long nrows, int Hq, int Hkv, int topk) {
 }
 
 // Paged plan: which kernel and how many KV splits. MSA_PATH_AUTO takes the
+// kv-centric path under the contiguous rule (max_pages blocks per sequence), else the
 // q-centric kernel: on the 32 x 8-query decode workload with random per-query
 // blocks it measured faster than the union (decode) kernel, which reads each
 // distinct block of a (b, hkv) once and pays off when the Sq index rows share
-// blocks; the caller asks for it explicitly. The decode kernel splits the union
+// blocks; the caller asks for it explicitly. The kv-centric path does not split
+// (its partials are per block already). The decode kernel splits the union
 // into `splits` contiguous shares; the q-centric kernel splits each index row's
 // slots. Automatic splits aim at about three workgroups per compute unit
 // (decode) or about 1024 single-wave workgroups (q-centric: on the 32 x 8 x 4
@@ -189,11 +191,18 @@ struct PagedPlan {
   int splits;
 };
 
-PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int num_splits, int path) {
+PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int max_pages, int num_splits, int path) {
   PagedPlan pl;
-  if (path == MSA_PATH_AUTO) path = MSA_PATH_QCENTRIC;
+  if (path == MSA_PATH_AUTO)
+    path = max_pages <= kMaxCsrRows &&
+                   kv_pays(static_cast<long long>(B) * Sq, Hkv, topk, max_pages,
+                           static_cast<long long>(B) * max_pages)
+               ? MSA_PATH_KVCENTRIC
+               : MSA_PATH_QCENTRIC;
   pl.path = path;
-  if (path == MSA_PATH_DECODE) {
+  if (path == MSA_PATH_KVCENTRIC) {
+    pl.splits = 1;
+  } else if (path == MSA_PATH_DECODE) {
     const long long cap = std::min<long long>(static_cast<long long>(Sq) * topk, kMaxDecodeSplits);
     long long s = num_splits;
     if (s <= 0) {
@@ -213,9 +222,18 @@ PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int num_splits, int path)
   return pl;
 }
 
-// fp32 partials [splits][rows][D], then the split LSEs and temperature-scaled LSEs
-// [splits][rows], rows = B * Sq * Hq
-size_t paged_workspace(int B, int Sq, int Hq, int splits) {
+// q-centric and decode: fp32 partials [splits][rows][D], then the split LSEs and
+// temperature-scaled LSEs [splits][rows], rows = B * Sq * Hq. kv-centric: the
+// contiguous path's workspace for its largest sub-batch.
+size_t paged_workspace(int B, int Sq, int Hq, int Hkv, int topk, int max_pages,
+                       const PagedPlan& pl) {
+  if (pl.path == MSA_PATH_KVCENTRIC) {
+    const int bc = kv_sub_batch(B, max_pages);
+    if (bc == 0) return 0;
+    return kv_layout(static_cast<long long>(bc) * Sq, static_cast<long long>(bc) * max_pages, Hq,
+                     Hkv, topk).total;
+  }
+  const int splits = pl.splits;
   if (splits <= 1) return 0;
   const size_t rows = static_cast<size_t>(B) * Sq * Hq;
   return align256(splits * rows * kD * 4) + 2 * align256(splits * rows * 4);
@@ -842,14 +860,16 @@ int msa_paged_decode_run(const void* q, const void* k_pool, const void* v_pool,
   return MSA_OK;
 }
 
-int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path) {
+int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int max_pages, int path) {
   if (path != MSA_PATH_AUTO) return path;
-  return paged_plan(B, Sq, Hkv, topk, 0, path).path;
+  if (B <= 0 || Sq <= 0 || Hkv <= 0 || topk <= 0 || max_pages <= 0) return MSA_PATH_QCENTRIC;
+  return paged_plan(B, Sq, Hkv, topk, max_pages, 0, path).path;
 }
 
-int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int num_splits, int path) {
-  if (B <= 0 || Sq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < 0) return 0;
-  return paged_plan(B, Sq, Hkv, topk, num_splits, path).splits;
+int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int max_pages, int num_splits,
+                                int path) {
+  if (B <= 0 || Sq <= 0 || Hkv <= 0 || topk <= 0 || max_pages <= 0 || num_splits < 0) return 0;
+  return paged_plan(B, Sq, Hkv, topk, max_pages, num_splits, path).splits;
 }
 
 size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
@@ -858,8 +878,11 @@ size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D
   if (B <= 0 || Sq <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD || page_size != kBlk ||
       max_pages <= 0 || Hq % Hkv || num_splits < 0)
     return 0;
-  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE) return 0;
-  return paged_workspace(B, Sq, Hq, paged_plan(B, Sq, Hkv, topk, num_splits, path).splits);
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE &&
+      path != MSA_PATH_KVCENTRIC)
+    return 0;
+  return paged_workspace(B, Sq, Hq, Hkv, topk, max_pages,
+                         paged_plan(B, Sq, Hkv, topk, max_pages, num_splits, path));
 }
 
 int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
@@ -882,19 +905,64 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
       !aligned(q2k, 4) || !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seqused_k, 4))
     return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
   if (num_splits < 0) return fail(MSA_ERR_INVALID_VALUE, "num_splits must be >= 0");
-  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE)
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_DECODE &&
+      path != MSA_PATH_KVCENTRIC)
     return fail(MSA_ERR_INVALID_VALUE, "unknown paged path %d", path);
   if (path == MSA_PATH_DECODE && !paged_decode_supported(Sq, topk))
     return fail(MSA_ERR_NOT_SUPPORTED,
                 "decode path needs Sq <= %d and Sq * topk <= %d (got Sq %d, topk %d)",
                 4 * kMaxQPerWave, kDecMaxEntries, Sq, topk);
-  const PagedPlan plan = paged_plan(B, Sq, Hkv, topk, num_splits, path);
+  const PagedPlan plan = paged_plan(B, Sq, Hkv, topk, max_pages, num_splits, path);
   const int splits = plan.splits;
   rc = check_kv_dtype(kv_dtype, plan.path);
   if (rc) return rc;
   const int qpk = Hq / Hkv;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const float inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
+
+  if (plan.path == MSA_PATH_KVCENTRIC) {
+    // the contiguous kv-centric pipeline over max_pages blocks per sequence, each block
+    // read through the page table; sub-batches of whole sequences past the CSR limit
+    const int bc = kv_sub_batch(B, max_pages);
+    if (bc == 0)
+      return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: max_pages = %d exceeds %d", max_pages,
+                  kMaxCsrRows);
+    const size_t need = paged_workspace(B, Sq, Hq, Hkv, topk, max_pages, plan);
+    if (!workspace || workspace_bytes < need)
+      return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 256))
+      return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+    for (int b0 = 0; b0 < B; b0 += bc) {
+      const int nb = std::min(bc, B - b0);
+      const long long q_off = static_cast<long long>(b0) * Sq * Hq * D;  // elements
+      const long long l_off = static_cast<long long>(b0) * Hq * Sq;
+      const KvLayout L = kv_layout(static_cast<long long>(nb) * Sq,
+                                   static_cast<long long>(nb) * max_pages, Hq, Hkv, topk);
+      KvParams p{};
+      p.q = static_cast<const uint16_t*>(q) + q_off;
+      p.k = k_pool;
+      p.v = v_pool;
+      p.kv_fp8 = kv_dtype == MSA_DTYPE_FP8_E4M3;
+      p.B = nb; p.Sq = Sq; p.Skv = max_pages * kBlk; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk;
+      p.topk = topk; p.nblk = max_pages; p.nrows = nb * max_pages;
+      p.cap = static_cast<long long>(nb) * Sq * topk;
+      p.causal = causal ? 1 : 0;
+      p.scale_log2 = scale * kLog2e;
+      p.inv_temp = inv_temp;
+      p.page_table = page_table + static_cast<long long>(b0) * max_pages;
+      p.seqused = seqused_k + b0;
+      p.num_pages = num_pages;
+      rc = run_kvcentric(p, q2k + static_cast<long long>(b0) * Hkv * Sq * topk, nullptr, nullptr,
+                         nullptr, L, static_cast<char*>(workspace), nullptr,
+                         static_cast<uint16_t*>(o) + q_off, lse + l_off,
+                         lse_temperature ? lse_temperature + l_off : nullptr, st);
+      if (rc) return rc;
+    }
+    return MSA_OK;
+  }
+
   QcParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = k_pool;
@@ -910,10 +978,10 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
   p.splits = splits;
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
-  p.inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
+  p.inv_temp = inv_temp;
   p.lse_t = lse_temperature;
   if (splits > 1) {
-    const size_t need = paged_workspace(B, Sq, Hq, splits);
+    const size_t need = paged_workspace(B, Sq, Hq, Hkv, topk, max_pages, plan);
     if (!workspace || workspace_bytes < need)
       return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
@@ -992,6 +1060,11 @@ int msa_paged_sparse_fwd_noalloc(const void* q, const void* k_pool, const void* 
                                  void* o, float* lse, float lse_temperature_scale,
                                  float* lse_temperature, void* stream) {
   g_last_error.clear();
+  // The automatic path never takes the kv-centric one here: its partials (a bf16 row per
+  // (query, head, slot)) outgrow the scratch on the problems it is chosen for.
+  if (path == MSA_PATH_AUTO && msa_paged_sparse_fwd_path(B, Sq, Hkv, topk, max_pages, path) ==
+                                   MSA_PATH_KVCENTRIC)
+    path = MSA_PATH_QCENTRIC;
   // The scratch this call needs is the workspace msa_paged_sparse_fwd would take (0 for
   // one split, and for argument errors, which msa_paged_sparse_fwd reports itself).
   const size_t need = msa_paged_sparse_fwd_workspace_size(B, Sq, Hq, Hkv, D, topk, page_size,

@@ -272,6 +272,11 @@ struct KvParams {
   const int32_t* rowbase;
   const int32_t* row_seq;
   long long total_q, total_k;
+  // paged K/V (page_table != nullptr): block s of sequence b is page page_table[b * nblk + s]
+  // of the pools [num_pages, Hkv, 128, D], and the sequence's keys are [0, seqused[b])
+  const int32_t* page_table;
+  const int32_t* seqused;
+  int num_pages;
 };
 // persistent grid (two workgroups per compute unit, at most max_items) over the
 // streams of the key-ordered item table

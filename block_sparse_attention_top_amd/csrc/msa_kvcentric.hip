@@ -24,6 +24,11 @@
 // a row's keys and queries live: row r is block r - rowbase[b] of sequence b
 // (from the per-row sequence table), the block's keys start at cu_seqlens_k[b]
 // and may end inside it, and the causal limit uses the sequence's own lengths.
+// A paged K/V cache (PAGED) differs only in where a block's keys live: block s of
+// sequence b is one page of the pools, page_table[b][s], and the sequence's keys end
+// at seqused[b]. A block past those keys, or whose page id is outside the pools,
+// contributes nothing (its partials are empty and nothing of it is read), as on the
+// paged q-centric kernel.
 //
 // Layout on gfx950. A work item is (KV head, CSR row = (b, block), a chunk of
 // up to `chunk_entries` CSR entries), listed in an item table by the CSR scatter
@@ -55,7 +60,7 @@ constexpr int kv_item_entries() {
 
 // One work item: stage the block's K/V tiles and the chunk's entries in LDS, then
 // each wave computes the partials of 32 gathered (query, head) rows per step.
-template <int QPK, bool TEMP, bool FP8>
+template <int QPK, bool TEMP, bool FP8, bool PAGED>
 __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint8_t* ks,
                                         uint8_t* vs, int* ent_q, int* ent_t) {
   const int tid = threadIdx.x;
@@ -64,7 +69,20 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
   // count, first key and key count
   int s;
   long long qbeg, sq_b, kbeg, kvlen;
-  if (p.cu_q) {
+  int page = 0;       // PAGED: the block's page
+  bool dead = false;  // PAGED: the block has no keys to read (past seqused, or a bad page)
+  if (PAGED) {
+    const int b = r / p.nblk;
+    s = r % p.nblk;
+    qbeg = static_cast<long long>(b) * p.Sq;
+    sq_b = p.Sq;
+    kbeg = 0;
+    kvlen = p.seqused[b];
+    if (static_cast<long long>(s) * kBlk < kvlen)
+      page = p.page_table[static_cast<long long>(b) * p.nblk + s];
+    dead = !(static_cast<long long>(s) * kBlk < kvlen && page >= 0 && page < p.num_pages);
+    if (dead) page = 0;
+  } else if (p.cu_q) {
     const int b = p.row_seq[r];
     if (b < 0) return;  // a row past the last sequence holds no entries
     s = r - p.rowbase[b];
@@ -114,6 +132,20 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
     for (int i = 0; i < kLpt; ++i) {
       const int ci = i * 256 + tid;
       const int row = ci / kCpr, c = ci % kCpr;
+      if (PAGED) {
+        // a dead block's tiles are zeros: its keys are all masked, and P V must not
+        // meet non-finite values
+        if (dead) {
+          rk[i] = rv[i] = u32x4{0, 0, 0, 0};
+          continue;
+        }
+        const long long j = min(blk0 + row, kvlen - 1) - blk0;  // in [0, 128): same page
+        const long long off =
+            (((static_cast<long long>(page) * p.Hkv + hkv) * kBlk + j) * kD + c * kEpc) * kEsz;
+        rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
+        rv[i] = *reinterpret_cast<const u32x4*>(vb + off);
+        continue;
+      }
       const long long tok = kbeg + min(blk0 + row, kvlen - 1);
       const long long off = ((tok * p.Hkv + hkv) * kD + c * kEpc) * kEsz;
       rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
@@ -148,7 +180,8 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
   const int head = hkv * QPK + head_i;
   const int j16 = lane >> 4, lq = lane & 15, rr = lq >> 2, cq = lq & 3;
   const long long lim_off = kvlen - sq_b;
-  const long long kend = min(kvlen - blk0, static_cast<long long>(kBlk));  // keys of the block
+  // keys of the block (none for a dead one)
+  const long long kend = PAGED && dead ? 0 : min(kvlen - blk0, static_cast<long long>(kBlk));
   const int nsteps = (ne + EPW - 1) / EPW;
   const float c2 = p.scale_log2;
   const float c2t = c2 * p.inv_temp;
@@ -380,7 +413,7 @@ template <bool TEMP>
 constexpr bool kv_persistent() {
   return !TEMP;
 }
-template <int QPK, bool TEMP, bool FP8>
+template <int QPK, bool TEMP, bool FP8, bool PAGED>
 __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
   constexpr int kEnt = kv_item_entries<QPK>();
   __shared__ __attribute__((aligned(16))) uint8_t ks[kBlk * kKStride];
@@ -413,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void kvcentric_kernel(KvParams p) {
     __syncthreads();
     const int w = s_item;
     if (w < 0) break;
-    kv_item<QPK, TEMP, FP8>(p, p.items[w], ks, vs, ent_q, ent_t);
+    kv_item<QPK, TEMP, FP8, PAGED>(p, p.items[w], ks, vs, ent_q, ent_t);
     if constexpr (!kv_persistent<TEMP>()) break;
     __syncthreads();  // LDS tiles and s_item are reused by the next item
   }
@@ -527,7 +560,7 @@ __global__ __launch_bounds__(256) void kv_sort_scatter(
   if (key >= 0) out[base[key] + rank] = it;
 }
 
-template <int QPK>
+template <int QPK, bool PAGED>
 void kv_launch(const KvParams& p, long long max_items, hipStream_t stream) {
   const dim3 blk(256);
   // persistent: two workgroups per compute unit (the kernel's occupancy), at most one
@@ -536,13 +569,25 @@ void kv_launch(const KvParams& p, long long max_items, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(
       persistent ? std::min<long long>(max_items, 2LL * device_cu_count()) : max_items));
   if (p.lse_t_part && p.kv_fp8)
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, true>), grid, blk, 0, stream, p);
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, true, PAGED>), grid, blk, 0, stream, p);
   else if (p.lse_t_part)
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, false>), grid, blk, 0, stream, p);
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, true, false, PAGED>), grid, blk, 0, stream, p);
   else if (p.kv_fp8)
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, true>), grid, blk, 0, stream, p);
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, true, PAGED>), grid, blk, 0, stream, p);
   else
-    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, false>), grid, blk, 0, stream, p);
+    hipLaunchKernelGGL((kvcentric_kernel<QPK, false, false, PAGED>), grid, blk, 0, stream, p);
+}
+template <bool PAGED>
+hipError_t kv_launch_qpk(const KvParams& p, long long max_items, hipStream_t stream) {
+  switch (p.qpk) {
+    case 1: kv_launch<1, PAGED>(p, max_items, stream); break;
+    case 2: kv_launch<2, PAGED>(p, max_items, stream); break;
+    case 4: kv_launch<4, PAGED>(p, max_items, stream); break;
+    case 8: kv_launch<8, PAGED>(p, max_items, stream); break;
+    case 16: kv_launch<16, PAGED>(p, max_items, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -573,15 +618,9 @@ hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t 
   if (max_items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (p.chunk_entries * p.qpk > kKvChunkRows || p.chunk_entries > kKvMaxEntries)
     return hipErrorInvalidValue;
-  switch (p.qpk) {
-    case 1: kv_launch<1>(p, max_items, stream); break;
-    case 2: kv_launch<2>(p, max_items, stream); break;
-    case 4: kv_launch<4>(p, max_items, stream); break;
-    case 8: kv_launch<8>(p, max_items, stream); break;
-    case 16: kv_launch<16>(p, max_items, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (p.page_table && (!p.seqused || p.num_pages <= 0 || p.cu_q)) return hipErrorInvalidValue;
+  return p.page_table ? kv_launch_qpk<true>(p, max_items, stream)
+                      : kv_launch_qpk<false>(p, max_items, stream);
 }
 
 }  // namespace msa

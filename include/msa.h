@@ -233,25 +233,38 @@ int msa_build_k2q_csr_varlen(const int32_t* q2k, const int32_t* cu_seqlens_q,
  *   num_splits  0 = automatic; else the number of KV splits, each a partial pass
  *               merged afterwards by log-sum-exp. q-centric: each index row's
  *               slots are split (clamped to 1..topk); decode: the union of the
- *               blocks of a (b, hkv) is split (clamped to 1..min(Sq*topk, 64))
- *   path        MSA_PATH_AUTO (= MSA_PATH_QCENTRIC), MSA_PATH_QCENTRIC or
- *               MSA_PATH_DECODE (reads each distinct block of a (b, hkv) once: for
- *               index rows that share blocks; MSA_ERR_NOT_SUPPORTED when
- *               Sq > 16 or Sq * topk > 512)
- *   kv_dtype    enum msa_dtype (fp8 with the q-centric path only)
+ *               blocks of a (b, hkv) is split (clamped to 1..min(Sq*topk, 64));
+ *               kv-centric: ignored (its partials are per block already)
+ *   path        MSA_PATH_AUTO, MSA_PATH_QCENTRIC, MSA_PATH_KVCENTRIC or
+ *               MSA_PATH_DECODE. Auto takes the kv-centric path under the rule of
+ *               msa_sparse_fwd with max_pages blocks per sequence (large problems
+ *               whose blocks each serve two or more (query, slot) entries, e.g. a
+ *               long prefill), else the q-centric one (decode batches).
+ *               kv-centric: the sparse_atten_func pipeline (k2q CSR, per-block
+ *               partials, combine) with each block read through the page table;
+ *               B * max_pages CSR rows, in sub-batches of floor(16384 / max_pages)
+ *               sequences past 16384, MSA_ERR_NOT_SUPPORTED when max_pages > 16384.
+ *               Decode reads each distinct block of a (b, hkv) once: for index
+ *               rows that share blocks; MSA_ERR_NOT_SUPPORTED when Sq > 16 or
+ *               Sq * topk > 512.
+ *   kv_dtype    enum msa_dtype (fp8 with the q-centric and kv-centric paths)
  *   o, lse, lse_temperature_scale, lse_temperature   as msa_sparse_fwd
  *   workspace   at least msa_paged_sparse_fwd_workspace_size(...) with the same
- *               num_splits and path (zero when one split results)
+ *               num_splits and path (zero when one q-centric or decode split
+ *               results; the kv-centric path always takes one)
+ * A block past seqused_k[b], or whose page id is outside [0, num_pages), adds
+ * nothing to a row on every path; nothing of it is read.
  * Duplicate ids within one index row: the decode path counts each block once;
- * the q-centric path requires distinct ids.
+ * the q-centric and kv-centric paths require distinct ids.
  */
 size_t msa_paged_sparse_fwd_workspace_size(int B, int Sq, int Hq, int Hkv, int D, int topk,
                                            int page_size, int max_pages, int num_splits,
                                            int path);
 /* The kernel msa_paged_sparse_fwd runs for these sizes (resolves MSA_PATH_AUTO)
  * and the number of splits it uses (0 for invalid sizes). */
-int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int path);
-int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int num_splits, int path);
+int msa_paged_sparse_fwd_path(int B, int Sq, int Hkv, int topk, int max_pages, int path);
+int msa_paged_sparse_fwd_splits(int B, int Sq, int Hkv, int topk, int max_pages, int num_splits,
+                                int path);
 int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seqused_k, const int32_t* q2k,
                          int B, int Sq, int Hq, int Hkv, int D, int topk, int page_size,
@@ -264,7 +277,10 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
  * msa_paged_sparse_fwd without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc. Arguments, results and errors are those of
- * msa_paged_sparse_fwd, and so are the kernels (results bit for bit equal).
+ * msa_paged_sparse_fwd, and so are the kernels (results bit for bit equal), except
+ * that MSA_PATH_AUTO never resolves to the kv-centric path here (it takes the
+ * q-centric one instead): that path's partials outgrow the scratch on the problems
+ * it is chosen for.
  *   Scratch: the split partials use a device array inside the library of
  *   MSA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
  *   until the process ends. Its device address is looked up on the first call

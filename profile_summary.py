@@ -94,10 +94,11 @@ def main() -> int:
                "paged-decode": bench.decode_instance(w).replace("TEMP", "false"),
                "paged-dense-decode": bench.decode_instance(w, f8 == "true").replace("TEMP",
                                                                                     "false"),
+               "paged-kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}, true>",
                }[args.path]
     else:
         dom = {"q-centric": f"qcentric_kernel<false, false, {f8},",
-               "kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}>",
+               "kv-centric": f"kvcentric_kernel<{w.qpk}, false, {f8}, false>",
                "query-tile": f"tile_kernel<{w.qpk}, false>"}[args.path]
     tag = "" if args.kv_dtype == "bf16" else "-fp8"
     lines = [f"# Kernel profile: {w.name}, {args.path} path"

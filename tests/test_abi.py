@@ -81,12 +81,16 @@ def test_workspace_queries():
         assert msa.msa_paged_sparse_fwd_workspace_size(32, 8, 64, 4, 128, 16, 128, 512, 4,
                                                        path) >= 4 * 32 * 8 * 64 * 128 * 4
     # the decode kernel splits the union of a (b, hkv)'s blocks: up to min(Sq*topk, 64) splits
-    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 100, 3) == 64
-    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 100, 1) == 16
-    assert msa.msa_paged_sparse_fwd_splits(1, 1, 1, 4, 0, 3) == 4
+    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 512, 100, 3) == 64
+    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 512, 100, 1) == 16
+    assert msa.msa_paged_sparse_fwd_splits(1, 1, 1, 4, 512, 0, 3) == 4
+    assert msa.msa_paged_sparse_fwd_splits(1, 8, 1, 16, 512, 100, 2) == 1  # kv: no splits
     assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 64, 3) >= \
         64 * 8 * 16 * 128 * 4
-    assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 4, 2) == 0
+    # the paged kv-centric path takes the contiguous one's workspace over max_pages blocks
+    assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 4, 2) == \
+        msa.msa_sparse_fwd_workspace_size(1, 8, 512 * 128, 16, 1, 128, 16, 128, 2) > 0
+    assert msa.msa_paged_sparse_fwd_workspace_size(1, 8, 16, 1, 128, 16, 128, 512, 4, 4) == 0
 
 
 def test_csr_and_paged_reject():
@@ -162,10 +166,15 @@ def test_auto_path_resolution():
     assert ws4 == ws2 > 0  # sized for one sub-batch of two sequences
     assert msa.msa_sparse_fwd_workspace_size(1, 8192, 128 * 20000, 64, 4, 128, 16, 128, 2) == 0
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 1) == 1
-    # paged: automatic is the q-centric kernel; the decode kernel is asked for
-    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16) == msa.MSA_PATH_QCENTRIC
-    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16, 3) == msa.MSA_PATH_DECODE
-    assert msa.msa_paged_sparse_fwd_splits(32, 8, 4, 16) == 1
+    # paged: automatic is the q-centric kernel on decode batches, the kv-centric path on
+    # prefills under the contiguous rule; the decode kernel is asked for
+    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16, 512) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_paged_sparse_fwd_path(64, 8, 4, 16, 512) == msa.MSA_PATH_QCENTRIC  # 0.25
+    assert msa.msa_paged_sparse_fwd_path(32, 8, 4, 16, 512, 3) == msa.MSA_PATH_DECODE
+    assert msa.msa_paged_sparse_fwd_splits(32, 8, 4, 16, 512) == 1
+    assert msa.msa_paged_sparse_fwd_path(1, 32768, 4, 16, 256) == msa.MSA_PATH_KVCENTRIC
+    assert msa.msa_paged_sparse_fwd_path(1, 32768, 4, 16, 20000) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_paged_sparse_fwd_path(4, 4096, 4, 16, 8192) == msa.MSA_PATH_KVCENTRIC
     # contiguous: the query tile is asked for
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 4) == msa.MSA_PATH_TILE
 

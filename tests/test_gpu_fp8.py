@@ -86,22 +86,22 @@ def test_varlen_fp8(path):
     compare(bf16_dev_to_f64(o8), l8.cpu().numpy().astype(np.float64), o_ref, lse_ref, "varlen")
 
 
-@pytest.mark.parametrize("splits", [1, 4])
-def test_paged_fp8(splits):
+@pytest.mark.parametrize("path,splits", [(Q, 1), (Q, 4), (KV, 0)])
+def test_paged_fp8(path, splits):
     import block_sparse_attention_top_amd as msa
     w = wl.Workload("fp", B=4, Sq=8, Skv=8192, Hkv=2, qpk=16, topk=16, causal=True,
                     mode=wl.MODE_CAUSAL, paged=True, seqused_trim=17, seed=84)
     inp = wl.make_inputs(w)
     f8 = wl.with_fp8_kv(inp)
-    say(f"[fp8] paged splits={splits}")
+    say(f"[fp8] paged path={path} splits={splits}")
     t = {n: to_dev(inp[n]) for n in ("q", "page_table", "seqused_k", "q2k")}
     k8, v8 = fp8_dev(f8["k_pool"]), fp8_dev(f8["v_pool"])
     args = (t["page_table"], t["seqused_k"], t["q2k"])
     o8, l8 = msa.msa_paged_sparse_fwd(t["q"], k8, v8, *args, causal=True, num_splits=splits,
-                                      path=Q)
+                                      path=path)
     od, ld = msa.msa_paged_sparse_fwd(t["q"], k8.to(torch.bfloat16).contiguous(),
                                       v8.to(torch.bfloat16).contiguous(), *args, causal=True,
-                                      num_splits=splits, path=Q)
+                                      num_splits=splits, path=path)
     torch.cuda.synchronize()
     assert bits_equal(o8, od) and bits_equal(l8, ld)
     o_ref, lse_ref = oracle.paged_sparse_attention(f8["q"], f8["k_pool"], f8["v_pool"],
@@ -138,25 +138,25 @@ def test_varlen_fp8_temperature(path):
     check_lse_t(t8.cpu().numpy(), lt_ref, f"varlen-fp8-T0.5-path{path}")
 
 
-@pytest.mark.parametrize("splits", [1, 4])
-def test_paged_fp8_temperature(splits):
+@pytest.mark.parametrize("path,splits", [(Q, 1), (Q, 4), (KV, 0)])
+def test_paged_fp8_temperature(path, splits):
     """fp8 cache with the temperature-scaled LSE on the paged q-centric kernel, one split
-    and four (the split combine merges both LSEs)."""
+    and four (the split combine merges both LSEs), and on the paged kv-centric path."""
     import block_sparse_attention_top_amd as msa
     w = wl.Workload("fpt", B=3, Sq=8, Skv=4096, Hkv=2, qpk=16, topk=8, causal=True,
                     mode=wl.MODE_CAUSAL, paged=True, seqused_trim=60, seed=88)
     inp = wl.make_inputs(w)
     f8 = wl.with_fp8_kv(inp)
-    say(f"[fp8] paged + temperature splits={splits}")
+    say(f"[fp8] paged + temperature path={path} splits={splits}")
     t = {n: to_dev(inp[n]) for n in ("q", "page_table", "seqused_k", "q2k")}
     k8, v8 = fp8_dev(f8["k_pool"]), fp8_dev(f8["v_pool"])
     args = (t["page_table"], t["seqused_k"], t["q2k"])
     tk = dict(return_temperature_lse=True, lse_temperature_scale=2.0)
     o8, l8, t8 = msa.msa_paged_sparse_fwd(t["q"], k8, v8, *args, causal=True,
-                                          num_splits=splits, path=Q, **tk)
+                                          num_splits=splits, path=path, **tk)
     od, ld, td = msa.msa_paged_sparse_fwd(t["q"], k8.to(torch.bfloat16).contiguous(),
                                           v8.to(torch.bfloat16).contiguous(), *args, causal=True,
-                                          num_splits=splits, path=Q, **tk)
+                                          num_splits=splits, path=path, **tk)
     torch.cuda.synchronize()
     assert bits_equal(o8, od) and bits_equal(l8, ld) and bits_equal(t8, td)
     o_ref, lse_ref, lt_ref = oracle.paged_sparse_attention(
@@ -164,7 +164,7 @@ def test_paged_fp8_temperature(splits):
         causal=True, temperature=2.0)
     compare(bf16_dev_to_f64(o8), l8.cpu().numpy().transpose(0, 2, 1).astype(np.float64), o_ref,
             lse_ref.transpose(0, 2, 1), "paged")
-    check_lse_t(t8.cpu().numpy(), lt_ref, f"paged-fp8-T2-splits{splits}")
+    check_lse_t(t8.cpu().numpy(), lt_ref, f"paged-fp8-T2-path{path}-splits{splits}")
 
 
 def test_fp8_rejected_by_the_bf16_only_paths():

@@ -276,10 +276,10 @@ def check_paged(w, inp, splits, label, path=0):
     return o, lse
 
 
-PQ, PD = 1, 3  # paged q-centric and decode (union of blocks) kernels
+PQ, PK, PD = 1, 2, 3  # paged q-centric, kv-centric and decode (union of blocks) paths
 
 
-@pytest.mark.parametrize("path,splits", [(PQ, 0), (PQ, 1), (PQ, 3), (PQ, 8),
+@pytest.mark.parametrize("path,splits", [(PQ, 0), (PQ, 1), (PQ, 3), (PQ, 8), (PK, 0),
                                          (PD, 0), (PD, 1), (PD, 3), (PD, 8), (PD, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_paged_small(path, splits, causal):
@@ -320,17 +320,18 @@ def test_paged_decode_rejects_long_query_sets():
     w, inp = paged_case(1, 17, 1024, 1, 16, 4, True, trims=[0])
     with pytest.raises(msa.MsaNotSupportedError):
         run_paged(inp, True, path=PD)
-    assert msa.msa_paged_sparse_fwd_path(1, 17, 1, 4) == PQ
-    assert msa.msa_paged_sparse_fwd_path(1, 16, 1, 4, PD) == PD
+    assert msa.msa_paged_sparse_fwd_path(1, 17, 1, 4, 8) == PQ
+    assert msa.msa_paged_sparse_fwd_path(1, 16, 1, 4, 8, PD) == PD
 
 
+@pytest.mark.parametrize("path", [0, PK])
 @pytest.mark.parametrize("qpk", [1, 4, 16])
-def test_paged_prefill_ragged(qpk):
+def test_paged_prefill_ragged(qpk, path):
     w, inp = paged_case(3, 150, 1024, 2, qpk, 4, True, trims=[0, 100, 900])
-    check_paged(w, inp, 0, f"paged-prefill-qpk{qpk}")
+    check_paged(w, inp, 0, f"paged-prefill-qpk{qpk}", path)
 
 
-@pytest.mark.parametrize("path", [PQ, PD])
+@pytest.mark.parametrize("path", [PQ, PK, PD])
 def test_paged_tail_poison_and_bad_page(path):
     """NaN and huge values past seqused_k change nothing; an out-of-range page id
     drops that block (as the oracle does)."""
@@ -352,7 +353,7 @@ def test_paged_tail_poison_and_bad_page(path):
     check_paged(w, dict(inp, page_table=bad), 0, "bad-page", path)
 
 
-@pytest.mark.parametrize("path", [PQ, PD])
+@pytest.mark.parametrize("path", [PQ, PK, PD])
 def test_paged_shuffled_equals_identity_bitwise(path):
     """The same logical K/V through a shuffled and through an identity page table."""
     B, Sq, Skv, Hkv, qpk, topk = 3, 8, 1024, 2, 16, 6
@@ -382,6 +383,10 @@ def test_paged_equals_contiguous():
                seqused_k=np.full(B, Skv, dtype=np.int32))
     op, lp = run_paged(pin, True, num_splits=1, path=PQ)
     oc, lc = run_contiguous(inp, True, Q)
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+    # the kv-centric path through the page table: the same items, the same bits
+    op, lp = run_paged(pin, True, path=PK)
+    oc, lc = run_contiguous(inp, True, KV)
     assert torch.equal(op, oc) and torch.equal(lp, lc)
 
 
@@ -451,6 +456,33 @@ def test_full_size(key):
     say(f"[full] {key}: {stats}")
 
 
+def test_full_size_paged_prefill():
+    """The paged prefill (32768 causal queries through a shuffled page table, seqused
+    trimmed by 17) at full size, on the path the benchmark times (auto = kv-centric),
+    with a poisoned workspace: the at-any-size properties on every row, sampled rows
+    against the oracle."""
+    import block_sparse_attention_top_amd as msa
+    w = wl.WORKLOADS["c3p"]
+    say(f"[full] c3p {w.name}: generating inputs")
+    inp = wl.make_inputs(w)
+    t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k", "q2k")}
+    path = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, w.max_pages)
+    assert path == PK
+    ws = poisoned_workspace(msa.msa_paged_sparse_fwd_workspace_size(
+        w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk, w.blk, w.max_pages, 0, path))
+    say("[full] c3p: running GPU (auto path = kv-centric, poisoned workspace)")
+    o, lse = msa.msa_paged_sparse_fwd(t["q"], t["k_pool"], t["v_pool"], t["page_table"],
+                                      t["seqused_k"], t["q2k"], causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    check_any_size_properties(w, inp["q2k"], o, lse, "c3p")
+    del ws
+    rows = sample_rows(w.B, w.Sq, 48, seed=1)
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   inp["q2k"], causal=True, rows=rows)
+    say(f"[full] c3p: {sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, 'c3p')}")
+
+
 @pytest.mark.parametrize("key", ["c2", "c4b"])
 def test_full_size_prebuilt_csr_bit_identical(key):
     """The forward given the public ordered CSR equals the forward that builds its own
@@ -486,8 +518,8 @@ def test_full_size_paged_decode(c5_case, path, splits):
     import block_sparse_attention_top_amd as msa
     w, inp, (o_ref, lse_ref) = c5_case
     t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k", "q2k")}
-    p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, path)
-    ns = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, splits, p)
+    p = msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, w.max_pages, path)
+    ns = msa.msa_paged_sparse_fwd_splits(w.B, w.Sq, w.Hkv, w.topk, w.max_pages, splits, p)
     ws = poisoned_workspace(msa.msa_paged_sparse_fwd_workspace_size(
         w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk, w.blk, w.max_pages, splits, p))
     say(f"[full] c5: running GPU (path {p}, {ns} splits, poisoned workspace)")
@@ -542,3 +574,52 @@ def test_kv_centric_sub_batches():
     qi = torch.zeros((1, w.B * w.Sq * w.topk), dtype=torch.int32, device="cuda")
     with pytest.raises(msa.MsaNotSupportedError):
         run_contiguous(inp, True, KV, csr=(rp, qi, qi))
+
+
+def to_pool(inp, perm=None):
+    """Contiguous K/V [B, Skv, Hkv, D] as page pools [B * Skv / 128, Hkv, 128, D] with a
+    page table: identity, or page i of the identity layout stored at perm[i]."""
+    B, Skv, Hkv, D = inp["k"].shape
+    mp = Skv // 128
+    def pool(x):
+        p = x.reshape(B, mp, 128, Hkv, D).transpose(0, 1, 3, 2, 4).reshape(B * mp, Hkv, 128, D)
+        if perm is None:
+            return np.ascontiguousarray(p)
+        out = np.empty_like(p)
+        out[perm] = p
+        return out
+    ids = np.arange(B * mp, dtype=np.int32) if perm is None else perm.astype(np.int32)
+    return dict(q=inp["q"], k_pool=pool(inp["k"]), v_pool=pool(inp["v"]), q2k=inp["q2k"],
+                page_table=ids.reshape(B, mp), seqused_k=np.full(B, Skv, dtype=np.int32))
+
+
+def test_paged_kv_centric_sub_batches():
+    """3 sequences of 5500 pages (16500 CSR rows): the paged kv-centric path runs
+    sub-batches of two sequences and one, through a shuffled page table, and gives the
+    contiguous kv-centric path's bits (itself checked against the oracle above)."""
+    w, inp = contiguous_case(3, 64, 5500 * 128, 1, 2, 8, True, wl.MODE_CAUSAL, seed=6)
+    say("[paged-kv] 3 x 5500 pages, shuffled: sub-batches")
+    perm = np.random.default_rng(9).permutation(w.B * 5500)
+    op, lp = run_paged(to_pool(inp, perm), True, path=PK)
+    oc, lc = run_contiguous(inp, True, KV)
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+@pytest.mark.parametrize("qpk", [2, 16])
+def test_paged_kv_centric_prefill(qpk):
+    """A paged prefill the automatic path sends to the kv-centric path (two sequences of
+    16384 keys, trimmed by 0 and 5000, 2048 causal queries each): sampled rows against the
+    oracle, every row against the paged q-centric kernel."""
+    import block_sparse_attention_top_amd as msa
+    w, inp = paged_case(2, 2048, 16384, 2, qpk, 16, True, trims=[0, 5000], seed=31)
+    assert msa.msa_paged_sparse_fwd_path(w.B, w.Sq, w.Hkv, w.topk, w.max_pages) == PK
+    say(f"[paged-kv] prefill qpk={qpk}: auto path")
+    o, lse = run_paged(inp, True)
+    rows = np.array([0, 1, 100, 1023, 2047, 2048, 2049, 3000, 4095])
+    o_ref, lse_ref = oracle.paged_sparse_attention(inp["q"], inp["k_pool"], inp["v_pool"],
+                                                   inp["page_table"], inp["seqused_k"],
+                                                   inp["q2k"], causal=True, rows=rows)
+    sampled_compare(o, lse, o_ref, lse_ref, rows, w.Sq, f"paged-kv qpk{qpk}")
+    oq, lq = run_paged(inp, True, num_splits=1, path=PQ)
+    full_compare(o, lse, bf16_dev_to_f64(oq).astype(np.float64),
+                 lq.cpu().numpy().astype(np.float64), f"paged-kv vs q-centric qpk{qpk}")

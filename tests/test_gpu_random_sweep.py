@@ -64,8 +64,9 @@ def draw_cases(n=N_CASES, seed=2026):
             if not c["causal"] and c["topk"] > nblk:
                 c["causal"] = True  # the causal recipe pads short rows with -1
             dec_ok = c["Sq"] <= 16 and c["Sq"] * c["topk"] <= 512 and not c["fp8"]
-            c["path"] = DEC if dec_ok and rng.random() < 0.4 else Q
-            c["splits"] = 0 if c["path"] == DEC else int(rng.choice([0, 1, 2, 3, 5, 8]))
+            u = rng.random()
+            c["path"] = DEC if dec_ok and u < 0.4 else (KV if u >= 0.7 else Q)
+            c["splits"] = 0 if c["path"] in (DEC, KV) else int(rng.choice([0, 1, 2, 3, 5, 8]))
             rows, keys = c["B"] * c["Sq"], min(c["topk"], nblk) * 128
         else:
             B = int(rng.integers(1, 5))

@@ -98,7 +98,7 @@ def test_varlen_temperature(path):
     check_lse_t(lt.cpu().numpy(), lt_ref, f"varlen-path{path}")
 
 
-@pytest.mark.parametrize("path,splits", [(Q, 1), (Q, 4), (DEC, 1), (DEC, 5)])
+@pytest.mark.parametrize("path,splits", [(Q, 1), (Q, 4), (KV, 0), (DEC, 1), (DEC, 5)])
 @pytest.mark.parametrize("temp", [2.0, 0.25])
 def test_paged_temperature(path, splits, temp):
     import block_sparse_attention_top_amd as msa

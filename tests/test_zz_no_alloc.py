@@ -15,7 +15,7 @@ from parity_util import full_compare, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-PQ, PD = 1, 3  # paged q-centric and decode (union of blocks) kernels
+PQ, PK, PD = 1, 2, 3  # paged q-centric, kv-centric and decode (union of blocks) paths
 
 
 def paged_inputs(B, Sq, Skv, Hkv, qpk, topk, trims, seed):
@@ -65,6 +65,38 @@ def test_noalloc_matches_workspace_entry_point(path, splits):
                 inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"], inp["seqused_k"],
                 inp["q2k"], causal=True)
             say(f"[noalloc] oracle: {full_compare(o2, l2, o_ref, lse_ref, 'noalloc-small')}")
+
+
+KV_CASES = [  # small enough for the kv-centric workspace to fit the scratch array
+    (2, 64, 4096, 2, 8, 8, [0, 1000]),
+    (1, 32, 2048, 1, 4, 4, [100]),
+]
+
+
+def test_noalloc_kv_centric_path():
+    """The kv-centric path asked for explicitly: its CSR, work items and partials in the
+    scratch array, two calls in a row, the second smaller."""
+    for i, (B, Sq, Skv, Hkv, qpk, topk, trims) in enumerate(KV_CASES):
+        say(f"[noalloc] path={PK} call {i}: B={B} Sq={Sq} Skv={Skv} Hkv={Hkv} qpk={qpk} "
+            f"topk={topk}")
+        w, inp = paged_inputs(B, Sq, Skv, Hkv, qpk, topk, trims, seed=51 + i)
+        (o1, l1), (o2, l2) = both(inp, 0, PK)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), "no-alloc output differs"
+
+
+def test_noalloc_auto_never_takes_the_kv_path():
+    """A paged prefill whose automatic path is the kv-centric one: through the no-alloc
+    entry point, auto runs the q-centric kernel (one split, no scratch) instead."""
+    import block_sparse_attention_top_amd as msa
+    w, inp = paged_inputs(1, 2048, 16384, 2, 2, 16, [300], seed=60)
+    assert msa.msa_paged_sparse_fwd_path(1, 2048, 2, 16, w.max_pages) == PK
+    say("[noalloc] auto on a kv-centric-sized paged prefill")
+    t = {n: to_dev(inp[n]) for n in ("q", "k_pool", "v_pool", "page_table", "seqused_k", "q2k")}
+    args = (t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"])
+    ref = msa.msa_paged_sparse_fwd(*args, causal=True, path=PQ)
+    got = msa.msa_paged_sparse_fwd_noalloc(*args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 
 
 def test_noalloc_temperature_lse():

@@ -113,6 +113,7 @@ class Workload:
     seqused_trim: int = 0          # paged: seqused_k = Skv - trim
     shuffle_pages: bool = True
     dense: bool = False            # paged: every key of the sequence (no index table)
+    prefill: bool = False          # paged: a prefill (TFLOP/s), not a decode batch (GB/s)
     seed: int = DEFAULT_SEED
     note: str = ""
 
@@ -123,6 +124,11 @@ class Workload:
     @property
     def max_pages(self) -> int:
         return (self.Skv + self.blk - 1) // self.blk
+
+    @property
+    def decode(self) -> bool:
+        """A paged decode batch, measured in GB/s (every other workload in TFLOP/s)."""
+        return self.paged and not self.prefill
 
     @property
     def kvlen(self) -> int:
@@ -154,6 +160,11 @@ WORKLOADS = {
     "c5": Workload("c5_paged_decode_b32_sq8_hq64_hkv4_kv64k_top16", B=32, Sq=8, Skv=65536,
                    Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL, paged=True,
                    seqused_trim=17),
+    # the test page's paged prefill benchmark: its default shape, causal, through a
+    # shuffled page table of 128-token pages, seqused trimmed by 17
+    "c3p": Workload("c3p_paged_prefill_b1_s32k_hq64_hkv4_top16_causal", B=1, Sq=32768,
+                    Skv=32768, Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL,
+                    paged=True, seqused_trim=17, prefill=True),
     # the same decode batch attending to every key (the dense decode path)
     "c5d": Workload("c5d_paged_dense_decode_b32_sq8_hq64_hkv4_kv64k", B=32, Sq=8, Skv=65536,
                     Hkv=4, qpk=16, topk=16, causal=True, mode=MODE_CAUSAL, paged=True,
