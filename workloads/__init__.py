@@ -257,7 +257,8 @@ class VarlenWorkload:
     D: int = 128
     blk: int = 128
     seed: int = DEFAULT_SEED
-    paged = False  # contiguous K/V only (class attribute, not a field)
+    paged = False  # contiguous K/V only (class attributes, not fields)
+    decode = False
 
     @property
     def Hq(self) -> int:
