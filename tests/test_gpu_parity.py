@@ -623,3 +623,23 @@ def test_paged_kv_centric_prefill(qpk):
     oq, lq = run_paged(inp, True, num_splits=1, path=PQ)
     full_compare(o, lse, bf16_dev_to_f64(oq).astype(np.float64),
                  lq.cpu().numpy().astype(np.float64), f"paged-kv vs q-centric qpk{qpk}")
+
+
+# the test page's paged forward grid (test_sparse_page_atten: causal, Hkv 2, page 128,
+# no trim), batch 3, qhead_per_kv 1 and 16, topk 4 and 16, all six length pairs
+@pytest.mark.parametrize("Sq,Skv", [(8192, 8192), (4096, 8192), (2048, 8192), (1024, 8192),
+                                    (8192, 4096), (4096, 4096)])
+@pytest.mark.parametrize("qpk,topk", [(1, 4), (1, 16), (16, 4), (16, 16)])
+def test_paged_kv_centric_page_grid(Sq, Skv, qpk, topk):
+    """The paged kv-centric path through a shuffled page table: bit for bit the
+    contiguous kv-centric path on the same K/V, and sampled rows against the oracle."""
+    w, inp = contiguous_case(3, Sq, Skv, 2, qpk, topk, True, wl.MODE_CAUSAL, seed=Sq + qpk)
+    say(f"[paged-grid] Sq={Sq} Skv={Skv} qpk={qpk} topk={topk}")
+    perm = np.random.default_rng(Skv + topk).permutation(3 * (Skv // 128))
+    op, lp = run_paged(to_pool(inp, perm), True, path=PK)
+    oc, lc = run_contiguous(inp, True, KV)
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+    rows = sample_rows(w.B, w.Sq, 24, seed=qpk)
+    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                             causal=True, rows=rows)
+    sampled_compare(op, lp, o_ref, lse_ref, rows, w.Sq, f"paged-grid {Sq}/{Skv}")
