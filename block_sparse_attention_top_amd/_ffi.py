@@ -93,6 +93,13 @@ def load_library():
     lib.msa_paged_sparse_fwd_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  I, I, I, P, P, F, P, P]
     lib.msa_paged_sparse_fwd_noalloc.restype = I
+    lib.msa_paged_sparse_fwd_varlen_workspace_size.argtypes = [I] * 9
+    lib.msa_paged_sparse_fwd_varlen_workspace_size.restype = S
+    lib.msa_paged_sparse_fwd_varlen_path.argtypes = [I] * 6
+    lib.msa_paged_sparse_fwd_varlen_path.restype = I
+    lib.msa_paged_sparse_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                                I, F, I, I, P, P, F, P, P, S, P]
+    lib.msa_paged_sparse_fwd_varlen.restype = I
     PL = ctypes.POINTER(MsaDecodePlan)
     lib.msa_paged_decode_plan_init.argtypes = [I, I, I, I, I, I, I, I, I, I, PL]
     lib.msa_paged_decode_plan_init.restype = I
@@ -455,6 +462,59 @@ def msa_paged_sparse_fwd_noalloc(q, k_pool, v_pool, page_table, seqused_k, q2k, 
 
 
 MSA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def msa_paged_sparse_fwd_varlen_workspace_size(B, total_q, Hq, Hkv, D, topk, page_size,
+                                               max_pages, path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_varlen_workspace_size(
+        B, total_q, Hq, Hkv, D, topk, page_size, max_pages, path))
+
+
+def msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages,
+                                     path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages,
+                                                                path))
+
+
+def msa_paged_sparse_fwd_varlen(q, k_pool, v_pool, page_table, seqused_k, cu_seqlens_q, q2k, *,
+                                causal: bool, softmax_scale: float = 0.0,
+                                path: int = MSA_PATH_AUTO, o=None, lse=None,
+                                return_temperature_lse: bool = False,
+                                lse_temperature_scale: Optional[float] = None,
+                                lse_temperature=None, temperature_fast_path: bool = True,
+                                workspace=None, stream=None):
+    """Paged K/V with a packed query batch: q [total_q, Hq, D], cu_seqlens_q [B+1],
+    q2k [Hkv, total_q, topk]. Returns (O [total_q, Hq, D], LSE [total_q, Hq][, LSE_T])."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16)
+    kv_dtype = _kv_dtype(k_pool, v_pool, ("k_pool", "v_pool"))
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seqused_k, "seqused_k", torch.int32), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(q2k, "q2k", torch.int32)
+    total_q, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pool.shape
+    B, max_pages = page_table.shape
+    topk = q2k.shape[-1]
+    if o is None:
+        o = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16), _dev(lse, "lse", torch.float32)
+    temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
+                                      lse_temperature, temperature_fast_path)
+    nbytes = int(lib.msa_paged_sparse_fwd_varlen_workspace_size(B, total_q, Hq, Hkv, D, topk,
+                                                                page_size, max_pages, path))
+    ws, wsn = _workspace(nbytes, q.device, workspace)
+    rc = lib.msa_paged_sparse_fwd_varlen(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                         _ptr(seqused_k), _ptr(cu_seqlens_q), _ptr(q2k), B,
+                                         total_q, Hq, Hkv, D, topk, page_size, num_pages,
+                                         max_pages, int(bool(causal)), float(softmax_scale),
+                                         int(path), kv_dtype, _ptr(o), _ptr(lse), temp,
+                                         _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
+    _check(rc)
+    if return_temperature_lse:
+        return o, lse, (lse if alias else lse_t)
+    return o, lse
 
 
 class DecodePlan:

@@ -1007,6 +1007,137 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
 }
 
 
+// Paged K/V with a packed (variable-length) query batch: the paged form of
+// sparse_atten_func with cu_seqlens_q. Sequence b owns max_pages CSR rows.
+int msa_paged_sparse_fwd_varlen_path(int B, int total_q, int Hkv, int topk, int max_pages,
+                                     int path) {
+  if (path != MSA_PATH_AUTO) return path;
+  if (B <= 0 || total_q <= 0 || Hkv <= 0 || topk <= 0 || max_pages <= 0) return MSA_PATH_QCENTRIC;
+  const long long nrows = static_cast<long long>(B) * max_pages;
+  return nrows <= kMaxCsrRows && kv_pays(total_q, Hkv, topk, max_pages, nrows)
+             ? MSA_PATH_KVCENTRIC
+             : MSA_PATH_QCENTRIC;
+}
+
+size_t msa_paged_sparse_fwd_varlen_workspace_size(int B, int total_q, int Hq, int Hkv, int D,
+                                                  int topk, int page_size, int max_pages,
+                                                  int path) {
+  if (B <= 0 || total_q <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
+      page_size != kBlk || max_pages <= 0 || Hq % Hkv)
+    return 0;
+  if (msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages, path) !=
+      MSA_PATH_KVCENTRIC)
+    return 0;
+  const long long nrows = static_cast<long long>(B) * max_pages;
+  if (nrows > kMaxCsrRows) return 0;
+  return align256(varlen_tables_bytes(B, total_q, nrows)) +
+         kv_layout(total_q, nrows, Hq, Hkv, topk).total;
+}
+
+int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* page_table, const int32_t* seqused_k,
+                                const int32_t* cu_seqlens_q, const int32_t* q2k, int B,
+                                int total_q, int Hq, int Hkv, int D, int topk, int page_size,
+                                int num_pages, int max_pages, int causal, float softmax_scale,
+                                int path, int kv_dtype, void* o, float* lse,
+                                float lse_temperature_scale, float* lse_temperature,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || total_q < 0)
+    return fail(MSA_ERR_INVALID_VALUE, "B must be positive and total_q non-negative");
+  int rc = check_common(B, 1, Hq, Hkv, D, topk, page_size);
+  if (rc) return rc;
+  rc = check_temperature(lse_temperature_scale, lse_temperature);
+  if (rc) return rc;
+  if (static_cast<long long>(total_q) * topk > 0x7FFFFFFFLL)
+    return fail(MSA_ERR_INVALID_VALUE, "total_q*topk exceeds the int32 index range");
+  if (num_pages <= 0 || max_pages <= 0)
+    return fail(MSA_ERR_INVALID_VALUE, "num_pages and max_pages must be positive");
+  if (path != MSA_PATH_AUTO && path != MSA_PATH_QCENTRIC && path != MSA_PATH_KVCENTRIC)
+    return fail(path == MSA_PATH_TILE || path == MSA_PATH_DECODE ? MSA_ERR_NOT_SUPPORTED
+                                                                 : MSA_ERR_INVALID_VALUE,
+                "path %d not available for variable-length paged batches", path);
+  if (!cu_seqlens_q || !page_table || !seqused_k)
+    return fail(MSA_ERR_INVALID_VALUE, "null pointer");
+  if (!aligned(cu_seqlens_q, 4) || !aligned(page_table, 4) || !aligned(seqused_k, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned int32 pointer");
+  if (total_q == 0) return MSA_OK;  // nothing to compute or write
+  if (!q || !k_pool || !v_pool || !q2k || !o || !lse)
+    return fail(MSA_ERR_INVALID_VALUE, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+      !aligned(q2k, 4) || !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_VALUE, "misaligned tensor pointer (bf16 tensors need 16 bytes)");
+  const int which = msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages, path);
+  rc = check_kv_dtype(kv_dtype, which);
+  if (rc) return rc;
+  const int qpk = Hq / Hkv;
+  const int kv_fp8 = kv_dtype == MSA_DTYPE_FP8_E4M3;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+  const float inv_temp = lse_temperature ? 1.f / lse_temperature_scale : 1.f;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (which == MSA_PATH_QCENTRIC) {
+    QcParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = k_pool;
+    p.v = v_pool;
+    p.kv_fp8 = kv_fp8;
+    p.q2k = q2k;
+    p.page_table = page_table;
+    p.seqused = seqused_k;
+    p.cu_q = cu_seqlens_q;
+    p.total_q = total_q;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+    p.nblk = max_pages; p.max_pages = max_pages; p.num_pages = num_pages;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.splits = 1;
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.inv_temp = inv_temp;
+    p.lse_t = lse_temperature;
+    prof_mark(g_prof_before, st);
+    hipError_t e = launch_qcentric(p, true, st);
+    prof_mark(g_prof_after, st);
+    return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric paged varlen forward");
+  }
+
+  // kv-centric: max_pages CSR rows per sequence, all held by the CSR passes at once
+  const long long nrows = static_cast<long long>(B) * max_pages;
+  if (nrows > kMaxCsrRows)
+    return fail(MSA_ERR_NOT_SUPPORTED, "kv-centric path: B*max_pages = %lld CSR rows exceed %d",
+                nrows, kMaxCsrRows);
+  const size_t tbytes = align256(varlen_tables_bytes(B, total_q, nrows));
+  const KvLayout L = kv_layout(total_q, nrows, Hq, Hkv, topk);
+  if (!workspace || workspace_bytes < tbytes + L.total)
+    return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes, got %zu",
+                tbytes + L.total, workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const VarlenTables vt = varlen_tables_at(ws, B, total_q, nrows);
+  hipError_t e = launch_varlen_tables(cu_seqlens_q, nullptr, B, total_q, 0, nrows, vt, st,
+                                      max_pages);
+  if (e != hipSuccess) return hip_fail(e, "varlen tables");
+  KvParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = k_pool;
+  p.v = v_pool;
+  p.kv_fp8 = kv_fp8;
+  p.B = 1; p.Sq = total_q; p.Skv = 0; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
+  p.nblk = max_pages; p.nrows = static_cast<int>(nrows);
+  p.cap = static_cast<long long>(total_q) * topk;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.cu_q = cu_seqlens_q;
+  p.total_q = total_q;
+  p.inv_temp = inv_temp;
+  p.page_table = page_table;
+  p.seqused = seqused_k;
+  p.num_pages = num_pages;
+  return run_kvcentric(p, q2k, nullptr, nullptr, nullptr, L, ws + tbytes, &vt,
+                       static_cast<uint16_t*>(o), lse, lse_temperature, st);
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -150,9 +150,10 @@ struct VarlenTables {
 size_t varlen_tables_bytes(int B, long long total_q, long long nrows);
 // carves the tables out of ws (varlen_tables_bytes(...) bytes, 256-byte aligned)
 VarlenTables varlen_tables_at(void* ws, int B, long long total_q, long long nrows);
+// cu_k == nullptr: every sequence has blocks_per_seq blocks (a paged batch's max_pages)
 hipError_t launch_varlen_tables(const int32_t* cu_q, const int32_t* cu_k, int B, long long total_q,
                                 long long total_k, long long nrows, const VarlenTables& t,
-                                hipStream_t stream);
+                                hipStream_t stream, int blocks_per_seq = 0);
 
 // ---------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() after its launches).
@@ -180,9 +181,10 @@ struct QcParams {
   float inv_temp;            // 1 / T
   float* lse_t;
   float* lse_t_part;
-  // variable-length batch (contiguous K/V only): cu_q != nullptr. Then q is
-  // [total_q,Hq,D], k/v [total_k,Hkv,D], q2k [Hkv,total_q,topk], o [total_q,Hq,D],
-  // lse [total_q,Hq]; B is the sequence count and Sq, Skv, nblk are unused.
+  // variable-length batch: cu_q != nullptr. Then q is [total_q,Hq,D], q2k
+  // [Hkv,total_q,topk], o [total_q,Hq,D], lse [total_q,Hq]; B is the sequence count
+  // and Sq is unused. Contiguous K/V: k/v [total_k,Hkv,D] by cu_k (Skv, nblk unused);
+  // paged: the pools, page_table and seqused as above (one split).
   const int32_t* cu_q;
   const int32_t* cu_k;
   long long total_q, total_k;
@@ -273,7 +275,8 @@ struct KvParams {
   const int32_t* row_seq;
   long long total_q, total_k;
   // paged K/V (page_table != nullptr): block s of sequence b is page page_table[b * nblk + s]
-  // of the pools [num_pages, Hkv, 128, D], and the sequence's keys are [0, seqused[b])
+  // of the pools [num_pages, Hkv, 128, D], and the sequence's keys are [0, seqused[b]);
+  // with packed queries (cu_q) the rows of sequence b are rowbase[b] .. + nblk
   const int32_t* page_table;
   const int32_t* seqused;
   int num_pages;

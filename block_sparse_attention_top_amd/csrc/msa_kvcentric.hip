@@ -26,7 +26,8 @@
 // and may end inside it, and the causal limit uses the sequence's own lengths.
 // A paged K/V cache (PAGED) differs only in where a block's keys live: block s of
 // sequence b is one page of the pools, page_table[b][s], and the sequence's keys end
-// at seqused[b]. A block past those keys, or whose page id is outside the pools,
+// at seqused[b]; its queries are uniform (b * Sq ..) or packed (cu_seqlens_q, with
+// max_pages CSR rows per sequence). A block past those keys, or whose page id is outside the pools,
 // contributes nothing (its partials are empty and nothing of it is read), as on the
 // paged q-centric kernel.
 //
@@ -72,10 +73,18 @@ __device__ __forceinline__ void kv_item(const KvParams& p, const int4 item, uint
   int page = 0;       // PAGED: the block's page
   bool dead = false;  // PAGED: the block has no keys to read (past seqused, or a bad page)
   if (PAGED) {
-    const int b = r / p.nblk;
-    s = r % p.nblk;
-    qbeg = static_cast<long long>(b) * p.Sq;
-    sq_b = p.Sq;
+    int b;
+    if (p.cu_q) {  // packed queries: rows rowbase[b] .. + nblk are sequence b's blocks
+      b = p.row_seq[r];
+      if (b < 0) return;
+      s = r - p.rowbase[b];
+      seq_range(p.cu_q, b, p.total_q, qbeg, sq_b);
+    } else {
+      b = r / p.nblk;
+      s = r % p.nblk;
+      qbeg = static_cast<long long>(b) * p.Sq;
+      sq_b = p.Sq;
+    }
     kbeg = 0;
     kvlen = p.seqused[b];
     if (static_cast<long long>(s) * kBlk < kvlen)
@@ -618,7 +627,7 @@ hipError_t launch_kvcentric(const KvParams& p, long long max_items, hipStream_t 
   if (max_items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (p.chunk_entries * p.qpk > kKvChunkRows || p.chunk_entries > kKvMaxEntries)
     return hipErrorInvalidValue;
-  if (p.page_table && (!p.seqused || p.num_pages <= 0 || p.cu_q)) return hipErrorInvalidValue;
+  if (p.page_table && (!p.seqused || p.num_pages <= 0 || p.nblk <= 0)) return hipErrorInvalidValue;
   return p.page_table ? kv_launch_qpk<true>(p, max_items, stream)
                       : kv_launch_qpk<false>(p, max_items, stream);
 }

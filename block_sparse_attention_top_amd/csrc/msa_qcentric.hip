@@ -54,8 +54,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// kWaves waves per index row (or split), each taking every kWaves-th slot
-template <bool PAGED, bool TEMP, bool FP8, int kWaves>
+// kWaves waves per index row (or split), each taking every kWaves-th slot. PVAR: a
+// paged pool with a variable-length query batch (cu_q; one split).
+template <bool PAGED, bool TEMP, bool FP8, int kWaves, bool PVAR = false>
 __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_all[kWaves][kSub * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vs_all[kWaves][kSub * kVStride];
@@ -67,8 +68,10 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   const int n = lane & 15;  // head column
   const int g = lane >> 4;  // 16-lane group
 
+  // packed queries: contiguous varlen batches, or paged ones (PVAR)
+  const bool varq = PAGED ? PVAR : p.cu_q != nullptr;
   long long item = blockIdx.x;
-  if (PAGED) {
+  if (PAGED && !PVAR) {
     // Workgroups are dealt round-robin over the 8 XCDs; this permutation puts the
     // Sq x splits items of one (b, hkv) on one XCD, so the blocks its query rows
     // share (the diagonal one at least) are fetched into a single L2. Groups past the
@@ -86,14 +89,19 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   int b, hkv;
   long long grow, qpos, sq_b, kbeg, kvlen;
   const int32_t* sel;
-  if (!PAGED && p.cu_q) {
+  if (varq) {
     grow = item % p.total_q;
     hkv = static_cast<int>(item / p.total_q);
     b = seq_search(p.cu_q, p.B, grow);
     long long qbeg;
     seq_range(p.cu_q, b, p.total_q, qbeg, sq_b);
     qpos = grow - qbeg;
-    seq_range(p.cu_k, b, p.total_k, kbeg, kvlen);
+    if (PAGED) {
+      kbeg = 0;
+      kvlen = p.seqused[b];
+    } else {
+      seq_range(p.cu_k, b, p.total_k, kbeg, kvlen);
+    }
     sel = p.q2k + (static_cast<long long>(hkv) * p.total_q + grow) * p.topk;
   } else {
     qpos = item % p.Sq;
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
     sel = p.q2k + ((static_cast<long long>(b) * p.Hkv + hkv) * p.Sq + qpos) * p.topk;
   }
   // valid block ids: [0, nblk) (uniform or paged) or the blocks of the sequence (varlen)
-  const long long nblk_b = (!PAGED && p.cu_q) ? (kvlen + kBlk - 1) / kBlk : p.nblk;
+  const long long nblk_b = (!PAGED && varq) ? (kvlen + kBlk - 1) / kBlk : p.nblk;
 
   const int head = hkv * p.qpk + n;
   const bool head_ok = n < p.qpk;
@@ -341,8 +349,8 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
       *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
     }
     if (g == 0) {
-      const long long li = (!PAGED && p.cu_q) ? grow * p.Hq + head
-                                              : (static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos;
+      const long long li = varq ? grow * p.Hq + head
+                                : (static_cast<long long>(b) * p.Hq + head) * p.Sq + qpos;
       p.lse[li] = lse_v;
       if (TEMP) p.lse_t[li] = lset_v;
     }
@@ -369,16 +377,21 @@ void qc_launch(int variant, const QcParams& p, dim3 grid, hipStream_t stream) {
     case 4: hipLaunchKernelGGL((qcentric_kernel<true, false, false, W>), grid, blk, 0, stream, p); break;
     case 5: hipLaunchKernelGGL((qcentric_kernel<true, false, true, W>), grid, blk, 0, stream, p); break;
     case 6: hipLaunchKernelGGL((qcentric_kernel<true, true, false, W>), grid, blk, 0, stream, p); break;
-    default: hipLaunchKernelGGL((qcentric_kernel<true, true, true, W>), grid, blk, 0, stream, p); break;
+    case 7: hipLaunchKernelGGL((qcentric_kernel<true, true, true, W>), grid, blk, 0, stream, p); break;
+    case 12: hipLaunchKernelGGL((qcentric_kernel<true, false, false, W, true>), grid, blk, 0, stream, p); break;
+    case 13: hipLaunchKernelGGL((qcentric_kernel<true, false, true, W, true>), grid, blk, 0, stream, p); break;
+    case 14: hipLaunchKernelGGL((qcentric_kernel<true, true, false, W, true>), grid, blk, 0, stream, p); break;
+    default: hipLaunchKernelGGL((qcentric_kernel<true, true, true, W, true>), grid, blk, 0, stream, p); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
-  const long long rows = (!paged && p.cu_q) ? p.total_q : static_cast<long long>(p.B) * p.Sq;
+  // packed queries (cu_q; contiguous or paged) take one split
+  const long long rows = p.cu_q ? p.total_q : static_cast<long long>(p.B) * p.Sq;
   const long long items = rows * p.Hkv * p.splits;
-  if (!paged && p.cu_q && p.splits != 1) return hipErrorInvalidValue;
+  if (p.cu_q && p.splits != 1) return hipErrorInvalidValue;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
@@ -386,7 +399,8 @@ hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
   // (decode: the 32 x 8-query paged workload has 1024 (row, KV head) items);
   // otherwise one (large prefill, where the second wave only adds Q loads and a merge).
   const bool two = items < 8LL * device_cu_count();
-  const int variant = (paged ? 4 : 0) + (p.lse_t ? 2 : 0) + (p.kv_fp8 ? 1 : 0);
+  const int variant =
+      (paged ? 4 : 0) + (paged && p.cu_q ? 8 : 0) + (p.lse_t ? 2 : 0) + (p.kv_fp8 ? 1 : 0);
   if (two)
     qc_launch<2>(variant, p, grid, stream);
   else

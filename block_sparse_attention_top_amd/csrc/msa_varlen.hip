@@ -2,7 +2,8 @@
 // cu_seqlens, the primary form of `sparse_atten_func` and `build_k2q_csr` on
 // the page "MSA interface.py"). Sequence b's KV blocks are the CSR rows
 // rowbase[b] .. rowbase[b+1]-1 with rowbase the prefix sum of ceil(Skv_b / 128)
-// (the `total_rows` of the CSR); its block ids count from its first key.
+// (the `total_rows` of the CSR); its block ids count from its first key. A paged
+// batch gives every sequence max_pages rows (its page-table width).
 //
 // Two launches: one workgroup scans the per-sequence block counts (wave
 // shuffles + a carry across 256-sequence rounds), then one thread per packed
@@ -18,6 +19,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void varlen_rowbase_kernel(const int32_t* __restrict__ cu_k,
                                                              int B, long long total_k,
+                                                             int blocks_per_seq,
                                                              int32_t* __restrict__ rowbase) {
   __shared__ long long wsum[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -25,7 +27,9 @@ __global__ __launch_bounds__(256) void varlen_rowbase_kernel(const int32_t* __re
   for (int base = 0; base < B; base += 256) {
     const int b = base + threadIdx.x;
     long long nb = 0;
-    if (b < B) {
+    if (b < B && !cu_k) {
+      nb = blocks_per_seq;
+    } else if (b < B) {
       long long beg, len;
       seq_range(cu_k, b, total_k, beg, len);
       nb = (len + kBlk - 1) / kBlk;
@@ -87,10 +91,10 @@ VarlenTables varlen_tables_at(void* ws, int B, long long total_q, long long nrow
 
 hipError_t launch_varlen_tables(const int32_t* cu_q, const int32_t* cu_k, int B, long long total_q,
                                 long long total_k, long long nrows, const VarlenTables& t,
-                                hipStream_t stream) {
-  if (B <= 0) return hipErrorInvalidValue;
+                                hipStream_t stream, int blocks_per_seq) {
+  if (B <= 0 || (!cu_k && blocks_per_seq <= 0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(varlen_rowbase_kernel, dim3(1), dim3(256), 0, stream, cu_k, B, total_k,
-                     t.rowbase);
+                     blocks_per_seq, t.rowbase);
   const long long n = total_q > nrows ? total_q : nrows;
   if (n > 0) {
     const long long blocks = (n + 255) / 256;

@@ -274,6 +274,47 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * Sparse forward, paged K/V with a packed variable-length query batch: the paged
+ * form of sparse_atten_func (page_table and seqused_k with cu_seqlens_q) on the
+ * page "MSA interface.py"; the test page's test_sparse_page_atten runs it.
+ *   q             bf16 [total_q, Hq, D]; sequence b's queries are rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   k_pool, v_pool, page_table, seqused_k, num_pages, max_pages
+ *                 as msa_paged_sparse_fwd (seqused_k[b] keys for sequence b)
+ *   cu_seqlens_q  int32 [B+1] on the device, non-decreasing from 0 to total_q
+ *   q2k           int32 [Hkv, total_q, topk], valid ids [0, max_pages)
+ *   causal        bottom-right with the limit q + seqused_k[b] - Sq_b, q counted
+ *                 from the sequence's first query
+ *   path          MSA_PATH_AUTO, MSA_PATH_QCENTRIC (one split) or
+ *                 MSA_PATH_KVCENTRIC (max_pages CSR rows per sequence, B * max_pages
+ *                 at most 16384, else MSA_ERR_NOT_SUPPORTED); auto takes the
+ *                 kv-centric path under the rule of msa_sparse_fwd with total_q
+ *                 queries over B * max_pages rows
+ *   kv_dtype      enum msa_dtype
+ *   o             bf16 [total_q, Hq, D]   (out)
+ *   lse           fp32 [total_q, Hq]      (out)
+ *   lse_temperature_scale, lse_temperature   fp32 [total_q, Hq] or NULL (out)
+ *   workspace     at least msa_paged_sparse_fwd_varlen_workspace_size(...) with the
+ *                 same path (zero for the q-centric path)
+ * A block past seqused_k[b], or whose page id is outside [0, num_pages), adds nothing.
+ * Index rows must hold distinct ids. total_q = 0 writes nothing and returns MSA_OK.
+ */
+size_t msa_paged_sparse_fwd_varlen_workspace_size(int B, int total_q, int Hq, int Hkv, int D,
+                                                  int topk, int page_size, int max_pages,
+                                                  int path);
+/* The path msa_paged_sparse_fwd_varlen takes for these sizes (resolves MSA_PATH_AUTO). */
+int msa_paged_sparse_fwd_varlen_path(int B, int total_q, int Hkv, int topk, int max_pages,
+                                     int path);
+int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* page_table, const int32_t* seqused_k,
+                                const int32_t* cu_seqlens_q, const int32_t* q2k, int B,
+                                int total_q, int Hq, int Hkv, int D, int topk, int page_size,
+                                int num_pages, int max_pages, int causal, float softmax_scale,
+                                int path, int kv_dtype, void* o, float* lse,
+                                float lse_temperature_scale, float* lse_temperature,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * msa_paged_sparse_fwd without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc. Arguments, results and errors are those of

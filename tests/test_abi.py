@@ -175,6 +175,14 @@ def test_auto_path_resolution():
     assert msa.msa_paged_sparse_fwd_path(1, 32768, 4, 16, 256) == msa.MSA_PATH_KVCENTRIC
     assert msa.msa_paged_sparse_fwd_path(1, 32768, 4, 16, 20000) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_paged_sparse_fwd_path(4, 4096, 4, 16, 8192) == msa.MSA_PATH_KVCENTRIC
+    # paged with packed queries: the same rule over B * max_pages rows, no sub-batches
+    assert msa.msa_paged_sparse_fwd_varlen_path(3, 8096, 2, 16, 71) == msa.MSA_PATH_KVCENTRIC
+    assert msa.msa_paged_sparse_fwd_varlen_path(64, 64, 4, 16, 512) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_paged_sparse_fwd_varlen_path(64, 65536, 4, 16, 512) == msa.MSA_PATH_QCENTRIC
+    assert msa.msa_paged_sparse_fwd_varlen_path(2, 8, 1, 4, 8, 2) == msa.MSA_PATH_KVCENTRIC
+    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(3, 8096, 32, 2, 128, 16, 128, 71) > 0
+    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(64, 64, 64, 4, 128, 16, 128, 512) == 0
+    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(3, 8096, 32, 2, 128, 16, 64, 71) == 0
     # contiguous: the query tile is asked for
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 4) == msa.MSA_PATH_TILE
 
