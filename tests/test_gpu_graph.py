@@ -136,3 +136,28 @@ def test_dense_decode_run_in_graph():
     other = lambda: msa.msa_paged_decode_run(plan2, t2["q"], t2["k_pool"], t2["v_pool"],
                                              t2["page_table"], t2["seqused_k"], causal=True)
     replay_and_check(g, [o, lse], [o_ref, l_ref], other, "dense decode run")
+
+
+def test_paged_kv_centric_in_graph():
+    """The paged prefill on the kv-centric path (CSR, items, partials and combine in the
+    caller's workspace), captured and replayed."""
+    import block_sparse_attention_top_amd as msa
+    w, t = paged(67, 2, 1024, 4096, [0, 700])
+    args = (t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["seqused_k"], t["q2k"])
+    nbytes = msa.msa_paged_sparse_fwd_workspace_size(w.B, w.Sq, w.Hq, w.Hkv, w.D, w.topk, w.blk,
+                                                     w.max_pages, 0, KV)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda")
+    fn = lambda: msa.msa_paged_sparse_fwd(*args, causal=True, path=KV, o=o, lse=lse,
+                                          workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    say("[graph] paged kv-centric: capturing")
+    g = capture(fn)
+    _, t2 = paged(68, 1, 512, 2048, [100])
+    other = lambda: msa.msa_paged_sparse_fwd(
+        t2["q"], t2["k_pool"], t2["v_pool"], t2["page_table"], t2["seqused_k"], t2["q2k"],
+        causal=True, path=KV)
+    replay_and_check(g, [o, lse], [o_ref, l_ref], other, "paged kv-centric")
