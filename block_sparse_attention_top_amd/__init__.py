@@ -15,7 +15,7 @@ from ._ffi import (MSA_DTYPE_BF16, MSA_DTYPE_FP8_E4M3, MSA_PATH_AUTO, MSA_PATH_D
                    msa_paged_sparse_fwd, msa_paged_sparse_fwd_path, msa_paged_sparse_fwd_splits,
                    msa_paged_sparse_fwd_noalloc, MSA_NOALLOC_SCRATCH_BYTES,
                    msa_paged_sparse_fwd_varlen, msa_paged_sparse_fwd_varlen_path,
-                   msa_paged_sparse_fwd_varlen_workspace_size,
+                   msa_paged_sparse_fwd_varlen_workspace_size, msa_paged_sparse_fwd_varlen_splits,
                    msa_paged_sparse_fwd_workspace_size, msa_set_profiling_events, msa_sparse_fwd,
                    msa_sparse_fwd_path, msa_sparse_fwd_workspace_size, msa_sparse_fwd_varlen,
                    msa_sparse_fwd_varlen_path, msa_sparse_fwd_varlen_workspace_size,
@@ -31,7 +31,7 @@ __all__ = [
     "msa_paged_sparse_fwd_splits", "msa_paged_sparse_fwd_workspace_size", "msa_last_error",
     "msa_paged_sparse_fwd_noalloc", "MSA_NOALLOC_SCRATCH_BYTES",
     "msa_paged_sparse_fwd_varlen", "msa_paged_sparse_fwd_varlen_path",
-    "msa_paged_sparse_fwd_varlen_workspace_size",
+    "msa_paged_sparse_fwd_varlen_workspace_size", "msa_paged_sparse_fwd_varlen_splits",
     "msa_set_profiling_events", "msa_version", "msa_sparse_fwd_varlen",
     "msa_sparse_fwd_varlen_path", "msa_sparse_fwd_varlen_workspace_size",
     "msa_build_k2q_csr_varlen", "msa_build_k2q_csr_varlen_workspace_size",

@@ -93,12 +93,14 @@ def load_library():
     lib.msa_paged_sparse_fwd_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
                                                  I, I, I, P, P, F, P, P]
     lib.msa_paged_sparse_fwd_noalloc.restype = I
-    lib.msa_paged_sparse_fwd_varlen_workspace_size.argtypes = [I] * 9
+    lib.msa_paged_sparse_fwd_varlen_workspace_size.argtypes = [I] * 10
     lib.msa_paged_sparse_fwd_varlen_workspace_size.restype = S
     lib.msa_paged_sparse_fwd_varlen_path.argtypes = [I] * 6
     lib.msa_paged_sparse_fwd_varlen_path.restype = I
+    lib.msa_paged_sparse_fwd_varlen_splits.argtypes = [I] * 7
+    lib.msa_paged_sparse_fwd_varlen_splits.restype = I
     lib.msa_paged_sparse_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
-                                                I, F, I, I, P, P, F, P, P, S, P]
+                                                I, F, I, I, I, P, P, F, P, P, S, P]
     lib.msa_paged_sparse_fwd_varlen.restype = I
     PL = ctypes.POINTER(MsaDecodePlan)
     lib.msa_paged_decode_plan_init.argtypes = [I, I, I, I, I, I, I, I, I, I, PL]
@@ -465,9 +467,16 @@ MSA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def msa_paged_sparse_fwd_varlen_workspace_size(B, total_q, Hq, Hkv, D, topk, page_size,
-                                               max_pages, path=MSA_PATH_AUTO) -> int:
+                                               max_pages, num_splits=0,
+                                               path=MSA_PATH_AUTO) -> int:
     return int(load_library().msa_paged_sparse_fwd_varlen_workspace_size(
-        B, total_q, Hq, Hkv, D, topk, page_size, max_pages, path))
+        B, total_q, Hq, Hkv, D, topk, page_size, max_pages, num_splits, path))
+
+
+def msa_paged_sparse_fwd_varlen_splits(B, total_q, Hkv, topk, max_pages, num_splits=0,
+                                       path=MSA_PATH_AUTO) -> int:
+    return int(load_library().msa_paged_sparse_fwd_varlen_splits(B, total_q, Hkv, topk,
+                                                                  max_pages, num_splits, path))
 
 
 def msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages,
@@ -477,7 +486,7 @@ def msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages,
 
 
 def msa_paged_sparse_fwd_varlen(q, k_pool, v_pool, page_table, seqused_k, cu_seqlens_q, q2k, *,
-                                causal: bool, softmax_scale: float = 0.0,
+                                causal: bool, softmax_scale: float = 0.0, num_splits: int = 0,
                                 path: int = MSA_PATH_AUTO, o=None, lse=None,
                                 return_temperature_lse: bool = False,
                                 lse_temperature_scale: Optional[float] = None,
@@ -503,13 +512,15 @@ def msa_paged_sparse_fwd_varlen(q, k_pool, v_pool, page_table, seqused_k, cu_seq
     temp, lse_t, alias = _temperature(lse, return_temperature_lse, lse_temperature_scale,
                                       lse_temperature, temperature_fast_path)
     nbytes = int(lib.msa_paged_sparse_fwd_varlen_workspace_size(B, total_q, Hq, Hkv, D, topk,
-                                                                page_size, max_pages, path))
+                                                                page_size, max_pages,
+                                                                num_splits, path))
     ws, wsn = _workspace(nbytes, q.device, workspace)
     rc = lib.msa_paged_sparse_fwd_varlen(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                                          _ptr(seqused_k), _ptr(cu_seqlens_q), _ptr(q2k), B,
                                          total_q, Hq, Hkv, D, topk, page_size, num_pages,
                                          max_pages, int(bool(causal)), float(softmax_scale),
-                                         int(path), kv_dtype, _ptr(o), _ptr(lse), temp,
+                                         int(num_splits), int(path), kv_dtype, _ptr(o),
+                                         _ptr(lse), temp,
                                          _ptr(lse_t), _ptr(ws), wsn, _stream(stream))
     _check(rc)
     if return_temperature_lse:

@@ -1019,15 +1019,37 @@ int msa_paged_sparse_fwd_varlen_path(int B, int total_q, int Hkv, int topk, int 
              : MSA_PATH_QCENTRIC;
 }
 
+// q-centric splits of a paged varlen batch: the uniform paged rule with total_q query rows
+int paged_varlen_splits(int total_q, int Hkv, int topk, int num_splits) {
+  long long s = num_splits;
+  if (s <= 0) {
+    const long long rows = static_cast<long long>(total_q) * Hkv;
+    s = std::min<long long>((1024 + rows - 1) / rows, 8);
+  }
+  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, topk)));
+}
+
+int msa_paged_sparse_fwd_varlen_splits(int B, int total_q, int Hkv, int topk, int max_pages,
+                                       int num_splits, int path) {
+  if (B <= 0 || total_q <= 0 || Hkv <= 0 || topk <= 0 || max_pages <= 0 || num_splits < 0)
+    return 0;
+  if (msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages, path) !=
+      MSA_PATH_QCENTRIC)
+    return 1;
+  return paged_varlen_splits(total_q, Hkv, topk, num_splits);
+}
+
 size_t msa_paged_sparse_fwd_varlen_workspace_size(int B, int total_q, int Hq, int Hkv, int D,
                                                   int topk, int page_size, int max_pages,
-                                                  int path) {
+                                                  int num_splits, int path) {
   if (B <= 0 || total_q <= 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || D != kD ||
-      page_size != kBlk || max_pages <= 0 || Hq % Hkv)
+      page_size != kBlk || max_pages <= 0 || Hq % Hkv || num_splits < 0)
     return 0;
   if (msa_paged_sparse_fwd_varlen_path(B, total_q, Hkv, topk, max_pages, path) !=
       MSA_PATH_KVCENTRIC)
-    return 0;
+    return paged_workspace(total_q, 1, Hq, Hkv, topk, max_pages,
+                           PagedPlan{MSA_PATH_QCENTRIC,
+                                     paged_varlen_splits(total_q, Hkv, topk, num_splits)});
   const long long nrows = static_cast<long long>(B) * max_pages;
   if (nrows > kMaxCsrRows) return 0;
   return align256(varlen_tables_bytes(B, total_q, nrows)) +
@@ -1039,10 +1061,11 @@ int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v
                                 const int32_t* cu_seqlens_q, const int32_t* q2k, int B,
                                 int total_q, int Hq, int Hkv, int D, int topk, int page_size,
                                 int num_pages, int max_pages, int causal, float softmax_scale,
-                                int path, int kv_dtype, void* o, float* lse,
+                                int num_splits, int path, int kv_dtype, void* o, float* lse,
                                 float lse_temperature_scale, float* lse_temperature,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
+  if (num_splits < 0) return fail(MSA_ERR_INVALID_VALUE, "num_splits must be >= 0");
   if (B <= 0 || total_q < 0)
     return fail(MSA_ERR_INVALID_VALUE, "B must be positive and total_q non-negative");
   int rc = check_common(B, 1, Hq, Hkv, D, topk, page_size);
@@ -1091,15 +1114,37 @@ int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v
     p.nblk = max_pages; p.max_pages = max_pages; p.num_pages = num_pages;
     p.causal = causal ? 1 : 0;
     p.scale_log2 = scale * kLog2e;
-    p.splits = 1;
+    p.splits = paged_varlen_splits(total_q, Hkv, topk, num_splits);
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
     p.inv_temp = inv_temp;
     p.lse_t = lse_temperature;
+    if (p.splits > 1) {  // partials over total_q rows: the uniform layout with B = total_q, Sq = 1
+      const PagedPlan pl{MSA_PATH_QCENTRIC, p.splits};
+      const size_t need = paged_workspace(total_q, 1, Hq, Hkv, topk, max_pages, pl);
+      if (!workspace || workspace_bytes < need)
+        return fail(MSA_ERR_INVALID_VALUE, "workspace too small: need %zu bytes", need);
+      if (!aligned(workspace, 256))
+        return fail(MSA_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+      const size_t rows = static_cast<size_t>(total_q) * Hq;
+      char* wsc = static_cast<char*>(workspace);
+      p.o_part = reinterpret_cast<float*>(wsc);
+      p.lse_part = reinterpret_cast<float*>(wsc + align256(p.splits * rows * kD * 4));
+      if (lse_temperature)
+        p.lse_t_part = reinterpret_cast<float*>(wsc + align256(p.splits * rows * kD * 4) +
+                                                align256(p.splits * rows * 4));
+    }
     prof_mark(g_prof_before, st);
     hipError_t e = launch_qcentric(p, true, st);
     prof_mark(g_prof_after, st);
-    return e == hipSuccess ? MSA_OK : hip_fail(e, "q-centric paged varlen forward");
+    if (e != hipSuccess) return hip_fail(e, "q-centric paged varlen forward");
+    if (p.splits > 1) {
+      // LSE [total_q, Hq] is the uniform [B, Hq, Sq] layout with B = total_q, Sq = 1
+      e = launch_combine_splits(p.o_part, p.lse_part, total_q, 1, Hq, p.splits,
+                                static_cast<uint16_t*>(o), lse, st, p.lse_t_part, lse_temperature);
+      if (e != hipSuccess) return hip_fail(e, "split combine");
+    }
+    return MSA_OK;
   }
 
   // kv-centric: max_pages CSR rows per sequence, all held by the CSR passes at once

@@ -184,7 +184,7 @@ struct QcParams {
   // variable-length batch: cu_q != nullptr. Then q is [total_q,Hq,D], q2k
   // [Hkv,total_q,topk], o [total_q,Hq,D], lse [total_q,Hq]; B is the sequence count
   // and Sq is unused. Contiguous K/V: k/v [total_k,Hkv,D] by cu_k (Skv, nblk unused);
-  // paged: the pools, page_table and seqused as above (one split).
+  // paged: the pools, page_table and seqused as above, split partials over total_q rows.
   const int32_t* cu_q;
   const int32_t* cu_k;
   long long total_q, total_k;

@@ -55,7 +55,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // kWaves waves per index row (or split), each taking every kWaves-th slot. PVAR: a
-// paged pool with a variable-length query batch (cu_q; one split).
+// paged pool with a variable-length query batch (cu_q).
 template <bool PAGED, bool TEMP, bool FP8, int kWaves, bool PVAR = false>
 __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_all[kWaves][kSub * kKStride];
@@ -355,7 +355,10 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
       if (TEMP) p.lse_t[li] = lset_v;
     }
   } else {
-    const long long prow = (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;  // paged
+    // paged: rows [splits][B * Sq or total_q][Hq]
+    const long long prow =
+        (PAGED && PVAR) ? (static_cast<long long>(sp) * p.total_q + grow) * p.Hq + head
+                        : (static_cast<long long>(sp) * p.B * p.Sq + grow) * p.Hq + head;
     float* orow = p.o_part + prow * kD + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = oacc[dt] * inv;
@@ -388,10 +391,10 @@ void qc_launch(int variant, const QcParams& p, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
-  // packed queries (cu_q; contiguous or paged) take one split
+  // packed queries (cu_q): contiguous K/V take one split
   const long long rows = p.cu_q ? p.total_q : static_cast<long long>(p.B) * p.Sq;
   const long long items = rows * p.Hkv * p.splits;
-  if (p.cu_q && p.splits != 1) return hipErrorInvalidValue;
+  if (p.cu_q && !paged && p.splits != 1) return hipErrorInvalidValue;
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));

@@ -285,7 +285,10 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
  *   q2k           int32 [Hkv, total_q, topk], valid ids [0, max_pages)
  *   causal        bottom-right with the limit q + seqused_k[b] - Sq_b, q counted
  *                 from the sequence's first query
- *   path          MSA_PATH_AUTO, MSA_PATH_QCENTRIC (one split) or
+ *   num_splits    q-centric: 0 = automatic (as msa_paged_sparse_fwd with total_q
+ *                 query rows), else the number of slot splits (clamped to 1..topk),
+ *                 merged by log-sum-exp; kv-centric: ignored
+ *   path          MSA_PATH_AUTO, MSA_PATH_QCENTRIC or
  *                 MSA_PATH_KVCENTRIC (max_pages CSR rows per sequence, B * max_pages
  *                 at most 16384, else MSA_ERR_NOT_SUPPORTED); auto takes the
  *                 kv-centric path under the rule of msa_sparse_fwd with total_q
@@ -295,22 +298,25 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
  *   lse           fp32 [total_q, Hq]      (out)
  *   lse_temperature_scale, lse_temperature   fp32 [total_q, Hq] or NULL (out)
  *   workspace     at least msa_paged_sparse_fwd_varlen_workspace_size(...) with the
- *                 same path (zero for the q-centric path)
+ *                 same num_splits and path (zero for one q-centric split)
  * A block past seqused_k[b], or whose page id is outside [0, num_pages), adds nothing.
  * Index rows must hold distinct ids. total_q = 0 writes nothing and returns MSA_OK.
  */
 size_t msa_paged_sparse_fwd_varlen_workspace_size(int B, int total_q, int Hq, int Hkv, int D,
                                                   int topk, int page_size, int max_pages,
-                                                  int path);
-/* The path msa_paged_sparse_fwd_varlen takes for these sizes (resolves MSA_PATH_AUTO). */
+                                                  int num_splits, int path);
+/* The path msa_paged_sparse_fwd_varlen takes for these sizes (resolves MSA_PATH_AUTO)
+ * and the number of splits it uses (1 on the kv-centric path, 0 for invalid sizes). */
 int msa_paged_sparse_fwd_varlen_path(int B, int total_q, int Hkv, int topk, int max_pages,
                                      int path);
+int msa_paged_sparse_fwd_varlen_splits(int B, int total_q, int Hkv, int topk, int max_pages,
+                                       int num_splits, int path);
 int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v_pool,
                                 const int32_t* page_table, const int32_t* seqused_k,
                                 const int32_t* cu_seqlens_q, const int32_t* q2k, int B,
                                 int total_q, int Hq, int Hkv, int D, int topk, int page_size,
                                 int num_pages, int max_pages, int causal, float softmax_scale,
-                                int path, int kv_dtype, void* o, float* lse,
+                                int num_splits, int path, int kv_dtype, void* o, float* lse,
                                 float lse_temperature_scale, float* lse_temperature,
                                 void* workspace, size_t workspace_bytes, void* stream);
 

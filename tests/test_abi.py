@@ -181,8 +181,15 @@ def test_auto_path_resolution():
     assert msa.msa_paged_sparse_fwd_varlen_path(64, 65536, 4, 16, 512) == msa.MSA_PATH_QCENTRIC
     assert msa.msa_paged_sparse_fwd_varlen_path(2, 8, 1, 4, 8, 2) == msa.MSA_PATH_KVCENTRIC
     assert msa.msa_paged_sparse_fwd_varlen_workspace_size(3, 8096, 32, 2, 128, 16, 128, 71) > 0
-    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(64, 64, 64, 4, 128, 16, 128, 512) == 0
     assert msa.msa_paged_sparse_fwd_varlen_workspace_size(3, 8096, 32, 2, 128, 16, 64, 71) == 0
+    # q-centric: the uniform split rule over total_q rows (1024 rows here: one split)
+    assert msa.msa_paged_sparse_fwd_varlen_splits(64, 256, 4, 16, 512) == 1
+    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(64, 256, 64, 4, 128, 16, 128, 512) == 0
+    assert msa.msa_paged_sparse_fwd_varlen_splits(4, 4, 4, 16, 512) == 8
+    assert msa.msa_paged_sparse_fwd_varlen_workspace_size(4, 4, 64, 4, 128, 16, 128, 512) >= \
+        8 * 4 * 64 * 128 * 4
+    assert msa.msa_paged_sparse_fwd_varlen_splits(4, 4, 4, 16, 512, 100) == 16
+    assert msa.msa_paged_sparse_fwd_varlen_splits(3, 8096, 2, 16, 71) == 1  # kv-centric
     # contiguous: the query tile is asked for
     assert msa.msa_sparse_fwd_path(1, 8192, 8192, 64, 4, 16, 4) == msa.MSA_PATH_TILE
 

@@ -91,7 +91,7 @@ def test_paged_varlen_equals_contiguous_varlen(case, path):
     pin = to_paged(inp, seed=case, spare_pages=case % 2)
     say(f"[paged-varlen] case {case} path={path} q_lens={q_lens} k_lens={k_lens} Hkv={Hkv} "
         f"qpk={qpk} topk={topk} causal={causal}")
-    o, lse = run_paged_varlen(pin, causal, path)
+    o, lse = run_paged_varlen(pin, causal, path, num_splits=1)  # as the contiguous varlen path
     oc, lc = run_varlen(inp, causal, path)
     assert torch.equal(o, oc) and torch.equal(lse, lc), "paged differs from contiguous"
     o_ref, lse_ref = oracle.sparse_attention_varlen(inp["q"], inp["k"], inp["v"], inp["q2k"],
@@ -133,12 +133,12 @@ def test_paged_varlen_fp8_and_temperature(path):
     pin = to_paged(inp, seed=3)  # fp8 byte pools
     say(f"[paged-varlen] fp8 + temperature path={path}")
     tk = dict(return_temperature_lse=True, lse_temperature_scale=0.5)
-    o8, l8, t8 = run_paged_varlen(pin, True, path, fp8=True, **tk)
+    o8, l8, t8 = run_paged_varlen(pin, True, path, fp8=True, num_splits=2, **tk)
     deq = dict(pin, k_pool=to_dev(pin["k_pool"]).view(torch.float8_e4m3fn).to(torch.bfloat16)
                .view(torch.uint16).cpu().numpy(),
                v_pool=to_dev(pin["v_pool"]).view(torch.float8_e4m3fn).to(torch.bfloat16)
                .view(torch.uint16).cpu().numpy())
-    od, ld, td = run_paged_varlen(deq, True, path, **tk)
+    od, ld, td = run_paged_varlen(deq, True, path, num_splits=2, **tk)
     assert torch.equal(o8, od) and torch.equal(l8, ld) and torch.equal(t8, td)
     o_ref, lse_ref, lt_ref = oracle.sparse_attention_varlen(
         inp["q"], inp["k"], inp["v"], inp["q2k"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
@@ -158,3 +158,27 @@ def test_paged_varlen_empty_batch_and_refusals():
     pin = to_paged(inp, seed=2)
     with pytest.raises(msa.MsaNotSupportedError):  # no union decode for packed queries
         run_paged_varlen(pin, True, 3)
+
+
+@pytest.mark.parametrize("splits", [0, 3, 16])
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_paged_varlen_q_centric_splits(case, splits):
+    """The q-centric path with its slots split (automatic, 3 and 16) and merged by
+    log-sum-exp, with the temperature LSE: against the varlen oracle."""
+    import block_sparse_attention_top_amd as msa
+    q_lens, k_lens, Hkv, qpk, topk, causal = CASES[case]
+    inp = wl.make_varlen_inputs(80 + case, q_lens, k_lens, Hkv, qpk, topk, wl.MODE_CAUSAL)
+    pin = to_paged(inp, seed=10 + case)
+    ns = msa.msa_paged_sparse_fwd_varlen_splits(len(q_lens), sum(q_lens), Hkv, topk,
+                                                pin["page_table"].shape[1], splits, Q)
+    say(f"[paged-varlen] case {case} q-centric splits={splits} ({ns} used)")
+    if case == 1 and splits == 0:
+        assert ns == 8  # 16 (query, KV head) rows: the automatic rule splits
+    o, lse, lt = run_paged_varlen(pin, True, Q, num_splits=splits, return_temperature_lse=True,
+                                  lse_temperature_scale=2.0)
+    o_ref, lse_ref, lt_ref = oracle.sparse_attention_varlen(
+        inp["q"], inp["k"], inp["v"], inp["q2k"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+        causal=True, temperature=2.0)
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+            f"paged-varlen splits case {case}")
+    check_lse_t(lt.cpu().numpy(), lt_ref, f"paged-varlen splits {splits} T2")
