@@ -354,7 +354,7 @@ class Case:
             cus = torch.cuda.get_device_properties(0).multi_processor_count
             waves = 2 if items < 8 * cus else 1
             paged = "true" if w.paged else "false"
-            return f"qcentric_kernel<{paged}, {t}, {f}, {waves}>"
+            return f"qcentric_kernel<{paged}, {t}, {f}, {waves}, false>"
         if self.path_name in ("kv-centric", "paged-kv-centric"):
             paged = "true" if w.paged else "false"
             return f"kvcentric_kernel<{w.qpk}, {t}, {f}, {paged}>"
