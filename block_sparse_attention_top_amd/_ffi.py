@@ -504,6 +504,10 @@ def msa_paged_sparse_fwd_varlen(q, k_pool, v_pool, page_table, seqused_k, cu_seq
     num_pages, Hkv, page_size, _ = k_pool.shape
     B, max_pages = page_table.shape
     topk = q2k.shape[-1]
+    if cu_seqlens_q.numel() != B + 1 or seqused_k.numel() != B:
+        raise ValueError("cu_seqlens_q needs B + 1 entries and seqused_k B (B = page_table rows)")
+    if tuple(q2k.shape) != (Hkv, total_q, topk):
+        raise ValueError("q2k must be [Hkv, total_q, topk]")
     if o is None:
         o = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
     if lse is None:
