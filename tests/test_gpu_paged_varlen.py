@@ -182,3 +182,50 @@ def test_paged_varlen_q_centric_splits(case, splits):
     compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
             f"paged-varlen splits case {case}")
     check_lse_t(lt.cpu().numpy(), lt_ref, f"paged-varlen splits {splits} T2")
+
+
+def draw_random_cases(n=16, seed=2031):
+    """Seeded ragged batches for the paged varlen entry point: lengths (empty sequences
+    and sequences without keys included), heads, topk, causality, path, splits, the fp8
+    cache and the temperature LSE."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 6))
+        c = dict(q_lens=[0 if rng.random() < 0.15 else int(rng.integers(1, 300)) for _ in range(B)],
+                 k_lens=[0 if rng.random() < 0.1 else int(rng.integers(1, 2500)) for _ in range(B)],
+                 Hkv=int(rng.choice([1, 2, 4])), qpk=int(rng.choice([1, 2, 4, 8, 16])),
+                 topk=int(rng.choice([1, 4, 8, 16, 32])), causal=bool(rng.random() < 0.7),
+                 path=int(rng.choice([AUTO, Q, KV])), splits=int(rng.choice([0, 1, 4])),
+                 fp8=bool(rng.random() < 0.3), temp=[None, 0.5, 2.0][int(rng.integers(3))],
+                 seed=int(rng.integers(1, 1 << 30)))
+        c["q_lens"][0] = max(c["q_lens"][0], 1)
+        out.append(c)
+    return out
+
+
+RANDOM = draw_random_cases()
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM)))
+def test_paged_varlen_random(i):
+    c = RANDOM[i]
+    say(f"[paged-varlen] random {i}: { {k: v for k, v in c.items() if k != 'seed'} }")
+    short = any(0 < k < 128 * c["topk"] for k in c["k_lens"])
+    mode = wl.MODE_CAUSAL if c["causal"] or short else wl.MODE_PERM
+    inp = wl.make_varlen_inputs(c["seed"], c["q_lens"], c["k_lens"], c["Hkv"], c["qpk"],
+                                c["topk"], mode)
+    if c["fp8"]:
+        inp = wl.with_fp8_kv(inp)
+    pin = to_paged(inp, seed=c["seed"] % 1000, spare_pages=i % 3)
+    tk = {} if c["temp"] is None else dict(return_temperature_lse=True,
+                                           lse_temperature_scale=c["temp"])
+    out = run_paged_varlen(pin, c["causal"], c["path"], fp8=c["fp8"], num_splits=c["splits"],
+                           **tk)
+    ref = oracle.sparse_attention_varlen(inp["q"], inp["k"], inp["v"], inp["q2k"],
+                                         inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                                         causal=c["causal"], temperature=c["temp"])
+    compare(bf16_dev_to_f64(out[0]), out[1].cpu().numpy().astype(np.float64), ref[0], ref[1],
+            f"paged-varlen random {i}")
+    if c["temp"] is not None:
+        check_lse_t(out[2].cpu().numpy(), ref[2], f"paged-varlen random {i} T")
