@@ -161,3 +161,43 @@ def test_paged_kv_centric_in_graph():
         t2["q"], t2["k_pool"], t2["v_pool"], t2["page_table"], t2["seqused_k"], t2["q2k"],
         causal=True, path=KV)
     replay_and_check(g, [o, lse], [o_ref, l_ref], other, "paged kv-centric")
+
+
+def test_paged_varlen_kv_centric_in_graph():
+    """A ragged batch through the paged varlen entry point on the kv-centric path (its
+    per-sequence tables, CSR, items, partials and combine), captured and replayed."""
+    import block_sparse_attention_top_amd as msa
+    inp = wl.make_varlen_inputs(69, [300, 0, 700], [1000, 500, 2000], 2, 8, 8, wl.MODE_CAUSAL)
+    B, mp = 3, 16
+    k_lens = np.diff(inp["cu_seqlens_k"])
+    pool_k = np.zeros((B * mp, 2, 128, 128), dtype=np.uint16)
+    pool_v = np.zeros_like(pool_k)
+    pt = np.arange(B * mp, dtype=np.int32).reshape(B, mp)
+    for b in range(B):
+        for s in range((int(k_lens[b]) + 127) // 128):
+            lo = int(inp["cu_seqlens_k"][b]) + 128 * s
+            hi = min(int(inp["cu_seqlens_k"][b + 1]), lo + 128)
+            pool_k[pt[b, s], :, :hi - lo] = inp["k"][lo:hi].transpose(1, 0, 2)
+            pool_v[pt[b, s], :, :hi - lo] = inp["v"][lo:hi].transpose(1, 0, 2)
+    t = {n: to_dev(x) for n, x in dict(q=inp["q"], kp=pool_k, vp=pool_v, pt=pt,
+                                        su=k_lens.astype(np.int32), cu=inp["cu_seqlens_q"],
+                                        q2k=inp["q2k"]).items()}
+    total_q = int(inp["cu_seqlens_q"][-1])
+    nbytes = msa.msa_paged_sparse_fwd_varlen_workspace_size(B, total_q, 16, 2, 128, 8, 128, mp,
+                                                            0, KV)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((total_q, 16, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((total_q, 16), dtype=torch.float32, device="cuda")
+    fn = lambda: msa.msa_paged_sparse_fwd_varlen(t["q"], t["kp"], t["vp"], t["pt"], t["su"],
+                                                 t["cu"], t["q2k"], causal=True, path=KV, o=o,
+                                                 lse=lse, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    say("[graph] paged varlen kv-centric: capturing")
+    g = capture(fn)
+    w2, t2 = paged(70, 1, 256, 2048, [0])
+    other = lambda: msa.msa_paged_sparse_fwd(
+        t2["q"], t2["k_pool"], t2["v_pool"], t2["page_table"], t2["seqused_k"], t2["q2k"],
+        causal=True, path=KV)
+    replay_and_check(g, [o, lse], [o_ref, l_ref], other, "paged varlen kv-centric")
