@@ -354,7 +354,10 @@ class Case:
             cus = torch.cuda.get_device_properties(0).multi_processor_count
             waves = 2 if items < 8 * cus else 1
             paged = "true" if w.paged else "false"
-            return f"qcentric_kernel<{paged}, {t}, {f}, {waves}, false>"
+            # paged blocks read about once (fewer than 2 (query, slot) entries per block)
+            # take the non-temporal instance
+            nt = w.paged and w.Sq * min(w.topk, w.max_pages) < 2 * w.max_pages
+            return f"qcentric_kernel<{paged}, {t}, {f}, {waves}, false, {'true' if nt else 'false'}>"
         if self.path_name in ("kv-centric", "paged-kv-centric"):
             paged = "true" if w.paged else "false"
             return f"kvcentric_kernel<{w.qpk}, {t}, {f}, {paged}>"

@@ -973,6 +973,10 @@ int msa_paged_sparse_fwd(const void* q, const void* k_pool, const void* v_pool,
   p.seqused = seqused_k;
   p.B = B; p.Sq = Sq; p.Skv = max_pages * kBlk; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
   p.nblk = max_pages; p.max_pages = max_pages; p.num_pages = num_pages;
+  // fewer than two (query, slot) entries per block on average: each block is read about
+  // once per (b, hkv), so its loads bypass the cache's retention
+  p.kv_stream = static_cast<long long>(Sq) * std::min(topk, max_pages) <
+                kKvMinEntriesPerRow * max_pages;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
   p.splits = splits;
@@ -1112,6 +1116,8 @@ int msa_paged_sparse_fwd_varlen(const void* q, const void* k_pool, const void* v
     p.total_q = total_q;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
     p.nblk = max_pages; p.max_pages = max_pages; p.num_pages = num_pages;
+    p.kv_stream = static_cast<long long>(total_q) * std::min(topk, max_pages) <
+                  kKvMinEntriesPerRow * B * static_cast<long long>(max_pages);
     p.causal = causal ? 1 : 0;
     p.scale_log2 = scale * kLog2e;
     p.splits = paged_varlen_splits(total_q, Hkv, topk, num_splits);

@@ -224,8 +224,8 @@ __global__ __launch_bounds__(256, QPW <= 2 ? 2 : 1) void paged_decode_kernel(QcP
       const long long rs = r < last ? r : last;
       const uint16_t* ksrc = static_cast<const uint16_t*>(p.k) + (base + rs) * kD + 8 * (lpos ^ swz_k(r));
       const uint16_t* vsrc = static_cast<const uint16_t*>(p.v) + (base + rs) * kD + 8 * (lpos ^ swz_v(r));
-      lds_load16(ksrc, lds_addr(kd) + 4 * (2 * wave_u + j) * kRow);
-      lds_load16(vsrc, lds_addr(vd) + 4 * (2 * wave_u + j) * kRow);
+      lds_load16_nt(ksrc, lds_addr(kd) + 4 * (2 * wave_u + j) * kRow);
+      lds_load16_nt(vsrc, lds_addr(vd) + 4 * (2 * wave_u + j) * kRow);
     }
   };
 

@@ -188,10 +188,10 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
       o1 = min(r1, tail - 1) * kRow + 16 * (lpos ^ swz(r1));
     }
     const uint32_t kd = lds_addr(buf), vd = kd + kTile;
-    lds_load16_s(kb, o0, kd + 8 * wave_u * kRow);
-    lds_load16_s(vb, o0, vd + 8 * wave_u * kRow);
-    lds_load16_s(kb, o1, kd + (8 * wave_u + 4) * kRow);
-    lds_load16_s(vb, o1, vd + (8 * wave_u + 4) * kRow);
+    lds_load16_s_nt(kb, o0, kd + 8 * wave_u * kRow);
+    lds_load16_s_nt(vb, o0, vd + 8 * wave_u * kRow);
+    lds_load16_s_nt(kb, o1, kd + (8 * wave_u + 4) * kRow);
+    lds_load16_s_nt(vb, o1, vd + (8 * wave_u + 4) * kRow);
   };
 
   // LDS lane offsets (bytes): K fragment = row n32, logical chunk 2 kq + h32 at
@@ -284,10 +284,10 @@ __global__ __launch_bounds__(256, 2) void dense_decode_kernel(QcParams p) {
       o1 = min(rw8 + 8, tail - 1) * kD + 16 * (pw8 ^ swz8(rw8 + 8));
     }
     const uint32_t kd = lds_addr(buf) + 16 * wave_u * kD, vd = kd + kTile8;
-    lds_load16_s(kb, o0, kd);
-    lds_load16_s(vb, o0, vd);
-    lds_load16_s(kb, o1, kd + 8 * kD);
-    lds_load16_s(vb, o1, vd + 8 * kD);
+    lds_load16_s_nt(kb, o0, kd);
+    lds_load16_s_nt(vb, o0, vd);
+    lds_load16_s_nt(kb, o1, kd + 8 * kD);
+    lds_load16_s_nt(vb, o1, vd + 8 * kD);
   };
   // fp8 fragment offsets. K (A of S^T = K Q^T, 32x32x64): lane (n32, h32) reads row
   // 32 tt + n32, dims 64 kq + 32 h32 .. +31 = logical chunks 4 kq + 2 h32 (+1). V^T (A of

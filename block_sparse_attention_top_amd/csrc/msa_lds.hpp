@@ -36,4 +36,15 @@ __device__ __forceinline__ void lds_load16_s(const void* sbase, uint32_t voff, u
                : "memory");
 }
 
+// The same two copies with the non-temporal hint, for K/V streamed once (the decode
+// kernels: 5% faster on the union decode, 2% on the dense decode, same bits).
+__device__ __forceinline__ void lds_load16_nt(const void* src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_load16_s_nt(const void* sbase, uint32_t voff,
+                                                uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+               : "memory");
+}
+
 }  // namespace msa
