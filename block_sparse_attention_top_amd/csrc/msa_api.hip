@@ -191,6 +191,14 @@ struct PagedPlan {
   int splits;
 };
 
+// q-centric split count for `rows` (query, KV head) rows: num_splits (0 = about 1024
+// single-wave workgroups, at most 8), clamped to 1..topk
+int qcentric_splits(long long rows, int topk, int num_splits) {
+  long long s = num_splits;
+  if (s <= 0) s = std::min<long long>((1024 + rows - 1) / rows, 8);
+  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, topk)));
+}
+
 PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int max_pages, int num_splits, int path) {
   PagedPlan pl;
   if (path == MSA_PATH_AUTO)
@@ -211,13 +219,7 @@ PagedPlan paged_plan(int B, int Sq, int Hkv, int topk, int max_pages, int num_sp
     }
     pl.splits = static_cast<int>(std::max<long long>(1, std::min(s, cap)));
   } else {
-    long long s = num_splits;
-    if (s <= 0) {
-      const long long rows = static_cast<long long>(B) * Hkv * Sq;
-      s = (1024 + rows - 1) / rows;
-      s = std::min<long long>(s, 8);
-    }
-    pl.splits = static_cast<int>(std::max<long long>(1, std::min<long long>(s, topk)));
+    pl.splits = qcentric_splits(static_cast<long long>(B) * Hkv * Sq, topk, num_splits);
   }
   return pl;
 }
@@ -1025,12 +1027,7 @@ int msa_paged_sparse_fwd_varlen_path(int B, int total_q, int Hkv, int topk, int 
 
 // q-centric splits of a paged varlen batch: the uniform paged rule with total_q query rows
 int paged_varlen_splits(int total_q, int Hkv, int topk, int num_splits) {
-  long long s = num_splits;
-  if (s <= 0) {
-    const long long rows = static_cast<long long>(total_q) * Hkv;
-    s = std::min<long long>((1024 + rows - 1) / rows, 8);
-  }
-  return static_cast<int>(std::max<long long>(1, std::min<long long>(s, topk)));
+  return qcentric_splits(static_cast<long long>(total_q) * Hkv, topk, num_splits);
 }
 
 int msa_paged_sparse_fwd_varlen_splits(int B, int total_q, int Hkv, int topk, int max_pages,
