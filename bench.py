@@ -356,7 +356,8 @@ class Case:
             paged = "true" if w.paged else "false"
             # paged blocks read about once (fewer than 2 (query, slot) entries per block)
             # take the non-temporal instance
-            nt = w.paged and w.Sq * min(w.topk, w.max_pages) < 2 * w.max_pages
+            nblk = w.max_pages if w.paged else w.Skv // w.blk
+            nt = not self.varlen and w.Sq * min(w.topk, nblk) < 2 * nblk
             return f"qcentric_kernel<{paged}, {t}, {f}, {waves}, false, {'true' if nt else 'false'}>"
         if self.path_name in ("kv-centric", "paged-kv-centric"):
             paged = "true" if w.paged else "false"

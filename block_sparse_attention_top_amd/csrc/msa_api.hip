@@ -438,6 +438,7 @@ int msa_sparse_fwd(const void* q, const void* k, const void* v, const int32_t* q
     p.q2k = q2k;
     p.B = B; p.Sq = Sq; p.Skv = Skv; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
     p.nblk = nblk; p.causal = causal ? 1 : 0;
+    p.kv_stream = static_cast<long long>(Sq) * std::min(topk, nblk) < kKvMinEntriesPerRow * nblk;
     p.scale_log2 = scale * kLog2e;
     p.splits = 1;
     p.o = static_cast<uint16_t*>(o);
@@ -608,6 +609,9 @@ int msa_sparse_fwd_varlen(const void* q, const void* k, const void* v, const int
     p.total_k = total_k;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.qpk = qpk; p.topk = topk;
     p.causal = causal ? 1 : 0;
+    p.kv_stream = static_cast<long long>(total_q) *
+                      std::min<long long>(topk, (total_k + kBlk - 1) / kBlk) <
+                  kKvMinEntriesPerRow * varlen_rows_bound(B, total_k);
     p.scale_log2 = scale * kLog2e;
     p.splits = 1;
     p.o = static_cast<uint16_t*>(o);

@@ -169,7 +169,7 @@ struct QcParams {
   int B, Sq, Skv, Hq, Hkv, qpk, topk;
   int nblk;                  // valid block ids are [0, nblk)
   int max_pages, num_pages;
-  int kv_stream;             // paged: blocks are read about once (load them non-temporally)
+  int kv_stream;             // blocks are read about once (load them non-temporally)
   int causal;
   float scale_log2;          // softmax_scale * log2(e)
   int splits;                // 1 = write final O/LSE

@@ -55,8 +55,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // kWaves waves per index row (or split), each taking every kWaves-th slot. PVAR: a
-// paged pool with a variable-length query batch (cu_q). NT: paged blocks read about
-// once (decode), loaded non-temporally.
+// paged pool with a variable-length query batch (cu_q). NT: blocks read about once
+// (decode-like batches), loaded non-temporally.
 template <bool PAGED, bool TEMP, bool FP8, int kWaves, bool PVAR = false, bool NT = false>
 __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_all[kWaves][kSub * kKStride];
@@ -181,10 +181,10 @@ __global__ __launch_bounds__(64 * kWaves) void qcentric_kernel(QcParams p) {
       else  // rows past the sequence's last key re-read that key (stored as zeros)
         off = ((kbeg + min(static_cast<long long>(s) * kBlk + kSub * u + row, kvlen - 1)) * p.Hkv +
                hkv) * kD + c * kEpc;
-      if (PAGED && NT) {
+      if (NT) {
         // blocks read about once (decode): non-temporal loads measured 6% faster on 32 x 8
-        // queries over 65 536 keys (0.171 -> 0.161 ms, same bits); where blocks serve many
-        // queries (prefill) they cost the reuse from L2 (8192 queries: 1.71 -> 2.44 ms)
+        // paged queries over 65 536 keys (0.171 -> 0.161 ms, same bits); where blocks serve
+        // many queries (prefill) they cost the reuse from L2 (8192 queries: 1.71 -> 2.44 ms)
         kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off * kEsz));
         vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off * kEsz));
       } else {
@@ -395,6 +395,7 @@ void qc_launch(int variant, const QcParams& p, dim3 grid, hipStream_t stream) {
   switch (variant >> 2) {  // paged (1), packed queries (2), streamed blocks (4)
     case 0: qc_launch_tf<W, false, false, false>(tf, p, grid, stream); break;
     case 1: qc_launch_tf<W, true, false, false>(tf, p, grid, stream); break;
+    case 4: qc_launch_tf<W, false, false, true>(tf, p, grid, stream); break;
     case 3: qc_launch_tf<W, true, true, false>(tf, p, grid, stream); break;
     case 5: qc_launch_tf<W, true, false, true>(tf, p, grid, stream); break;
     default: qc_launch_tf<W, true, true, true>(tf, p, grid, stream); break;
@@ -415,7 +416,7 @@ hipError_t launch_qcentric(const QcParams& p, bool paged, hipStream_t stream) {
   // (decode: the 32 x 8-query paged workload has 1024 (row, KV head) items);
   // otherwise one (large prefill, where the second wave only adds Q loads and a merge).
   const bool two = items < 8LL * device_cu_count();
-  const int variant = (paged ? 4 : 0) + (paged && p.cu_q ? 8 : 0) + (paged && p.kv_stream ? 16 : 0) +
+  const int variant = (paged ? 4 : 0) + (paged && p.cu_q ? 8 : 0) + (p.kv_stream ? 16 : 0) +
                       (p.lse_t ? 2 : 0) + (p.kv_fp8 ? 1 : 0);
   if (two)
     qc_launch<2>(variant, p, grid, stream);
